@@ -1,0 +1,14 @@
+"""fp64 CPU oracle for one tensor-parallel rank of the Megatron paired MLP.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``, never by the GPU library or its
+binding.  See ``oracle/mlp.py`` for what it computes and which passages it
+follows.
+"""
+from .mlp import (ACTS, act_backward, act_forward, bf16_bits_to_f64,
+                  column_block, column_sum, reduce_partials, shard_backward,
+                  shard_forward, shard_weights, tp_backward, tp_forward)
+
+__all__ = ["ACTS", "act_backward", "act_forward", "bf16_bits_to_f64",
+           "column_block", "column_sum", "reduce_partials", "shard_backward",
+           "shard_forward", "shard_weights", "tp_backward", "tp_forward"]

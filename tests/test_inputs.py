@@ -1,0 +1,45 @@
+"""The seeded input generator: deterministic, bf16 round-to-nearest-even
+(checked against torch's own float32 -> bfloat16 conversion), shards that
+concatenate to the full matrices."""
+import numpy as np
+import torch
+
+from megatron_tensor_transformer_rank_amd import inputs
+
+
+def test_rne_matches_torch():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32) * 10,
+        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -1.0 - 2.0 ** -8, 0.0, -0.0,
+                  np.inf, -np.inf, 3.0e38, 1e-40, -1e-42], dtype=np.float32),
+        # exact ties at every mantissa parity
+        (np.arange(1, 2000, dtype=np.uint32) << 15 | 0x3F800000).view(np.float32)])
+    ours = inputs.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_nan_is_quiet_nan():
+    assert inputs.f32_to_bf16_bits(np.array([np.nan], np.float32))[0] == 0x7FC0
+
+
+def test_deterministic_and_distinct_streams():
+    a = inputs.gen_x(9, 4, 8)
+    assert np.array_equal(a, inputs.gen_x(9, 4, 8))
+    assert not np.array_equal(a, inputs.gen_dy(9, 4, 8))
+    assert not np.array_equal(inputs.gen_w_up_shard(9, 8, 16, 0), inputs.gen_w_up_shard(9, 8, 16, 1))
+
+
+def test_full_weights_are_rank_blocks():
+    W1, W2, Wg = inputs.gen_full_weights(3, 16, 64, 4, swiglu=True)
+    assert W1.shape == (16, 64) and W2.shape == (64, 16) and Wg.shape == (16, 64)
+    assert np.array_equal(W1[:, 16:32], inputs.gen_w_up_shard(3, 16, 16, 1))
+    assert np.array_equal(W2[48:64, :], inputs.gen_w_down_shard(3, 16, 16, 3))
+    assert np.array_equal(Wg[:, 0:16], inputs.gen_w_gate_shard(3, 16, 16, 0))
+
+
+def test_distribution_scale():
+    w = inputs.gen_w_up_shard(4, 256, 512, 0).view(np.uint16)
+    v = (w.astype(np.uint32) << 16).view(np.float32)
+    assert abs(v.std() - 0.02) < 0.001
