@@ -1,0 +1,238 @@
+/*
+ * tp_mlp.h -- one tensor-parallel rank of the Megatron paired MLP block on
+ * MI355X (gfx950).  C ABI of libtpmlp.so.
+ *
+ * The method (column-parallel up-projection, elementwise activation on the
+ * local shard, row-parallel down-projection to a full-shape partial sum, one
+ * reduction of the partials, output bias added once after it, and the matching
+ * sharded backward) is described by:
+ *   - "02 -- Tensor Parallelism" (project-fortress roadmap), sections
+ *     "Column-parallel", "Row-parallel" and "The MLP pairing";
+ *   - "Tensor Parallelism's Communication Boundary" (aryanputta.com), sections
+ *     "Follow the coordinates" and the bias caveat under "Count the object,
+ *     then the collective";
+ *   - "Parallelism Strategies #1 - Tensor Parallelism" (deeplearningresearch
+ *     substack), the sharded backward derivation;
+ *   - "Tensor and sequence parallelism" (AI infra handbooks), the f / g
+ *     operator table;
+ *   - "Megatron-LM: Tensor Parallelism" (vanos001 placement prep), section
+ *     "MLP Block".
+ *
+ * Conventions for every entry point
+ *   Layout     All matrices are dense, row-major, math layout (input dim
+ *              first): X [N, h], W1_i and Wg_i [h, F_i], W2_i [F_i, h], with
+ *              N = n_tokens, h = hidden, F_i = ffn / t.  Row strides equal the
+ *              row lengths (no padding).
+ *   Types      Activations and weights are bfloat16 (passed as void*);
+ *              weight gradients and db2 are float32.  Every product
+ *              accumulates in float32; bf16 outputs are rounded to nearest
+ *              even once.
+ *   Pointers   Every pointer except the host array of
+ *              tp_mlp_reduce_partials_local and the shape struct is a DEVICE
+ *              pointer, 16-byte aligned.  h and F_i must be multiples of 8.
+ *              Buffers must not overlap unless stated.
+ *   Ownership  The caller allocates and owns every buffer.  The library never
+ *              allocates, frees or keeps a pointer after returning.
+ *   Streams    All work is enqueued on `stream` (0 = the null stream) and is
+ *              never synchronised; inputs must stay valid until the stream
+ *              has passed the work.  Asynchronous faults surface at the
+ *              caller's next synchronisation.
+ *   Outputs    Overwritten, never accumulated into.
+ *   Errors     Arguments are validated on the host before any launch; an
+ *              invalid call returns TP_MLP_ERR_INVALID_ARG and enqueues
+ *              nothing.  A failed launch returns TP_MLP_ERR_HIP.  Nothing is
+ *              printed and no C++ exception crosses the ABI.
+ *   Threads    Entry points are reentrant; the only process-wide state is a
+ *              once-initialised per-device property cache.
+ */
+#ifndef TP_MLP_H
+#define TP_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TP_MLP_OK = 0,
+  TP_MLP_ERR_INVALID_ARG = 1, /* bad pointer, shape, alignment, rank or act */
+  TP_MLP_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. t > 64)   */
+  TP_MLP_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required   */
+  TP_MLP_ERR_HIP = 4          /* a HIP launch or query failed              */
+} tp_mlp_status;
+
+/* Elementwise activation on the rank's hidden columns.
+ * RELU:   A = max(U, 0); derivative [U > 0] (0 at U == 0).
+ * GELU:   exact erf form, A = U * Phi(U); derivative Phi(U) + U * phi(U).
+ * SWIGLU: A = SiLU(G) * U with G = X @ Wg_i (gate) and U = X @ W1_i (up),
+ *         SiLU(z) = z * sigmoid(z); gate and up hold the same columns. */
+typedef enum {
+  TP_MLP_ACT_RELU = 0,
+  TP_MLP_ACT_GELU = 1,
+  TP_MLP_ACT_SWIGLU = 2
+} tp_mlp_act;
+
+/* The problem as the pages state it: replicated input X [N, h], the full
+ * intermediate width F split over t ranks, this shard's rank (it owns the
+ * contiguous hidden columns [rank*F/t, (rank+1)*F/t), rank 0 lowest), and the
+ * activation.  Requires N >= 1, h >= 8, F % t == 0, 1 <= t <= 64,
+ * 0 <= rank < t, h % 8 == 0 and (F / t) % 8 == 0. */
+typedef struct {
+  int64_t n_tokens; /* N = b * s                                   */
+  int64_t hidden;   /* h                                           */
+  int64_t ffn;      /* F, the full intermediate width (all ranks)  */
+  int32_t t;        /* tensor-parallel degree                      */
+  int32_t rank;     /* this shard's rank                           */
+  int32_t act;      /* tp_mlp_act                                  */
+} tp_mlp_shape;
+
+/* ------------------------------------------------------------------------
+ * Composite entry points (one call per direction per rank)
+ * ------------------------------------------------------------------------ */
+
+/* Forward of one rank's shard ("02 -- Tensor Parallelism", "The MLP
+ * pairing"): U_i = X @ W1_i (SwiGLU: also G_i = X @ Wg_i), A_i = act(...),
+ * Y_i = A_i @ W2_i, the full-shape PARTIAL sum with no bias.  The ranks'
+ * partials are summed (and the bias added) by tp_mlp_reduce_partials_local.
+ *   X    bf16 [N, h]        replicated input
+ *   W1_i bf16 [h, F_i]      column shard of W1 (= W_up for SwiGLU)
+ *   Wg_i bf16 [h, F_i]      column shard of W_gate; non-NULL iff SWIGLU
+ *   W2_i bf16 [F_i, h]      row shard of W2 (= W_down)
+ *   Y_i  bf16 [N, h]        out: partial sum
+ *   A_i  bf16 [N, F_i]      out: activation (input of the backward)
+ *   U_i  bf16 [N, F_i]      out or NULL: pre-activation (SwiGLU: up
+ *                           projection) stash for the backward
+ *   G_i  bf16 [N, F_i]      out or NULL: SwiGLU gate stash; must be NULL
+ *                           unless SWIGLU, and given iff U_i is given
+ * N == 1 runs the decode path: a split-K GEMV that reads each weight once
+ * (HBM bound), which needs workspace; other N run the MFMA GEMMs, which need
+ * none.  workspace: device memory of at least tp_mlp_workspace_bytes(s, 0)
+ * bytes, zero-filled before its first use (every call leaves it zero-filled
+ * again); NULL is allowed when that size is 0.  Calls that share one
+ * workspace must be ordered on one stream. */
+tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X,
+                               const void* W1_i, const void* Wg_i,
+                               const void* W2_i, void* Y_i, void* A_i,
+                               void* U_i, void* G_i, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Backward of one rank's shard ("Parallelism Strategies #1 - Tensor
+ * Parallelism", sharded backward, in math layout).  dY is the same on every
+ * rank (g's backward is the identity).
+ *   dA_i = dY @ W2_i^T, then through the activation:
+ *     RELU/GELU: dU_i = dA_i * act'(U_i)               -> dU  bf16 [N, F_i]
+ *     SWIGLU:    dG = dA*U*s*(1+G*(1-s)), dP = dA*SiLU(G), s = sigmoid(G)
+ *                                                     -> dU  bf16 [N, 2*F_i]
+ *                laid out as [dG | dP] (columns [0,F_i) then [F_i,2F_i)).
+ *   dW2_i = A_i^T @ dY                                 -> fp32 [F_i, h]
+ *   dW1_i = X^T @ dU_i (SWIGLU: X^T @ dP = dW_up)     -> fp32 [h, F_i]
+ *   dWg_i = X^T @ dG (SWIGLU only; else must be NULL) -> fp32 [h, F_i]
+ *   dX_partial = dU_i @ W1_i^T (SWIGLU: dG @ Wg_i^T + dP @ W1_i^T, one
+ *     product over K = 2*F_i)                          -> bf16 [N, h]
+ *     The ranks' dX_partial must be summed (f's backward); use
+ *     tp_mlp_reduce_partials_local with bias NULL.
+ *   db2 = sum over rows of dY -> fp32 [h], or NULL to skip.  The output bias
+ *     is added once, so pass db2 on one rank only.
+ * Inputs A_i, U_i (and G_i for SwiGLU) are the forward's outputs; U_i is
+ * required.  The products need no workspace; db2 != NULL needs
+ * tp_mlp_workspace_bytes(s, 1) bytes of device scratch (no initial contents
+ * required).  With db2 == NULL, workspace may be NULL. */
+tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X,
+                               const void* W1_i, const void* Wg_i,
+                               const void* W2_i, const void* dY,
+                               const void* A_i, const void* U_i,
+                               const void* G_i, void* dU_i, float* dW1_i,
+                               float* dWg_i, float* dW2_i, void* dX_partial,
+                               float* db2, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Local stand-in for the all-reduce of g's forward and f's backward ("Tensor
+ * and sequence parallelism", table of f and g; "Tensor Parallelism's
+ * Communication Boundary" on adding the bias once):
+ *   out[r][c] = bf16( (sum_{k=0}^{t-1} float(partials[k][r][c])) + bias[c] )
+ * summed in float32 in rank order, the bias (if non-NULL) added once after
+ * the sum, one final rounding.
+ *   partials  HOST array of t DEVICE pointers, each bf16 [rows, cols]
+ *   bias      bf16 [cols] or NULL
+ *   out       bf16 [rows, cols]; may coincide exactly with any partials[k]
+ *             (each output chunk is written after its inputs are read), no
+ *             other overlap.
+ * Requires 1 <= t <= 64, rows >= 1, cols % 8 == 0, 16-byte alignment. */
+tp_mlp_status tp_mlp_reduce_partials_local(int32_t t,
+                                           const void* const* partials,
+                                           int64_t rows, int64_t cols,
+                                           const void* bias, void* out,
+                                           hipStream_t stream);
+
+/* Workspace bytes needed by tp_mlp_fwd_shard (backward = 0) or
+ * tp_mlp_bwd_shard (backward = 1) for shape s; 0 means none.  Returns 0 for
+ * an invalid shape. */
+size_t tp_mlp_workspace_bytes(const tp_mlp_shape* s, int backward);
+
+/* Static, NUL-terminated description of a status code. */
+const char* tp_mlp_status_string(tp_mlp_status st);
+
+/* ------------------------------------------------------------------------
+ * Step-level entry points: the column-parallel and row-parallel pieces the
+ * composite calls are made of, one GPU kernel each, on the same shapes and
+ * buffers as above.  They exist for callers that schedule the pieces
+ * themselves (e.g. to put a collective between them) and for per-kernel
+ * timing.
+ * ------------------------------------------------------------------------ */
+
+/* Column-parallel up-projection with the activation fused in its epilogue:
+ * A_i = act(X @ W1_i) (SwiGLU: SiLU(X @ Wg_i) * (X @ W1_i)), stashing U_i /
+ * G_i when non-NULL.  MFMA path for every N (no decode dispatch). */
+tp_mlp_status tp_mlp_up_act_shard(const tp_mlp_shape* s, const void* X,
+                                  const void* W1_i, const void* Wg_i,
+                                  void* A_i, void* U_i, void* G_i,
+                                  hipStream_t stream);
+
+/* Row-parallel down-projection: Y_i = A_i @ W2_i (partial sum, no bias). */
+tp_mlp_status tp_mlp_down_shard(const tp_mlp_shape* s, const void* A_i,
+                                const void* W2_i, void* Y_i,
+                                hipStream_t stream);
+
+/* dgrad through W2 fused with the activation derivative:
+ * dU_i = (dY @ W2_i^T) * act'(U_i) (SwiGLU: [dG | dP] from G_i, U_i). */
+tp_mlp_status tp_mlp_down_dgrad_act_shard(const tp_mlp_shape* s,
+                                          const void* dY, const void* W2_i,
+                                          const void* U_i, const void* G_i,
+                                          void* dU_i, hipStream_t stream);
+
+/* wgrad of W2: dW2_i = A_i^T @ dY (fp32). */
+tp_mlp_status tp_mlp_down_wgrad_shard(const tp_mlp_shape* s, const void* A_i,
+                                      const void* dY, float* dW2_i,
+                                      hipStream_t stream);
+
+/* wgrad of W1 (and W_gate): dW1_i = X^T @ dU_i (SwiGLU: dWg_i = X^T @ dG,
+ * dW1_i = X^T @ dP) (fp32). */
+tp_mlp_status tp_mlp_up_wgrad_shard(const tp_mlp_shape* s, const void* X,
+                                    const void* dU_i, float* dW1_i,
+                                    float* dWg_i, hipStream_t stream);
+
+/* dgrad through W1: dX_partial = dU_i @ W1_i^T (SwiGLU: [dG | dP] @
+ * [Wg_i | W1_i]^T). */
+tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i,
+                                    const void* W1_i, const void* Wg_i,
+                                    void* dX_partial, hipStream_t stream);
+
+/* db2 = column sums of dY [rows, cols] (fp32 out [cols]): the gradient of the
+ * output bias that is added once after the reduction.  Deterministic
+ * (fixed-order float32 sums).  workspace: device scratch of at least
+ * tp_mlp_bias_grad_workspace_bytes(rows, cols) bytes, no initial contents
+ * required.  Requires rows >= 1, cols % 8 == 0. */
+tp_mlp_status tp_mlp_bias_grad(const void* dY, int64_t rows, int64_t cols,
+                               float* db2, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+size_t tp_mlp_bias_grad_workspace_bytes(int64_t rows, int64_t cols);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_MLP_H */

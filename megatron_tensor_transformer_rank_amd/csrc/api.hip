@@ -1,0 +1,394 @@
+// C ABI of libtpmlp.so: host-side validation, workspace layout and dispatch
+// of one tensor-parallel rank's MLP shard onto the gfx950 kernels.
+//
+// Every check runs before the first launch, so an invalid call enqueues
+// nothing.  No exception crosses the ABI; nothing is printed.
+#include <atomic>
+#include <new>
+
+#include "common.h"
+#include "gemm.h"
+#include "gemv.h"
+#include "reduce.h"
+#include "tp_mlp.h"
+
+using namespace tpmlp;
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+// CUs per device, queried once per device (0 = not yet known).
+std::atomic<int> g_num_cu[MAX_DEVICES];
+
+int num_cu_current() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 256;
+  int n = g_num_cu[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  g_num_cu[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Decode plans depend only on the shape (a fixed 256-CU target), so the
+// workspace size never depends on the device.
+constexpr int PLAN_CU = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool opt_aligned(const void* p) { return p == nullptr || aligned16(p); }
+bool req(const void* p) { return p != nullptr && aligned16(p); }
+
+struct Dims {
+  int64_t N, h, Fi;
+  int act, g;
+};
+
+bool check_shape(const tp_mlp_shape* s, Dims& d) {
+  if (s == nullptr) return false;
+  if (s->n_tokens < 1 || s->hidden < 8 || s->ffn < 1) return false;
+  if (s->t < 1 || s->t > MAX_T) return false;  // t > MAX_T: see shape_status
+  if (s->rank < 0 || s->rank >= s->t) return false;
+  if (s->act != TP_MLP_ACT_RELU && s->act != TP_MLP_ACT_GELU && s->act != TP_MLP_ACT_SWIGLU) return false;
+  if (s->ffn % s->t != 0) return false;
+  d.N = s->n_tokens;
+  d.h = s->hidden;
+  d.Fi = s->ffn / s->t;
+  d.act = s->act;
+  d.g = s->act == TP_MLP_ACT_SWIGLU ? 2 : 1;
+  if (d.h % 8 != 0 || d.Fi % 8 != 0 || d.Fi < 8) return false;
+  // GEMM extents are int32 inside the kernels
+  const int64_t lim = 0x7fffffffLL;
+  if (d.N > lim || d.h > lim || 2 * d.Fi > lim) return false;
+  return true;
+}
+
+// INVALID_ARG for a malformed shape, UNSUPPORTED for a well-formed one with
+// t above the supported maximum.
+tp_mlp_status shape_status(const tp_mlp_shape* s, Dims& d) {
+  if (check_shape(s, d)) return TP_MLP_OK;
+  if (s != nullptr && s->t > MAX_T && s->rank >= 0 && s->rank < s->t) return TP_MLP_ERR_UNSUPPORTED;
+  return TP_MLP_ERR_INVALID_ARG;
+}
+
+struct DecodeLayout {
+  GemvPlan up, down;
+  size_t off_part_up, off_part_down, off_cnt_up, off_cnt_down, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodeLayout decode_layout(const Dims& d) {
+  DecodeLayout L;
+  L.up = gemv_plan((int)d.h, (int)d.Fi, d.g, PLAN_CU);
+  L.down = gemv_plan((int)d.Fi, (int)d.h, 1, PLAN_CU);
+  size_t off = 0;
+  L.off_part_up = off;
+  off = round256(off + L.up.part_floats * sizeof(float));
+  L.off_part_down = off;
+  off = round256(off + L.down.part_floats * sizeof(float));
+  L.off_cnt_up = off;
+  off = round256(off + (size_t)L.up.strips * sizeof(unsigned));
+  L.off_cnt_down = off;
+  off = round256(off + (size_t)L.down.strips * sizeof(unsigned));
+  L.total = off;
+  return L;
+}
+
+tp_mlp_status hip_status(hipError_t e) { return e == hipSuccess ? TP_MLP_OK : TP_MLP_ERR_HIP; }
+
+const uint16_t* cu16(const void* p) { return static_cast<const uint16_t*>(p); }
+uint16_t* u16(void* p) { return static_cast<uint16_t*>(p); }
+
+// ----------------------------------------------------------------- launchers
+hipError_t run_up_act(const Dims& d, const void* X, const void* W1, const void* Wg, void* A, void* U, void* G,
+                      hipStream_t st) {
+  GemmArgs g = {};
+  g.M = (int)d.N;
+  g.N = (int)d.Fi;
+  g.K = (int)d.h;
+  g.a0 = g.a1 = cu16(X);
+  g.lda = d.h;
+  g.a_ksplit = g.K;
+  g.ldb = d.Fi;
+  g.c0 = A;
+  g.ldc = d.Fi;
+  if (d.act == ACT_SWIGLU) {
+    g.b0 = cu16(Wg);
+    g.b1 = cu16(W1);
+    g.e0 = G;
+    g.e1 = U;
+    return gemm_launch(GEMM_UP_SWIGLU, d.act, g, num_cu_current(), st);
+  }
+  g.b0 = g.b1 = cu16(W1);
+  g.e0 = U;
+  return gemm_launch(GEMM_UP_ACT, d.act, g, num_cu_current(), st);
+}
+
+hipError_t run_down(const Dims& d, const void* A, const void* W2, void* Y, hipStream_t st) {
+  GemmArgs g = {};
+  g.M = (int)d.N;
+  g.N = (int)d.h;
+  g.K = (int)d.Fi;
+  g.a0 = g.a1 = cu16(A);
+  g.lda = d.Fi;
+  g.a_ksplit = g.K;
+  g.b0 = g.b1 = cu16(W2);
+  g.ldb = d.h;
+  g.c0 = Y;
+  g.ldc = d.h;
+  return gemm_launch(GEMM_DOWN, d.act, g, num_cu_current(), st);
+}
+
+hipError_t run_dgrad_act(const Dims& d, const void* dY, const void* W2, const void* U, const void* G, void* dU,
+                         hipStream_t st) {
+  GemmArgs g = {};
+  g.M = (int)d.N;
+  g.N = (int)d.Fi;
+  g.K = (int)d.h;
+  g.a0 = g.a1 = cu16(dY);
+  g.lda = d.h;
+  g.a_ksplit = g.K;
+  g.b0 = g.b1 = cu16(W2);  // W2_i [F_i][h] is [n][k]
+  g.ldb = d.h;
+  g.b_ksplit = g.K;
+  g.c0 = dU;
+  if (d.act == ACT_SWIGLU) {
+    g.ldc = 2 * d.Fi;
+    g.e0 = const_cast<void*>(G);
+    g.e1 = const_cast<void*>(U);
+    g.lde = d.Fi;
+  } else {
+    g.ldc = d.Fi;
+    g.e0 = const_cast<void*>(U);
+    g.lde = d.Fi;
+  }
+  return gemm_launch(GEMM_DGRAD_ACT, d.act, g, num_cu_current(), st);
+}
+
+hipError_t run_wgrad_down(const Dims& d, const void* A, const void* dY, float* dW2, hipStream_t st) {
+  GemmArgs g = {};
+  g.M = (int)d.Fi;
+  g.N = (int)d.h;
+  g.K = (int)d.N;
+  g.a0 = g.a1 = cu16(A);  // A_i [N][F_i] is [k][m]
+  g.lda = d.Fi;
+  g.b0 = g.b1 = cu16(dY);  // dY [N][h] is [k][n]
+  g.ldb = d.h;
+  g.c0 = g.c1 = dW2;
+  g.ldc = d.h;
+  g.c_split = (int)d.h;
+  return gemm_launch(GEMM_WGRAD, d.act, g, num_cu_current(), st);
+}
+
+hipError_t run_wgrad_up(const Dims& d, const void* X, const void* dU, float* dW1, float* dWg, hipStream_t st) {
+  GemmArgs g = {};
+  g.M = (int)d.h;
+  g.N = (int)(d.g * d.Fi);
+  g.K = (int)d.N;
+  g.a0 = g.a1 = cu16(X);  // X [N][h] is [k][m]
+  g.lda = d.h;
+  g.b0 = g.b1 = cu16(dU);  // dU [N][g*F_i] is [k][n]
+  g.ldb = d.g * d.Fi;
+  g.c0 = d.act == ACT_SWIGLU ? dWg : dW1;  // columns [0, F_i): dG -> dWg
+  g.c1 = dW1;                              // columns [F_i, 2F_i): dP -> dW_up
+  g.ldc = d.Fi;
+  g.c_split = (int)d.Fi;
+  return gemm_launch(GEMM_WGRAD, d.act, g, num_cu_current(), st);
+}
+
+hipError_t run_dgrad_up(const Dims& d, const void* dU, const void* W1, const void* Wg, void* dX, hipStream_t st) {
+  GemmArgs g = {};
+  g.M = (int)d.N;
+  g.N = (int)d.h;
+  g.K = (int)(d.g * d.Fi);
+  g.a0 = g.a1 = cu16(dU);
+  g.lda = d.g * d.Fi;
+  g.a_ksplit = g.K;
+  // B = [Wg_i | W1_i] read as [n = h][k]: k < F_i from Wg_i (SwiGLU), the rest from W1_i
+  if (d.act == ACT_SWIGLU) {
+    g.b0 = cu16(Wg);
+    g.b1 = cu16(W1);
+    g.b_ksplit = (int)d.Fi;
+  } else {
+    g.b0 = g.b1 = cu16(W1);
+    g.b_ksplit = g.K;
+  }
+  g.ldb = d.Fi;
+  g.c0 = dX;
+  g.ldc = d.h;
+  return gemm_launch(GEMM_DGRAD, d.act, g, num_cu_current(), st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_mlp_status_string(tp_mlp_status st) {
+  switch (st) {
+    case TP_MLP_OK: return "ok";
+    case TP_MLP_ERR_INVALID_ARG: return "invalid argument (pointer, shape, alignment, rank or activation)";
+    case TP_MLP_ERR_UNSUPPORTED: return "valid but unsupported option";
+    case TP_MLP_ERR_WORKSPACE: return "workspace missing or too small";
+    case TP_MLP_ERR_HIP: return "HIP launch or query failed";
+  }
+  return "unknown status";
+}
+
+size_t tp_mlp_workspace_bytes(const tp_mlp_shape* s, int backward) {
+  Dims d;
+  if (!check_shape(s, d)) return 0;
+  if (backward) return col_sum_workspace_bytes(d.N, d.h);
+  if (d.N == 1) return decode_layout(d).total;
+  return 0;
+}
+
+size_t tp_mlp_bias_grad_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1) return 0;
+  return col_sum_workspace_bytes(rows, cols);
+}
+
+tp_mlp_status tp_mlp_up_act_shard(const tp_mlp_shape* s, const void* X, const void* W1_i, const void* Wg_i,
+                                  void* A_i, void* U_i, void* G_i, hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  const bool sw = d.act == ACT_SWIGLU;
+  if (!req(X) || !req(W1_i) || !req(A_i) || !opt_aligned(U_i) || !opt_aligned(G_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (sw != (Wg_i != nullptr) || !opt_aligned(Wg_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (!sw && G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  if (sw && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(run_up_act(d, X, W1_i, Wg_i, A_i, U_i, G_i, stream));
+}
+
+tp_mlp_status tp_mlp_down_shard(const tp_mlp_shape* s, const void* A_i, const void* W2_i, void* Y_i,
+                                hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  if (!req(A_i) || !req(W2_i) || !req(Y_i)) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(run_down(d, A_i, W2_i, Y_i, stream));
+}
+
+tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X, const void* W1_i, const void* Wg_i,
+                               const void* W2_i, void* Y_i, void* A_i, void* U_i, void* G_i, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  const bool sw = d.act == ACT_SWIGLU;
+  if (!req(X) || !req(W1_i) || !req(W2_i) || !req(Y_i) || !req(A_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (!opt_aligned(U_i) || !opt_aligned(G_i) || !opt_aligned(Wg_i) || !opt_aligned(workspace))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (sw != (Wg_i != nullptr)) return TP_MLP_ERR_INVALID_ARG;
+  if (!sw && G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  if (sw && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
+
+  if (d.N == 1) {
+    const DecodeLayout L = decode_layout(d);
+    if (workspace == nullptr || workspace_bytes < L.total) return TP_MLP_ERR_WORKSPACE;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* part_up = reinterpret_cast<float*>(ws + L.off_part_up);
+    float* part_dn = reinterpret_cast<float*>(ws + L.off_part_down);
+    unsigned* cnt_up = reinterpret_cast<unsigned*>(ws + L.off_cnt_up);
+    unsigned* cnt_dn = reinterpret_cast<unsigned*>(ws + L.off_cnt_down);
+    hipError_t e;
+    if (sw)
+      e = gemv_launch(GV_EPI_SWIGLU, d.act, cu16(X), cu16(Wg_i), cu16(W1_i), (int)d.h, (int)d.Fi, L.up, part_up,
+                      cnt_up, u16(A_i), u16(G_i), u16(U_i), stream);
+    else
+      e = gemv_launch(GV_EPI_ACT, d.act, cu16(X), cu16(W1_i), cu16(W1_i), (int)d.h, (int)d.Fi, L.up, part_up,
+                      cnt_up, u16(A_i), u16(U_i), nullptr, stream);
+    if (e != hipSuccess) return TP_MLP_ERR_HIP;
+    e = gemv_launch(GV_EPI_STORE, d.act, cu16(A_i), cu16(W2_i), cu16(W2_i), (int)d.Fi, (int)d.h, L.down, part_dn,
+                    cnt_dn, u16(Y_i), nullptr, nullptr, stream);
+    return hip_status(e);
+  }
+  hipError_t e = run_up_act(d, X, W1_i, Wg_i, A_i, U_i, G_i, stream);
+  if (e != hipSuccess) return TP_MLP_ERR_HIP;
+  return hip_status(run_down(d, A_i, W2_i, Y_i, stream));
+}
+
+tp_mlp_status tp_mlp_down_dgrad_act_shard(const tp_mlp_shape* s, const void* dY, const void* W2_i, const void* U_i,
+                                          const void* G_i, void* dU_i, hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  const bool sw = d.act == ACT_SWIGLU;
+  if (!req(dY) || !req(W2_i) || !req(U_i) || !req(dU_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (sw ? !req(G_i) : G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(run_dgrad_act(d, dY, W2_i, U_i, G_i, dU_i, stream));
+}
+
+tp_mlp_status tp_mlp_down_wgrad_shard(const tp_mlp_shape* s, const void* A_i, const void* dY, float* dW2_i,
+                                      hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  if (!req(A_i) || !req(dY) || !req(dW2_i)) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(run_wgrad_down(d, A_i, dY, dW2_i, stream));
+}
+
+tp_mlp_status tp_mlp_up_wgrad_shard(const tp_mlp_shape* s, const void* X, const void* dU_i, float* dW1_i,
+                                    float* dWg_i, hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  const bool sw = d.act == ACT_SWIGLU;
+  if (!req(X) || !req(dU_i) || !req(dW1_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (sw ? !req(dWg_i) : dWg_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(run_wgrad_up(d, X, dU_i, dW1_i, dWg_i, stream));
+}
+
+tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i, const void* W1_i, const void* Wg_i,
+                                    void* dX_partial, hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  const bool sw = d.act == ACT_SWIGLU;
+  if (!req(dU_i) || !req(W1_i) || !req(dX_partial)) return TP_MLP_ERR_INVALID_ARG;
+  if (sw ? !req(Wg_i) : Wg_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(run_dgrad_up(d, dU_i, W1_i, Wg_i, dX_partial, stream));
+}
+
+tp_mlp_status tp_mlp_bias_grad(const void* dY, int64_t rows, int64_t cols, float* db2, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  if (rows < 1 || cols < 8 || cols % 8 != 0 || !req(dY) || !req(db2) || !opt_aligned(workspace))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < col_sum_workspace_bytes(rows, cols)) return TP_MLP_ERR_WORKSPACE;
+  return hip_status(col_sum_launch(cu16(dY), rows, cols, db2, static_cast<float*>(workspace), stream));
+}
+
+tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X, const void* W1_i, const void* Wg_i,
+                               const void* W2_i, const void* dY, const void* A_i, const void* U_i, const void* G_i,
+                               void* dU_i, float* dW1_i, float* dWg_i, float* dW2_i, void* dX_partial, float* db2,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  const bool sw = d.act == ACT_SWIGLU;
+  if (!req(X) || !req(W1_i) || !req(W2_i) || !req(dY) || !req(A_i) || !req(U_i) || !req(dU_i) || !req(dW1_i) ||
+      !req(dW2_i) || !req(dX_partial) || !opt_aligned(db2) || !opt_aligned(workspace))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (sw ? (!req(Wg_i) || !req(G_i) || !req(dWg_i)) : (Wg_i != nullptr || G_i != nullptr || dWg_i != nullptr))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (db2 != nullptr && (workspace == nullptr || workspace_bytes < col_sum_workspace_bytes(d.N, d.h)))
+    return TP_MLP_ERR_WORKSPACE;
+
+  hipError_t e = run_dgrad_act(d, dY, W2_i, U_i, G_i, dU_i, stream);
+  if (e == hipSuccess) e = run_wgrad_down(d, A_i, dY, dW2_i, stream);
+  if (e == hipSuccess) e = run_wgrad_up(d, X, dU_i, dW1_i, dWg_i, stream);
+  if (e == hipSuccess) e = run_dgrad_up(d, dU_i, W1_i, Wg_i, dX_partial, stream);
+  if (e == hipSuccess && db2 != nullptr)
+    e = col_sum_launch(cu16(dY), d.N, d.h, db2, static_cast<float*>(workspace), stream);
+  return hip_status(e);
+}
+
+tp_mlp_status tp_mlp_reduce_partials_local(int32_t t, const void* const* partials, int64_t rows, int64_t cols,
+                                           const void* bias, void* out, hipStream_t stream) {
+  if (t < 1 || t > MAX_T || partials == nullptr || rows < 1 || cols < 8 || cols % 8 != 0) {
+    if (t > MAX_T && partials != nullptr) return TP_MLP_ERR_UNSUPPORTED;
+    return TP_MLP_ERR_INVALID_ARG;
+  }
+  if (!req(out) || !opt_aligned(bias)) return TP_MLP_ERR_INVALID_ARG;
+  PartialPtrs pp = {};
+  for (int r = 0; r < t; ++r) {
+    if (!req(partials[r])) return TP_MLP_ERR_INVALID_ARG;
+    pp.p[r] = cu16(partials[r]);
+  }
+  if (rows > (int64_t)1 << 40 || cols > (int64_t)1 << 40) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(reduce_partials_launch(pp, t, rows, cols, cu16(bias), u16(out), num_cu_current(), stream));
+}
+
+}  // extern "C"

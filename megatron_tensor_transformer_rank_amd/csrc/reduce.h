@@ -1,0 +1,22 @@
+// Internal interface of the reduction kernels (reduce.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+constexpr int MAX_T = 64;
+
+struct PartialPtrs {
+  const uint16_t* p[MAX_T];
+};
+
+hipError_t reduce_partials_launch(const PartialPtrs& pp, int t, int64_t rows, int64_t cols, const uint16_t* bias,
+                                  uint16_t* out, int num_cu, hipStream_t st);
+// db2 = column sums of dY; part is col_sum_workspace_bytes(rows, cols) of
+// device scratch.
+size_t col_sum_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t col_sum_launch(const uint16_t* dY, int64_t rows, int64_t cols, float* db, float* part, hipStream_t st);
+
+}  // namespace tpmlp

@@ -1,0 +1,130 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+the header declares, and rejects invalid arguments before touching the GPU
+(no compute calls are made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from megatron_tensor_transformer_rank_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_mlp.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced by validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tp_mlp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(B.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    for required in ("tp_mlp_fwd_shard", "tp_mlp_bwd_shard", "tp_mlp_reduce_partials_local"):
+        assert required in names
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.status_string(s)
+    assert B.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert B.workspace_bytes(B.make_shape(128, 1024, 4096, 2, 0, "gelu"), False) == 0
+    dec = B.workspace_bytes(B.make_shape(1, 8192, 28672, 4, 0, "swiglu"), False)
+    assert dec > 0 and dec % 256 == 0
+    # bias-gradient scratch: at most 64 row slabs of float32 columns
+    assert 0 < B.workspace_bytes(B.make_shape(16384, 8192, 28672, 4, 0, "swiglu"), True) <= 64 * 8192 * 4
+    assert B.workspace_bytes(B.make_shape(4, 8, 12, 5, 0, "gelu"), False) == 0  # invalid: F % t
+    assert B.bias_grad_workspace_bytes(1, 8) == 8 * 4
+
+
+def _fwd(shape, **over):
+    a = dict(X=FAKE, W1=FAKE, Wg=None, W2=FAKE, Y=FAKE, A=FAKE, U=None, G=None, ws=None, wsb=0)
+    a.update(over)
+    return B.lib().tp_mlp_fwd_shard(ctypes.byref(shape), a["X"], a["W1"], a["Wg"], a["W2"], a["Y"],
+                                    a["A"], a["U"], a["G"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("shape,expect", [
+    (B.make_shape(0, 64, 128, 1, 0, "gelu"), INVALID),         # N = 0
+    (B.make_shape(4, 60, 128, 1, 0, "gelu"), INVALID),         # h % 8
+    (B.make_shape(4, 64, 100, 2, 0, "gelu"), INVALID),         # F_i = 50, not a multiple of 8
+    (B.make_shape(4, 64, 130, 4, 0, "gelu"), INVALID),         # F % t
+    (B.make_shape(4, 64, 128, 2, 2, "gelu"), INVALID),         # rank >= t
+    (B.make_shape(4, 64, 128, 2, -1, "gelu"), INVALID),        # rank < 0
+    (B.make_shape(4, 64, 128, 2, 0, 7), INVALID),              # unknown activation
+    (B.make_shape(4, 64, 128 * 80, 80, 0, "gelu"), UNSUPPORTED),  # t > 64
+])
+def test_fwd_rejects_bad_shapes(shape, expect):
+    assert _fwd(shape) == expect
+
+
+def test_fwd_rejects_bad_pointers():
+    s = B.make_shape(4, 64, 128, 2, 0, "gelu")
+    assert _fwd(s, X=None) == INVALID
+    assert _fwd(s, W2=None) == INVALID
+    assert _fwd(s, Y=FAKE + 2) == INVALID                       # misaligned
+    assert _fwd(s, Wg=FAKE) == INVALID                          # gate weight given without SwiGLU
+    assert _fwd(s, G=FAKE) == INVALID                           # gate stash without SwiGLU
+    sw = B.make_shape(4, 64, 128, 2, 0, "swiglu")
+    assert _fwd(sw) == INVALID                                  # SwiGLU needs the gate shard
+    assert _fwd(sw, Wg=FAKE, U=FAKE) == INVALID                 # U and G stashes come together
+    dec = B.make_shape(1, 64, 128, 2, 0, "gelu")
+    assert _fwd(dec) == WORKSPACE                               # decode path needs workspace
+    assert _fwd(dec, ws=FAKE, wsb=16) == WORKSPACE
+
+
+def test_bwd_rejects_bad_arguments():
+    s = B.make_shape(4, 64, 128, 2, 0, "gelu")
+    args = [FAKE] * 13 + [None, None, 0, None]
+    base = dict(zip(["X", "W1", "Wg", "W2", "dY", "A", "U", "G", "dU", "dW1", "dWg", "dW2", "dX",
+                     "db2", "ws", "wsb", "st"], args))
+    base.update(Wg=None, G=None, dWg=None)
+
+    def call(**o):
+        a = dict(base)
+        a.update(o)
+        return B.lib().tp_mlp_bwd_shard(ctypes.byref(s), *a.values())
+
+    assert call(U=None) == INVALID
+    assert call(dW2=FAKE + 4) == INVALID
+    assert call(dWg=FAKE) == INVALID
+    assert call(db2=FAKE) == WORKSPACE
+
+
+def test_reduce_rejects_bad_arguments():
+    L = B.lib()
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert L.tp_mlp_reduce_partials_local(0, ptrs, 4, 8, None, FAKE, None) == INVALID
+    assert L.tp_mlp_reduce_partials_local(2, None, 4, 8, None, FAKE, None) == INVALID
+    assert L.tp_mlp_reduce_partials_local(2, ptrs, 4, 12, None, FAKE, None) == INVALID
+    assert L.tp_mlp_reduce_partials_local(2, ptrs, 0, 8, None, FAKE, None) == INVALID
+    assert L.tp_mlp_reduce_partials_local(2, ptrs, 4, 8, FAKE + 8, FAKE, None) == INVALID
+    bad = (ctypes.c_void_p * 2)(FAKE, None)
+    assert L.tp_mlp_reduce_partials_local(2, bad, 4, 8, None, FAKE, None) == INVALID
+    big = (ctypes.c_void_p * 65)(*([FAKE] * 65))
+    assert L.tp_mlp_reduce_partials_local(65, big, 4, 8, None, FAKE, None) == UNSUPPORTED
+
+
+def test_step_entry_points_validate():
+    L = B.lib()
+    s = B.make_shape(4, 64, 128, 2, 0, "swiglu")
+    r = ctypes.byref(s)
+    assert L.tp_mlp_up_act_shard(r, FAKE, FAKE, None, FAKE, None, None, None) == INVALID
+    assert L.tp_mlp_down_shard(r, FAKE, None, FAKE, None) == INVALID
+    assert L.tp_mlp_down_dgrad_act_shard(r, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
+    assert L.tp_mlp_down_wgrad_shard(r, FAKE, FAKE, FAKE + 1, None) == INVALID
+    assert L.tp_mlp_up_wgrad_shard(r, FAKE, FAKE, FAKE, None, None) == INVALID
+    assert L.tp_mlp_up_dgrad_shard(r, FAKE, FAKE, None, FAKE, None) == INVALID
+    assert L.tp_mlp_bias_grad(FAKE, 4, 12, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert L.tp_mlp_bias_grad(FAKE, 4, 8, FAKE, None, 0, None) == WORKSPACE

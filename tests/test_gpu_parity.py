@@ -1,0 +1,297 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Small and ragged shapes that span several tiles and leave tails in every
+dimension; every rank of the tensor-parallel group is run, the partials are
+reduced by the library's reduction kernel, and every output (U, G, A, Y_i, Y,
+dU, dW1, dWg, dW2, dX_i, dX, db2) is compared elementwise with the oracle on
+the same bf16 inputs: relative Frobenius error <= 5e-3 and max error <=
+3e-2 * max|ref| (bf16 inputs, float32 accumulation).  Integer work is
+bit-exact: the zero-padded worked example and the reduction of exactly
+representable sums.
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_transformer_rank_amd import binding as B
+from megatron_tensor_transformer_rank_amd import inputs as I
+from tests.helpers import Shard, assert_close, bf16_dev, f64
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_group(wid, N, h, F, t, act, bias, stash=True):
+    """Run all t shards fwd+bwd on the GPU and the oracle on the same bf16
+    inputs; compare everything."""
+    say(f"[group] wid={wid} N={N} h={h} F={F} t={t} act={act} bias={bias}")
+    sw = act == "swiglu"
+    Fi = F // t
+    Xb, dYb = I.gen_x(wid, N, h), I.gen_dy(wid, N, h)
+    W1b, W2b, Wgb = I.gen_full_weights(wid, h, F, t, sw)
+    b2b = I.gen_b2(wid, h) if bias else None
+    X, dY = oracle.bf16_bits_to_f64(Xb), oracle.bf16_bits_to_f64(dYb)
+    W1, W2 = oracle.bf16_bits_to_f64(W1b), oracle.bf16_bits_to_f64(W2b)
+    Wg = oracle.bf16_bits_to_f64(Wgb) if sw else None
+    b2 = oracle.bf16_bits_to_f64(b2b) if bias else None
+    Yref, fr = oracle.tp_forward(act, X, W1, W2, t, Wg=Wg, b2=b2)
+    dXref, db2ref, br = oracle.tp_backward(act, X, W1, W2, dY, t, Wg=Wg)
+
+    Xd, dYd = bf16_dev(Xb), bf16_dev(dYb)
+    shards = []
+    for r in range(t):
+        c = oracle.column_block(r, t, F)
+        s = Shard(N, h, F, t, r, act, Xd, bf16_dev(np.ascontiguousarray(W1b[:, c])),
+                  bf16_dev(np.ascontiguousarray(W2b[c, :])),
+                  bf16_dev(np.ascontiguousarray(Wgb[:, c])) if sw else None, stash=stash)
+        s.forward()
+        s.backward(dYd, db2=(r == 0))
+        shards.append(s)
+    Y = torch.empty(N, h, dtype=torch.bfloat16, device="cuda")
+    B.tp_mlp_reduce_partials_local([s.Y for s in shards], Y, bias=bf16_dev(b2b) if bias else None)
+    dX = torch.empty(N, h, dtype=torch.bfloat16, device="cuda")
+    B.tp_mlp_reduce_partials_local([s.dX for s in shards], dX)
+    torch.cuda.synchronize()
+
+    for r, s in enumerate(shards):
+        f, b = fr[r], br[r]
+        assert_close(f"A[{r}]", f64(s.A), f["A"])
+        if stash:
+            assert_close(f"U[{r}]", f64(s.U), f["U"])
+            if sw:
+                assert_close(f"G[{r}]", f64(s.G), f["G"])
+        assert_close(f"Y_i[{r}]", f64(s.Y), f["Y"])
+        dU = f64(s.dU)
+        if sw:
+            assert_close(f"dG[{r}]", dU[:, :Fi], b["dG"])
+            assert_close(f"dP[{r}]", dU[:, Fi:], b["dU"])
+            assert_close(f"dWg[{r}]", f64(s.dWg), b["dWg"])
+        else:
+            assert_close(f"dU[{r}]", dU, b["dU"])
+        assert_close(f"dW1[{r}]", f64(s.dW1), b["dW1"])
+        assert_close(f"dW2[{r}]", f64(s.dW2), b["dW2"])
+        assert_close(f"dX_i[{r}]", f64(s.dX), b["dX"])
+    assert_close("Y", f64(Y), Yref)
+    assert_close("dX", f64(dX), dXref)
+    assert_close("db2", f64(shards[0].db2), db2ref, rel_fro=1e-5, max_rel=1e-5)
+    return shards, Y, dX
+
+
+# (wid, N, h, F, t, act, bias): several 256-wide tiles plus ragged tails in
+# N (tokens), h (a K tail for the up-projection) and F_i
+CASES = [
+    (101, 128, 1024, 4096, 2, "gelu", False),    # the pages' 128 x 1024 x 4096 example, t = 2
+    (102, 300, 520, 2328, 3, "relu", True),      # ragged everywhere, F_i = 776
+    (103, 257, 264, 784, 2, "swiglu", True),     # F_i = 392, SwiGLU
+    (104, 77, 136, 512, 4, "gelu", False),       # small N, t = 4
+    (105, 530, 384, 1536, 1, "swiglu", False),   # unsplit block
+    (106, 8, 64, 128, 2, "relu", False),         # a single partial tile
+    (107, 2, 1032, 2080, 2, "gelu", False),      # two tokens (MFMA path, 1 row tile)
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"N{c[1]}_h{c[2]}_F{c[3]}_t{c[4]}_{c[5]}" for c in CASES])
+def test_group_matches_oracle(case):
+    run_group(*case)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu", "relu"])
+def test_decode_one_token(act):
+    """N = 1 routes the forward to the split-K GEMV path (the backward stays
+    on the MFMA path)."""
+    run_group(200 + len(act), 1, 1024, 3 * 1024, 2, act, False)
+
+
+def test_decode_without_stash():
+    """Inference: forward only, no stash buffers."""
+    sw = True
+    N, h, F, t = 1, 520, 1040, 2
+    Xb = I.gen_x(211, N, h)
+    W1b, W2b, Wgb = I.gen_full_weights(211, h, F, t, sw)
+    Yref, _ = oracle.tp_forward("swiglu", oracle.bf16_bits_to_f64(Xb), oracle.bf16_bits_to_f64(W1b),
+                                oracle.bf16_bits_to_f64(W2b), t, Wg=oracle.bf16_bits_to_f64(Wgb))
+    parts = []
+    for r in range(t):
+        c = oracle.column_block(r, t, F)
+        s = Shard(N, h, F, t, r, "swiglu", bf16_dev(Xb), bf16_dev(np.ascontiguousarray(W1b[:, c])),
+                  bf16_dev(np.ascontiguousarray(W2b[c, :])), bf16_dev(np.ascontiguousarray(Wgb[:, c])),
+                  stash=False)
+        s.forward()
+        parts.append(s.Y)
+    Y = torch.empty(N, h, dtype=torch.bfloat16, device="cuda")
+    B.tp_mlp_reduce_partials_local(parts, Y)
+    assert_close("Y", f64(Y), Yref)
+
+
+def test_split_sum_equals_unsplit_on_gpu():
+    """The pages' invariant on the GPU: the reduced partials of t = 4 match
+    the GPU's own unsplit (t = 1) run."""
+    N, h, F, act = 192, 512, 2048, "gelu"
+    Xb = I.gen_x(300, N, h)
+    W1b, W2b, _ = I.gen_full_weights(300, h, F, 4, False)
+    Xd = bf16_dev(Xb)
+    one = Shard(N, h, F, 1, 0, act, Xd, bf16_dev(W1b), bf16_dev(W2b))
+    one.forward()
+    parts = []
+    for r in range(4):
+        c = oracle.column_block(r, 4, F)
+        s = Shard(N, h, F, 4, r, act, Xd, bf16_dev(np.ascontiguousarray(W1b[:, c])),
+                  bf16_dev(np.ascontiguousarray(W2b[c, :])))
+        s.forward()
+        parts.append(s)
+        # the concatenated activation shards equal the unsplit activation exactly
+        assert torch.equal(s.A, one.A[:, c])
+    Y = torch.empty(N, h, dtype=torch.bfloat16, device="cuda")
+    B.tp_mlp_reduce_partials_local([p.Y for p in parts], Y)
+    assert_close("sum of partials vs unsplit", f64(Y), f64(one.Y))
+
+
+def _pad(a, shape):
+    out = np.zeros(shape, dtype=np.float32)
+    out[tuple(slice(0, s) for s in a.shape)] = a
+    return I.f32_to_bf16_bits(out)
+
+
+@pytest.mark.parametrize("N_pad", [1, 16])
+def test_worked_example_exact(N_pad):
+    """The pages' worked example, zero-padded to the ABI's multiples of 8
+    (exact: act(0) = 0 and padded weights are 0), bit-exact on the GPU on the
+    decode path (one row) and on the MFMA path (16 rows, the real one first)."""
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    bw = json.load(open(os.path.join(GOLDEN, "worked_example_backward.json")))["cases"][0]
+    x = np.array([g["x"]], np.float32)
+    w1, w2 = np.array(g["w1"], np.float32), np.array(g["w2"], np.float32)
+    h, Fi, t = 8, 8, 2
+    Xb = _pad(x, (N_pad, h))
+    dYb = _pad(np.array([bw["dY"]], np.float32), (N_pad, h))
+    shards, parts, dparts = [], [], []
+    for r in range(t):
+        cols = slice(2 * r, 2 * r + 2)
+        W1b = _pad(w1[:, cols], (h, Fi))
+        W2b = _pad(w2[cols, :], (Fi, h))
+        s = Shard(N_pad, h, Fi * t, t, r, "relu", bf16_dev(Xb), bf16_dev(W1b), bf16_dev(W2b))
+        s.forward()
+        s.backward(bf16_dev(dYb))
+        shards.append(s)
+        parts.append(s.Y)
+        dparts.append(s.dX)
+    Y = torch.empty(N_pad, h, dtype=torch.bfloat16, device="cuda")
+    B.tp_mlp_reduce_partials_local(parts, Y)
+    dX = torch.empty(N_pad, h, dtype=torch.bfloat16, device="cuda")
+    B.tp_mlp_reduce_partials_local(dparts, dX)
+    torch.cuda.synchronize()
+    for r in range(t):
+        assert f64(shards[r].A)[0, :2].tolist() == g["local_hidden"][r]
+        assert f64(shards[r].Y)[0, :2].tolist() == g["partials"][r]
+        assert f64(shards[r].dX)[0, :2].tolist() == bw["dX_partials"][r]
+        assert np.all(f64(shards[r].Y)[1:] == 0) and np.all(f64(shards[r].Y)[0, 2:] == 0)
+    assert f64(Y)[0, :2].tolist() == g["output"]
+    assert f64(dX)[0, :2].tolist() == bw["dX"]
+    dW1 = np.hstack([f64(s.dW1)[:2, :2] for s in shards])
+    dW2 = np.vstack([f64(s.dW2)[:2, :2] for s in shards])
+    assert dW1.tolist() == bw["dW1"]
+    assert dW2.tolist() == bw["dW2"]
+
+
+def test_reduce_bitexact_on_representable_sums():
+    """Partials that are small multiples of 1/8 sum exactly in float32, so the
+    reduction (+ bias) must equal the oracle's sum bit for bit."""
+    rng = np.random.default_rng(5)
+    t, rows, cols = 5, 333, 1032
+    parts = [rng.integers(-64, 64, size=(rows, cols)).astype(np.float32) / 8 for _ in range(t)]
+    bias = rng.integers(-16, 16, size=cols).astype(np.float32) / 4
+    pb = [I.f32_to_bf16_bits(p) for p in parts]
+    bb = I.f32_to_bf16_bits(bias)
+    ref = oracle.reduce_partials([oracle.bf16_bits_to_f64(p) for p in pb], oracle.bf16_bits_to_f64(bb))
+    out = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+    B.tp_mlp_reduce_partials_local([bf16_dev(p) for p in pb], out, bias=bf16_dev(bb))
+    ref_bits = I.f32_to_bf16_bits(ref.astype(np.float32))
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref_bits)
+
+
+def test_reduce_in_place_and_random():
+    rng = np.random.default_rng(6)
+    t, rows, cols = 8, 1000, 2048
+    pb = [I.normal_bf16([7, i], (rows, cols)) for i in range(t)]
+    ref = oracle.reduce_partials([oracle.bf16_bits_to_f64(p) for p in pb])
+    ds = [bf16_dev(p) for p in pb]
+    B.tp_mlp_reduce_partials_local(ds, ds[0])        # out aliases partials[0]
+    torch.cuda.synchronize()
+    assert_close("reduce in place", f64(ds[0]), ref, rel_fro=5e-3, max_rel=1e-2)
+    del rng
+
+
+def test_deterministic_and_guard_bands():
+    """Every output is bitwise identical across two runs, and nothing is
+    written outside the output buffers (canary bytes around each)."""
+    N, h, F, t, act = 300, 520, 2 * 776, 2, "swiglu"
+    Xb, dYb = I.gen_x(400, N, h), I.gen_dy(400, N, h)
+    W1b, W2b, Wgb = I.gen_full_weights(400, h, F, t, True)
+    c = oracle.column_block(0, t, F)
+    Fi = F // t
+    s = Shard(N, h, F, t, 0, act, bf16_dev(Xb), bf16_dev(np.ascontiguousarray(W1b[:, c])),
+              bf16_dev(np.ascontiguousarray(W2b[c, :])), bf16_dev(np.ascontiguousarray(Wgb[:, c])))
+    # replace outputs with views into canary-padded buffers
+    PAD = 4096
+    guards = {}
+    for name, shape, dt in [("Y", (N, h), torch.bfloat16), ("A", (N, Fi), torch.bfloat16),
+                            ("U", (N, Fi), torch.bfloat16), ("G", (N, Fi), torch.bfloat16),
+                            ("dU", (N, 2 * Fi), torch.bfloat16), ("dW1", (h, Fi), torch.float32),
+                            ("dWg", (h, Fi), torch.float32), ("dW2", (Fi, h), torch.float32),
+                            ("dX", (N, h), torch.bfloat16)]:
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * PAD,), 7.0, dtype=dt, device="cuda")
+        guards[name] = buf
+        setattr(s, name, buf[PAD:PAD + n].view(*shape))
+    dYd = bf16_dev(dYb)
+    s.forward()
+    s.backward(dYd)
+    first = {k: getattr(s, k).clone() for k in guards}
+    s.forward()
+    s.backward(dYd)
+    torch.cuda.synchronize()
+    for k, buf in guards.items():
+        assert torch.equal(getattr(s, k), first[k]), f"{k} differs between runs"
+        assert torch.all(buf[:PAD] == 7.0) and torch.all(buf[-PAD:] == 7.0), f"{k}: write outside buffer"
+
+
+def test_step_entry_points_match_composite():
+    """The one-kernel step entry points give bitwise the composite results."""
+    N, h, F, t, act = 260, 392, 2 * 520, 2, "gelu"
+    Xb, dYb = I.gen_x(500, N, h), I.gen_dy(500, N, h)
+    W1b, W2b, _ = I.gen_full_weights(500, h, F, t, False)
+    c = oracle.column_block(1, t, F)
+    s = Shard(N, h, F, t, 1, act, bf16_dev(Xb), bf16_dev(np.ascontiguousarray(W1b[:, c])),
+              bf16_dev(np.ascontiguousarray(W2b[c, :])))
+    dYd = bf16_dev(dYb)
+    s.forward()
+    s.backward(dYd, db2=True)
+    sh = s.shape
+    A = torch.empty_like(s.A); U = torch.empty_like(s.U); Y = torch.empty_like(s.Y)
+    dU = torch.empty_like(s.dU); dW1 = torch.empty_like(s.dW1); dW2 = torch.empty_like(s.dW2)
+    dX = torch.empty_like(s.dX); db2 = torch.empty_like(s.db2)
+    B.tp_mlp_up_act_shard(sh, s.X, s.W1, None, A, U, None)
+    B.tp_mlp_down_shard(sh, A, s.W2, Y)
+    B.tp_mlp_down_dgrad_act_shard(sh, dYd, s.W2, U, None, dU)
+    B.tp_mlp_down_wgrad_shard(sh, A, dYd, dW2)
+    B.tp_mlp_up_wgrad_shard(sh, s.X, dU, dW1)
+    B.tp_mlp_up_dgrad_shard(sh, dU, s.W1, None, dX)
+    ws = B.alloc_workspace(B.bias_grad_workspace_bytes(N, h))
+    B.tp_mlp_bias_grad(dYd, db2, ws)
+    torch.cuda.synchronize()
+    for a, b, n in [(A, s.A, "A"), (U, s.U, "U"), (Y, s.Y, "Y"), (dU, s.dU, "dU"), (dW1, s.dW1, "dW1"),
+                    (dW2, s.dW2, "dW2"), (dX, s.dX, "dX"), (db2, s.db2, "db2")]:
+        assert torch.equal(a, b), n
