@@ -1,0 +1,270 @@
+"""Benchmark of one tensor-parallel rank's MLP shard on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path for one rank: the fused
+column-parallel up-projection + activation, the row-parallel down-projection,
+the local reduction of the t partial sums (the other ranks' partials are
+stand-in buffers resident in HBM, the bias added once), the backward (dgrad
+through W2 with the activation derivative, both weight gradients, dgrad
+through W1) and the reduction of the t partial input gradients.  Inputs are
+seeded synthetic bf16 tensors already resident in HBM.  Prints one JSON line.
+
+Also reported in the same line: per-kernel average durations (HIP events on
+the launch stream, from a second pass through the one-kernel entry points),
+the roofline of the dominant kernel, the one-token decode GEMV path
+(``llama3_70b_decode_t4``, weights rotated over several copies so the
+256 MiB Infinity Cache cannot hold them), and the fp64 oracle timed on the
+host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "per-rank TP MLP fwd+bwd TFLOP/s (bf16) and % MFMA peak; decode GB/s % HBM"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="gpt3_train_t8")
+    p.add_argument("--decode-workload", default="llama3_70b_decode_t4")
+    p.add_argument("--decode-steps", type=int, default=200)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=256)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs one tensor-parallel rank's shard on a single "
+              f"MI355X (the t shards of a group are run one after another on it); --gpus {args.gpus} "
+              f"is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from megatron_tensor_transformer_rank_amd import binding as B
+    from megatron_tensor_transformer_rank_amd import inputs as I
+    from megatron_tensor_transformer_rank_amd.configs import WORKLOADS
+
+    B.lib()  # raises if libtpmlp.so is missing: there is no other path
+    w = WORKLOADS[args.workload]
+    dev = "cuda"
+    bf, f32 = torch.bfloat16, torch.float32
+    sw = w.act == "swiglu"
+    N, h, Fi, t = w.N, w.h, w.Fi, w.t
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(bf).to(dev)
+
+    log(f"[bench] generating inputs for {w.name}: N={N} h={h} F_i={Fi} t={t} act={w.act}")
+    X, dY = to_dev(I.gen_x(w.wid, N, h)), to_dev(I.gen_dy(w.wid, N, h))
+    W1 = to_dev(I.gen_w_up_shard(w.wid, h, Fi, 0))
+    W2 = to_dev(I.gen_w_down_shard(w.wid, h, Fi, 0))
+    Wg = to_dev(I.gen_w_gate_shard(w.wid, h, Fi, 0)) if sw else None
+    b2 = to_dev(I.gen_b2(w.wid, h)) if w.bias else None
+    shape = B.make_shape(N, h, w.F, t, 0, w.act)
+    Y = torch.empty(N, h, dtype=bf, device=dev)
+    A = torch.empty(N, Fi, dtype=bf, device=dev)
+    U = torch.empty(N, Fi, dtype=bf, device=dev)
+    G = torch.empty(N, Fi, dtype=bf, device=dev) if sw else None
+    dU = torch.empty(N, w.g * Fi, dtype=bf, device=dev)
+    dW1 = torch.empty(h, Fi, dtype=f32, device=dev)
+    dWg = torch.empty(h, Fi, dtype=f32, device=dev) if sw else None
+    dW2 = torch.empty(Fi, h, dtype=f32, device=dev)
+    dX = torch.empty(N, h, dtype=bf, device=dev)
+    db2 = torch.empty(h, dtype=f32, device=dev) if w.bias else None
+    Yred = torch.empty(N, h, dtype=bf, device=dev)
+    dXred = torch.empty(N, h, dtype=bf, device=dev)
+    ws_f = B.alloc_workspace(B.workspace_bytes(shape, False))
+    ws_b = B.alloc_workspace(B.workspace_bytes(shape, True))
+    # the other ranks' partial sums (stand-ins: resident bf16 buffers)
+    B.tp_mlp_fwd_shard(shape, X, W1, Wg, W2, Y, A, U, G, ws_f)
+    others_y = [Y.clone() for _ in range(t - 1)]
+    B.tp_mlp_bwd_shard(shape, X, W1, Wg, W2, dY, A, U, G, dU, dW1, dWg, dW2, dX, db2, ws_b)
+    others_dx = [dX.clone() for _ in range(t - 1)]
+    torch.cuda.synchronize()
+
+    def step():
+        B.tp_mlp_fwd_shard(shape, X, W1, Wg, W2, Y, A, U, G, ws_f)
+        B.tp_mlp_reduce_partials_local([Y] + others_y, Yred, bias=b2)
+        B.tp_mlp_bwd_shard(shape, X, W1, Wg, W2, dY, A, U, G, dU, dW1, dWg, dW2, dX, db2, ws_b)
+        B.tp_mlp_reduce_partials_local([dX] + others_dx, dXred)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = w.flops_train()
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
+
+    # ---- per-kernel durations: the same step through the one-kernel entry points,
+    # HIP events recorded on the launch stream between consecutive launches
+    ws_db = B.alloc_workspace(B.bias_grad_workspace_bytes(N, h)) if w.bias else None
+    kernels = [
+        ("up_act", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_act_shard(shape, X, W1, Wg, A, U, G)),
+        ("down", 2 * N * h * Fi, lambda: B.tp_mlp_down_shard(shape, A, W2, Y)),
+        ("reduce_y", 0, lambda: B.tp_mlp_reduce_partials_local([Y] + others_y, Yred, bias=b2)),
+        ("down_dgrad_act", 2 * N * h * Fi, lambda: B.tp_mlp_down_dgrad_act_shard(shape, dY, W2, U, G, dU)),
+        ("down_wgrad", 2 * N * h * Fi, lambda: B.tp_mlp_down_wgrad_shard(shape, A, dY, dW2)),
+        ("up_wgrad", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_wgrad_shard(shape, X, dU, dW1, dWg)),
+        ("up_dgrad", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_dgrad_shard(shape, dU, W1, Wg, dX)),
+        ("reduce_dx", 0, lambda: B.tp_mlp_reduce_partials_local([dX] + others_dx, dXred)),
+    ]
+    if w.bias:
+        kernels.append(("bias_grad", 0, lambda: B.tp_mlp_bias_grad(dY, db2, ws_db)))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    for _ in range(2):
+        for _, _, fn in kernels:
+            fn()
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        evs[s][0].record(stream)
+        for j, (_, _, fn) in enumerate(kernels):
+            fn()
+            evs[s][j + 1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = {name: float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(args.steps)]))
+               for j, (name, _, _) in enumerate(kernels)}
+    gemms = [(n, fl) for n, fl, _ in kernels if fl > 0]
+    dom, dom_fl = max(gemms, key=lambda x: kern_ms[x[0]])
+    achieved = dom_fl / (kern_ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": dom_fl}
+    log("[bench] per-kernel ms: " + ", ".join(f"{k}={v:.3f}" for k, v in kern_ms.items()))
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": N, "h": h, "F": w.F, "t": t, "F_i": Fi, "act": w.act,
+                   "bias": w.bias, "step": "one rank fwd+bwd + local reduce of t partials (Y and dX)",
+                   "flops_per_step": flops, "tokens_per_s": round(N / (ms * 1e-3), 1),
+                   "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
+        "roofline": roofline,
+        "kernels_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+    }
+
+    # ---- decode (one token), HBM bound; weights rotated over copies
+    if not args.no_decode:
+        result["decode"] = bench_decode(args, WORKLOADS[args.decode_workload], B, I, torch, np, to_dev)
+    del X, dY, W1, W2, Wg, others_y, others_dx
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows, I)
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(args, w, B, I, torch, np, to_dev):
+    bf = torch.bfloat16
+    h, Fi = w.h, w.Fi
+    sw = w.act == "swiglu"
+    log(f"[bench] decode {w.name}: h={h} F_i={Fi} act={w.act}")
+    x = to_dev(I.gen_x(w.wid, 1, h))
+    W1 = to_dev(I.gen_w_up_shard(w.wid, h, Fi, 0))
+    W2 = to_dev(I.gen_w_down_shard(w.wid, h, Fi, 0))
+    Wg = to_dev(I.gen_w_gate_shard(w.wid, h, Fi, 0)) if sw else None
+    wbytes = w.weight_bytes()
+    nsets = max(4, int(np.ceil(1.5e9 / wbytes)))      # > 1.5 GB of weights: no cache holds them
+    sets = [(W1, Wg, W2)] + [(W1.clone(), Wg.clone() if sw else None, W2.clone()) for _ in range(nsets - 1)]
+    shape = B.make_shape(1, h, w.F, w.t, 0, w.act)
+    ws = B.alloc_workspace(B.workspace_bytes(shape, False))
+    Y = torch.empty(1, h, dtype=bf, device="cuda")
+    A = torch.empty(1, Fi, dtype=bf, device="cuda")
+    for i in range(10):
+        a, g, b = sets[i % nsets]
+        B.tp_mlp_fwd_shard(shape, x, a, g, b, Y, A, None, None, ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = args.decode_steps
+    e0.record(stream)
+    for i in range(n):
+        a, g, b = sets[i % nsets]
+        B.tp_mlp_fwd_shard(shape, x, a, g, b, Y, A, None, None, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    # warm (same weights every call) for context
+    e0.record(stream)
+    for i in range(n):
+        B.tp_mlp_fwd_shard(shape, x, W1, Wg, W2, Y, A, None, None, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_warm = e0.elapsed_time(e1) * 1e3 / n
+    gbs = wbytes / (us * 1e-6) / 1e9
+    log(f"[bench] decode: {us:.2f} us/token cold ({gbs:.0f} GB/s), {us_warm:.2f} us warm")
+    return {"workload": w.name, "value": round(gbs, 1), "unit": "GB/s", "us_per_token": round(us, 3),
+            "bytes_per_token": wbytes, "weight_sets_rotated": nsets,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "scope": "whole decode call (gate/up GEMV + down GEMV)"},
+            "us_per_token_warm_cache": round(us_warm, 3)}
+
+
+def cpu_baseline(w, rows, I):
+    """The fp64 oracle (as it stands) on a bounded sample: `rows` token rows of
+    rank 0's shard, forward + backward, on the host's BLAS threads."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas")
+    except Exception:
+        cores = os.cpu_count()
+    rows = min(rows, w.N)
+    f = oracle.bf16_bits_to_f64
+    sw = w.act == "swiglu"
+    X = f(I.gen_x(w.wid, w.N, w.h)[:rows])
+    dY = f(I.gen_dy(w.wid, w.N, w.h)[:rows])
+    W1 = f(I.gen_w_up_shard(w.wid, w.h, w.Fi, 0))
+    W2 = f(I.gen_w_down_shard(w.wid, w.h, w.Fi, 0))
+    Wg = f(I.gen_w_gate_shard(w.wid, w.h, w.Fi, 0)) if sw else None
+    log(f"[bench] cpu baseline: oracle on {rows} token rows, {cores} BLAS threads")
+    t0 = time.perf_counter()
+    oracle.shard_forward(w.act, X, W1, W2, Wg)
+    oracle.shard_backward(w.act, X, W1, W2, dY, Wg)
+    dt = time.perf_counter() - t0
+    fl = 6 * rows * w.h * w.Fi * (w.g + 1)
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{rows} of {w.N} token rows of rank 0's shard of {w.name}, forward + backward "
+                      f"(algorithmic FLOPs {fl:.3e}), numpy float64 on the host BLAS"}
+
+
+if __name__ == "__main__":
+    main()

@@ -97,8 +97,8 @@ def bias_grad_workspace_bytes(rows: int, cols: int) -> int:
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
-    """Zero-filled device workspace (the decode path needs zeroed counters
-    before its first use), or None when no workspace is needed."""
+    """Device workspace of nbytes (zero-filled; no entry point needs particular
+    initial contents), or None when no workspace is needed."""
     if nbytes == 0:
         return None
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)

@@ -30,10 +30,6 @@ int num_cu_current() {
   return n;
 }
 
-// Decode plans depend only on the shape (a fixed 256-CU target), so the
-// workspace size never depends on the device.
-constexpr int PLAN_CU = 256;
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool opt_aligned(const void* p) { return p == nullptr || aligned16(p); }
 bool req(const void* p) { return p != nullptr && aligned16(p); }
@@ -62,34 +58,40 @@ bool check_shape(const tp_mlp_shape* s, Dims& d) {
   return true;
 }
 
+// Every GEMM operand is addressed through a 32-bit buffer resource.
+bool fits_buffers(const Dims& d) {
+  const uint64_t cap = GEMM_MAX_OPERAND_BYTES / 2;  // elements
+  const uint64_t N = (uint64_t)d.N, h = (uint64_t)d.h, Fi = (uint64_t)d.Fi, g = (uint64_t)d.g;
+  return N * h <= cap && N * g * Fi <= cap && h * Fi <= cap;
+}
+
 // INVALID_ARG for a malformed shape, UNSUPPORTED for a well-formed one with
 // t above the supported maximum.
 tp_mlp_status shape_status(const tp_mlp_shape* s, Dims& d) {
-  if (check_shape(s, d)) return TP_MLP_OK;
+  if (check_shape(s, d)) return fits_buffers(d) ? TP_MLP_OK : TP_MLP_ERR_UNSUPPORTED;
   if (s != nullptr && s->t > MAX_T && s->rank >= 0 && s->rank < s->t) return TP_MLP_ERR_UNSUPPORTED;
   return TP_MLP_ERR_INVALID_ARG;
 }
 
 struct DecodeLayout {
   GemvPlan up, down;
-  size_t off_part_up, off_part_down, off_cnt_up, off_cnt_down, total;
+  size_t off_part_up, off_part_down, total;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// ~448 blocks per GEMV (1.75 per CU): measured best for the one-token stream.
+constexpr int DECODE_TARGET_BLOCKS = 448;
+
 DecodeLayout decode_layout(const Dims& d) {
   DecodeLayout L;
-  L.up = gemv_plan((int)d.h, (int)d.Fi, d.g, PLAN_CU);
-  L.down = gemv_plan((int)d.Fi, (int)d.h, 1, PLAN_CU);
+  L.up = gemv_plan((int)d.h, (int)d.Fi, d.g, DECODE_TARGET_BLOCKS);
+  L.down = gemv_plan((int)d.Fi, (int)d.h, 1, DECODE_TARGET_BLOCKS);
   size_t off = 0;
   L.off_part_up = off;
   off = round256(off + L.up.part_floats * sizeof(float));
   L.off_part_down = off;
   off = round256(off + L.down.part_floats * sizeof(float));
-  L.off_cnt_up = off;
-  off = round256(off + (size_t)L.up.strips * sizeof(unsigned));
-  L.off_cnt_down = off;
-  off = round256(off + (size_t)L.down.strips * sizeof(unsigned));
   L.total = off;
   return L;
 }
@@ -100,39 +102,46 @@ const uint16_t* cu16(const void* p) { return static_cast<const uint16_t*>(p); }
 uint16_t* u16(void* p) { return static_cast<uint16_t*>(p); }
 
 // ----------------------------------------------------------------- launchers
+uint32_t nbytes(int64_t rows, int64_t cols) { return (uint32_t)(rows * cols * 2); }
+
+GemmArgs one_segment(int M, int N, int K) {
+  GemmArgs g = {};
+  g.M = M;
+  g.N = N;
+  g.nseg = 1;
+  g.K[0] = K;
+  return g;
+}
+
 hipError_t run_up_act(const Dims& d, const void* X, const void* W1, const void* Wg, void* A, void* U, void* G,
                       hipStream_t st) {
-  GemmArgs g = {};
-  g.M = (int)d.N;
-  g.N = (int)d.Fi;
-  g.K = (int)d.h;
-  g.a0 = g.a1 = cu16(X);
+  GemmArgs g = one_segment((int)d.N, (int)d.Fi, (int)d.h);
+  g.a[0] = g.a[1] = cu16(X);
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.h);
   g.lda = d.h;
-  g.a_ksplit = g.K;
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(d.h, d.Fi);
   g.ldb = d.Fi;
   g.c0 = A;
   g.ldc = d.Fi;
   if (d.act == ACT_SWIGLU) {
-    g.b0 = cu16(Wg);
-    g.b1 = cu16(W1);
+    g.b[0] = cu16(Wg);  // gate
+    g.b[1] = cu16(W1);  // up
     g.e0 = G;
     g.e1 = U;
     return gemm_launch(GEMM_UP_SWIGLU, d.act, g, num_cu_current(), st);
   }
-  g.b0 = g.b1 = cu16(W1);
+  g.b[0] = g.b[1] = cu16(W1);
   g.e0 = U;
   return gemm_launch(GEMM_UP_ACT, d.act, g, num_cu_current(), st);
 }
 
 hipError_t run_down(const Dims& d, const void* A, const void* W2, void* Y, hipStream_t st) {
-  GemmArgs g = {};
-  g.M = (int)d.N;
-  g.N = (int)d.h;
-  g.K = (int)d.Fi;
-  g.a0 = g.a1 = cu16(A);
+  GemmArgs g = one_segment((int)d.N, (int)d.h, (int)d.Fi);
+  g.a[0] = g.a[1] = cu16(A);
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.Fi);
   g.lda = d.Fi;
-  g.a_ksplit = g.K;
-  g.b0 = g.b1 = cu16(W2);
+  g.b[0] = g.b[1] = cu16(W2);
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(d.Fi, d.h);
   g.ldb = d.h;
   g.c0 = Y;
   g.ldc = d.h;
@@ -141,38 +150,33 @@ hipError_t run_down(const Dims& d, const void* A, const void* W2, void* Y, hipSt
 
 hipError_t run_dgrad_act(const Dims& d, const void* dY, const void* W2, const void* U, const void* G, void* dU,
                          hipStream_t st) {
-  GemmArgs g = {};
-  g.M = (int)d.N;
-  g.N = (int)d.Fi;
-  g.K = (int)d.h;
-  g.a0 = g.a1 = cu16(dY);
+  GemmArgs g = one_segment((int)d.N, (int)d.Fi, (int)d.h);
+  g.a[0] = g.a[1] = cu16(dY);
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.h);
   g.lda = d.h;
-  g.a_ksplit = g.K;
-  g.b0 = g.b1 = cu16(W2);  // W2_i [F_i][h] is [n][k]
+  g.b[0] = g.b[1] = cu16(W2);  // W2_i [F_i][h] is [n][k]
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(d.Fi, d.h);
   g.ldb = d.h;
-  g.b_ksplit = g.K;
   g.c0 = dU;
+  g.lde = d.Fi;
   if (d.act == ACT_SWIGLU) {
     g.ldc = 2 * d.Fi;
     g.e0 = const_cast<void*>(G);
     g.e1 = const_cast<void*>(U);
-    g.lde = d.Fi;
   } else {
     g.ldc = d.Fi;
     g.e0 = const_cast<void*>(U);
-    g.lde = d.Fi;
   }
   return gemm_launch(GEMM_DGRAD_ACT, d.act, g, num_cu_current(), st);
 }
 
 hipError_t run_wgrad_down(const Dims& d, const void* A, const void* dY, float* dW2, hipStream_t st) {
-  GemmArgs g = {};
-  g.M = (int)d.Fi;
-  g.N = (int)d.h;
-  g.K = (int)d.N;
-  g.a0 = g.a1 = cu16(A);  // A_i [N][F_i] is [k][m]
+  GemmArgs g = one_segment((int)d.Fi, (int)d.h, (int)d.N);
+  g.a[0] = g.a[1] = cu16(A);  // A_i [N][F_i] is [k][m]
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.Fi);
   g.lda = d.Fi;
-  g.b0 = g.b1 = cu16(dY);  // dY [N][h] is [k][n]
+  g.b[0] = g.b[1] = cu16(dY);  // dY [N][h] is [k][n]
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(d.N, d.h);
   g.ldb = d.h;
   g.c0 = g.c1 = dW2;
   g.ldc = d.h;
@@ -181,13 +185,12 @@ hipError_t run_wgrad_down(const Dims& d, const void* A, const void* dY, float* d
 }
 
 hipError_t run_wgrad_up(const Dims& d, const void* X, const void* dU, float* dW1, float* dWg, hipStream_t st) {
-  GemmArgs g = {};
-  g.M = (int)d.h;
-  g.N = (int)(d.g * d.Fi);
-  g.K = (int)d.N;
-  g.a0 = g.a1 = cu16(X);  // X [N][h] is [k][m]
+  GemmArgs g = one_segment((int)d.h, (int)(d.g * d.Fi), (int)d.N);
+  g.a[0] = g.a[1] = cu16(X);  // X [N][h] is [k][m]
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.h);
   g.lda = d.h;
-  g.b0 = g.b1 = cu16(dU);  // dU [N][g*F_i] is [k][n]
+  g.b[0] = g.b[1] = cu16(dU);  // dU [N][g*F_i] is [k][n]
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(d.N, d.g * d.Fi);
   g.ldb = d.g * d.Fi;
   g.c0 = d.act == ACT_SWIGLU ? dWg : dW1;  // columns [0, F_i): dG -> dWg
   g.c1 = dW1;                              // columns [F_i, 2F_i): dP -> dW_up
@@ -197,23 +200,22 @@ hipError_t run_wgrad_up(const Dims& d, const void* X, const void* dU, float* dW1
 }
 
 hipError_t run_dgrad_up(const Dims& d, const void* dU, const void* W1, const void* Wg, void* dX, hipStream_t st) {
-  GemmArgs g = {};
-  g.M = (int)d.N;
-  g.N = (int)d.h;
-  g.K = (int)(d.g * d.Fi);
-  g.a0 = g.a1 = cu16(dU);
+  GemmArgs g = one_segment((int)d.N, (int)d.h, (int)d.Fi);
+  g.a[0] = g.a[1] = cu16(dU);
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.g * d.Fi);
   g.lda = d.g * d.Fi;
-  g.a_ksplit = g.K;
-  // B = [Wg_i | W1_i] read as [n = h][k]: k < F_i from Wg_i (SwiGLU), the rest from W1_i
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(d.h, d.Fi);
+  g.ldb = d.Fi;  // W [h][F_i] read as [n][k]
   if (d.act == ACT_SWIGLU) {
-    g.b0 = cu16(Wg);
-    g.b1 = cu16(W1);
-    g.b_ksplit = (int)d.Fi;
+    // [dG | dP] @ [Wg_i | W1_i]^T as two k segments
+    g.nseg = 2;
+    g.K[1] = (int)d.Fi;
+    g.a_koff[1] = (int)d.Fi;
+    g.b[0] = cu16(Wg);
+    g.b[1] = cu16(W1);
   } else {
-    g.b0 = g.b1 = cu16(W1);
-    g.b_ksplit = g.K;
+    g.b[0] = g.b[1] = cu16(W1);
   }
-  g.ldb = d.Fi;
   g.c0 = dX;
   g.ldc = d.h;
   return gemm_launch(GEMM_DGRAD, d.act, g, num_cu_current(), st);
@@ -286,19 +288,9 @@ tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X, const void*
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     float* part_up = reinterpret_cast<float*>(ws + L.off_part_up);
     float* part_dn = reinterpret_cast<float*>(ws + L.off_part_down);
-    unsigned* cnt_up = reinterpret_cast<unsigned*>(ws + L.off_cnt_up);
-    unsigned* cnt_dn = reinterpret_cast<unsigned*>(ws + L.off_cnt_down);
-    hipError_t e;
-    if (sw)
-      e = gemv_launch(GV_EPI_SWIGLU, d.act, cu16(X), cu16(Wg_i), cu16(W1_i), (int)d.h, (int)d.Fi, L.up, part_up,
-                      cnt_up, u16(A_i), u16(G_i), u16(U_i), stream);
-    else
-      e = gemv_launch(GV_EPI_ACT, d.act, cu16(X), cu16(W1_i), cu16(W1_i), (int)d.h, (int)d.Fi, L.up, part_up,
-                      cnt_up, u16(A_i), u16(U_i), nullptr, stream);
-    if (e != hipSuccess) return TP_MLP_ERR_HIP;
-    e = gemv_launch(GV_EPI_STORE, d.act, cu16(A_i), cu16(W2_i), cu16(W2_i), (int)d.Fi, (int)d.h, L.down, part_dn,
-                    cnt_dn, u16(Y_i), nullptr, nullptr, stream);
-    return hip_status(e);
+    return hip_status(decode_launch(d.act, cu16(X), cu16(sw ? Wg_i : W1_i), cu16(W1_i), cu16(W2_i), (int)d.h,
+                                    (int)d.Fi, L.up, L.down, part_up, part_dn, u16(A_i), u16(sw ? G_i : U_i),
+                                    u16(sw ? U_i : nullptr), u16(Y_i), stream));
   }
   hipError_t e = run_up_act(d, X, W1_i, Wg_i, A_i, U_i, G_i, stream);
   if (e != hipSuccess) return TP_MLP_ERR_HIP;

@@ -11,7 +11,7 @@ enum Epi : int {
   EPI_STORE_F32_SPLIT = 1,  // fp32; columns < c_split -> c0, the rest -> c1 (col - c_split), both ld = ldc
   EPI_ACT_FWD = 2,          // c0 = act(acc) bf16; e0 (or NULL) = acc bf16 (pre-activation stash)
   EPI_SWIGLU_FWD = 3,       // c0 = SiLU(gate) * up; e0 = gate stash, e1 = up stash (or NULL)
-  EPI_ACT_BWD = 4,          // c0 = acc * act'(e0), e0 = pre-activation stash [M, ldc]
+  EPI_ACT_BWD = 4,          // c0 = acc * act'(e0), e0 = pre-activation stash [M, lde]
   EPI_SWIGLU_BWD = 5        // c0 row = [dG | dP] (ldc = 2*lde); e0 = gate, e1 = up stash (ld = lde)
 };
 
@@ -21,23 +21,27 @@ enum GemmKind : int {
   GEMM_DOWN = 2,       // A_i @ W2_i
   GEMM_DGRAD_ACT = 3,  // dY @ W2_i^T with the activation derivative
   GEMM_WGRAD = 4,      // A^T @ B, both operands contiguous along m / n, fp32 out
-  GEMM_DGRAD = 5       // dU @ W^T (B read [n][k], optionally two buffers along k)
+  GEMM_DGRAD = 5       // dU @ W^T (B read [n][k]), one or two k segments
 };
 
+// The product runs over one or two k segments; segment s pairs A columns
+// [a_koff[s], a_koff[s] + K[s]) (k-contiguous A) with B buffer b[s].  Every
+// operand buffer is addressed through a buffer resource of its byte size
+// (< 4 GiB), which also zero-fills out-of-range tile lanes.
 struct GemmArgs {
-  int M, N, K;
-  // A operand: k-contiguous [m][k] (lda) with an optional split along k into
-  // a0 / a1, or m-contiguous [k][m] (lda) for the weight gradients.
-  const uint16_t* a0;
-  const uint16_t* a1;
+  int M, N;
+  int nseg;
+  int K[2];
+  // A: k-contiguous [m][k] (lda) or m-contiguous [k][m] (lda)
+  const uint16_t* a[2];
+  uint32_t a_bytes[2];
+  int a_koff[2];
   int64_t lda;
-  int a_ksplit;
-  // B operand: k-contiguous [n][k] (ldb, optional k split into b0 / b1) or
-  // n-contiguous [k][n] (ldb); for the SwiGLU forward b0 = gate, b1 = up.
-  const uint16_t* b0;
-  const uint16_t* b1;
+  // B: k-contiguous [n][k] (ldb) or n-contiguous [k][n] (ldb); SwiGLU
+  // forward: b[0] = gate, b[1] = up, one segment
+  const uint16_t* b[2];
+  uint32_t b_bytes[2];
   int64_t ldb;
-  int b_ksplit;
   // outputs / epilogue operands
   void* c0;
   void* c1;
@@ -49,6 +53,9 @@ struct GemmArgs {
   // filled by the launcher
   int tiles_m, tiles_n;
 };
+
+// Largest operand buffer a GEMM accepts (bytes): buffer resources are 32-bit.
+constexpr uint64_t GEMM_MAX_OPERAND_BYTES = 0xFFFFFF00ull;
 
 hipError_t gemm_launch(GemmKind kind, int act, const GemmArgs& g, int num_cu, hipStream_t st);
 

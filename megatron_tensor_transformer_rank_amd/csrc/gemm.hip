@@ -11,29 +11,36 @@
 //   dgrad W2+act' A = dY [N,h] (k-contiguous)     B = W2_i read as [n=F_i][k=h]
 //   wgrad W2      A = A_i read as [k=N][m=F_i]    B = dY [k=N][n=h]
 //   wgrad W1      A = X read as [k=N][m=h]        B = dU [k=N][n=gF_i]
-//   dgrad W1      A = dU [N,gF_i] (k-contiguous)  B = [Wg_i|W1_i] read as [n=h][k]
+//   dgrad W1      A = dU [N,gF_i] (k-contiguous)  B = Wg_i, then W1_i, read as [n=h][k]
+//                 (two k segments: [dG | dP] against [Wg_i | W1_i])
 //
 // Design (MI355X-first):
 //  * 256 threads = 4 wave64s in a 2x2 grid; block tile BM x BN x 64, each wave
-//    owns (BM/2) x (BN/2) of the output in AGPR/VGPR accumulators.
-//  * Both operands are staged in LDS as [row = m or n][64 k] bf16, 128 bytes
-//    per row, 16-byte chunks XOR-swizzled by the row so that the b128 fragment
-//    reads and the b128 stores are bank-conflict free.  Operands that are
-//    contiguous along m/n in HBM (the weight matrices in the forward, both
-//    operands of the weight gradients) are loaded as 8x8 bf16 blocks with
-//    coalesced 16-byte loads and transposed in registers before the LDS store.
-//  * Two LDS stages; the next k-tile is fetched from HBM into registers while
-//    the current one feeds the MFMAs, one barrier per k-tile.
-//  * The MFMA is issued with the operands swapped (B fragment first) so each
-//    lane ends up holding 4 consecutive output columns: 8-byte bf16 and
-//    16-byte fp32 stores in the epilogue.
+//    owns (BM/2) x (BN/2) of the output in accumulator registers.
+//  * Tiles move HBM -> LDS with buffer-load-to-LDS (16 bytes per lane, no
+//    VGPR staging, no ds_write).  Each operand is addressed through a buffer
+//    resource of its own size; tile lanes outside the matrix get an offset past
+//    the end, for which the buffer unit returns zeros, so ragged tails need no
+//    other masking.
+//  * LDS layouts (16-byte chunks XOR-swizzled against bank conflicts):
+//      k-contiguous operand [row][64 k]: chunk c of row r at slot c ^ (r & 7),
+//        fragments read with ds_read_b128;
+//      m/n-contiguous operand [64 k][R]: chunk c of k-row r at c ^ 2(r & 3),
+//        fragments read with ds_read_b64_tr_b16 (the LDS transpose read), two
+//        per 8-k fragment.
+//  * Two LDS stages.  Per k-tile: step-1 fragments are read while the step-0
+//    MFMAs run; one barrier; the DMA of the tile after next is issued into the
+//    stage just released and the next tile's step-0 fragments are read while
+//    the step-1 MFMAs run.  DMA has a whole k-tile to land.
+//  * The MFMA takes the operands swapped (B fragment first) so each lane holds
+//    4 consecutive output columns: 8-byte bf16 / 16-byte fp32 stores.
 //  * Block ids are remapped so consecutive tiles land on one XCD (blocks are
 //    dispatched round-robin over the 8 XCDs), then grouped GROUP_M tiles along
 //    M so the tiles an XCD runs together share operand panels in its L2.
-//  * Epilogues: plain bf16 / fp32 store (with a column split into two output
-//    buffers), activation (ReLU / GeLU) with the pre-activation stash, SwiGLU
-//    with gate and up accumulated in the same wave (the B tile interleaves the
-//    two weight shards), and the activation derivative that reads the stash.
+//  * Epilogues: plain bf16 / fp32 store (column split into two buffers),
+//    ReLU / GeLU with the pre-activation stash, SwiGLU with gate and up
+//    accumulated in the same wave (separate gate / up LDS regions), and the
+//    activation derivative reading the stash.
 #include "common.h"
 #include "gemm.h"
 
@@ -42,119 +49,142 @@ namespace tpmlp {
 constexpr int BK = 64;
 constexpr int NT = 256;
 constexpr int GROUP_M = 4;
+constexpr uint32_t OOB = 0xFFFFFFF0u;         // past the end of any accepted buffer
+constexpr int RSRC_FLAGS = 0x00020000;        // raw buffer, 32-bit data
 
-// Slot of a 16-byte chunk inside a 128-byte LDS row.  Depends on row mod 16
-// only, so fragment addresses of row blocks 16 apart differ by an immediate.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-__device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-__device__ __forceinline__ uint32_t w_of(const uint4& v, int q) {
-  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_FLAGS);
 }
-
-// Output element i (0..7) of an 8x8 bf16 transpose: the 8 k-values of column i.
-__device__ __forceinline__ uint4 transpose_col(const uint4 (&in)[8], int i) {
-  const int q = i >> 1;
-  uint4 o;
-  if (i & 1) {
-    o.x = pick_hi(w_of(in[0], q), w_of(in[1], q));
-    o.y = pick_hi(w_of(in[2], q), w_of(in[3], q));
-    o.z = pick_hi(w_of(in[4], q), w_of(in[5], q));
-    o.w = pick_hi(w_of(in[6], q), w_of(in[7], q));
-  } else {
-    o.x = pick_lo(w_of(in[0], q), w_of(in[1], q));
-    o.y = pick_lo(w_of(in[2], q), w_of(in[3], q));
-    o.z = pick_lo(w_of(in[4], q), w_of(in[5], q));
-    o.w = pick_lo(w_of(in[6], q), w_of(in[7], q));
-  }
-  return o;
+__device__ __forceinline__ void dma16(rsrc_t r, uint8_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+}
+// s_waitcnt with only the vector-memory counter constrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // ---------------------------------------------------------------------------
-// Operand tile loaders: HBM -> registers (load) and registers -> LDS (store).
-// ROWS is the tile extent along m (A) or n (B).
+// DMA of a k-contiguous operand tile: R rows x 64 k into [row][8 chunks].
+// One wave instruction fills 1 KiB = 8 rows; lane i of segment sg holds the
+// LDS chunk q = sg*64 + i: row q/8, slot q%8, logical chunk slot ^ (row&7).
 // ---------------------------------------------------------------------------
-
-// Operand stored [row][k], k contiguous; optionally the k range is the
-// concatenation of two buffers (k < ksplit from p0, the rest from p1 at
-// k - ksplit), both with leading dimension ld.
-template <int ROWS>
-struct LoadK {
-  static constexpr int NL = ROWS / 32;  // 16-byte chunks per thread
-  uint4 r[NL];
-  __device__ __forceinline__ void load(const uint16_t* p0, const uint16_t* p1, int64_t ld, int ksplit,
-                                       int rows, int K, int row0, int k0, int tid) {
-    const int c = tid & 7;
-    const int gk = k0 + c * 8;
-    const bool kok = gk < K;
-    const uint16_t* base = gk < ksplit ? p0 + gk : p1 + (gk - ksplit);
+template <int R>
+struct DmaK {
+  static constexpr int NI = R / 32;  // instructions per wave per tile
+  uint32_t rowbyte[NI];              // byte offset of the lane's row, or OOB
+  int kc[NI];                        // element offset of the lane's chunk in the tile
+  __device__ __forceinline__ void init(int row0, int rows, int64_t ld, int lane, int w) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int row = row0 + (tid >> 3) + 32 * i;
-      if (kok && row < rows)
-        r[i] = *reinterpret_cast<const uint4*>(base + (int64_t)row * ld);
-      else
-        r[i] = make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < NI; ++j) {
+      const int q = (w + 4 * j) * 64 + lane;
+      const int r = q >> 3;
+      const int chunk = (q & 7) ^ (r & 7);
+      const int grow = row0 + r;
+      rowbyte[j] = grow < rows ? (uint32_t)((int64_t)grow * ld * 2) : OOB;
+      kc[j] = chunk * 8;
     }
   }
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
-    const int c = tid & 7;
-    const int rr = tid >> 3;
-    uint8_t* p = lds + rr * 128 + ((c ^ swz(rr)) << 4);
+  // k range of this tile in buffer elements: [kbase, kbase + 64), valid below kend
+  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int kbase, int kend, int w) const {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4*>(p + i * 32 * 128) = r[i];
-  }
-};
-
-// Operand stored [k][col], col contiguous.  Loaded as 8 (k) x 8 (col) blocks;
-// block b: k-chunk kc = b % 8, col block cb = b / 8.  MAP = 0: tile column n
-// is buffer column col0 + n of p0.  MAP = 1 (SwiGLU up-projection B tile):
-// the tile's BN columns are, per half (one wave column), QW gate columns then
-// the QW up columns of the same features: n -> (w = n / (2QW), r = n % (2QW)),
-// buffer = r < QW ? p0 (gate) : p1 (up), column f0 + w*QW + r % QW.
-template <int ROWS, int MAP>
-struct LoadMN {
-  uint4 r[8];
-  bool active;
-  __device__ __forceinline__ void load(const uint16_t* p0, const uint16_t* p1, int64_t ld, int cols, int K,
-                                       int col0, int k0, int tid) {
-    active = tid < ROWS;
-    if (!active) return;
-    const int kc = tid & 7, cb = tid >> 3;
-    const int n = cb * 8;
-    const uint16_t* buf;
-    int col;
-    if constexpr (MAP == 0) {
-      buf = p0;
-      col = col0 + n;
-    } else {
-      constexpr int QW = ROWS / 4;
-      const int w = n / (2 * QW), rr = n % (2 * QW);
-      buf = rr < QW ? p0 : p1;
-      col = col0 + w * QW + (rr % QW);
-    }
-    const bool cok = col < cols;
-    const uint16_t* base = buf + col;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = k0 + kc * 8 + j;
-      if (cok && k < K)
-        r[j] = *reinterpret_cast<const uint4*>(base + (int64_t)k * ld);
-      else
-        r[j] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
-    if (!active) return;
-    const int kc = tid & 7, cb = tid >> 3;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = cb * 8 + i;
-      *reinterpret_cast<uint4*>(lds + row * 128 + ((kc ^ swz(row)) << 4)) = transpose_col(r, i);
+    for (int j = 0; j < NI; ++j) {
+      const int k = kbase + kc[j];
+      const uint32_t v = (rowbyte[j] != OOB && k < kend) ? rowbyte[j] + (uint32_t)k * 2u : OOB;
+      dma16(rs, region + (w + 4 * j) * 1024, v);
     }
   }
 };
+
+// ---------------------------------------------------------------------------
+// DMA of an m/n-contiguous operand tile: 64 k-rows x RW columns into
+// [k][RW/8 chunks]; chunk c of k-row r at slot c ^ 2(r&3).
+// ---------------------------------------------------------------------------
+template <int RW>
+struct DmaMN {
+  static constexpr int CPR = RW / 8;
+  static constexpr int NI = RW / 32;
+  uint32_t colbyte[NI];  // byte offset of the lane's column in a row, or OOB
+  int krow[NI];
+  __device__ __forceinline__ void init(int col0, int cols, int lane, int w) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int q = (w + 4 * j) * 64 + lane;
+      const int kr = q / CPR;
+      const int chunk = (q % CPR) ^ (2 * (kr & 3));
+      const int col = col0 + chunk * 8;
+      colbyte[j] = col < cols ? (uint32_t)col * 2u : OOB;
+      krow[j] = kr;
+    }
+  }
+  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int k0, int K, int64_t ld, int w) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int k = k0 + krow[j];
+      const uint32_t v = (colbyte[j] != OOB && k < K) ? (uint32_t)k * (uint32_t)(ld * 2) + colbyte[j] : OOB;
+      dma16(rs, region + (w + 4 * j) * 1024, v);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Fragment reads (16 rows/columns x 32 k of one MFMA operand, 8 bf16 per lane:
+// lane l holds index l%16, k = 8*(l/16) .. +7 of the k-step).
+// ---------------------------------------------------------------------------
+// k-contiguous region: byte offset of lane's fragment for block row base rb,
+// k-step s; block i adds i*2048.
+__device__ __forceinline__ int kfrag_off(int rb, int s, int lane) {
+  const int l16 = lane & 15, lq = lane >> 4;
+  return (rb + l16) * 128 + (((s * 4 + lq) ^ (l16 & 7)) << 4);
+}
+__device__ __forceinline__ bf16x8 ld_b128(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// m/n-contiguous region of width RW: per-lane k-row byte base and the column
+// part of block i (columns cb + 16 i .. +15).
+template <int RW>
+__device__ __forceinline__ int mn_kbase(int lane) {
+  const int g = lane >> 4, src = lane & 15;
+  return (8 * g + (src >> 2)) * (RW * 2);
+}
+__device__ __forceinline__ int mn_coloff(int cb, int i, int lane) {
+  const int src = lane & 15;
+  const int chunk = (cb + 16 * i + 4 * (src & 3)) >> 3;
+  return ((chunk ^ (2 * (src >> 2))) << 4) + (src & 1) * 8;
+}
+// The LDS transpose read is issued through inline asm: the intrinsic form
+// carries no alias information, so the compiler would wait for every
+// outstanding buffer-to-LDS load before each one, serialising the DMA latency
+// into every k-tile.  Its results are consumed only after settle() (below).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+template <int OFF>
+__device__ __forceinline__ v4i16 tr16(uint32_t addr) {
+  v4i16 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+template <int OFF0, int OFF1>
+__device__ __forceinline__ bf16x8 ld_tr2(uint32_t addr) {
+  const v4i16 lo = tr16<OFF0>(addr);
+  const v4i16 hi = tr16<OFF1>(addr);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// Wait for every outstanding LDS read and make the fragments depend on that
+// wait, so no consumer can be scheduled before the data has arrived.
+template <int N>
+__device__ __forceinline__ void settle(bf16x8 (&f)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[i]));
+}
 
 // ---------------------------------------------------------------------------
 // Block id -> tile: XCD-contiguous, then grouped along M.
@@ -179,32 +209,118 @@ gemm_kernel(const GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  constexpr int QW = BN / 4;  // SwiGLU: features per wave column
+  static_assert(BKD != 2 || (BN == 128 || BN == 256), "SwiGLU tile width");
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM;
-  // For the SwiGLU forward the tile covers BN/2 features (gate + up).
   const int n0 = (BKD == 2) ? tn * (BN / 2) : tn * BN;
 
-  using ALd = typename std::conditional<AK == 0, LoadK<BM>, LoadMN<BM, 0>>::type;
-  using BLd = typename std::conditional<BKD == 0, LoadK<BN>,
-              typename std::conditional<BKD == 1, LoadMN<BN, 0>, LoadMN<BN, 1>>::type>::type;
-  ALd la;
-  BLd lb;
+  // ---- buffer resources per k segment
+  rsrc_t ra0 = make_rsrc(g.a[0], g.a_bytes[0]);
+  rsrc_t rb0 = make_rsrc(g.b[0], g.b_bytes[0]);
+  rsrc_t ra1 = ra0, rb1 = rb0;
+  if (g.nseg > 1 || BKD == 2) {
+    ra1 = make_rsrc(g.a[1], g.a_bytes[1]);
+    rb1 = make_rsrc(g.b[1], g.b_bytes[1]);
+  }
 
-  auto load = [&](int k0) {
-    if constexpr (AK == 0) la.load(g.a0, g.a1, g.lda, g.a_ksplit, g.M, g.K, m0, k0, tid);
-    else la.load(g.a0, g.a1, g.lda, g.M, g.K, m0, k0, tid);
-    if constexpr (BKD == 0) lb.load(g.b0, g.b1, g.ldb, g.b_ksplit, g.N, g.K, n0, k0, tid);
-    else lb.load(g.b0, g.b1, g.ldb, g.N, g.K, n0, k0, tid);
+  // ---- DMA descriptors
+  typename std::conditional<AK == 0, DmaK<BM>, DmaMN<BM>>::type da;
+  typename std::conditional<BKD == 0, DmaK<BN>, DmaMN<(BKD == 2 ? BN / 2 : BN)>>::type db, dbu;
+  if constexpr (AK == 0) da.init(m0, g.M, g.lda, lane, w);
+  else da.init(m0, g.M, lane, w);
+  if constexpr (BKD == 0) db.init(n0, g.N, g.ldb, lane, w);
+  else db.init(n0, g.N, lane, w);
+  if constexpr (BKD == 2) dbu = db;  // gate and up shards share columns and layout
+
+  const int nk0 = (g.K[0] + BK - 1) / BK;
+  const int nk = nk0 + (g.nseg > 1 ? (g.K[1] + BK - 1) / BK : 0);
+
+  auto issue_tile = [&](int t, uint8_t* st) {
+    const bool s1 = t >= nk0;
+    const int k0 = (s1 ? t - nk0 : t) * BK;
+    const int Ks = s1 ? g.K[1] : g.K[0];
+    const rsrc_t ra = s1 ? ra1 : ra0;
+    const rsrc_t rb = s1 ? rb1 : rb0;
+    if constexpr (AK == 0) {
+      const int ko = s1 ? g.a_koff[1] : g.a_koff[0];
+      da.issue(ra, st, ko + k0, ko + Ks, w);
+    } else {
+      da.issue(ra, st, k0, Ks, g.lda, w);
+    }
+    if constexpr (BKD == 0) db.issue(rb, st + A_BYTES, k0, Ks, w);
+    else if constexpr (BKD == 1) db.issue(rb, st + A_BYTES, k0, Ks, g.ldb, w);
+    else {
+      db.issue(rb0, st + A_BYTES, k0, Ks, g.ldb, w);
+      dbu.issue(rb1, st + A_BYTES + B_BYTES / 2, k0, Ks, g.ldb, w);
+    }
   };
-  auto store = [&](int stage) {
-    la.store(smem + stage * STAGE, tid);
-    lb.store(smem + stage * STAGE + A_BYTES, tid);
+  constexpr int NI_TILE = (BM + BN) / 32;  // DMA instructions per wave per tile
+
+  // ---- fragment addressing (loop invariant)
+  int a_koff_s[2], b_koff_s[2];
+  uint32_t a_col[AK == 1 ? TM : 1], b_col[BKD != 0 ? TN : 1];
+  uint32_t a_kb = 0, b_kb = 0;
+  if constexpr (AK == 0) {
+    a_koff_s[0] = kfrag_off(wm * WM, 0, lane);
+    a_koff_s[1] = kfrag_off(wm * WM, 1, lane);
+  } else {
+    a_kb = mn_kbase<BM>(lane);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a_col[i] = mn_coloff(wm * WM, i, lane);
+  }
+  if constexpr (BKD == 0) {
+    b_koff_s[0] = kfrag_off(wn * WN, 0, lane);
+    b_koff_s[1] = kfrag_off(wn * WN, 1, lane);
+  } else if constexpr (BKD == 1) {
+    b_kb = mn_kbase<BN>(lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b_col[j] = mn_coloff(wn * WN, j, lane);
+  } else {
+    b_kb = mn_kbase<BN / 2>(lane);
+#pragma unroll
+    for (int j = 0; j < TN / 2; ++j) {
+      b_col[j] = mn_coloff(wn * QW, j, lane);
+      b_col[j + TN / 2] = b_col[j] + B_BYTES / 2;  // same columns in the up region
+    }
+  }
+
+  // fragments of k-step S of the tile in stage st
+  auto read_frags = [&](auto S_, const uint8_t* st, bf16x8 (&af)[TM], bf16x8 (&bfv)[TN]) {
+    constexpr int S = decltype(S_)::value;
+    if constexpr (AK == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = ld_b128(st + a_koff_s[S] + i * 2048);
+    } else {
+      constexpr int RS = BM * 2;  // k-row stride
+      const uint32_t base = lds_addr(st) + a_kb;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(base + a_col[i]);
+    }
+    const uint8_t* sb = st + A_BYTES;
+    if constexpr (BKD == 0) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfv[j] = ld_b128(sb + b_koff_s[S] + j * 2048);
+    } else {
+      constexpr int RS = (BKD == 2 ? BN / 2 : BN) * 2;
+      const uint32_t base = lds_addr(sb) + b_kb;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfv[j] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(base + b_col[j]);
+    }
   };
+  auto settle_frags = [&](bf16x8 (&af)[TM], bf16x8 (&bfv)[TN]) {
+    if constexpr (AK == 1) settle(af);
+    if constexpr (BKD != 0) settle(bfv);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -212,43 +328,49 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int l16 = lane & 15, lq = lane >> 4;
-  const int a_row = wm * WM + l16;
-  const int b_row = wn * WN + l16;
-  const int sw = swz(l16);
-
-  const int nk = (g.K + BK - 1) / BK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * BK);
-    const uint8_t* As = smem + cur * STAGE;
-    const uint8_t* Bs = As + A_BYTES;
+  auto mfma_all = [&](const bf16x8 (&af)[TM], const bf16x8 (&bfv)[TN]) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int slot = ((s * 4 + lq) ^ sw) << 4;
-      bf16x8 af[TM], bfv[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + (a_row + i * 16) * 128 + slot);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bfv[j] = *reinterpret_cast<const bf16x8*>(Bs + (b_row + j * 16) * 128 + slot);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfv[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store(cur ^ 1);
-    __syncthreads();
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfv[j], af[i], acc[i][j], 0, 0, 0);
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight, wait for tile 0
+  issue_tile(0, stage0);
+  if (nk > 1) {
+    issue_tile(1, stage1);
+    wait_vmcnt<NI_TILE>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+  read_frags(S0{}, stage0, a0, b0);
+
+  for (int t = 0; t < nk; ++t) {
+    uint8_t* cur = (t & 1) ? stage1 : stage0;
+    uint8_t* nxt = (t & 1) ? stage0 : stage1;
+    settle_frags(a0, b0);  // read during the previous step-1 MFMAs: free
+    read_frags(S1{}, cur, a1, b1);
+    mfma_all(a0, b0);
+    // keep the phases in this order (the scheduler would otherwise hoist the
+    // DMA wait above most of the step-0 MFMAs and sink the DMA issue below
+    // the step-1 MFMAs)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();  // this wave's DMA of tile t+1 has landed
+    __syncthreads();  // everyone's has; everyone is done reading stage cur
+    settle_frags(a1, b1);
+    if (t + 2 < nk) issue_tile(t + 2, cur);
+    if (t + 1 < nk) read_frags(S0{}, nxt, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_all(a1, b1);
   }
 
   // ------------------------------------------------------------------ epilogue
   // Lane holds C[m][n .. n+3] of block (i, j) with m = m0 + wm*WM + i*16 + l16,
-  // n = n0 + wn*WN + j*16 + 4*lq (SwiGLU: feature f = n0 + wn*WN/2 + j*16 + 4*lq).
+  // n = n0 + wn*WN + j*16 + 4*lq (SwiGLU: feature f = n0 + wn*QW + j*16 + 4*lq).
+  const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + wm * WM + i * 16 + l16;
@@ -291,7 +413,7 @@ gemm_kernel(const GemmArgs g) {
     } else if constexpr (EPI == EPI_SWIGLU_FWD) {
 #pragma unroll
       for (int j = 0; j < TN / 2; ++j) {
-        const int f = n0 + wn * (WN / 2) + j * 16 + 4 * lq;
+        const int f = n0 + wn * QW + j * 16 + 4 * lq;
         if (f < g.N) {
           const int64_t off = (int64_t)m * g.ldc + f;
           const f32x4 gt = acc[i][j], up = acc[i][j + TN / 2];
@@ -312,7 +434,7 @@ gemm_kernel(const GemmArgs g) {
         const int n = n0 + wn * WN + j * 16 + 4 * lq;
         if (n < g.N) {
           const int64_t off = (int64_t)m * g.ldc + n;
-          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.e0) + off);
+          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.e0) + (int64_t)m * g.lde + n);
           const float uu[4] = {bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y)};
           float d[4];
 #pragma unroll
@@ -353,18 +475,19 @@ struct TileCfg {
   int bm, bn;
 };
 
-// Pick the block tile that minimises (waves of 256 blocks) x (cost per tile),
-// cost per tile ~ bm*bn / efficiency.  Larger tiles re-read less from L2 and
-// LDS per flop; the wave count captures quantisation on 256 CUs.
-TileCfg choose_tile(int M, int N_tiles_cols, bool swiglu_fwd, int num_cu) {
+// Pick the block tile that minimises (waves of num_cu blocks) x (cost per
+// tile), cost per tile ~ bm*bn / efficiency.  Larger tiles re-read less from
+// L2 and LDS per flop; the wave count captures quantisation on the CUs.
+TileCfg choose_tile(int M, int N_cols, bool swiglu_fwd, int num_cu) {
   static const TileCfg cands[] = {{256, 256}, {256, 192}, {192, 256}, {256, 128}, {128, 256}, {128, 128}};
   static const double eff[] = {1.0, 0.97, 0.97, 0.90, 0.90, 0.75};
   double best = 1e300;
   TileCfg bc = {256, 256};
   for (int c = 0; c < 6; ++c) {
     const int bm = cands[c].bm, bn = cands[c].bn;
+    if (swiglu_fwd && bn == 192) continue;
     const int cols_per_tile = swiglu_fwd ? bn / 2 : bn;
-    const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N_tiles_cols + cols_per_tile - 1) / cols_per_tile);
+    const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N_cols + cols_per_tile - 1) / cols_per_tile);
     const int64_t waves = (tiles + num_cu - 1) / num_cu;
     const double cost = (double)waves * bm * bn / eff[c];
     if (cost < best * 0.999) {
@@ -390,7 +513,9 @@ hipError_t launch_cfg(GemmArgs g, hipStream_t st) {
 template <int AK, int BKD, int EPI, int ACT>
 hipError_t launch_any(const GemmArgs& g, TileCfg t, hipStream_t st) {
   if (t.bm == 256 && t.bn == 256) return launch_cfg<256, 256, AK, BKD, EPI, ACT>(g, st);
-  if (t.bm == 256 && t.bn == 192) return launch_cfg<256, 192, AK, BKD, EPI, ACT>(g, st);
+  if constexpr (BKD != 2) {
+    if (t.bm == 256 && t.bn == 192) return launch_cfg<256, 192, AK, BKD, EPI, ACT>(g, st);
+  }
   if (t.bm == 192 && t.bn == 256) return launch_cfg<192, 256, AK, BKD, EPI, ACT>(g, st);
   if (t.bm == 256 && t.bn == 128) return launch_cfg<256, 128, AK, BKD, EPI, ACT>(g, st);
   if (t.bm == 128 && t.bn == 256) return launch_cfg<128, 256, AK, BKD, EPI, ACT>(g, st);

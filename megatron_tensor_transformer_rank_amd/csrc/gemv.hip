@@ -1,19 +1,27 @@
-// Decode path (one token): split-K GEMV for gfx950, HBM bound.
+// Decode path (one token): split-K GEMVs for gfx950, HBM bound.
 //
 // With one token the up-projection is x @ [Wg_i, W1_i] and the
 // down-projection A_i @ W2_i: each weight byte is used exactly once, so the
-// kernels are sized to stream the shards from HBM at full rate ("02 -- Tensor
+// kernels are built to stream the shards from HBM at full rate ("02 -- Tensor
 // Parallelism": decode is memory-bandwidth bound work that TP splits across
 // HBMs).  No MFMA: every lane owns 8 adjacent output columns, reads 16 bytes
 // of a weight row per load (a wave covers 1 KiB of a row, fully coalesced),
-// and accumulates in float32 registers.
+// with non-temporal loads (streamed data is not kept in the caches), and
+// accumulates in float32 registers.
 //
-// Grid = strips (512 columns) x matrices x k-splits.  A block's 4 waves take
-// interleaved rows of its k range; their sums meet in LDS, the block writes
-// one float32 partial row to the workspace, and the last block of a strip to
-// finish (device-scope counter, fenced) adds the k-split partials in fixed
-// order, applies the epilogue and resets the counter for the next call.  The
-// result is deterministic; nothing spins.
+// Three launches, no cross-block synchronisation inside a kernel (an
+// agent-scope fence per block costs more than the whole stream):
+//   1. up:    blocks = 512-column strips x matrices x k-splits; a block's 4
+//             waves take interleaved rows of its k range, meet in LDS and write
+//             one float32 partial row per (k-split, matrix).
+//   2. down:  same streaming over W2_i; its prologue adds the up-projection's
+//             k-split partials for the block's rows in fixed order, applies the
+//             activation and rounds A to bf16 (the value the MFMA path would
+//             read back), while the block's first weight loads are in flight.
+//             Blocks of the first column strip also write A_i and the stash.
+//   3. final: adds the down-projection's k-split partials in fixed order and
+//             rounds Y_i to bf16.
+// The result is deterministic.
 #include "common.h"
 #include "gemv.h"
 
@@ -21,16 +29,25 @@ namespace tpmlp {
 
 constexpr int GV_THREADS = 256;
 constexpr int GV_STRIP = 512;  // columns per block (64 lanes x 8)
-constexpr int GV_UNROLL = 8;   // rows in flight per wave per iteration
+constexpr int GV_UNROLL = 16;  // rows in flight per wave
+constexpr int GV_STEP = 4 * GV_UNROLL;
 
-template <int NMAT, int EPI, int ACT>
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// PRO = 0: x is the bf16 input vector.  PRO = 1: x[k] = act(sum of the
+// up-projection partials pg[q][*][k]) rounded to bf16 (ACT selects ReLU /
+// GeLU over one matrix or SwiGLU over gate and up).
+template <int NMAT, int PRO, int ACT>
 __global__ void __launch_bounds__(GV_THREADS)
-gemv_splitk(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-            int K, int ncols, int KS, int KR, float* __restrict__ part, unsigned* __restrict__ counters,
-            uint16_t* __restrict__ out, uint16_t* __restrict__ st0, uint16_t* __restrict__ st1) {
+gemv_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+             int K, int ncols, int KR, float* __restrict__ part, const float* __restrict__ pg, int ks_up,
+             uint16_t* __restrict__ a_out, uint16_t* __restrict__ st0, uint16_t* __restrict__ st1) {
   __shared__ float xs[GV_MAX_KR];
   __shared__ float red[4][GV_STRIP];
-  __shared__ int is_last;
 
   const int S = (ncols + GV_STRIP - 1) / GV_STRIP;
   const int b = blockIdx.x;
@@ -39,122 +56,152 @@ gemv_splitk(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, con
   const int mat = rest % NMAT;
   const int ks = rest / NMAT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-
   const int kb = ks * KR;
   const int ke = min(K, kb + KR);
-  for (int i = tid; i < ke - kb; i += GV_THREADS) xs[i] = bf16_to_f32(x[kb + i]);
-  __syncthreads();
 
   const uint16_t* Wm = (NMAT == 2 && mat == 1) ? W1 : W0;
   const int col = s * GV_STRIP + lane * 8;
   const bool cok = col < ncols;
+  const uint16_t* base = Wm + col;
+
+  // first batch of weight loads before x is staged: they do not depend on it
+  u32x4 v[GV_UNROLL];
+  int k = kb + w;
+#pragma unroll
+  for (int u = 0; u < GV_UNROLL; ++u) {
+    const int kk = k + 4 * u;
+    v[u] = (cok && kk < ke) ? ld_stream(base + (int64_t)kk * ncols) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  if constexpr (PRO == 0) {
+    for (int i = tid; i < ke - kb; i += GV_THREADS) xs[i] = bf16_to_f32(x[kb + i]);
+  } else {
+    constexpr int NU = ACT == ACT_SWIGLU ? 2 : 1;
+    for (int i = tid; i < ke - kb; i += GV_THREADS) {
+      const int kk = kb + i;
+      float sum[NU];
+#pragma unroll
+      for (int m = 0; m < NU; ++m) sum[m] = 0.f;
+      for (int q = 0; q < ks_up; ++q) {
+#pragma unroll
+        for (int m = 0; m < NU; ++m) sum[m] += pg[((int64_t)q * NU + m) * K + kk];
+      }
+      float a;
+      if constexpr (ACT == ACT_SWIGLU) a = swiglu_f(sum[0], sum[1]);
+      else a = act_f<ACT>(sum[0]);
+      const uint32_t ab = f32_to_bf16_rne(a);
+      xs[i] = __uint_as_float(ab << 16);
+      if (s == 0) {
+        a_out[kk] = (uint16_t)ab;
+        if (st0) st0[kk] = (uint16_t)f32_to_bf16_rne(sum[0]);
+        if (ACT == ACT_SWIGLU && st1) st1[kk] = (uint16_t)f32_to_bf16_rne(sum[NU - 1]);
+      }
+    }
+  }
+  __syncthreads();
+
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (cok) {
-    const uint16_t* base = Wm + col;
-    for (int k = kb + w; k < ke; k += 4 * GV_UNROLL) {
-      uint4 v[GV_UNROLL];
+  for (; k < ke; k += GV_STEP) {
+    u32x4 cur[GV_UNROLL];
+#pragma unroll
+    for (int u = 0; u < GV_UNROLL; ++u) cur[u] = v[u];
+    if (k + GV_STEP < ke) {
 #pragma unroll
       for (int u = 0; u < GV_UNROLL; ++u) {
-        const int kk = k + 4 * u;
-        v[u] = kk < ke ? *reinterpret_cast<const uint4*>(base + (int64_t)kk * ncols) : make_uint4(0, 0, 0, 0);
+        const int kk = k + GV_STEP + 4 * u;
+        v[u] = (cok && kk < ke) ? ld_stream(base + (int64_t)kk * ncols) : u32x4{0u, 0u, 0u, 0u};
       }
+    }
 #pragma unroll
-      for (int u = 0; u < GV_UNROLL; ++u) {
-        const int kk = k + 4 * u;
-        const float xv = kk < ke ? xs[kk - kb] : 0.f;
-        acc[0] += xv * bf16lo(v[u].x);
-        acc[1] += xv * bf16hi(v[u].x);
-        acc[2] += xv * bf16lo(v[u].y);
-        acc[3] += xv * bf16hi(v[u].y);
-        acc[4] += xv * bf16lo(v[u].z);
-        acc[5] += xv * bf16hi(v[u].z);
-        acc[6] += xv * bf16lo(v[u].w);
-        acc[7] += xv * bf16hi(v[u].w);
-      }
+    for (int u = 0; u < GV_UNROLL; ++u) {
+      const int kk = k + 4 * u;
+      const float xv = kk < ke ? xs[kk - kb] : 0.f;
+      acc[0] += xv * bf16lo(cur[u].x);
+      acc[1] += xv * bf16hi(cur[u].x);
+      acc[2] += xv * bf16lo(cur[u].y);
+      acc[3] += xv * bf16hi(cur[u].y);
+      acc[4] += xv * bf16lo(cur[u].z);
+      acc[5] += xv * bf16hi(cur[u].z);
+      acc[6] += xv * bf16lo(cur[u].w);
+      acc[7] += xv * bf16hi(cur[u].w);
     }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[w][lane * 8 + e] = acc[e];
   __syncthreads();
 
-  // block partial: 2 columns per thread, fixed wave order
-  float* prow = part + ((int64_t)ks * NMAT + mat) * ncols;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = tid * 2 + h;
-    const int gc = s * GV_STRIP + c;
-    if (gc < ncols) prow[gc] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+  // block partial row: 2 columns per thread, waves added in fixed order
+  const int c = tid * 2;
+  const int gc = s * GV_STRIP + c;
+  if (gc < ncols) {
+    float* prow = part + ((int64_t)ks * NMAT + mat) * ncols + gc;
+    *reinterpret_cast<float2*>(prow) =
+        make_float2(((red[0][c] + red[1][c]) + red[2][c]) + red[3][c],
+                    ((red[0][c + 1] + red[1][c + 1]) + red[2][c + 1]) + red[3][c + 1]);
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned done = atomicAdd(&counters[s], 1u);
-    is_last = done == (unsigned)(KS * NMAT - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = tid * 2 + h;
-    const int gc = s * GV_STRIP + c;
-    if (gc >= ncols) continue;
-    float sum[NMAT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      float a = 0.f;
-      for (int q = 0; q < KS; ++q) a += __builtin_nontemporal_load(part + ((int64_t)q * NMAT + m) * ncols + gc);
-      sum[m] = a;
-    }
-    if constexpr (EPI == GV_EPI_STORE) {
-      out[gc] = (uint16_t)f32_to_bf16_rne(sum[0]);
-    } else if constexpr (EPI == GV_EPI_ACT) {
-      out[gc] = (uint16_t)f32_to_bf16_rne(act_f<ACT>(sum[0]));
-      if (st0) st0[gc] = (uint16_t)f32_to_bf16_rne(sum[0]);
-    } else {  // SwiGLU: matrix 0 = gate, matrix 1 = up
-      out[gc] = (uint16_t)f32_to_bf16_rne(swiglu_f(sum[0], sum[NMAT - 1]));
-      if (st0) st0[gc] = (uint16_t)f32_to_bf16_rne(sum[0]);
-      if (st1) st1[gc] = (uint16_t)f32_to_bf16_rne(sum[NMAT - 1]);
-    }
-  }
-  if (tid == 0) counters[s] = 0u;
 }
 
-GemvPlan gemv_plan(int K, int ncols, int nmat, int num_cu) {
+// out[c] = bf16(sum_q part[q][c]), q in order; 4 columns per thread.
+__global__ void __launch_bounds__(GV_THREADS)
+gemv_final(const float* __restrict__ part, int ks, int ncols, uint16_t* __restrict__ out) {
+  const int c = (blockIdx.x * GV_THREADS + threadIdx.x) * 4;
+  if (c >= ncols) return;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int TU = 8;
+  for (int q = 0; q < ks; q += TU) {
+    float4 t[TU];
+#pragma unroll
+    for (int u = 0; u < TU; ++u)
+      t[u] = q + u < ks ? *reinterpret_cast<const float4*>(part + (int64_t)(q + u) * ncols + c)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      a.x += t[u].x; a.y += t[u].y; a.z += t[u].z; a.w += t[u].w;
+    }
+  }
+  *reinterpret_cast<uint2*>(out + c) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+}
+
+GemvPlan gemv_plan(int K, int ncols, int nmat, int target_blocks) {
   GemvPlan p;
   p.strips = (ncols + GV_STRIP - 1) / GV_STRIP;
-  // aim for ~4 blocks per CU, at least 64 rows per block, KR <= GV_MAX_KR
-  const int target = 4 * num_cu;
-  int ks = (target + p.strips * nmat - 1) / (p.strips * nmat);
-  ks = max(1, min(ks, (K + 63) / 64));
+  int ks = (target_blocks + p.strips * nmat - 1) / (p.strips * nmat);
+  ks = max(1, min(ks, (K + GV_STEP - 1) / GV_STEP));
   int kr = (K + ks - 1) / ks;
-  kr = ((kr + 3) / 4) * 4;
+  kr = ((kr + GV_STEP - 1) / GV_STEP) * GV_STEP;  // whole unrolled steps per wave
   if (kr > GV_MAX_KR) kr = GV_MAX_KR;
-  ks = (K + kr - 1) / kr;
-  p.ks = ks;
+  p.ks = (K + kr - 1) / kr;
   p.kr = kr;
-  p.part_floats = (size_t)ks * nmat * ncols;
+  p.part_floats = (size_t)p.ks * nmat * ncols;
   return p;
 }
 
-hipError_t gemv_launch(int epi, int act, const uint16_t* x, const uint16_t* W0, const uint16_t* W1, int K,
-                       int ncols, const GemvPlan& p, float* part, unsigned* counters, uint16_t* out,
-                       uint16_t* st0, uint16_t* st1, hipStream_t st) {
-  const int nmat = epi == GV_EPI_SWIGLU ? 2 : 1;
-  const dim3 grid((unsigned)(p.strips * nmat * p.ks)), block(GV_THREADS);
-  if (epi == GV_EPI_SWIGLU)
-    hipLaunchKernelGGL((gemv_splitk<2, GV_EPI_SWIGLU, ACT_SWIGLU>), grid, block, 0, st, x, W0, W1, K, ncols, p.ks,
-                       p.kr, part, counters, out, st0, st1);
-  else if (epi == GV_EPI_ACT && act == ACT_RELU)
-    hipLaunchKernelGGL((gemv_splitk<1, GV_EPI_ACT, ACT_RELU>), grid, block, 0, st, x, W0, W1, K, ncols, p.ks, p.kr,
-                       part, counters, out, st0, st1);
-  else if (epi == GV_EPI_ACT)
-    hipLaunchKernelGGL((gemv_splitk<1, GV_EPI_ACT, ACT_GELU>), grid, block, 0, st, x, W0, W1, K, ncols, p.ks, p.kr,
-                       part, counters, out, st0, st1);
+hipError_t decode_launch(int act, const uint16_t* x, const uint16_t* Wa, const uint16_t* Wb, const uint16_t* W2,
+                         int h, int Fi, const GemvPlan& up, const GemvPlan& down, float* part_up, float* part_down,
+                         uint16_t* A, uint16_t* st0, uint16_t* st1, uint16_t* Y, hipStream_t st) {
+  const dim3 blk(GV_THREADS);
+  if (act == ACT_SWIGLU) {
+    hipLaunchKernelGGL((gemv_partial<2, 0, 0>), dim3(up.strips * 2 * up.ks), blk, 0, st, x, Wa, Wb, h, Fi, up.kr,
+                       part_up, nullptr, 0, nullptr, nullptr, nullptr);
+  } else {
+    hipLaunchKernelGGL((gemv_partial<1, 0, 0>), dim3(up.strips * up.ks), blk, 0, st, x, Wa, Wa, h, Fi, up.kr,
+                       part_up, nullptr, 0, nullptr, nullptr, nullptr);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 gd(down.strips * down.ks);
+  if (act == ACT_SWIGLU)
+    hipLaunchKernelGGL((gemv_partial<1, 1, ACT_SWIGLU>), gd, blk, 0, st, nullptr, W2, W2, Fi, h, down.kr, part_down,
+                       part_up, up.ks, A, st0, st1);
+  else if (act == ACT_RELU)
+    hipLaunchKernelGGL((gemv_partial<1, 1, ACT_RELU>), gd, blk, 0, st, nullptr, W2, W2, Fi, h, down.kr, part_down,
+                       part_up, up.ks, A, st0, nullptr);
   else
-    hipLaunchKernelGGL((gemv_splitk<1, GV_EPI_STORE, 0>), grid, block, 0, st, x, W0, W1, K, ncols, p.ks, p.kr, part,
-                       counters, out, st0, st1);
+    hipLaunchKernelGGL((gemv_partial<1, 1, ACT_GELU>), gd, blk, 0, st, nullptr, W2, W2, Fi, h, down.kr, part_down,
+                       part_up, up.ks, A, st0, nullptr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemv_final, dim3((h / 4 + GV_THREADS - 1) / GV_THREADS), blk, 0, st, part_down, down.ks, h, Y);
   return hipGetLastError();
 }
 
