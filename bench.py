@@ -235,9 +235,11 @@ def bench_decode(args, w, B, I, torch, np, to_dev):
             "us_per_token_warm_cache": round(us_warm, 3)}
 
 
-def cpu_baseline(w, rows, I):
-    """The fp64 oracle (as it stands) on a bounded sample: `rows` token rows of
-    rank 0's shard, forward + backward, on the host's BLAS threads."""
+def cpu_baseline(w, rows, I, target_s=10.0, cap_s=30.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload:
+    chunks of `rows` token rows of rank 0's shard, forward + backward, on the
+    host's BLAS threads, repeated (wrapping over the tokens) until about
+    target_s seconds of CPU work have run."""
     import numpy as np
 
     import oracle
@@ -249,21 +251,28 @@ def cpu_baseline(w, rows, I):
     rows = min(rows, w.N)
     f = oracle.bf16_bits_to_f64
     sw = w.act == "swiglu"
-    X = f(I.gen_x(w.wid, w.N, w.h)[:rows])
-    dY = f(I.gen_dy(w.wid, w.N, w.h)[:rows])
+    Xall = I.gen_x(w.wid, w.N, w.h)
+    dYall = I.gen_dy(w.wid, w.N, w.h)
     W1 = f(I.gen_w_up_shard(w.wid, w.h, w.Fi, 0))
     W2 = f(I.gen_w_down_shard(w.wid, w.h, w.Fi, 0))
     Wg = f(I.gen_w_gate_shard(w.wid, w.h, w.Fi, 0)) if sw else None
-    log(f"[bench] cpu baseline: oracle on {rows} token rows, {cores} BLAS threads")
-    t0 = time.perf_counter()
-    oracle.shard_forward(w.act, X, W1, W2, Wg)
-    oracle.shard_backward(w.act, X, W1, W2, dY, Wg)
-    dt = time.perf_counter() - t0
-    fl = 6 * rows * w.h * w.Fi * (w.g + 1)
+    log(f"[bench] cpu baseline: oracle on chunks of {rows} token rows, {cores} BLAS threads")
+    done_rows, dt, r0 = 0, 0.0, 0
+    while dt < target_s and dt < cap_s:
+        sl = slice(r0, r0 + rows)
+        X, dY = f(Xall[sl]), f(dYall[sl])
+        t0 = time.perf_counter()
+        oracle.shard_forward(w.act, X, W1, W2, Wg)
+        oracle.shard_backward(w.act, X, W1, W2, dY, Wg)
+        dt += time.perf_counter() - t0
+        done_rows += X.shape[0]
+        r0 = (r0 + rows) % w.N
+    fl = 6 * done_rows * w.h * w.Fi * (w.g + 1)
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 3),
-            "sample": f"{rows} of {w.N} token rows of rank 0's shard of {w.name}, forward + backward "
-                      f"(algorithmic FLOPs {fl:.3e}), numpy float64 on the host BLAS"}
+            "sample": f"{done_rows} token rows (chunks of {rows}, wrapping over the {w.N}) of rank 0's shard "
+                      f"of {w.name}, forward + backward, {fl:.3e} algorithmic FLOPs; numpy float64 on the "
+                      f"host BLAS; GPU/CPU ratio = value / this value"}
 
 
 if __name__ == "__main__":

@@ -78,7 +78,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int R>
 struct DmaK {
   static constexpr int NI = R / 32;  // instructions per wave per tile
-  uint32_t rowbyte[NI];              // byte offset of the lane's row, or OOB
+  uint32_t voff[NI];                 // row*ld*2 + chunk*16 (bytes from the tile's k0), or OOB
   int kc[NI];                        // element offset of the lane's chunk in the tile
   __device__ __forceinline__ void init(int row0, int rows, int64_t ld, int lane, int w) {
 #pragma unroll
@@ -87,18 +87,15 @@ struct DmaK {
       const int r = q >> 3;
       const int chunk = (q & 7) ^ (r & 7);
       const int grow = row0 + r;
-      rowbyte[j] = grow < rows ? (uint32_t)((int64_t)grow * ld * 2) : OOB;
       kc[j] = chunk * 8;
+      voff[j] = grow < rows ? (uint32_t)((int64_t)grow * ld * 2) + (uint32_t)kc[j] * 2u : OOB;
     }
   }
-  // k range of this tile in buffer elements: [kbase, kbase + 64), valid below kend
-  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int kbase, int kend, int w) const {
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int k = kbase + kc[j];
-      const uint32_t v = (rowbyte[j] != OOB && k < kend) ? rowbyte[j] + (uint32_t)k * 2u : OOB;
-      dma16(rs, region + (w + 4 * j) * 1024, v);
-    }
+  // instruction J of a tile; rs addresses the operand from the tile's first
+  // k; chunks at or past kvalid (elements from the tile's first k) read zeros
+  template <int J>
+  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int kvalid, int w) const {
+    dma16(rs, region + (w + 4 * J) * 1024, kc[J] < kvalid ? voff[J] : OOB);
   }
 };
 
@@ -110,26 +107,22 @@ template <int RW>
 struct DmaMN {
   static constexpr int CPR = RW / 8;
   static constexpr int NI = RW / 32;
-  uint32_t colbyte[NI];  // byte offset of the lane's column in a row, or OOB
-  int krow[NI];
-  __device__ __forceinline__ void init(int col0, int cols, int lane, int w) {
+  uint32_t voff[NI];  // krow*ld*2 + col*2 (bytes from the tile's first k row), or OOB
+  __device__ __forceinline__ void init(int col0, int cols, int64_t ld, int lane, int w) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int q = (w + 4 * j) * 64 + lane;
       const int kr = q / CPR;
       const int chunk = (q % CPR) ^ (2 * (kr & 3));
       const int col = col0 + chunk * 8;
-      colbyte[j] = col < cols ? (uint32_t)col * 2u : OOB;
-      krow[j] = kr;
+      voff[j] = col < cols ? (uint32_t)((int64_t)kr * ld * 2) + (uint32_t)col * 2u : OOB;
     }
   }
-  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int k0, int K, int64_t ld, int w) const {
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int k = k0 + krow[j];
-      const uint32_t v = (colbyte[j] != OOB && k < K) ? (uint32_t)k * (uint32_t)(ld * 2) + colbyte[j] : OOB;
-      dma16(rs, region + (w + 4 * j) * 1024, v);
-    }
+  // instruction J of a tile; rs addresses the operand from the tile's first k
+  // row and ends with the operand, so k rows past the end read zeros
+  template <int J>
+  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int w) const {
+    dma16(rs, region + (w + 4 * J) * 1024, voff[J]);
   }
 };
 
@@ -143,7 +136,6 @@ __device__ __forceinline__ int kfrag_off(int rb, int s, int lane) {
   const int l16 = lane & 15, lq = lane >> 4;
   return (rb + l16) * 128 + (((s * 4 + lq) ^ (l16 & 7)) << 4);
 }
-__device__ __forceinline__ bf16x8 ld_b128(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // m/n-contiguous region of width RW: per-lane k-row byte base and the column
 // part of block i (columns cb + 16 i .. +15).
@@ -157,12 +149,21 @@ __device__ __forceinline__ int mn_coloff(int cb, int i, int lane) {
   const int chunk = (cb + 16 * i + 4 * (src & 3)) >> 3;
   return ((chunk ^ (2 * (src >> 2))) << 4) + (src & 1) * 8;
 }
-// The LDS transpose read is issued through inline asm: the intrinsic form
-// carries no alias information, so the compiler would wait for every
-// outstanding buffer-to-LDS load before each one, serialising the DMA latency
-// into every k-tile.  Its results are consumed only after settle() (below).
+// The k loop is hand-scheduled: LDS reads and MFMAs are volatile inline asm,
+// so they issue in source order, interleaved one memory operation per MFMA.
+// (The compiler's own schedule issued the next tile's DMA and fragment reads
+// in a block between the barrier and the MFMAs, idling the MFMA pipe, and the
+// intrinsic form of the transpose read carries no alias information, which
+// makes the compiler wait for all in-flight buffer-to-LDS loads before it.)
+// LDS read results are consumed only after an explicit lgkmcnt(0) wait.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+template <int OFF>
+__device__ __forceinline__ bf16x8 ld_b128(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
 }
 template <int OFF>
 __device__ __forceinline__ v4i16 tr16(uint32_t addr) {
@@ -178,13 +179,17 @@ __device__ __forceinline__ bf16x8 ld_tr2(uint32_t addr) {
   const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
-// Wait for every outstanding LDS read and make the fragments depend on that
-// wait, so no consumer can be scheduled before the data has arrived.
-template <int N>
-__device__ __forceinline__ void settle(bf16x8 (&f)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[i]));
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
 }
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
 
 // ---------------------------------------------------------------------------
 // Block id -> tile: XCD-contiguous, then grouped along M.
@@ -222,50 +227,84 @@ gemm_kernel(const GemmArgs g) {
   const int m0 = tm * BM;
   const int n0 = (BKD == 2) ? tn * (BN / 2) : tn * BN;
 
-  // ---- buffer resources per k segment
-  rsrc_t ra0 = make_rsrc(g.a[0], g.a_bytes[0]);
-  rsrc_t rb0 = make_rsrc(g.b[0], g.b_bytes[0]);
-  rsrc_t ra1 = ra0, rb1 = rb0;
-  if (g.nseg > 1 || BKD == 2) {
-    ra1 = make_rsrc(g.a[1], g.a_bytes[1]);
-    rb1 = make_rsrc(g.b[1], g.b_bytes[1]);
-  }
+  // ---- operand buffers per k segment (the buffer resources are built where
+  // they are used: captured by reference they would be demoted to scratch)
+  const int nseg = g.nseg;
+  const uint16_t* const a0p = g.a[0];
+  const uint16_t* const b0p = g.b[0];
+  const uint16_t* const a1p = (nseg > 1 || BKD == 2) ? g.a[1] : g.a[0];
+  const uint16_t* const b1p = (nseg > 1 || BKD == 2) ? g.b[1] : g.b[0];
+  const uint32_t a0n = g.a_bytes[0], b0n = g.b_bytes[0];
+  const uint32_t a1n = (nseg > 1 || BKD == 2) ? g.a_bytes[1] : g.a_bytes[0];
+  const uint32_t b1n = (nseg > 1 || BKD == 2) ? g.b_bytes[1] : g.b_bytes[0];
+  const int K0 = g.K[0], K1 = nseg > 1 ? g.K[1] : 0;
+  const int ako0 = g.a_koff[0], ako1 = g.a_koff[1];
 
   // ---- DMA descriptors
   typename std::conditional<AK == 0, DmaK<BM>, DmaMN<BM>>::type da;
-  typename std::conditional<BKD == 0, DmaK<BN>, DmaMN<(BKD == 2 ? BN / 2 : BN)>>::type db, dbu;
-  if constexpr (AK == 0) da.init(m0, g.M, g.lda, lane, w);
-  else da.init(m0, g.M, lane, w);
-  if constexpr (BKD == 0) db.init(n0, g.N, g.ldb, lane, w);
-  else db.init(n0, g.N, lane, w);
-  if constexpr (BKD == 2) dbu = db;  // gate and up shards share columns and layout
+  typename std::conditional<BKD == 0, DmaK<BN>, DmaMN<(BKD == 2 ? BN / 2 : BN)>>::type db;
+  da.init(m0, g.M, g.lda, lane, w);
+  db.init(n0, g.N, g.ldb, lane, w);  // SwiGLU: gate and up shards share columns and layout
+  const uint32_t lda2 = (uint32_t)(g.lda * 2), ldb2 = (uint32_t)(g.ldb * 2);
 
-  const int nk0 = (g.K[0] + BK - 1) / BK;
-  const int nk = nk0 + (g.nseg > 1 ? (g.K[1] + BK - 1) / BK : 0);
+  const int nk0 = (K0 + BK - 1) / BK;
+  const int nk = nk0 + (nseg > 1 ? (K1 + BK - 1) / BK : 0);
 
-  auto issue_tile = [&](int t, uint8_t* st) {
+  constexpr int NIA = BM / 32;             // DMA instructions per wave per tile: A
+  constexpr int NIB = BN / 32;             // and B
+  constexpr int NI_TILE = NIA + NIB;
+  // Per-tile DMA state: buffer resources that start at the tile's first k
+  // (k-contiguous: column ko + k0 of every row; m/n-contiguous: row k0) and
+  // end with the operand.  Tiles at or past nk get empty resources (every
+  // lane reads zeros into a stage nobody reads again), so the loop needs no
+  // branches.
+  struct TileDma {
+    rsrc_t ra, rb, rb2;
+    int kvalid;  // valid k elements of the tile (k-contiguous masking)
+  };
+  // (readfirstlane keeps the descriptor in SGPRs: the values are uniform, but
+  // a descriptor the compiler believes divergent is issued in a waterfall loop)
+  auto shifted = [](const uint16_t* p, uint32_t bytes, uint32_t skip) __attribute__((always_inline)) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p) + skip;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(skip < bytes ? bytes - skip : 0u);
+    return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), n);
+  };
+  auto tile_dma = [&](int t) __attribute__((always_inline)) {
+    TileDma d;
     const bool s1 = t >= nk0;
     const int k0 = (s1 ? t - nk0 : t) * BK;
-    const int Ks = s1 ? g.K[1] : g.K[0];
-    const rsrc_t ra = s1 ? ra1 : ra0;
-    const rsrc_t rb = s1 ? rb1 : rb0;
-    if constexpr (AK == 0) {
-      const int ko = s1 ? g.a_koff[1] : g.a_koff[0];
-      da.issue(ra, st, ko + k0, ko + Ks, w);
+    const int Ks = s1 ? K1 : K0;
+    const bool live = k0 < Ks;
+    d.kvalid = live ? Ks - k0 : 0;
+    const uint16_t* ap = s1 ? a1p : a0p;
+    const uint32_t an = live ? (s1 ? a1n : a0n) : 0u;
+    const uint16_t* bp = s1 ? b1p : b0p;
+    const uint32_t bn = live ? (s1 ? b1n : b0n) : 0u;
+    if constexpr (AK == 0) d.ra = shifted(ap, an, (uint32_t)((s1 ? ako1 : ako0) + k0) * 2u);
+    else d.ra = shifted(ap, an, (uint32_t)k0 * lda2);
+    if constexpr (BKD == 0) d.rb = shifted(bp, bn, (uint32_t)k0 * 2u);
+    else d.rb = shifted(b0p, live ? b0n : 0u, (uint32_t)k0 * ldb2);
+    if constexpr (BKD == 2) d.rb2 = shifted(b1p, live ? b1n : 0u, (uint32_t)k0 * ldb2);
+    else d.rb2 = d.rb;
+    return d;
+  };
+  auto dma_op = [&](auto J_, const TileDma& d, uint8_t* st) __attribute__((always_inline)) {
+    constexpr int J = decltype(J_)::value;
+    if constexpr (J < NIA) {
+      if constexpr (AK == 0) da.template issue<J>(d.ra, st, d.kvalid, w);
+      else da.template issue<J>(d.ra, st, w);
     } else {
-      da.issue(ra, st, k0, Ks, g.lda, w);
-    }
-    if constexpr (BKD == 0) db.issue(rb, st + A_BYTES, k0, Ks, w);
-    else if constexpr (BKD == 1) db.issue(rb, st + A_BYTES, k0, Ks, g.ldb, w);
-    else {
-      db.issue(rb0, st + A_BYTES, k0, Ks, g.ldb, w);
-      dbu.issue(rb1, st + A_BYTES + B_BYTES / 2, k0, Ks, g.ldb, w);
+      constexpr int JB = J - NIA;
+      if constexpr (BKD == 0) db.template issue<JB>(d.rb, st + A_BYTES, d.kvalid, w);
+      else if constexpr (BKD == 1 || JB < NIB / 2) db.template issue<JB % NIB>(d.rb, st + A_BYTES, w);
+      else db.template issue<JB - NIB / 2>(d.rb2, st + A_BYTES + B_BYTES / 2, w);
     }
   };
-  constexpr int NI_TILE = (BM + BN) / 32;  // DMA instructions per wave per tile
 
   // ---- fragment addressing (loop invariant)
-  int a_koff_s[2], b_koff_s[2];
+  uint32_t a_koff_s[2], b_koff_s[2];
   uint32_t a_col[AK == 1 ? TM : 1], b_col[BKD != 0 ? TN : 1];
   uint32_t a_kb = 0, b_kb = 0;
   if constexpr (AK == 0) {
@@ -274,53 +313,46 @@ gemm_kernel(const GemmArgs g) {
   } else {
     a_kb = mn_kbase<BM>(lane);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a_col[i] = mn_coloff(wm * WM, i, lane);
+    for (int i = 0; i < TM; ++i) a_col[i] = a_kb + mn_coloff(wm * WM, i, lane);
   }
   if constexpr (BKD == 0) {
-    b_koff_s[0] = kfrag_off(wn * WN, 0, lane);
-    b_koff_s[1] = kfrag_off(wn * WN, 1, lane);
+    b_koff_s[0] = A_BYTES + kfrag_off(wn * WN, 0, lane);
+    b_koff_s[1] = A_BYTES + kfrag_off(wn * WN, 1, lane);
   } else if constexpr (BKD == 1) {
-    b_kb = mn_kbase<BN>(lane);
+    b_kb = A_BYTES + mn_kbase<BN>(lane);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b_col[j] = mn_coloff(wn * WN, j, lane);
+    for (int j = 0; j < TN; ++j) b_col[j] = b_kb + mn_coloff(wn * WN, j, lane);
   } else {
-    b_kb = mn_kbase<BN / 2>(lane);
+    b_kb = A_BYTES + mn_kbase<BN / 2>(lane);
 #pragma unroll
     for (int j = 0; j < TN / 2; ++j) {
-      b_col[j] = mn_coloff(wn * QW, j, lane);
+      b_col[j] = b_kb + mn_coloff(wn * QW, j, lane);
       b_col[j + TN / 2] = b_col[j] + B_BYTES / 2;  // same columns in the up region
     }
   }
 
-  // fragments of k-step S of the tile in stage st
-  auto read_frags = [&](auto S_, const uint8_t* st, bf16x8 (&af)[TM], bf16x8 (&bfv)[TN]) {
-    constexpr int S = decltype(S_)::value;
-    if constexpr (AK == 0) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = ld_b128(st + a_koff_s[S] + i * 2048);
+  // Read op R (0 <= R < TM + TN) of k-step S from the stage at LDS address sa:
+  // A fragment R, then B fragment R - TM.
+  constexpr int NRD = TM + TN;
+  auto read_op = [&](auto S_, auto R_, uint32_t sa, bf16x8 (&af)[TM], bf16x8 (&bfv)[TN]) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value, R = decltype(R_)::value;
+    if constexpr (R < TM) {
+      if constexpr (AK == 0) {
+        af[R] = ld_b128<R * 2048>(sa + a_koff_s[S]);
+      } else {
+        constexpr int RS = BM * 2;  // k-row stride
+        af[R] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(sa + a_col[R]);
+      }
     } else {
-      constexpr int RS = BM * 2;  // k-row stride
-      const uint32_t base = lds_addr(st) + a_kb;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(base + a_col[i]);
-    }
-    const uint8_t* sb = st + A_BYTES;
-    if constexpr (BKD == 0) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfv[j] = ld_b128(sb + b_koff_s[S] + j * 2048);
-    } else {
-      constexpr int RS = (BKD == 2 ? BN / 2 : BN) * 2;
-      const uint32_t base = lds_addr(sb) + b_kb;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfv[j] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(base + b_col[j]);
+      constexpr int J = R - TM;
+      if constexpr (BKD == 0) {
+        bfv[J] = ld_b128<J * 2048>(sa + b_koff_s[S]);
+      } else {
+        constexpr int RS = (BKD == 2 ? BN / 2 : BN) * 2;
+        bfv[J] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(sa + b_col[J]);
+      }
     }
   };
-  auto settle_frags = [&](bf16x8 (&af)[TM], bf16x8 (&bfv)[TN]) {
-    if constexpr (AK == 1) settle(af);
-    if constexpr (BKD != 0) settle(bfv);
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -328,44 +360,88 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mfma_all = [&](const bf16x8 (&af)[TM], const bf16x8 (&bfv)[TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfv[j], af[i], acc[i][j], 0, 0, 0);
+  // MFMA I of a phase: block (I / TN, I % TN).  Inline asm with the
+  // accumulator tied in place ("+a"): with the builtin the register allocator
+  // rotates the accumulator tile between AGPRs and VGPRs every k-tile (~3
+  // moves per MFMA), which halves the MFMA issue rate.  An accumulator is
+  // reused only TM*TN MFMAs later, far beyond the dependent-MFMA latency.
+  constexpr int NMF = TM * TN;
+  auto mfma_op = [](auto I_, f32x4 (&c)[TM][TN], const bf16x8 (&af)[TM], const bf16x8 (&bfv)[TN]) __attribute__((always_inline)) {
+    constexpr int I = decltype(I_)::value;
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+a"(c[I / TN][I % TN])
+                 : "v"(bfv[I % TN]), "v"(af[I / TN]));
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // First memory op of a phase waits this many MFMAs, so the MFMAs that read
+  // the fragment registers of the previous phase have issued.  Ops that do
+  // not fit between the MFMAs (small tiles) follow them.
+  constexpr int LAG = 2;
 
-  // ---- prologue: tiles 0 and 1 in flight, wait for tile 0
-  issue_tile(0, stage0);
-  if (nk > 1) {
-    issue_tile(1, stage1);
-    wait_vmcnt<NI_TILE>();
-  } else {
-    wait_vmcnt<0>();
+  // ---- prologue: tiles 0 and 1 in flight, tile 0 published, its step-0
+  // fragments read
+  {
+    const TileDma d0 = tile_dma(0), d1 = tile_dma(1);
+    static_for<NI_TILE>([&](auto J) __attribute__((always_inline)) { dma_op(J, d0, stage0); });
+    static_for<NI_TILE>([&](auto J) __attribute__((always_inline)) { dma_op(J, d1, stage1); });
   }
+  wait_vmcnt<NI_TILE>();
   __syncthreads();
   bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-  read_frags(S0{}, stage0, a0, b0);
+  const uint32_t st0 = lds_addr(stage0), st1 = lds_addr(stage1);
+  static_for<NRD>([&](auto R) __attribute__((always_inline)) { read_op(S0{}, R, st0, a0, b0); });
 
   for (int t = 0; t < nk; ++t) {
-    uint8_t* cur = (t & 1) ? stage1 : stage0;
-    uint8_t* nxt = (t & 1) ? stage0 : stage1;
-    settle_frags(a0, b0);  // read during the previous step-1 MFMAs: free
-    read_frags(S1{}, cur, a1, b1);
-    mfma_all(a0, b0);
-    // keep the phases in this order (the scheduler would otherwise hoist the
-    // DMA wait above most of the step-0 MFMAs and sink the DMA issue below
-    // the step-1 MFMAs)
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<0>();  // this wave's DMA of tile t+1 has landed
-    __syncthreads();  // everyone's has; everyone is done reading stage cur
-    settle_frags(a1, b1);
-    if (t + 2 < nk) issue_tile(t + 2, cur);
-    if (t + 1 < nk) read_frags(S0{}, nxt, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_all(a1, b1);
+    const uint32_t cur = (t & 1) ? st1 : st0, nxt = (t & 1) ? st0 : st1;
+    uint8_t* cur_p = (t & 1) ? stage1 : stage0;
+    const TileDma dn = tile_dma(t + 2);
+    // phase A: step-0 MFMAs of tile t; step-1 fragments of tile t read in between
+    wait_lgkm0();
+    static_for<NMF>([&](auto I) __attribute__((always_inline)) {
+      mfma_op(I, acc, a0, b0);
+      constexpr int R = decltype(I)::value - LAG;
+      if constexpr (R >= 0 && R < NRD) read_op(S1{}, std::integral_constant<int, R>{}, cur, a1, b1);
+    });
+    static_for<NRD>([&](auto R) __attribute__((always_inline)) {
+      if constexpr (decltype(R)::value + LAG >= NMF) read_op(S1{}, R, cur, a1, b1);
+    });
+    // this wave's DMA of tile t+1 has landed, its reads of stage cur are done;
+    // after the barrier, everyone's are
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    // phase B: step-1 MFMAs of tile t; step-0 fragments of tile t+1 read from
+    // stage nxt, then the DMA of tile t+2 issued into stage cur
+    auto phase_b_op = [&](auto P_) __attribute__((always_inline)) {
+      constexpr int P = decltype(P_)::value;
+      if constexpr (P < NRD) read_op(S0{}, P_, nxt, a0, b0);
+      else dma_op(std::integral_constant<int, P - NRD>{}, dn, cur_p);
+    };
+    // Reads in MFMA slots 1..NRD; DMA op d after MFMA 1 + 3d (a burst of
+    // buffer loads stalls MFMA issue; spread out they cost ~6% less).
+    constexpr int DMA_STRIDE = 3;
+    static_for<NMF>([&](auto I) __attribute__((always_inline)) {
+      mfma_op(I, acc, a1, b1);
+      constexpr int Iv = decltype(I)::value;
+      if constexpr (Iv >= 1 && Iv - 1 < NRD) phase_b_op(std::integral_constant<int, Iv - 1>{});
+      constexpr int D = (Iv - 1) / DMA_STRIDE;
+      if constexpr (Iv >= 1 && (Iv - 1) % DMA_STRIDE == 0 && D < NI_TILE)
+        phase_b_op(std::integral_constant<int, NRD + D>{});
+    });
+    static_for<NI_TILE>([&](auto D) __attribute__((always_inline)) {
+      if constexpr (1 + decltype(D)::value * DMA_STRIDE >= NMF)
+        phase_b_op(std::integral_constant<int, NRD + decltype(D)::value>{});
+    });
+    static_for<NRD>([&](auto P) __attribute__((always_inline)) {
+      if constexpr (decltype(P)::value + 1 >= NMF) phase_b_op(P);
+    });
   }
+  wait_vmcnt<0>();  // no DMA may land after the block has left
+  wait_lgkm0();
+
+  // The compiler cannot see the asm MFMAs: give the last ones time to write
+  // their results before the epilogue reads the accumulators.
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
 
   // ------------------------------------------------------------------ epilogue
   // Lane holds C[m][n .. n+3] of block (i, j) with m = m0 + wm*WM + i*16 + l16,
