@@ -82,9 +82,19 @@ gemv_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, co
       float sum[NU];
 #pragma unroll
       for (int m = 0; m < NU; ++m) sum[m] = 0.f;
-      for (int q = 0; q < ks_up; ++q) {
+      // all partial loads of a batch in flight at once, added in k-split order
+      constexpr int QB = 16;
+      for (int q0 = 0; q0 < ks_up; q0 += QB) {
+        float pv[QB][NU];
 #pragma unroll
-        for (int m = 0; m < NU; ++m) sum[m] += pg[((int64_t)q * NU + m) * K + kk];
+        for (int u = 0; u < QB; ++u)
+#pragma unroll
+          for (int m = 0; m < NU; ++m)
+            pv[u][m] = q0 + u < ks_up ? pg[((int64_t)(q0 + u) * NU + m) * K + kk] : 0.f;
+#pragma unroll
+        for (int u = 0; u < QB; ++u)
+#pragma unroll
+          for (int m = 0; m < NU; ++m) sum[m] += pv[u][m];
       }
       float a;
       if constexpr (ACT == ACT_SWIGLU) a = swiglu_f(sum[0], sum[1]);
