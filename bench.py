@@ -105,31 +105,10 @@ def main():
     others_dx = [dX.clone() for _ in range(t - 1)]
     torch.cuda.synchronize()
 
-    def step():
-        B.tp_mlp_fwd_shard(shape, X, W1, Wg, W2, Y, A, U, G, ws_f)
-        B.tp_mlp_reduce_partials_local([Y] + others_y, Yred, bias=b2)
-        B.tp_mlp_bwd_shard(shape, X, W1, Wg, W2, dY, A, U, G, dU, dW1, dWg, dW2, dX, db2, ws_b)
-        B.tp_mlp_reduce_partials_local([dX] + others_dx, dXred)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
-    flops = w.flops_train()
-    tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] {w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
-
-    # ---- per-kernel durations: the same step through the one-kernel entry points,
-    # HIP events recorded on the launch stream between consecutive launches
+    # one step = the whole hot path through the one-kernel entry points (the
+    # composite entry points launch exactly these kernels in this order); a HIP
+    # event on the launch stream after every kernel gives per-kernel durations
+    # measured inside the timed region itself
     ws_db = B.alloc_workspace(B.bias_grad_workspace_bytes(N, h)) if w.bias else None
     kernels = [
         ("up_act", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_act_shard(shape, X, W1, Wg, A, U, G)),
@@ -139,30 +118,46 @@ def main():
         ("down_wgrad", 2 * N * h * Fi, lambda: B.tp_mlp_down_wgrad_shard(shape, A, dY, dW2)),
         ("up_wgrad", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_wgrad_shard(shape, X, dU, dW1, dWg)),
         ("up_dgrad", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_dgrad_shard(shape, dU, W1, Wg, dX)),
-        ("reduce_dx", 0, lambda: B.tp_mlp_reduce_partials_local([dX] + others_dx, dXred)),
     ]
     if w.bias:
         kernels.append(("bias_grad", 0, lambda: B.tp_mlp_bias_grad(dY, db2, ws_db)))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
-    for _ in range(2):
+    kernels.append(("reduce_dx", 0, lambda: B.tp_mlp_reduce_partials_local([dX] + others_dx, dXred)))
+
+    for _ in range(args.warmup):
         for _, _, fn in kernels:
             fn()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    nk = len(kernels)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * nk + 1)]
+    t_wall = time.perf_counter()
+    evs[0].record(stream)
     for s in range(args.steps):
-        evs[s][0].record(stream)
         for j, (_, _, fn) in enumerate(kernels):
             fn()
-            evs[s][j + 1].record(stream)
+            evs[s * nk + j + 1].record(stream)
     torch.cuda.synchronize()
-    kern_ms = {name: float(np.mean([evs[s][j].elapsed_time(evs[s][j + 1]) for s in range(args.steps)]))
+    t_wall = time.perf_counter() - t_wall
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    flops = w.flops_train()
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
+    kern_ms = {name: float(np.mean([evs[s * nk + j].elapsed_time(evs[s * nk + j + 1]) for s in range(args.steps)]))
                for j, (name, _, _) in enumerate(kernels)}
     gemms = [(n, fl) for n, fl, _ in kernels if fl > 0]
     dom, dom_fl = max(gemms, key=lambda x: kern_ms[x[0]])
     achieved = dom_fl / (kern_ms[dom] * 1e-3) / 1e12
+    traffic = counter_traffic(f"gemm_hbm_traffic_{w.name}.md", GEMM_SOURCES, dom)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic["bytes"] if traffic else None,
                 "flops_per_launch": dom_fl}
+    if traffic:
+        roofline["traffic_unit"] = "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        roofline["algorithmic_bytes"] = traffic["algorithmic_bytes"]
     log("[bench] per-kernel ms: " + ", ".join(f"{k}={v:.3f}" for k, v in kern_ms.items()))
+    copy = copy_probe(torch)
+    log(f"[bench] copy probe: {copy['GB/s']:.0f} GB/s")
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -175,6 +170,7 @@ def main():
                    "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
         "roofline": roofline,
         "kernels_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+        "copy_probe": copy,
     }
 
     # ---- decode (one token), HBM bound; weights rotated over copies
@@ -187,6 +183,56 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows, I)
     print(json.dumps(result), flush=True)
 
+
+
+GEMM_SOURCES = ("gemm.hip", "gemm.h", "common.h", "api.hip")
+GEMV_SOURCES = ("gemv.hip", "gemv.h", "common.h", "api.hip")
+
+
+def source_hash(files):
+    """sha256 over the named kernel sources (csrc/)."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "megatron_tensor_transformer_rank_amd", "csrc", f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()
+
+
+def counter_traffic(summary, files, kernel):
+    """HBM bytes per launch of `kernel`, from a committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter
+    reads for a plain copy of known size).  None when there is no summary or
+    the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    info = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic_json: "):
+                info = json.loads(line[len("traffic_json: "):])
+    if not info or info.get("source_sha256") != source_hash(files):
+        return None
+    return info.get("kernels", {}).get(kernel)
+
+
+def copy_probe(torch, nbytes=1 << 30, reps=5):
+    """Device-to-device copy of a 1 GiB buffer: the plain streaming rate."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return {"bytes_moved": 2 * nbytes, "GB/s": round(2 * nbytes / sec / 1e9, 1)}
 
 def bench_decode(args, w, B, I, torch, np, to_dev):
     bf = torch.bfloat16
@@ -226,11 +272,13 @@ def bench_decode(args, w, B, I, torch, np, to_dev):
     torch.cuda.synchronize()
     us_warm = e0.elapsed_time(e1) * 1e3 / n
     gbs = wbytes / (us * 1e-6) / 1e9
+    traffic = counter_traffic(f"gemv_hbm_traffic_{w.name}.md", GEMV_SOURCES, "decode")
     log(f"[bench] decode: {us:.2f} us/token cold ({gbs:.0f} GB/s), {us_warm:.2f} us warm")
     return {"workload": w.name, "value": round(gbs, 1), "unit": "GB/s", "us_per_token": round(us, 3),
             "bytes_per_token": wbytes, "weight_sets_rotated": nsets,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic["bytes"] if traffic else None,
                          "scope": "whole decode call (gate/up GEMV + down GEMV)"},
             "us_per_token_warm_cache": round(us_warm, 3)}
 
