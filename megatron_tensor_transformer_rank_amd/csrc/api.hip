@@ -80,13 +80,16 @@ struct DecodeLayout {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// ~448 blocks per GEMV (1.75 per CU): measured best for the one-token stream.
-constexpr int DECODE_TARGET_BLOCKS = 448;
+// Blocks per GEMV, measured best for the one-token stream on 256 CUs: the
+// up-projection ~224 (fewer k-splits leave fewer partials for the
+// down-projection's prologue to add), the down-projection ~256 (one per CU).
+constexpr int DECODE_UP_BLOCKS = 224;
+constexpr int DECODE_DOWN_BLOCKS = 256;
 
 DecodeLayout decode_layout(const Dims& d) {
   DecodeLayout L;
-  L.up = gemv_plan((int)d.h, (int)d.Fi, d.g, DECODE_TARGET_BLOCKS);
-  L.down = gemv_plan((int)d.Fi, (int)d.h, 1, DECODE_TARGET_BLOCKS);
+  L.up = gemv_plan((int)d.h, (int)d.Fi, d.g, DECODE_UP_BLOCKS);
+  L.down = gemv_plan((int)d.Fi, (int)d.h, 1, DECODE_DOWN_BLOCKS);
   size_t off = 0;
   L.off_part_up = off;
   off = round256(off + L.up.part_floats * sizeof(float));

@@ -11,14 +11,17 @@
 //
 // Three launches, no cross-block synchronisation inside a kernel (an
 // agent-scope fence per block costs more than the whole stream):
-//   1. up:    blocks = 512-column strips x matrices x k-splits; a block's 4
-//             waves take interleaved rows of its k range, meet in LDS and write
-//             one float32 partial row per (k-split, matrix).
-//   2. down:  same streaming over W2_i; its prologue adds the up-projection's
-//             k-split partials for the block's rows in fixed order, applies the
-//             activation and rounds A to bf16 (the value the MFMA path would
-//             read back), while the block's first weight loads are in flight.
-//             Blocks of the first column strip also write A_i and the stash.
+//   1. up:    blocks = 512-column strips x matrices x k-splits; a block's 16
+//             waves take interleaved rows of its k range, each lane keeping 8
+//             weight loads in flight in a rolling pipeline; the waves meet in
+//             LDS and write one float32 partial row per (k-split, matrix).
+//   2. down:  same streaming over W2_i, about one block per CU (fewer, longer
+//             blocks stream this shape faster than 1-2 per CU); its prologue
+//             adds the up-projection's k-split partials for the block's rows
+//             in fixed order, applies the activation and rounds A to bf16
+//             (the value the MFMA path would read back), while the block's
+//             first weight loads are in flight.  Blocks of the first column
+//             strip also write A_i and the stash.
 //   3. final: adds the down-projection's k-split partials in fixed order and
 //             rounds Y_i to bf16.
 // The result is deterministic.
@@ -27,10 +30,11 @@
 
 namespace tpmlp {
 
-constexpr int GV_THREADS = 256;
+constexpr int GV_WAVES = 16;
+constexpr int GV_THREADS = 64 * GV_WAVES;
 constexpr int GV_STRIP = 512;  // columns per block (64 lanes x 8)
-constexpr int GV_UNROLL = 16;  // rows in flight per wave
-constexpr int GV_STEP = 4 * GV_UNROLL;
+constexpr int GV_UNROLL = 8;   // weight loads in flight per lane
+constexpr int GV_FINAL_COLS = 128;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -41,13 +45,18 @@ __device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
 // PRO = 0: x is the bf16 input vector.  PRO = 1: x[k] = act(sum of the
 // up-projection partials pg[q][*][k]) rounded to bf16 (ACT selects ReLU /
 // GeLU over one matrix or SwiGLU over gate and up).
+//
+// Wave w of the block takes rows kb + w, kb + w + GV_WAVES, ...; its weight
+// loads form a rolling pipeline: slot u holds row j = step * GV_UNROLL + u,
+// and is refilled with row j + GV_UNROLL as soon as it has been consumed, so
+// GV_UNROLL loads stay in flight per lane through the whole k range.
 template <int NMAT, int PRO, int ACT>
 __global__ void __launch_bounds__(GV_THREADS)
 gemv_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
              int K, int ncols, int KR, float* __restrict__ part, const float* __restrict__ pg, int ks_up,
              uint16_t* __restrict__ a_out, uint16_t* __restrict__ st0, uint16_t* __restrict__ st1) {
   __shared__ float xs[GV_MAX_KR];
-  __shared__ float red[4][GV_STRIP];
+  __shared__ float red[GV_WAVES][GV_STRIP];
 
   const int S = (ncols + GV_STRIP - 1) / GV_STRIP;
   const int b = blockIdx.x;
@@ -62,16 +71,14 @@ gemv_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, co
   const uint16_t* Wm = (NMAT == 2 && mat == 1) ? W1 : W0;
   const int col = s * GV_STRIP + lane * 8;
   const bool cok = col < ncols;
-  const uint16_t* base = Wm + col;
+  const uint16_t* base = Wm + col + (int64_t)(kb + w) * ncols;
+  const int64_t rstride = (int64_t)GV_WAVES * ncols;
+  const int nrows = cok && ke - kb > w ? (ke - kb - w + GV_WAVES - 1) / GV_WAVES : 0;  // rows of this lane
 
-  // first batch of weight loads before x is staged: they do not depend on it
+  // first loads before x is staged: they do not depend on it
   u32x4 v[GV_UNROLL];
-  int k = kb + w;
 #pragma unroll
-  for (int u = 0; u < GV_UNROLL; ++u) {
-    const int kk = k + 4 * u;
-    v[u] = (cok && kk < ke) ? ld_stream(base + (int64_t)kk * ncols) : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int u = 0; u < GV_UNROLL; ++u) v[u] = u < nrows ? ld_stream(base + u * rstride) : u32x4{0u, 0u, 0u, 0u};
 
   if constexpr (PRO == 0) {
     for (int i = tid; i < ke - kb; i += GV_THREADS) xs[i] = bf16_to_f32(x[kb + i]);
@@ -111,74 +118,86 @@ gemv_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, co
   __syncthreads();
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (; k < ke; k += GV_STEP) {
-    u32x4 cur[GV_UNROLL];
-#pragma unroll
-    for (int u = 0; u < GV_UNROLL; ++u) cur[u] = v[u];
-    if (k + GV_STEP < ke) {
-#pragma unroll
-      for (int u = 0; u < GV_UNROLL; ++u) {
-        const int kk = k + GV_STEP + 4 * u;
-        v[u] = (cok && kk < ke) ? ld_stream(base + (int64_t)kk * ncols) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+  const int nsteps = (nrows + GV_UNROLL - 1) / GV_UNROLL;
+  for (int step = 0; step < nsteps; ++step) {
 #pragma unroll
     for (int u = 0; u < GV_UNROLL; ++u) {
-      const int kk = k + 4 * u;
-      const float xv = kk < ke ? xs[kk - kb] : 0.f;
-      acc[0] += xv * bf16lo(cur[u].x);
-      acc[1] += xv * bf16hi(cur[u].x);
-      acc[2] += xv * bf16lo(cur[u].y);
-      acc[3] += xv * bf16hi(cur[u].y);
-      acc[4] += xv * bf16lo(cur[u].z);
-      acc[5] += xv * bf16hi(cur[u].z);
-      acc[6] += xv * bf16lo(cur[u].w);
-      acc[7] += xv * bf16hi(cur[u].w);
+      const int j = step * GV_UNROLL + u;
+      const float xv = j < nrows ? xs[w + GV_WAVES * j] : 0.f;
+      const u32x4 c = v[u];
+      acc[0] += xv * bf16lo(c.x);
+      acc[1] += xv * bf16hi(c.x);
+      acc[2] += xv * bf16lo(c.y);
+      acc[3] += xv * bf16hi(c.y);
+      acc[4] += xv * bf16lo(c.z);
+      acc[5] += xv * bf16hi(c.z);
+      acc[6] += xv * bf16lo(c.w);
+      acc[7] += xv * bf16hi(c.w);
+      const int jn = j + GV_UNROLL;
+      v[u] = jn < nrows ? ld_stream(base + jn * rstride) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[w][lane * 8 + e] = acc[e];
   __syncthreads();
 
-  // block partial row: 2 columns per thread, waves added in fixed order
-  const int c = tid * 2;
-  const int gc = s * GV_STRIP + c;
-  if (gc < ncols) {
-    float* prow = part + ((int64_t)ks * NMAT + mat) * ncols + gc;
-    *reinterpret_cast<float2*>(prow) =
-        make_float2(((red[0][c] + red[1][c]) + red[2][c]) + red[3][c],
-                    ((red[0][c + 1] + red[1][c + 1]) + red[2][c + 1]) + red[3][c + 1]);
+  // block partial row: waves added in fixed order
+  for (int c = tid; c < GV_STRIP; c += GV_THREADS) {
+    const int gc = s * GV_STRIP + c;
+    if (gc < ncols) {
+      float t = red[0][c];
+#pragma unroll
+      for (int q = 1; q < GV_WAVES; ++q) t += red[q][c];
+      part[((int64_t)ks * NMAT + mat) * ncols + gc] = t;
+    }
   }
 }
 
-// out[c] = bf16(sum_q part[q][c]), q in order; 4 columns per thread.
-__global__ void __launch_bounds__(GV_THREADS)
+// out[c] = bf16(sum_q part[q][c]).  A block owns GV_FINAL_COLS columns; its
+// 8 thread groups each add every 8th partial in increasing q, then group
+// sums are added in group order: a fixed order, so the result is
+// deterministic.
+__global__ void __launch_bounds__(256)
 gemv_final(const float* __restrict__ part, int ks, int ncols, uint16_t* __restrict__ out) {
-  const int c = (blockIdx.x * GV_THREADS + threadIdx.x) * 4;
-  if (c >= ncols) return;
+  __shared__ float4 red[8][GV_FINAL_COLS / 4];
+  const int c4 = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int c = blockIdx.x * GV_FINAL_COLS + c4 * 4;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int TU = 8;
-  for (int q = 0; q < ks; q += TU) {
-    float4 t[TU];
+  if (c < ncols) {
+    constexpr int TU = 4;
+    for (int q0 = grp; q0 < ks; q0 += 8 * TU) {
+      float4 t[TU];
 #pragma unroll
-    for (int u = 0; u < TU; ++u)
-      t[u] = q + u < ks ? *reinterpret_cast<const float4*>(part + (int64_t)(q + u) * ncols + c)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int u = 0; u < TU; ++u) {
+        const int q = q0 + 8 * u;
+        t[u] = q < ks ? *reinterpret_cast<const float4*>(part + (int64_t)q * ncols + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
-    for (int u = 0; u < TU; ++u) {
-      a.x += t[u].x; a.y += t[u].y; a.z += t[u].z; a.w += t[u].w;
+      for (int u = 0; u < TU; ++u) {
+        a.x += t[u].x; a.y += t[u].y; a.z += t[u].z; a.w += t[u].w;
+      }
     }
   }
-  *reinterpret_cast<uint2*>(out + c) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+  red[grp][c4] = a;
+  __syncthreads();
+  if (grp == 0 && c < ncols) {
+    float4 r = red[0][c4];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+      const float4 o = red[q][c4];
+      r.x += o.x; r.y += o.y; r.z += o.z; r.w += o.w;
+    }
+    *reinterpret_cast<uint2*>(out + c) = make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+  }
 }
 
 GemvPlan gemv_plan(int K, int ncols, int nmat, int target_blocks) {
   GemvPlan p;
   p.strips = (ncols + GV_STRIP - 1) / GV_STRIP;
   int ks = (target_blocks + p.strips * nmat - 1) / (p.strips * nmat);
-  ks = max(1, min(ks, (K + GV_STEP - 1) / GV_STEP));
+  ks = max(1, min(ks, (K + GV_WAVES - 1) / GV_WAVES));
   int kr = (K + ks - 1) / ks;
-  kr = ((kr + GV_STEP - 1) / GV_STEP) * GV_STEP;  // whole unrolled steps per wave
+  kr = ((kr + GV_WAVES - 1) / GV_WAVES) * GV_WAVES;  // whole rows for every wave
   if (kr > GV_MAX_KR) kr = GV_MAX_KR;
   p.ks = (K + kr - 1) / kr;
   p.kr = kr;
@@ -211,7 +230,7 @@ hipError_t decode_launch(int act, const uint16_t* x, const uint16_t* Wa, const u
                        part_up, up.ks, A, st0, nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemv_final, dim3((h / 4 + GV_THREADS - 1) / GV_THREADS), blk, 0, st, part_down, down.ks, h, Y);
+  hipLaunchKernelGGL(gemv_final, dim3((h + GV_FINAL_COLS - 1) / GV_FINAL_COLS), dim3(256), 0, st, part_down, down.ks, h, Y);
   return hipGetLastError();
 }
 

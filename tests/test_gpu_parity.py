@@ -114,6 +114,14 @@ def test_decode_one_token(act):
     run_group(200 + len(act), 1, 1024, 3 * 1024, 2, act, False)
 
 
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_decode_ragged_splits(act):
+    """h = 4104, F_i = 1544: the last k-split of both GEMVs is short, the last
+    column strip of the down-projection holds 8 columns, and the final reduce
+    ends in a partial block."""
+    run_group(220 + len(act), 1, 4104, 2 * 1544, 2, act, False)
+
+
 def test_decode_without_stash():
     """Inference: forward only, no stash buffers."""
     sw = True
