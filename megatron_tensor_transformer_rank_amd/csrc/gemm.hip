@@ -15,23 +15,31 @@
 //                 (two k segments: [dG | dP] against [Wg_i | W1_i])
 //
 // Design (MI355X-first):
-//  * 256 threads = 4 wave64s in a 2x2 grid; block tile BM x BN x 64, each wave
-//    owns (BM/2) x (BN/2) of the output in accumulator registers.
+//  * 512 threads = 8 wave64s, two per SIMD, in two groups of four.  Group G
+//    owns rows G*BM/2 .. +BM/2 of the block tile, wave q of a group owns
+//    columns q*BN/4 .. +BN/4, accumulated in AGPRs.
+//  * Ping-pong: the groups alternate between a compute phase (the 2*TM*TN
+//    MFMAs of one 64-deep k-tile, from fragments already in registers) and a
+//    memory phase (the next k-tile's fragments LDS -> registers, plus its share
+//    of the HBM -> LDS DMA).  A barrier ends every phase, so on each SIMD one
+//    wave issues MFMAs while the other one's loads and waits run beside it.
 //  * Tiles move HBM -> LDS with buffer-load-to-LDS (16 bytes per lane, no
-//    VGPR staging, no ds_write).  Each operand is addressed through a buffer
-//    resource of its own size; tile lanes outside the matrix get an offset past
-//    the end, for which the buffer unit returns zeros, so ragged tails need no
-//    other masking.
+//    VGPR staging).  Each operand is addressed through a buffer resource of
+//    its own size; tile lanes outside the matrix get an offset past the end,
+//    for which the buffer unit returns zeros, so ragged tails need no other
+//    masking.
+//  * Two LDS stages, each [A rows of group 0 | A rows of group 1 | B].  The
+//    DMA is split by region so that every region is rewritten only after the
+//    group(s) reading it are done and lands two or three phases before use:
+//      group 0, memory phase of tile s: B of tile s+1;
+//      group 1, memory phase of tile s: group-1 A rows of tile s+1 and
+//      group-0 A rows of tile s+2.
 //  * LDS layouts (16-byte chunks XOR-swizzled against bank conflicts):
 //      k-contiguous operand [row][64 k]: chunk c of row r at slot c ^ (r & 7),
 //        fragments read with ds_read_b128;
 //      m/n-contiguous operand [64 k][R]: chunk c of k-row r at c ^ 2(r & 3),
 //        fragments read with ds_read_b64_tr_b16 (the LDS transpose read), two
 //        per 8-k fragment.
-//  * Two LDS stages.  Per k-tile: step-1 fragments are read while the step-0
-//    MFMAs run; one barrier; the DMA of the tile after next is issued into the
-//    stage just released and the next tile's step-0 fragments are read while
-//    the step-1 MFMAs run.  DMA has a whole k-tile to land.
 //  * The MFMA takes the operands swapped (B fragment first) so each lane holds
 //    4 consecutive output columns: 8-byte bf16 / 16-byte fp32 stores.
 //  * Block ids are remapped so consecutive tiles land on one XCD (blocks are
@@ -40,21 +48,21 @@
 //  * Epilogues: plain bf16 / fp32 store (column split into two buffers),
 //    ReLU / GeLU with the pre-activation stash, SwiGLU with gate and up
 //    accumulated in the same wave (separate gate / up LDS regions), and the
-//    activation derivative reading the stash.
+//    activation derivative reading the stash.  Group 0's epilogue overlaps
+//    group 1's last compute phase.
 #include "common.h"
 #include "gemm.h"
 
 namespace tpmlp {
 
 constexpr int BK = 64;
-constexpr int NT = 256;
+constexpr int NT = 512;
 constexpr int GROUP_M = 4;
 constexpr uint32_t OOB = 0xFFFFFFF0u;         // past the end of any accepted buffer
 constexpr int RSRC_FLAGS = 0x00020000;        // raw buffer, 32-bit data
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -69,51 +77,69 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// A bare barrier: no implied waits (outstanding DMA stays in flight), and a
+// compiler barrier for memory operations.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // DMA of a k-contiguous operand tile: R rows x 64 k into [row][8 chunks].
-// One wave instruction fills 1 KiB = 8 rows; lane i of segment sg holds the
-// LDS chunk q = sg*64 + i: row q/8, slot q%8, logical chunk slot ^ (row&7).
+// One wave instruction fills 1 KiB = 8 rows; lane i of instruction j of wave
+// q holds LDS chunk p = (q + 4j)*64 + i: row p/8, slot p%8, which holds the
+// logical chunk slot ^ (row & 7) -- the same chunk for every j.
 // ---------------------------------------------------------------------------
 template <int R>
 struct DmaK {
   static constexpr int NI = R / 32;  // instructions per wave per tile
-  uint32_t voff[NI];                 // row*ld*2 + chunk*16 (bytes from the tile's k0), or OOB
-  int kc[NI];                        // element offset of the lane's chunk in the tile
-  __device__ __forceinline__ void init(int row0, int rows, int64_t ld, int lane, int w) {
+  uint32_t voff[NI];                 // row*ld*2 + chunk*16 (bytes from the tile's first k), or OOB
+  int kc;                            // element offset of the lane's chunk in the tile
+  __device__ __forceinline__ void init(int row0, int rows, int64_t ld, int lane, int q) {
+    kc = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int q = (w + 4 * j) * 64 + lane;
-      const int r = q >> 3;
-      const int chunk = (q & 7) ^ (r & 7);
+      const int r = (q + 4 * j) * 8 + (lane >> 3);
       const int grow = row0 + r;
-      kc[j] = chunk * 8;
-      voff[j] = grow < rows ? (uint32_t)((int64_t)grow * ld * 2) + (uint32_t)kc[j] * 2u : OOB;
+      voff[j] = grow < rows ? (uint32_t)((int64_t)grow * ld * 2) + (uint32_t)kc * 2u : OOB;
     }
   }
   // instruction J of a tile; rs addresses the operand from the tile's first
   // k; chunks at or past kvalid (elements from the tile's first k) read zeros
   template <int J>
-  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int kvalid, int w) const {
-    dma16(rs, region + (w + 4 * J) * 1024, kc[J] < kvalid ? voff[J] : OOB);
+  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int kvalid, int q) const {
+    dma16(rs, region + (q + 4 * J) * 1024, kc < kvalid ? voff[J] : OOB);
   }
 };
 
 // ---------------------------------------------------------------------------
 // DMA of an m/n-contiguous operand tile: 64 k-rows x RW columns into
-// [k][RW/8 chunks]; chunk c of k-row r at slot c ^ 2(r&3).
+// [k][RW/8 chunks]; chunk c of k-row r at slot c ^ mn_swz(r).
+//
+// The transposed fragment read has each 16-lane group read 32 bytes from each
+// of 4 k-rows (8g + 0..3, g = lane / 16), and 32 lanes are served per pass
+// over the 64 four-byte banks.  2(r&3) spreads one group's 4 rows over 128
+// bytes of banks; bit 3 of r (g odd) moves the other group of the pass to the
+// other 128 bytes: XOR 8 chunks when a k-row is a multiple of 256 bytes long,
+// XOR 2 chunks when it is an odd multiple of 128 bytes (rows then alternate
+// bank halves by themselves).
 // ---------------------------------------------------------------------------
+template <int RW>
+__device__ __forceinline__ int mn_swz(int r) {
+  static_assert((RW * 2) % 128 == 0, "k-row length");
+  constexpr int X = ((RW * 2) % 256 == 0) ? 8 : 2;
+  return (2 * (r & 3)) ^ (X * ((r >> 3) & 1));
+}
 template <int RW>
 struct DmaMN {
   static constexpr int CPR = RW / 8;
   static constexpr int NI = RW / 32;
+  static_assert(CPR % 8 == 0, "tile width");
   uint32_t voff[NI];  // krow*ld*2 + col*2 (bytes from the tile's first k row), or OOB
-  __device__ __forceinline__ void init(int col0, int cols, int64_t ld, int lane, int w) {
+  __device__ __forceinline__ void init(int col0, int cols, int64_t ld, int lane, int q) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int q = (w + 4 * j) * 64 + lane;
-      const int kr = q / CPR;
-      const int chunk = (q % CPR) ^ (2 * (kr & 3));
+      const int p = (q + 4 * j) * 64 + lane;
+      const int kr = p / CPR;
+      const int chunk = (p % CPR) ^ mn_swz<RW>(kr);
       const int col = col0 + chunk * 8;
       voff[j] = col < cols ? (uint32_t)((int64_t)kr * ld * 2) + (uint32_t)col * 2u : OOB;
     }
@@ -121,8 +147,8 @@ struct DmaMN {
   // instruction J of a tile; rs addresses the operand from the tile's first k
   // row and ends with the operand, so k rows past the end read zeros
   template <int J>
-  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int w) const {
-    dma16(rs, region + (w + 4 * J) * 1024, voff[J]);
+  __device__ __forceinline__ void issue(rsrc_t rs, uint8_t* region, int q) const {
+    dma16(rs, region + (q + 4 * J) * 1024, voff[J]);
   }
 };
 
@@ -130,13 +156,12 @@ struct DmaMN {
 // Fragment reads (16 rows/columns x 32 k of one MFMA operand, 8 bf16 per lane:
 // lane l holds index l%16, k = 8*(l/16) .. +7 of the k-step).
 // ---------------------------------------------------------------------------
-// k-contiguous region: byte offset of lane's fragment for block row base rb,
-// k-step s; block i adds i*2048.
+// k-contiguous region: byte offset of the lane's fragment for block row base
+// rb, k-step s; block i adds i*2048.
 __device__ __forceinline__ int kfrag_off(int rb, int s, int lane) {
   const int l16 = lane & 15, lq = lane >> 4;
   return (rb + l16) * 128 + (((s * 4 + lq) ^ (l16 & 7)) << 4);
 }
-
 // m/n-contiguous region of width RW: per-lane k-row byte base and the column
 // part of block i (columns cb + 16 i .. +15).
 template <int RW>
@@ -144,18 +169,19 @@ __device__ __forceinline__ int mn_kbase(int lane) {
   const int g = lane >> 4, src = lane & 15;
   return (8 * g + (src >> 2)) * (RW * 2);
 }
+// (the lane's k-row is 8*(lane/16) + (lane%16)/4 plus multiples of 4 and 32,
+// which leave its low two bits and bit 3 unchanged)
+template <int RW>
 __device__ __forceinline__ int mn_coloff(int cb, int i, int lane) {
   const int src = lane & 15;
   const int chunk = (cb + 16 * i + 4 * (src & 3)) >> 3;
-  return ((chunk ^ (2 * (src >> 2))) << 4) + (src & 1) * 8;
+  const int r = 8 * (lane >> 4) + (src >> 2);
+  return ((chunk ^ mn_swz<RW>(r)) << 4) + (src & 1) * 8;
 }
-// The k loop is hand-scheduled: LDS reads and MFMAs are volatile inline asm,
-// so they issue in source order, interleaved one memory operation per MFMA.
-// (The compiler's own schedule issued the next tile's DMA and fragment reads
-// in a block between the barrier and the MFMAs, idling the MFMA pipe, and the
-// intrinsic form of the transpose read carries no alias information, which
-// makes the compiler wait for all in-flight buffer-to-LDS loads before it.)
-// LDS read results are consumed only after an explicit lgkmcnt(0) wait.
+// The LDS reads and MFMAs are volatile inline asm: they issue in source
+// order, and the compiler inserts no waits for the buffer-to-LDS loads in
+// flight (it cannot tell the regions apart).  LDS read results are consumed
+// only after an explicit lgkmcnt(0) wait.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -179,7 +205,6 @@ __device__ __forceinline__ bf16x8 ld_tr2(uint32_t addr) {
   const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for_impl(F&& f) {
@@ -208,62 +233,35 @@ __device__ __forceinline__ void tile_of(int pid, int nb, int tiles_m, int tiles_
 }
 
 template <int BM, int BN, int AK, int BKD, int EPI, int ACT>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 gemm_kernel(const GemmArgs g) {
-  constexpr int TM = BM / 32, TN = BN / 32;  // 16x16 blocks per wave
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int QW = BN / 4;  // SwiGLU: features per wave column
+  constexpr int HM = BM / 2;                 // rows per group
+  constexpr int QN = BN / 4;                 // B-region columns per wave
+  constexpr int TM = HM / 16, TN = QN / 16;  // 16x16 blocks per wave
+  constexpr int AH_BYTES = HM * 128;         // one group's A rows x 64 k
+  constexpr int B_BYTES = BN * 128;
+  constexpr int STAGE = 2 * AH_BYTES + B_BYTES;
+  constexpr int QF = BN / 8;                 // SwiGLU: features per wave
   static_assert(BKD != 2 || (BN == 128 || BN == 256), "SwiGLU tile width");
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
+  static_assert(HM % 64 == 0 && QN % 16 == 0, "tile shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int G = w >> 2, q = w & 3;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM;
   const int n0 = (BKD == 2) ? tn * (BN / 2) : tn * BN;
 
-  // ---- operand buffers per k segment (the buffer resources are built where
-  // they are used: captured by reference they would be demoted to scratch)
   const int nseg = g.nseg;
-  const uint16_t* const a0p = g.a[0];
-  const uint16_t* const b0p = g.b[0];
-  const uint16_t* const a1p = (nseg > 1 || BKD == 2) ? g.a[1] : g.a[0];
-  const uint16_t* const b1p = (nseg > 1 || BKD == 2) ? g.b[1] : g.b[0];
-  const uint32_t a0n = g.a_bytes[0], b0n = g.b_bytes[0];
-  const uint32_t a1n = (nseg > 1 || BKD == 2) ? g.a_bytes[1] : g.a_bytes[0];
-  const uint32_t b1n = (nseg > 1 || BKD == 2) ? g.b_bytes[1] : g.b_bytes[0];
   const int K0 = g.K[0], K1 = nseg > 1 ? g.K[1] : 0;
-  const int ako0 = g.a_koff[0], ako1 = g.a_koff[1];
-
-  // ---- DMA descriptors
-  typename std::conditional<AK == 0, DmaK<BM>, DmaMN<BM>>::type da;
-  typename std::conditional<BKD == 0, DmaK<BN>, DmaMN<(BKD == 2 ? BN / 2 : BN)>>::type db;
-  da.init(m0, g.M, g.lda, lane, w);
-  db.init(n0, g.N, g.ldb, lane, w);  // SwiGLU: gate and up shards share columns and layout
-  const uint32_t lda2 = (uint32_t)(g.lda * 2), ldb2 = (uint32_t)(g.ldb * 2);
-
   const int nk0 = (K0 + BK - 1) / BK;
   const int nk = nk0 + (nseg > 1 ? (K1 + BK - 1) / BK : 0);
 
-  constexpr int NIA = BM / 32;             // DMA instructions per wave per tile: A
-  constexpr int NIB = BN / 32;             // and B
-  constexpr int NI_TILE = NIA + NIB;
-  // Per-tile DMA state: buffer resources that start at the tile's first k
-  // (k-contiguous: column ko + k0 of every row; m/n-contiguous: row k0) and
-  // end with the operand.  Tiles at or past nk get empty resources (every
-  // lane reads zeros into a stage nobody reads again), so the loop needs no
-  // branches.
-  struct TileDma {
-    rsrc_t ra, rb, rb2;
-    int kvalid;  // valid k elements of the tile (k-contiguous masking)
-  };
-  // (readfirstlane keeps the descriptor in SGPRs: the values are uniform, but
-  // a descriptor the compiler believes divergent is issued in a waterfall loop)
+  // Buffer resource that starts `skip` bytes into an operand and ends with it
+  // (readfirstlane keeps it in SGPRs: the values are uniform, but a descriptor
+  // the compiler believes divergent is issued in a waterfall loop).
   auto shifted = [](const uint16_t* p, uint32_t bytes, uint32_t skip) __attribute__((always_inline)) {
     const uint64_t a = reinterpret_cast<uint64_t>(p) + skip;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
@@ -271,87 +269,72 @@ gemm_kernel(const GemmArgs g) {
     const uint32_t n = __builtin_amdgcn_readfirstlane(skip < bytes ? bytes - skip : 0u);
     return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), n);
   };
-  auto tile_dma = [&](int t) __attribute__((always_inline)) {
-    TileDma d;
-    const bool s1 = t >= nk0;
-    const int k0 = (s1 ? t - nk0 : t) * BK;
-    const int Ks = s1 ? K1 : K0;
-    const bool live = k0 < Ks;
-    d.kvalid = live ? Ks - k0 : 0;
-    const uint16_t* ap = s1 ? a1p : a0p;
-    const uint32_t an = live ? (s1 ? a1n : a0n) : 0u;
-    const uint16_t* bp = s1 ? b1p : b0p;
-    const uint32_t bn = live ? (s1 ? b1n : b0n) : 0u;
-    if constexpr (AK == 0) d.ra = shifted(ap, an, (uint32_t)((s1 ? ako1 : ako0) + k0) * 2u);
-    else d.ra = shifted(ap, an, (uint32_t)k0 * lda2);
-    if constexpr (BKD == 0) d.rb = shifted(bp, bn, (uint32_t)k0 * 2u);
-    else d.rb = shifted(b0p, live ? b0n : 0u, (uint32_t)k0 * ldb2);
-    if constexpr (BKD == 2) d.rb2 = shifted(b1p, live ? b1n : 0u, (uint32_t)k0 * ldb2);
-    else d.rb2 = d.rb;
-    return d;
+  // k range of tile t: segment, first k within it, valid k count (0 past the end)
+  struct KTile {
+    bool s1;
+    int k0, kvalid;
   };
-  auto dma_op = [&](auto J_, const TileDma& d, uint8_t* st) __attribute__((always_inline)) {
-    constexpr int J = decltype(J_)::value;
-    if constexpr (J < NIA) {
-      if constexpr (AK == 0) da.template issue<J>(d.ra, st, d.kvalid, w);
-      else da.template issue<J>(d.ra, st, w);
-    } else {
-      constexpr int JB = J - NIA;
-      if constexpr (BKD == 0) db.template issue<JB>(d.rb, st + A_BYTES, d.kvalid, w);
-      else if constexpr (BKD == 1 || JB < NIB / 2) db.template issue<JB % NIB>(d.rb, st + A_BYTES, w);
-      else db.template issue<JB - NIB / 2>(d.rb2, st + A_BYTES + B_BYTES / 2, w);
-    }
+  auto ktile = [&](int t) __attribute__((always_inline)) {
+    KTile r;
+    r.s1 = t >= nk0;
+    r.k0 = (r.s1 ? t - nk0 : t) * BK;
+    const int Ks = r.s1 ? K1 : K0;
+    r.kvalid = r.k0 < Ks ? Ks - r.k0 : 0;
+    return r;
   };
 
-  // ---- fragment addressing (loop invariant)
-  uint32_t a_koff_s[2], b_koff_s[2];
+  // ---- fragment addressing (relative to a stage)
+  uint32_t a_koff[2] = {0, 0}, b_koff[2] = {0, 0};
   uint32_t a_col[AK == 1 ? TM : 1], b_col[BKD != 0 ? TN : 1];
-  uint32_t a_kb = 0, b_kb = 0;
+  const uint32_t a_region = G * AH_BYTES;
   if constexpr (AK == 0) {
-    a_koff_s[0] = kfrag_off(wm * WM, 0, lane);
-    a_koff_s[1] = kfrag_off(wm * WM, 1, lane);
+    a_koff[0] = a_region + kfrag_off(0, 0, lane);
+    a_koff[1] = a_region + kfrag_off(0, 1, lane);
   } else {
-    a_kb = mn_kbase<BM>(lane);
+    const uint32_t kb = a_region + mn_kbase<HM>(lane);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a_col[i] = a_kb + mn_coloff(wm * WM, i, lane);
+    for (int i = 0; i < TM; ++i) a_col[i] = kb + mn_coloff<HM>(0, i, lane);
   }
   if constexpr (BKD == 0) {
-    b_koff_s[0] = A_BYTES + kfrag_off(wn * WN, 0, lane);
-    b_koff_s[1] = A_BYTES + kfrag_off(wn * WN, 1, lane);
+    b_koff[0] = 2 * AH_BYTES + kfrag_off(q * QN, 0, lane);
+    b_koff[1] = 2 * AH_BYTES + kfrag_off(q * QN, 1, lane);
   } else if constexpr (BKD == 1) {
-    b_kb = A_BYTES + mn_kbase<BN>(lane);
+    const uint32_t kb = 2 * AH_BYTES + mn_kbase<BN>(lane);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b_col[j] = b_kb + mn_coloff(wn * WN, j, lane);
+    for (int j = 0; j < TN; ++j) b_col[j] = kb + mn_coloff<BN>(q * QN, j, lane);
   } else {
-    b_kb = A_BYTES + mn_kbase<BN / 2>(lane);
+    const uint32_t kb = 2 * AH_BYTES + mn_kbase<BN / 2>(lane);
 #pragma unroll
     for (int j = 0; j < TN / 2; ++j) {
-      b_col[j] = b_kb + mn_coloff(wn * QW, j, lane);
-      b_col[j + TN / 2] = b_col[j] + B_BYTES / 2;  // same columns in the up region
+      b_col[j] = kb + mn_coloff<BN / 2>(q * QF, j, lane);
+      b_col[j + TN / 2] = b_col[j] + B_BYTES / 2;  // same features in the up region
     }
   }
 
-  // Read op R (0 <= R < TM + TN) of k-step S from the stage at LDS address sa:
-  // A fragment R, then B fragment R - TM.
-  constexpr int NRD = TM + TN;
-  auto read_op = [&](auto S_, auto R_, uint32_t sa, bf16x8 (&af)[TM], bf16x8 (&bfv)[TN]) __attribute__((always_inline)) {
-    constexpr int S = decltype(S_)::value, R = decltype(R_)::value;
-    if constexpr (R < TM) {
-      if constexpr (AK == 0) {
-        af[R] = ld_b128<R * 2048>(sa + a_koff_s[S]);
-      } else {
-        constexpr int RS = BM * 2;  // k-row stride
-        af[R] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(sa + a_col[R]);
-      }
-    } else {
-      constexpr int J = R - TM;
-      if constexpr (BKD == 0) {
-        bfv[J] = ld_b128<J * 2048>(sa + b_koff_s[S]);
-      } else {
-        constexpr int RS = (BKD == 2 ? BN / 2 : BN) * 2;
-        bfv[J] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(sa + b_col[J]);
-      }
-    }
+  // All fragments of one k-tile (two k-steps of 32) from the stage at sa.
+  bf16x8 af[2][TM], bfr[2][TN];
+  auto read_tile = [&](uint32_t sa) __attribute__((always_inline)) {
+    static_for<2>([&](auto S_) __attribute__((always_inline)) {
+      constexpr int S = decltype(S_)::value;
+      static_for<TM>([&](auto I_) __attribute__((always_inline)) {
+        constexpr int I = decltype(I_)::value;
+        if constexpr (AK == 0) {
+          af[S][I] = ld_b128<I * 2048>(sa + a_koff[S]);
+        } else {
+          constexpr int RS = HM * 2;
+          af[S][I] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(sa + a_col[I]);
+        }
+      });
+      static_for<TN>([&](auto J_) __attribute__((always_inline)) {
+        constexpr int J = decltype(J_)::value;
+        if constexpr (BKD == 0) {
+          bfr[S][J] = ld_b128<J * 2048>(sa + b_koff[S]);
+        } else {
+          constexpr int RS = (BKD == 2 ? BN / 2 : BN) * 2;
+          bfr[S][J] = ld_tr2<S * 32 * RS, S * 32 * RS + 4 * RS>(sa + b_col[J]);
+        }
+      });
+    });
   };
 
   f32x4 acc[TM][TN];
@@ -360,83 +343,135 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // MFMA I of a phase: block (I / TN, I % TN).  Inline asm with the
-  // accumulator tied in place ("+a"): with the builtin the register allocator
-  // rotates the accumulator tile between AGPRs and VGPRs every k-tile (~3
-  // moves per MFMA), which halves the MFMA issue rate.  An accumulator is
-  // reused only TM*TN MFMAs later, far beyond the dependent-MFMA latency.
-  constexpr int NMF = TM * TN;
-  auto mfma_op = [](auto I_, f32x4 (&c)[TM][TN], const bf16x8 (&af)[TM], const bf16x8 (&bfv)[TN]) __attribute__((always_inline)) {
-    constexpr int I = decltype(I_)::value;
+  // The 2*TM*TN MFMAs of one k-tile.  Inline asm with the accumulator tied in
+  // place ("+a"): with the builtin the register allocator rotates accumulators
+  // between AGPRs and VGPRs.  An accumulator is reused only TM*TN MFMAs later.
+  auto mfma_op = [](auto S_, auto I_, f32x4 (&c)[TM][TN], const bf16x8 (&a)[2][TM], const bf16x8 (&b)[2][TN])
+      __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value, I = decltype(I_)::value;
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
                  : "+a"(c[I / TN][I % TN])
-                 : "v"(bfv[I % TN]), "v"(af[I / TN]));
+                 : "v"(b[S][I % TN]), "v"(a[S][I / TN]));
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  // First memory op of a phase waits this many MFMAs, so the MFMAs that read
-  // the fragment registers of the previous phase have issued.  Ops that do
-  // not fit between the MFMAs (small tiles) follow them.
-  constexpr int LAG = 2;
-
-  // ---- prologue: tiles 0 and 1 in flight, tile 0 published, its step-0
-  // fragments read
-  {
-    const TileDma d0 = tile_dma(0), d1 = tile_dma(1);
-    static_for<NI_TILE>([&](auto J) __attribute__((always_inline)) { dma_op(J, d0, stage0); });
-    static_for<NI_TILE>([&](auto J) __attribute__((always_inline)) { dma_op(J, d1, stage1); });
-  }
-  wait_vmcnt<NI_TILE>();
-  __syncthreads();
-  bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-  const uint32_t st0 = lds_addr(stage0), st1 = lds_addr(stage1);
-  static_for<NRD>([&](auto R) __attribute__((always_inline)) { read_op(S0{}, R, st0, a0, b0); });
-
-  for (int t = 0; t < nk; ++t) {
-    const uint32_t cur = (t & 1) ? st1 : st0, nxt = (t & 1) ? st0 : st1;
-    uint8_t* cur_p = (t & 1) ? stage1 : stage0;
-    const TileDma dn = tile_dma(t + 2);
-    // phase A: step-0 MFMAs of tile t; step-1 fragments of tile t read in between
-    wait_lgkm0();
-    static_for<NMF>([&](auto I) __attribute__((always_inline)) {
-      mfma_op(I, acc, a0, b0);
-      constexpr int R = decltype(I)::value - LAG;
-      if constexpr (R >= 0 && R < NRD) read_op(S1{}, std::integral_constant<int, R>{}, cur, a1, b1);
+  auto compute_tile = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    static_for<TM * TN>([&](auto I) __attribute__((always_inline)) {
+      mfma_op(std::integral_constant<int, 0>{}, I, acc, af, bfr);
     });
-    static_for<NRD>([&](auto R) __attribute__((always_inline)) {
-      if constexpr (decltype(R)::value + LAG >= NMF) read_op(S1{}, R, cur, a1, b1);
+    static_for<TM * TN>([&](auto I) __attribute__((always_inline)) {
+      mfma_op(std::integral_constant<int, 1>{}, I, acc, af, bfr);
     });
-    // this wave's DMA of tile t+1 has landed, its reads of stage cur are done;
-    // after the barrier, everyone's are
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-    // phase B: step-1 MFMAs of tile t; step-0 fragments of tile t+1 read from
-    // stage nxt, then the DMA of tile t+2 issued into stage cur
-    auto phase_b_op = [&](auto P_) __attribute__((always_inline)) {
-      constexpr int P = decltype(P_)::value;
-      if constexpr (P < NRD) read_op(S0{}, P_, nxt, a0, b0);
-      else dma_op(std::integral_constant<int, P - NRD>{}, dn, cur_p);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  const uint32_t st0 = lds_addr(smem);
+  auto stage_addr = [&](int t) __attribute__((always_inline)) { return st0 + (t & 1) * STAGE; };
+  auto stage_ptr = [&](int t) __attribute__((always_inline)) { return smem + (t & 1) * STAGE; };
+
+  if (G == 0) {
+    // -------- group 0: rows 0 .. HM-1 of the tile; DMA of B
+    typename std::conditional<BKD == 0, DmaK<BN>, DmaMN<(BKD == 2 ? BN / 2 : BN)>>::type db;
+    db.init(n0, g.N, g.ldb, lane, q);
+    const uint32_t ldb2 = (uint32_t)(g.ldb * 2);
+    constexpr int NIB = BN / 32;  // B instructions per wave per tile
+    auto issue_b = [&](int t) __attribute__((always_inline)) {
+      const KTile kt = ktile(t);
+      const bool live = kt.kvalid > 0;
+      uint8_t* region = stage_ptr(t) + 2 * AH_BYTES;
+      if constexpr (BKD == 0) {
+        const rsrc_t rb = shifted(kt.s1 ? g.b[1] : g.b[0], live ? (kt.s1 ? g.b_bytes[1] : g.b_bytes[0]) : 0u,
+                                  (uint32_t)kt.k0 * 2u);
+        static_for<NIB>([&](auto J) __attribute__((always_inline)) {
+          db.template issue<decltype(J)::value>(rb, region, kt.kvalid, q);
+        });
+      } else if constexpr (BKD == 1) {
+        const rsrc_t rb = shifted(g.b[0], live ? g.b_bytes[0] : 0u, (uint32_t)kt.k0 * ldb2);
+        static_for<NIB>([&](auto J) __attribute__((always_inline)) {
+          db.template issue<decltype(J)::value>(rb, region, q);
+        });
+      } else {
+        const rsrc_t rg = shifted(g.b[0], live ? g.b_bytes[0] : 0u, (uint32_t)kt.k0 * ldb2);
+        const rsrc_t ru = shifted(g.b[1], live ? g.b_bytes[1] : 0u, (uint32_t)kt.k0 * ldb2);
+        static_for<NIB / 2>([&](auto J) __attribute__((always_inline)) {
+          db.template issue<decltype(J)::value>(rg, region, q);
+        });
+        static_for<NIB / 2>([&](auto J) __attribute__((always_inline)) {
+          db.template issue<decltype(J)::value>(ru, region + B_BYTES / 2, q);
+        });
+      }
     };
-    // Reads in MFMA slots 1..NRD; DMA op d after MFMA 1 + 3d (a burst of
-    // buffer loads stalls MFMA issue; spread out they cost ~6% less).
-    constexpr int DMA_STRIDE = 3;
-    static_for<NMF>([&](auto I) __attribute__((always_inline)) {
-      mfma_op(I, acc, a1, b1);
-      constexpr int Iv = decltype(I)::value;
-      if constexpr (Iv >= 1 && Iv - 1 < NRD) phase_b_op(std::integral_constant<int, Iv - 1>{});
-      constexpr int D = (Iv - 1) / DMA_STRIDE;
-      if constexpr (Iv >= 1 && (Iv - 1) % DMA_STRIDE == 0 && D < NI_TILE)
-        phase_b_op(std::integral_constant<int, NRD + D>{});
-    });
-    static_for<NI_TILE>([&](auto D) __attribute__((always_inline)) {
-      if constexpr (1 + decltype(D)::value * DMA_STRIDE >= NMF)
-        phase_b_op(std::integral_constant<int, NRD + decltype(D)::value>{});
-    });
-    static_for<NRD>([&](auto P) __attribute__((always_inline)) {
-      if constexpr (decltype(P)::value + 1 >= NMF) phase_b_op(P);
-    });
+    // prologue: B of tile 0 (group 1 loads the A rows of tile 0 and group 0's
+    // A rows of tile 1)
+    issue_b(0);
+    wait_vmcnt<0>();
+    barrier();
+    for (int s = 0; s < nk; ++s) {
+      // memory phase: fragments of tile s, DMA of B of tile s+1
+      read_tile(stage_addr(s));
+      issue_b(s + 1);
+      wait_lgkm0();
+      barrier();
+      // compute phase: tile s; B of tile s+1 must land before the next memory phase
+      compute_tile();
+      wait_vmcnt<0>();
+      barrier();
+    }
+  } else {
+    // -------- group 1: rows HM .. BM-1 of the tile; DMA of both A halves
+    typename std::conditional<AK == 0, DmaK<HM>, DmaMN<HM>>::type dtop, dbot;
+    dtop.init(m0, g.M, g.lda, lane, q);
+    dbot.init(m0 + HM, g.M, g.lda, lane, q);
+    const uint32_t lda2 = (uint32_t)(g.lda * 2);
+    constexpr int NIA = HM / 32;  // instructions per wave per half tile
+    // A rows of group `half` (0: rows 0..HM-1, 1: rows HM..BM-1) of tile t
+    auto issue_a = [&](int t, auto half_) __attribute__((always_inline)) {
+      constexpr int HALF = decltype(half_)::value;
+      const KTile kt = ktile(t);
+      const bool live = kt.kvalid > 0;
+      const uint16_t* ap = kt.s1 ? g.a[1] : g.a[0];
+      const uint32_t an = live ? (kt.s1 ? g.a_bytes[1] : g.a_bytes[0]) : 0u;
+      uint8_t* region = stage_ptr(t) + HALF * AH_BYTES;
+      const auto& d = HALF == 0 ? dtop : dbot;
+      if constexpr (AK == 0) {
+        const rsrc_t ra = shifted(ap, an, (uint32_t)((kt.s1 ? g.a_koff[1] : g.a_koff[0]) + kt.k0) * 2u);
+        static_for<NIA>([&](auto J) __attribute__((always_inline)) {
+          d.template issue<decltype(J)::value>(ra, region, kt.kvalid, q);
+        });
+      } else {
+        const rsrc_t ra = shifted(ap, an, (uint32_t)kt.k0 * lda2);
+        static_for<NIA>([&](auto J) __attribute__((always_inline)) {
+          d.template issue<decltype(J)::value>(ra, region, q);
+        });
+      }
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    issue_a(0, H1{});
+    issue_a(0, H0{});
+    issue_a(1, H0{});
+    wait_vmcnt<0>();
+    barrier();
+    barrier();  // group 0's first memory phase
+    for (int s = 0; s < nk; ++s) {
+      // memory phase: fragments of tile s; DMA of this group's rows of tile
+      // s+1 and group 0's rows of tile s+2; group 0's rows of tile s+1 must
+      // land before its next memory phase
+      read_tile(stage_addr(s));
+      issue_a(s + 1, H1{});
+      issue_a(s + 2, H0{});
+      wait_lgkm0();
+      wait_vmcnt<2 * NIA>();
+      barrier();
+      // compute phase: tile s; this group's rows of tile s+1 must land before
+      // its next memory phase
+      compute_tile();
+      if (s + 1 < nk) {
+        wait_vmcnt<NIA>();
+        barrier();
+      }
+    }
   }
-  wait_vmcnt<0>();  // no DMA may land after the block has left
+  wait_vmcnt<0>();  // no DMA may land after the wave has left
   wait_lgkm0();
 
   // The compiler cannot see the asm MFMAs: give the last ones time to write
@@ -444,17 +479,17 @@ gemm_kernel(const GemmArgs g) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
 
   // ------------------------------------------------------------------ epilogue
-  // Lane holds C[m][n .. n+3] of block (i, j) with m = m0 + wm*WM + i*16 + l16,
-  // n = n0 + wn*WN + j*16 + 4*lq (SwiGLU: feature f = n0 + wn*QW + j*16 + 4*lq).
+  // Lane holds C[m][n .. n+3] of block (i, j) with m = m0 + G*HM + i*16 + l16,
+  // n = n0 + q*QN + j*16 + 4*lq (SwiGLU: feature f = n0 + q*QF + j*16 + 4*lq).
   const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WM + i * 16 + l16;
+    const int m = m0 + G * HM + i * 16 + l16;
     if (m >= g.M) continue;
     if constexpr (EPI == EPI_STORE_BF16) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 16 + 4 * lq;
+        const int n = n0 + q * QN + j * 16 + 4 * lq;
         if (n < g.N) {
           uint2 v = make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.c0) + (int64_t)m * g.ldc + n) = v;
@@ -463,7 +498,7 @@ gemm_kernel(const GemmArgs g) {
     } else if constexpr (EPI == EPI_STORE_F32_SPLIT) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 16 + 4 * lq;
+        const int n = n0 + q * QN + j * 16 + 4 * lq;
         if (n < g.N) {
           float* dst = n < g.c_split ? static_cast<float*>(g.c0) + (int64_t)m * g.ldc + n
                                      : static_cast<float*>(g.c1) + (int64_t)m * g.ldc + (n - g.c_split);
@@ -473,7 +508,7 @@ gemm_kernel(const GemmArgs g) {
     } else if constexpr (EPI == EPI_ACT_FWD) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 16 + 4 * lq;
+        const int n = n0 + q * QN + j * 16 + 4 * lq;
         if (n < g.N) {
           const int64_t off = (int64_t)m * g.ldc + n;
           float a[4];
@@ -489,7 +524,7 @@ gemm_kernel(const GemmArgs g) {
     } else if constexpr (EPI == EPI_SWIGLU_FWD) {
 #pragma unroll
       for (int j = 0; j < TN / 2; ++j) {
-        const int f = n0 + wn * QW + j * 16 + 4 * lq;
+        const int f = n0 + q * QF + j * 16 + 4 * lq;
         if (f < g.N) {
           const int64_t off = (int64_t)m * g.ldc + f;
           const f32x4 gt = acc[i][j], up = acc[i][j + TN / 2];
@@ -507,7 +542,7 @@ gemm_kernel(const GemmArgs g) {
     } else if constexpr (EPI == EPI_ACT_BWD) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 16 + 4 * lq;
+        const int n = n0 + q * QN + j * 16 + 4 * lq;
         if (n < g.N) {
           const int64_t off = (int64_t)m * g.ldc + n;
           const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.e0) + (int64_t)m * g.lde + n);
@@ -522,7 +557,7 @@ gemm_kernel(const GemmArgs g) {
     } else {  // EPI_SWIGLU_BWD: dU row is [dG | dP], ldc = 2 * F_i, stashes have ld = lde
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 16 + 4 * lq;
+        const int n = n0 + q * QN + j * 16 + 4 * lq;
         if (n < g.N) {
           const int64_t so = (int64_t)m * g.lde + n;
           const uint2 gb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.e0) + so);
@@ -552,14 +587,18 @@ struct TileCfg {
 };
 
 // Pick the block tile that minimises (waves of num_cu blocks) x (cost per
-// tile), cost per tile ~ bm*bn / efficiency.  Larger tiles re-read less from
-// L2 and LDS per flop; the wave count captures quantisation on the CUs.
+// tile), cost per tile ~ bm*bn / efficiency.  Larger tiles move fewer bytes
+// from L2 per flop, which matters twice on a power-limited chip (the clock
+// drops with data movement); the wave count captures quantisation on the CUs.
+// The 256x192 weight was fitted to timings of both tiles on the weight-
+// gradient, down-projection and up-projection shapes of the 7B-, GPT-3- and
+// 70B-class shards; the smaller tiles' weights are estimates.
 TileCfg choose_tile(int M, int N_cols, bool swiglu_fwd, int num_cu) {
-  static const TileCfg cands[] = {{256, 256}, {256, 192}, {192, 256}, {256, 128}, {128, 256}, {128, 128}};
-  static const double eff[] = {1.0, 0.97, 0.97, 0.90, 0.90, 0.75};
+  static const TileCfg cands[] = {{256, 256}, {256, 192}, {256, 128}, {128, 256}, {128, 128}};
+  static const double eff[] = {1.0, 0.87, 0.72, 0.72, 0.5};
   double best = 1e300;
   TileCfg bc = {256, 256};
-  for (int c = 0; c < 6; ++c) {
+  for (int c = 0; c < 5; ++c) {
     const int bm = cands[c].bm, bn = cands[c].bn;
     if (swiglu_fwd && bn == 192) continue;
     const int cols_per_tile = swiglu_fwd ? bn / 2 : bn;
@@ -592,7 +631,6 @@ hipError_t launch_any(const GemmArgs& g, TileCfg t, hipStream_t st) {
   if constexpr (BKD != 2) {
     if (t.bm == 256 && t.bn == 192) return launch_cfg<256, 192, AK, BKD, EPI, ACT>(g, st);
   }
-  if (t.bm == 192 && t.bn == 256) return launch_cfg<192, 256, AK, BKD, EPI, ACT>(g, st);
   if (t.bm == 256 && t.bn == 128) return launch_cfg<256, 128, AK, BKD, EPI, ACT>(g, st);
   if (t.bm == 128 && t.bn == 256) return launch_cfg<128, 256, AK, BKD, EPI, ACT>(g, st);
   return launch_cfg<128, 128, AK, BKD, EPI, ACT>(g, st);
