@@ -5,10 +5,12 @@ and the ``cpu_baseline`` leg of ``bench.py``, never by the GPU library or its
 binding.  See ``oracle/mlp.py`` for what it computes and which passages it
 follows.
 """
-from .mlp import (ACTS, act_backward, act_forward, bf16_bits_to_f64,
-                  column_block, column_sum, reduce_partials, shard_backward,
+from .mlp import (ACTS, act_backward, act_forward, all_gather,
+                  bf16_bits_to_f64, column_block, column_sum, reduce_partials,
+                  reduce_scatter, sequence_block, shard_backward,
                   shard_forward, shard_weights, tp_backward, tp_forward)
 
-__all__ = ["ACTS", "act_backward", "act_forward", "bf16_bits_to_f64",
-           "column_block", "column_sum", "reduce_partials", "shard_backward",
+__all__ = ["ACTS", "act_backward", "act_forward", "all_gather",
+           "bf16_bits_to_f64", "column_block", "column_sum", "reduce_partials",
+           "reduce_scatter", "sequence_block", "shard_backward",
            "shard_forward", "shard_weights", "tp_backward", "tp_forward"]

@@ -26,7 +26,13 @@ tensor-parallel split, in float64, with no intermediate rounding:
   derivative, local weight gradients, and a per-rank partial input gradient
   that must be summed over ranks ("Parallelism Strategies #1 - Tensor
   Parallelism", the sharded backward derivation and its code; "Tensor and
-  sequence parallelism", the table of the f and g operators).
+  sequence parallelism", the table of the f and g operators);
+* the sequence-parallel boundary of that region: on leaving it, the partial
+  sums are added and split back into contiguous sequence blocks (a
+  reduce-scatter; the output bias once and the residual branch are added on
+  the rank's block); on entering it, the blocks are concatenated in rank order
+  (an all-gather) ("Tensor and sequence parallelism", section "Sequence
+  parallelism").
 
 Matrices are in math layout (input dim first): X [N, h], W1 [h, F],
 W2 [F, h].  The pages that store weights PyTorch-style as (out, in) describe
@@ -261,3 +267,44 @@ def tp_backward(act: str, X, W1, W2, dY, t: int, Wg=None):
 def column_sum(dY):
     """db2 = sum over token rows of dY (gradient of the once-added bias)."""
     return np.asarray(dY, dtype=np.float64).sum(axis=0)
+
+
+# --------------------------------------------------------------------------
+# Sequence-parallel boundary of the tensor-parallel region
+# --------------------------------------------------------------------------
+def sequence_block(rank: int, t: int, rows: int) -> slice:
+    """Token rows handled by ``rank`` outside the tensor-parallel region under
+    sequence parallelism: the contiguous block [rank*rows/t, (rank+1)*rows/t)
+    ("Tensor and sequence parallelism", section "Sequence parallelism" and
+    the rows slice of its check script).  rows must divide by t."""
+    if t < 1 or rows % t != 0:
+        raise ValueError(f"rows={rows} must be a multiple of t={t}")
+    if not 0 <= rank < t:
+        raise ValueError(f"rank {rank} outside [0, {t})")
+    n = rows // t
+    return slice(rank * n, (rank + 1) * n)
+
+
+def reduce_scatter(partials, rank: int, bias=None, residual=None):
+    """Leaving the tensor-parallel region under sequence parallelism: the t
+    ranks' full-shape partial sums are added (rank order) and only rank
+    ``rank``'s sequence block is kept; the output bias is added once and the
+    residual branch (the rank's block, [rows/t, cols]) is added on it
+    ("Tensor and sequence parallelism", section "Sequence parallelism": the
+    partial sums are summed and split back into sequence shards; the residual
+    additions are in the sequence-parallel region).  Returns the rank's block
+    of reduce_partials(partials, bias), plus the residual."""
+    t = len(partials)
+    rows = np.asarray(partials[0]).shape[0]
+    blk = sequence_block(rank, t, rows)
+    out = reduce_partials([np.asarray(p)[blk] for p in partials], bias)
+    if residual is not None:
+        out = out + np.asarray(residual, dtype=np.float64)
+    return out
+
+
+def all_gather(shards):
+    """Entering the tensor-parallel region under sequence parallelism: the t
+    sequence blocks are concatenated along the token rows in rank order
+    ("Tensor and sequence parallelism", section "Sequence parallelism")."""
+    return np.concatenate([np.asarray(x, dtype=np.float64) for x in shards], axis=0)
