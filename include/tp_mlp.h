@@ -159,14 +159,61 @@ tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X,
  *   partials  HOST array of t DEVICE pointers, each bf16 [rows, cols]
  *   bias      bf16 [cols] or NULL
  *   out       bf16 [rows, cols]; may coincide exactly with any partials[k]
- *             (each output chunk is written after its inputs are read), no
- *             other overlap.
- * Requires 1 <= t <= 64, rows >= 1, cols % 8 == 0, 16-byte alignment. */
+ *             (each output chunk is written after its inputs are read); any
+ *             other overlap with a partial is rejected (INVALID_ARG).
+ * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), rows >= 1, cols % 8 == 0,
+ * 16-byte alignment. */
 tp_mlp_status tp_mlp_reduce_partials_local(int32_t t,
                                            const void* const* partials,
                                            int64_t rows, int64_t cols,
                                            const void* bias, void* out,
                                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sequence-parallel boundary ("Tensor and sequence parallelism", section
+ * "Sequence parallelism").  Outside the tensor-parallel region the token rows
+ * are split into t contiguous blocks, rank r holding rows
+ * [r*rows/t, (r+1)*rows/t).  Leaving the region, the partial sums are added
+ * and split back into those blocks (a reduce-scatter); entering it, the
+ * blocks are concatenated (an all-gather).  Together they move the same data
+ * as the all-reduce they replace.  These are the local stand-ins: all t
+ * inputs are on this GPU.
+ * ------------------------------------------------------------------------ */
+
+/* Leaving the region (and the backward of entering it, for the partial input
+ * gradients): rank `rank`'s block of the reduced sum, with the output bias
+ * added once and the residual branch of that block fused in:
+ *   out[i][c] = bf16( sum_{k<t} float(partials[k][rank*rows/t + i][c])
+ *                     + bias[c] + residual[i][c] )
+ * summed in float32 in rank order, then the bias, then the residual, one
+ * rounding.
+ *   partials  HOST array of t DEVICE pointers, each bf16 [rows, cols]
+ *   rank      0 <= rank < t; rows % t == 0
+ *   bias      bf16 [cols] or NULL
+ *   residual  bf16 [rows/t, cols] or NULL
+ *   out       bf16 [rows/t, cols]; may coincide exactly with the residual or
+ *             with rank's block of any partials[k]; other overlap with an
+ *             input is rejected (INVALID_ARG).
+ * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), cols % 8 == 0, 16-byte
+ * alignment. */
+tp_mlp_status tp_mlp_reduce_scatter_local(int32_t t,
+                                          const void* const* partials,
+                                          int64_t rows, int64_t cols,
+                                          int32_t rank, const void* bias,
+                                          const void* residual, void* out,
+                                          hipStream_t stream);
+
+/* Entering the region (and the backward of leaving it, for the output
+ * gradient): the t blocks stacked in rank order,
+ *   out[r*shard_rows + i][c] = shards[r][i][c]   (a bitwise copy).
+ *   shards  HOST array of t DEVICE pointers, each bf16 [shard_rows, cols]
+ *   out     bf16 [t*shard_rows, cols]; must not overlap any shard
+ *           (INVALID_ARG).
+ * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), shard_rows >= 1,
+ * cols % 8 == 0, 16-byte alignment. */
+tp_mlp_status tp_mlp_all_gather_local(int32_t t, const void* const* shards,
+                                      int64_t shard_rows, int64_t cols,
+                                      void* out, hipStream_t stream);
 
 /* Workspace bytes needed by tp_mlp_fwd_shard (backward = 0) or
  * tp_mlp_bwd_shard (backward = 1) for shape s; 0 means none.  Returns 0 for

@@ -52,6 +52,9 @@ _SIGS = {
     "tp_mlp_fwd_shard": [POINTER(Shape)] + [c_void_p] * 9 + [c_size_t, c_void_p],
     "tp_mlp_bwd_shard": [POINTER(Shape)] + [c_void_p] * 15 + [c_size_t, c_void_p],
     "tp_mlp_reduce_partials_local": [c_int32, POINTER(c_void_p), c_int64, c_int64, c_void_p, c_void_p, c_void_p],
+    "tp_mlp_reduce_scatter_local": [c_int32, POINTER(c_void_p), c_int64, c_int64, c_int32, c_void_p, c_void_p,
+                                    c_void_p, c_void_p],
+    "tp_mlp_all_gather_local": [c_int32, POINTER(c_void_p), c_int64, c_int64, c_void_p, c_void_p],
     "tp_mlp_up_act_shard": [POINTER(Shape)] + [c_void_p] * 6 + [c_void_p],
     "tp_mlp_down_shard": [POINTER(Shape)] + [c_void_p] * 3 + [c_void_p],
     "tp_mlp_down_dgrad_act_shard": [POINTER(Shape)] + [c_void_p] * 5 + [c_void_p],
@@ -181,6 +184,37 @@ def tp_mlp_reduce_partials_local(partials, out, bias=None, stream=None):
     _check("tp_mlp_reduce_partials_local",
            lib().tp_mlp_reduce_partials_local(t, ptrs, rows, cols, _p(bias, BF16, cols, "bias", optional=True),
                                               _p(out, BF16, rows * cols, "out"), _stream(stream)))
+
+
+def _ptr_list(tensors, name):
+    t = len(tensors)
+    if t == 0:
+        raise ValueError(f"need at least one of {name}")
+    rows, cols = tensors[0].shape
+    for x in tensors:
+        if tuple(x.shape) != (rows, cols):
+            raise ValueError(f"{name} must share one shape")
+    ptrs = (c_void_p * t)(*[_p(x, BF16, rows * cols, f"{name}[{i}]") for i, x in enumerate(tensors)])
+    return t, rows, cols, ptrs
+
+
+def tp_mlp_reduce_scatter_local(partials, out, rank, bias=None, residual=None, stream=None):
+    """out = rank's block of rows of sum(partials) (+ bias once, + residual);
+    partials: list of t equal-shape bf16 [rows, cols] device tensors, rows
+    divisible by t; out and residual are [rows / t, cols]."""
+    t, rows, cols, ptrs = _ptr_list(partials, "partials")
+    n = rows // t
+    _check("tp_mlp_reduce_scatter_local", lib().tp_mlp_reduce_scatter_local(
+        t, ptrs, rows, cols, rank, _p(bias, BF16, cols, "bias", optional=True),
+        _p(residual, BF16, n * cols, "residual", optional=True), _p(out, BF16, n * cols, "out"),
+        _stream(stream)))
+
+
+def tp_mlp_all_gather_local(shards, out, stream=None):
+    """out = the t bf16 [shard_rows, cols] shards stacked along rows in order."""
+    t, rows, cols, ptrs = _ptr_list(shards, "shards")
+    _check("tp_mlp_all_gather_local", lib().tp_mlp_all_gather_local(
+        t, ptrs, rows, cols, _p(out, BF16, t * rows * cols, "out"), _stream(stream)))
 
 
 def tp_mlp_up_act_shard(shape: Shape, X, W1_i, Wg_i, A_i, U_i=None, G_i=None, stream=None):

@@ -224,6 +224,30 @@ hipError_t run_dgrad_up(const Dims& d, const void* dU, const void* W1, const voi
   return gemm_launch(GEMM_DGRAD, d.act, g, num_cu_current(), st);
 }
 
+// A host array of t device pointers to bf16 [rows, cols] blocks: INVALID_ARG
+// for a malformed list or shape, UNSUPPORTED for t above MAX_T.
+tp_mlp_status partial_list(int32_t t, const void* const* ptrs, int64_t rows, int64_t cols, PartialPtrs& pp) {
+  if (ptrs == nullptr || t < 1) return TP_MLP_ERR_INVALID_ARG;
+  if (t > MAX_T) return TP_MLP_ERR_UNSUPPORTED;
+  if (rows < 1 || cols < 8 || cols % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
+  if (rows > (int64_t)1 << 40 || cols > (int64_t)1 << 40) return TP_MLP_ERR_INVALID_ARG;
+  for (int r = 0; r < t; ++r) {
+    if (!req(ptrs[r])) return TP_MLP_ERR_INVALID_ARG;
+    pp.p[r] = cu16(ptrs[r]);
+  }
+  return TP_MLP_OK;
+}
+
+// Byte ranges [a, a+na) and [b, b+nb) do not overlap (an empty range never does).
+bool disjoint(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na == 0 || nb == 0 || x + na <= y || y + nb <= x;
+}
+// ...or coincide exactly.
+bool same_or_disjoint(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  return (a == b && na == nb) || disjoint(a, na, b, nb);
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,18 +396,49 @@ tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X, const void*
 
 tp_mlp_status tp_mlp_reduce_partials_local(int32_t t, const void* const* partials, int64_t rows, int64_t cols,
                                            const void* bias, void* out, hipStream_t stream) {
-  if (t < 1 || t > MAX_T || partials == nullptr || rows < 1 || cols < 8 || cols % 8 != 0) {
-    if (t > MAX_T && partials != nullptr) return TP_MLP_ERR_UNSUPPORTED;
-    return TP_MLP_ERR_INVALID_ARG;
-  }
-  if (!req(out) || !opt_aligned(bias)) return TP_MLP_ERR_INVALID_ARG;
   PartialPtrs pp = {};
+  if (const tp_mlp_status ss = partial_list(t, partials, rows, cols, pp)) return ss;
+  if (!req(out) || !opt_aligned(bias)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t bytes = (uint64_t)rows * (uint64_t)cols * 2;
+  for (int r = 0; r < t; ++r)
+    if (!same_or_disjoint(out, bytes, pp.p[r], bytes)) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(
+      reduce_partials_launch(pp, t, rows, cols, 0, cu16(bias), nullptr, u16(out), num_cu_current(), stream));
+}
+
+tp_mlp_status tp_mlp_reduce_scatter_local(int32_t t, const void* const* partials, int64_t rows, int64_t cols,
+                                          int32_t rank, const void* bias, const void* residual, void* out,
+                                          hipStream_t stream) {
+  PartialPtrs pp = {};
+  if (const tp_mlp_status ss = partial_list(t, partials, rows, cols, pp)) return ss;
+  if (rows % t != 0 || rank < 0 || rank >= t) return TP_MLP_ERR_INVALID_ARG;
+  if (!req(out) || !opt_aligned(bias) || !opt_aligned(residual)) return TP_MLP_ERR_INVALID_ARG;
+  const int64_t shard = rows / t;
+  const uint64_t out_bytes = (uint64_t)shard * (uint64_t)cols * 2;
+  const uint64_t block_off = (uint64_t)rank * out_bytes;
+  // out may coincide with the rank's block of a partial or with the residual;
+  // it must not otherwise overlap any input
   for (int r = 0; r < t; ++r) {
-    if (!req(partials[r])) return TP_MLP_ERR_INVALID_ARG;
-    pp.p[r] = cu16(partials[r]);
+    const uint8_t* blk = reinterpret_cast<const uint8_t*>(pp.p[r]) + block_off;
+    if (!same_or_disjoint(out, out_bytes, blk, out_bytes)) return TP_MLP_ERR_INVALID_ARG;
+    if (!disjoint(out, out_bytes, pp.p[r], block_off) ||
+        !disjoint(out, out_bytes, blk + out_bytes, (uint64_t)(t - 1 - rank) * out_bytes))
+      return TP_MLP_ERR_INVALID_ARG;
   }
-  if (rows > (int64_t)1 << 40 || cols > (int64_t)1 << 40) return TP_MLP_ERR_INVALID_ARG;
-  return hip_status(reduce_partials_launch(pp, t, rows, cols, cu16(bias), u16(out), num_cu_current(), stream));
+  if (residual && !same_or_disjoint(out, out_bytes, residual, out_bytes)) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(reduce_partials_launch(pp, t, shard, cols, (int64_t)rank * shard, cu16(bias), cu16(residual),
+                                           u16(out), num_cu_current(), stream));
+}
+
+tp_mlp_status tp_mlp_all_gather_local(int32_t t, const void* const* shards, int64_t shard_rows, int64_t cols,
+                                      void* out, hipStream_t stream) {
+  PartialPtrs pp = {};
+  if (const tp_mlp_status ss = partial_list(t, shards, shard_rows, cols, pp)) return ss;
+  if (!req(out)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t shard_bytes = (uint64_t)shard_rows * (uint64_t)cols * 2;
+  for (int r = 0; r < t; ++r)
+    if (!disjoint(out, shard_bytes * (uint64_t)t, pp.p[r], shard_bytes)) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(gather_launch(pp, t, shard_rows, cols, u16(out), num_cu_current(), stream));
 }
 
 }  // extern "C"

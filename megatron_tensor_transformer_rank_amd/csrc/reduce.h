@@ -12,8 +12,14 @@ struct PartialPtrs {
   const uint16_t* p[MAX_T];
 };
 
-hipError_t reduce_partials_launch(const PartialPtrs& pp, int t, int64_t rows, int64_t cols, const uint16_t* bias,
-                                  uint16_t* out, int num_cu, hipStream_t st);
+// out [rows, cols] = sum_{r<t} pp.p[r][row0 + i, :] (rank order, float32)
+// + bias (once, may be NULL) + residual[i, :] (may be NULL), one rounding.
+hipError_t reduce_partials_launch(const PartialPtrs& pp, int t, int64_t rows, int64_t cols, int64_t row0,
+                                  const uint16_t* bias, const uint16_t* residual, uint16_t* out, int num_cu,
+                                  hipStream_t st);
+// out [t * shard_rows, cols] = the t shards [shard_rows, cols] stacked in order.
+hipError_t gather_launch(const PartialPtrs& shards, int t, int64_t shard_rows, int64_t cols, uint16_t* out,
+                         int num_cu, hipStream_t st);
 // db2 = column sums of dY; part is col_sum_workspace_bytes(rows, cols) of
 // device scratch.
 size_t col_sum_workspace_bytes(int64_t rows, int64_t cols);

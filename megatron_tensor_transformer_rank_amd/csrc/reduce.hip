@@ -2,55 +2,116 @@
 // g's forward and f's backward, "Tensor and sequence parallelism", table of
 // f and g) with the output bias added once after the sum ("Tensor
 // Parallelism's Communication Boundary", on adding a bias before a
-// reduction), and the column sums of dY that are that bias's gradient.
+// reduction); its sequence-parallel form, the reduce-scatter that keeps one
+// rank's block of token rows and adds the residual branch there, and the
+// all-gather that concatenates the blocks ("Tensor and sequence
+// parallelism", section "Sequence parallelism"); and the column sums of dY
+// that are the bias's gradient.
 //
-// Both are HBM-bound streams: 16-byte loads, float32 accumulation in rank
-// order, one rounding to bf16, grid-stride over 8-element chunks.
+// All are HBM-bound streams of 16-byte chunks.  The partial sums are read
+// once, with non-temporal loads, four ranks and two chunks per thread in
+// flight at a time; float32 accumulation in rank order, then the bias, then
+// the residual, and one rounding to bf16.
 #include "common.h"
 #include "reduce.h"
 
 namespace tpmlp {
 
 constexpr int RD_THREADS = 256;
+constexpr int RD_UNROLL = 2;   // output chunks per thread per iteration
+constexpr int RD_BATCH = 4;    // ranks loaded before they are added
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld_stream(const uint16_t* p, int64_t chunk) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + chunk);
+}
+__device__ __forceinline__ void add8(float (&s)[8], u32x4 v) {
+  s[0] += bf16lo(v.x); s[1] += bf16hi(v.x);
+  s[2] += bf16lo(v.y); s[3] += bf16hi(v.y);
+  s[4] += bf16lo(v.z); s[5] += bf16hi(v.z);
+  s[6] += bf16lo(v.w); s[7] += bf16hi(v.w);
+}
+
+// out chunk q (0 <= q < n_out) = sum_{r<t} p[r][in_off + q] + bias[q % cols8]
+// + residual[q].  Consecutive threads take consecutive chunks.
 __global__ void __launch_bounds__(RD_THREADS)
-reduce_partials_kernel(PartialPtrs pp, int t, int64_t n_chunks, int cols8, const uint16_t* __restrict__ bias,
-                       uint16_t* out) {
-  for (int64_t q = (int64_t)blockIdx.x * RD_THREADS + threadIdx.x; q < n_chunks;
-       q += (int64_t)gridDim.x * RD_THREADS) {
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < t; ++r) {
-      const uint4 v = reinterpret_cast<const uint4*>(pp.p[r])[q];
-      s[0] += bf16lo(v.x); s[1] += bf16hi(v.x);
-      s[2] += bf16lo(v.y); s[3] += bf16hi(v.y);
-      s[4] += bf16lo(v.z); s[5] += bf16hi(v.z);
-      s[6] += bf16lo(v.w); s[7] += bf16hi(v.w);
+reduce_kernel(PartialPtrs pp, int t, int64_t n_out, int64_t in_off, int cols8, const uint16_t* __restrict__ bias,
+              const uint16_t* __restrict__ residual, uint16_t* out) {
+  const int64_t step = (int64_t)gridDim.x * RD_THREADS * RD_UNROLL;
+  for (int64_t q0 = (int64_t)blockIdx.x * RD_THREADS * RD_UNROLL + threadIdx.x; q0 < n_out; q0 += step) {
+    float s[RD_UNROLL][8];
+#pragma unroll
+    for (int u = 0; u < RD_UNROLL; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[u][e] = 0.f;
+    for (int r0 = 0; r0 < t; r0 += RD_BATCH) {
+      u32x4 v[RD_UNROLL][RD_BATCH];
+#pragma unroll
+      for (int u = 0; u < RD_UNROLL; ++u) {
+        const int64_t q = q0 + u * RD_THREADS;
+#pragma unroll
+        for (int j = 0; j < RD_BATCH; ++j)
+          v[u][j] = (r0 + j < t && q < n_out) ? ld_stream(pp.p[r0 + j], in_off + q) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < RD_UNROLL; ++u)
+#pragma unroll
+        for (int j = 0; j < RD_BATCH; ++j)
+          if (r0 + j < t) add8(s[u], v[u][j]);
     }
-    if (bias) {
-      const uint4 b = reinterpret_cast<const uint4*>(bias)[q % cols8];
-      s[0] += bf16lo(b.x); s[1] += bf16hi(b.x);
-      s[2] += bf16lo(b.y); s[3] += bf16hi(b.y);
-      s[4] += bf16lo(b.z); s[5] += bf16hi(b.z);
-      s[6] += bf16lo(b.w); s[7] += bf16hi(b.w);
+#pragma unroll
+    for (int u = 0; u < RD_UNROLL; ++u) {
+      const int64_t q = q0 + u * RD_THREADS;
+      if (q >= n_out) continue;
+      if (bias) add8(s[u], reinterpret_cast<const u32x4*>(bias)[q % cols8]);
+      if (residual) add8(s[u], ld_stream(residual, q));
+      uint4 o;
+      o.x = pack_bf16x2(s[u][0], s[u][1]);
+      o.y = pack_bf16x2(s[u][2], s[u][3]);
+      o.z = pack_bf16x2(s[u][4], s[u][5]);
+      o.w = pack_bf16x2(s[u][6], s[u][7]);
+      reinterpret_cast<uint4*>(out)[q] = o;
     }
-    uint4 o;
-    o.x = pack_bf16x2(s[0], s[1]);
-    o.y = pack_bf16x2(s[2], s[3]);
-    o.z = pack_bf16x2(s[4], s[5]);
-    o.w = pack_bf16x2(s[6], s[7]);
-    reinterpret_cast<uint4*>(out)[q] = o;
   }
 }
 
-hipError_t reduce_partials_launch(const PartialPtrs& pp, int t, int64_t rows, int64_t cols, const uint16_t* bias,
-                                  uint16_t* out, int num_cu, hipStream_t st) {
-  const int64_t n_chunks = rows * (cols / 8);
-  if (n_chunks == 0) return hipSuccess;
-  int64_t blocks = (n_chunks + RD_THREADS - 1) / RD_THREADS;
+namespace {
+int64_t stream_blocks(int64_t n_chunks, int num_cu) {
+  int64_t blocks = (n_chunks + RD_THREADS * RD_UNROLL - 1) / (RD_THREADS * RD_UNROLL);
   const int64_t cap = (int64_t)num_cu * 16;
-  if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)blocks), dim3(RD_THREADS), 0, st, pp, t, n_chunks,
-                     (int)(cols / 8), bias, out);
+  return blocks > cap ? cap : blocks;
+}
+}  // namespace
+
+hipError_t reduce_partials_launch(const PartialPtrs& pp, int t, int64_t rows, int64_t cols, int64_t row0,
+                                  const uint16_t* bias, const uint16_t* residual, uint16_t* out, int num_cu,
+                                  hipStream_t st) {
+  const int64_t n_out = rows * (cols / 8);
+  if (n_out == 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)stream_blocks(n_out, num_cu)), dim3(RD_THREADS), 0, st, pp, t,
+                     n_out, row0 * (cols / 8), (int)(cols / 8), bias, residual, out);
+  return hipGetLastError();
+}
+
+// out[s * shard_chunks + i] = shards[s][i]; blockIdx.y selects the shard.
+__global__ void __launch_bounds__(RD_THREADS)
+gather_kernel(PartialPtrs shards, int64_t shard_chunks, uint16_t* out) {
+  const uint16_t* src = shards.p[blockIdx.y];
+  u32x4* dst = reinterpret_cast<u32x4*>(out) + (int64_t)blockIdx.y * shard_chunks;
+  for (int64_t i = (int64_t)blockIdx.x * RD_THREADS + threadIdx.x; i < shard_chunks;
+       i += (int64_t)gridDim.x * RD_THREADS)
+    dst[i] = ld_stream(src, i);
+}
+
+hipError_t gather_launch(const PartialPtrs& shards, int t, int64_t shard_rows, int64_t cols, uint16_t* out,
+                         int num_cu, hipStream_t st) {
+  const int64_t chunks = shard_rows * (cols / 8);
+  if (chunks == 0) return hipSuccess;
+  int64_t bx = (chunks + RD_THREADS - 1) / RD_THREADS;
+  const int64_t cap = ((int64_t)num_cu * 16 + t - 1) / t;
+  if (bx > cap) bx = cap;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)bx, (unsigned)t), dim3(RD_THREADS), 0, st, shards, chunks, out);
   return hipGetLastError();
 }
 

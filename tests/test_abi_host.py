@@ -128,3 +128,52 @@ def test_step_entry_points_validate():
     assert L.tp_mlp_up_dgrad_shard(r, FAKE, FAKE, None, FAKE, None) == INVALID
     assert L.tp_mlp_bias_grad(FAKE, 4, 12, FAKE, FAKE, 1 << 20, None) == INVALID
     assert L.tp_mlp_bias_grad(FAKE, 4, 8, FAKE, None, 0, None) == WORKSPACE
+
+
+def test_reduce_rejects_partial_overlap():
+    L = B.lib()
+    p0, p1 = FAKE, FAKE + (1 << 20)
+    ptrs = (ctypes.c_void_p * 2)(p0, p1)
+    # rows 4, cols 8: each partial is 64 bytes; out exactly on a partial is allowed (checked on the GPU),
+    # out straddling one is not
+    assert L.tp_mlp_reduce_partials_local(2, ptrs, 4, 8, None, p1 + 16, None) == INVALID
+    assert L.tp_mlp_reduce_partials_local(2, ptrs, 4, 8, None, p0 - 16, None) == INVALID
+
+
+def test_reduce_scatter_rejects_bad_arguments():
+    L = B.lib()
+    p0, p1 = FAKE, FAKE + (1 << 20)
+    out = FAKE + (2 << 20)
+    ptrs = (ctypes.c_void_p * 2)(p0, p1)
+    rs = L.tp_mlp_reduce_scatter_local
+    assert rs(2, ptrs, 5, 8, 0, None, None, out, None) == INVALID         # rows % t
+    assert rs(2, ptrs, 4, 8, 2, None, None, out, None) == INVALID         # rank >= t
+    assert rs(2, ptrs, 4, 8, -1, None, None, out, None) == INVALID        # rank < 0
+    assert rs(2, ptrs, 4, 12, 0, None, None, out, None) == INVALID        # cols % 8
+    assert rs(2, None, 4, 8, 0, None, None, out, None) == INVALID
+    assert rs(2, ptrs, 4, 8, 0, FAKE + 8, None, out, None) == INVALID     # misaligned bias
+    assert rs(2, ptrs, 4, 8, 0, None, FAKE + 8, out, None) == INVALID     # misaligned residual
+    assert rs(2, ptrs, 4, 8, 0, None, None, out + 4, None) == INVALID     # misaligned out
+    # rows 4, cols 8, t 2: rank 1's block of each partial is bytes [32, 64); out is 32 bytes
+    assert rs(2, ptrs, 4, 8, 1, None, None, p1 + 16, None) == INVALID     # straddles rank 1's block
+    assert rs(2, ptrs, 4, 8, 1, None, None, p0, None) == INVALID          # on rank 0's block of a partial
+    assert rs(2, ptrs, 4, 8, 1, None, out + 16, out, None) == INVALID     # straddles the residual
+    big = (ctypes.c_void_p * 65)(*([FAKE] * 65))
+    assert rs(65, big, 65, 8, 0, None, None, out, None) == UNSUPPORTED
+
+
+def test_all_gather_rejects_bad_arguments():
+    L = B.lib()
+    s0, s1 = FAKE, FAKE + (1 << 20)
+    ptrs = (ctypes.c_void_p * 2)(s0, s1)
+    ag = L.tp_mlp_all_gather_local
+    assert ag(2, ptrs, 4, 12, FAKE + (2 << 20), None) == INVALID          # cols % 8
+    assert ag(2, ptrs, 0, 8, FAKE + (2 << 20), None) == INVALID           # no rows
+    assert ag(0, ptrs, 4, 8, FAKE + (2 << 20), None) == INVALID
+    assert ag(2, ptrs, 4, 8, None, None) == INVALID
+    assert ag(2, ptrs, 4, 8, s1 - 64, None) == INVALID                    # out (128 B) runs into shard 1
+    assert ag(2, ptrs, 4, 8, s0, None) == INVALID                         # out on shard 0
+    bad = (ctypes.c_void_p * 2)(s0, s1 + 8)
+    assert ag(2, bad, 4, 8, FAKE + (2 << 20), None) == INVALID            # misaligned shard
+    big = (ctypes.c_void_p * 65)(*([FAKE] * 65))
+    assert ag(65, big, 4, 8, FAKE + (2 << 20), None) == UNSUPPORTED
