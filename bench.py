@@ -185,7 +185,7 @@ def main():
 
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm.h", "common.h")
+GEMM_SOURCES = ("gemm.hip", "gemm.h", "tiles.h", "common.h")
 GEMV_SOURCES = ("gemv.hip", "gemv.h", "common.h", "api.hip")
 
 

@@ -108,12 +108,19 @@ typedef struct {
  *                           projection) stash for the backward
  *   G_i  bf16 [N, F_i]      out or NULL: SwiGLU gate stash; must be NULL
  *                           unless SWIGLU, and given iff U_i is given
- * N == 1 runs the decode path: split-K GEMVs that read each weight once
- * (HBM bound) and keep float32 k-split partials in the workspace; other N run
- * the MFMA GEMMs, which need none.  workspace: device memory of at least
- * tp_mlp_workspace_bytes(s, 0) bytes, no initial contents required; NULL is
- * allowed when that size is 0.  Calls that share one workspace must be
- * ordered on one stream.  The workspace size depends on the shape only. */
+ * Three regimes, picked by N:
+ *   N == 1       one-token decode: split-K GEMVs that read each weight once
+ *                (HBM bound), float32 k-split partials in the workspace;
+ *   2 <= N <= 64 small-batch decode: split-K MFMA products that also read
+ *                each weight once, float32 k-split partials in the workspace
+ *                ("02 -- Tensor Parallelism": decode batches stay memory
+ *                bound);
+ *   N > 64       the wide-tile MFMA GEMMs, which need no workspace.
+ * All three produce the same quantities to the same tolerance.  workspace:
+ * device memory of at least tp_mlp_workspace_bytes(s, 0) bytes, no initial
+ * contents required; NULL is allowed when that size is 0.  Calls that share
+ * one workspace must be ordered on one stream.  The workspace size depends
+ * on the shape only. */
 tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X,
                                const void* W1_i, const void* Wg_i,
                                const void* W2_i, void* Y_i, void* A_i,

@@ -10,6 +10,7 @@
 #include "gemm.h"
 #include "gemv.h"
 #include "reduce.h"
+#include "skinny.h"
 #include "tp_mlp.h"
 
 using namespace tpmlp;
@@ -79,6 +80,31 @@ struct DecodeLayout {
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Small-batch path (2 <= N <= SK_MAX_N): split-K plans aiming at one block
+// per CU of a 256-CU MI355X.  A constant, not the device's CU count, so the
+// workspace size depends on the shape only.
+constexpr int SKINNY_TARGET_BLOCKS = 256;
+
+struct SkinnyLayout {
+  SkinnyPlan up, down;
+  size_t off_part_up, off_part_down, total;
+};
+
+bool small_batch(const Dims& d) { return d.N >= 2 && d.N <= SK_MAX_N; }
+
+SkinnyLayout skinny_layout(const Dims& d) {
+  SkinnyLayout L;
+  L.up = skinny_plan((int)d.N, (int)d.h, (int)d.Fi, d.g, SKINNY_TARGET_BLOCKS);
+  L.down = skinny_plan((int)d.N, (int)d.Fi, (int)d.h, 1, SKINNY_TARGET_BLOCKS);
+  size_t off = 0;
+  L.off_part_up = off;
+  off = round256(off + L.up.part_floats * sizeof(float));
+  L.off_part_down = off;
+  off = round256(off + L.down.part_floats * sizeof(float));
+  L.total = off;
+  return L;
+}
 
 // Blocks per GEMV, measured best for the one-token stream on 256 CUs: the
 // up-projection ~224 (fewer k-splits leave fewer partials for the
@@ -268,6 +294,7 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_shape* s, int backward) {
   if (!check_shape(s, d)) return 0;
   if (backward) return col_sum_workspace_bytes(d.N, d.h);
   if (d.N == 1) return decode_layout(d).total;
+  if (small_batch(d)) return skinny_layout(d).total;
   return 0;
 }
 
@@ -317,6 +344,15 @@ tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X, const void*
     float* part_dn = reinterpret_cast<float*>(ws + L.off_part_down);
     return hip_status(decode_launch(d.act, cu16(X), cu16(sw ? Wg_i : W1_i), cu16(W1_i), cu16(W2_i), (int)d.h,
                                     (int)d.Fi, L.up, L.down, part_up, part_dn, u16(A_i), u16(sw ? G_i : U_i),
+                                    u16(sw ? U_i : nullptr), u16(Y_i), stream));
+  }
+  if (small_batch(d)) {
+    const SkinnyLayout L = skinny_layout(d);
+    if (workspace == nullptr || workspace_bytes < L.total) return TP_MLP_ERR_WORKSPACE;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    return hip_status(skinny_launch(d.act, (int)d.N, cu16(X), cu16(sw ? Wg_i : W1_i), cu16(W1_i), cu16(W2_i),
+                                    (int)d.h, (int)d.Fi, L.up, L.down, reinterpret_cast<float*>(ws + L.off_part_up),
+                                    reinterpret_cast<float*>(ws + L.off_part_down), u16(A_i), u16(sw ? G_i : U_i),
                                     u16(sw ? U_i : nullptr), u16(Y_i), stream));
   }
   hipError_t e = run_up_act(d, X, W1_i, Wg_i, A_i, U_i, G_i, stream);

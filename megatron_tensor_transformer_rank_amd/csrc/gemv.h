@@ -25,4 +25,7 @@ hipError_t decode_launch(int act, const uint16_t* x, const uint16_t* Wa, const u
                          int h, int Fi, const GemvPlan& up, const GemvPlan& down, float* part_up, float* part_down,
                          uint16_t* A, uint16_t* st0, uint16_t* st1, uint16_t* Y, hipStream_t st);
 
+// out[c] = bf16(sum_{q<ks} part[q][c]) for c < n (n % 4 == 0), in fixed order.
+hipError_t ksum_launch(const float* part, int ks, int64_t n, uint16_t* out, hipStream_t st);
+
 }  // namespace tpmlp

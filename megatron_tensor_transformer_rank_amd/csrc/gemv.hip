@@ -230,7 +230,13 @@ hipError_t decode_launch(int act, const uint16_t* x, const uint16_t* Wa, const u
                        part_up, up.ks, A, st0, nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemv_final, dim3((h + GV_FINAL_COLS - 1) / GV_FINAL_COLS), dim3(256), 0, st, part_down, down.ks, h, Y);
+  return ksum_launch(part_down, down.ks, h, Y, st);
+}
+
+hipError_t ksum_launch(const float* part, int ks, int64_t n, uint16_t* out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gemv_final, dim3((unsigned)((n + GV_FINAL_COLS - 1) / GV_FINAL_COLS)), dim3(256), 0, st, part, ks,
+                     (int)n, out);
   return hipGetLastError();
 }
 

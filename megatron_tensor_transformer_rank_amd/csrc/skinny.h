@@ -1,0 +1,35 @@
+// Internal interface of the small-batch decode path (skinny.hip): a forward
+// for 2 <= N <= SK_MAX_N tokens that streams each weight once, like the
+// one-token GEMVs, but multiplies on MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+constexpr int SK_MAX_N = 64;  // largest token count of the small-batch path
+
+struct SkinnyPlan {
+  int rows;       // token rows padded to the MFMA tile (16, 32 or 64)
+  int strips;     // 256-column strips of one weight matrix
+  int ks, kt;     // k-splits, 64-deep k-tiles per split
+  size_t part_floats;
+};
+
+// Split-K plan for X [N, K] @ W [K, ncols] over nmat matrices side by side,
+// aiming at target_blocks blocks.
+SkinnyPlan skinny_plan(int N, int K, int ncols, int nmat, int target_blocks);
+
+// Small-batch forward of one rank's shard: A = act(X @ [Wa, Wb]) (SwiGLU: Wa
+// = gate, Wb = up; otherwise Wa = W1, Wb unused), Y = A @ W2.  part_up /
+// part_down hold up.part_floats / down.part_floats floats of scratch (no
+// initial contents needed).  st0 / st1: stashes or NULL (SwiGLU: gate, up;
+// otherwise st0 = U).
+hipError_t skinny_launch(int act, int N, const uint16_t* X, const uint16_t* Wa, const uint16_t* Wb,
+                         const uint16_t* W2, int h, int Fi, const SkinnyPlan& up, const SkinnyPlan& down,
+                         float* part_up, float* part_down, uint16_t* A, uint16_t* st0, uint16_t* st1, uint16_t* Y,
+                         hipStream_t st);
+
+}  // namespace tpmlp

@@ -1,0 +1,263 @@
+// Small-batch decode path (2 <= N <= 64 tokens): split-K MFMA GEMMs for
+// gfx950 that stream each weight once.
+//
+// With a handful of tokens every weight byte is still used by only N
+// multiply-adds, so the forward is bound by reading the shards from HBM, as
+// in one-token decode ("02 -- Tensor Parallelism": decode is memory-bandwidth
+// bound work that TP splits across HBMs; batch sizes below ~32 stay in that
+// regime).  The wide-tile GEMM would cover the 70B-class shard's up
+// projection with only 56 column tiles; here every 256-column strip of a
+// weight is also split along k so that about one block runs per CU, each
+// streaming its [k-range x 256] slab through LDS.
+//
+//   1. skinny_partial (up):   X [N, h] @ W (gate and up side by side for
+//                             SwiGLU) -> float32 partials [ks][mat][N][F_i]
+//   2. skinny_act:            A = act(sum of the partials in k-split order),
+//                             rounded to bf16, plus the pre-activation stashes
+//   3. skinny_partial (down): A [N, F_i] @ W2 -> partials [ks][N][h]
+//   4. k-split sum:           Y = bf16(sum of the partials), the one-token
+//                             path's final reduction
+//
+// skinny_partial: 256 threads = 4 waves; the block's tile is MB token rows
+// (N padded to 16, 32 or 64) x 256 columns, each wave owning 64 columns.
+// Four LDS stages, each [64 k][256] of the weight (n-contiguous, read with
+// the LDS transpose read) and [MB][64 k] of the activations; the DMA of tile
+// t+3 is issued as tile t's fragments are read, so three tiles (about
+// 100 KiB per CU) stay in flight.  One barrier per 64-deep k-tile.  The MFMA
+// work per byte is tiny (2*MB flops per weight element).
+#include "common.h"
+#include "gemv.h"
+#include "skinny.h"
+#include "tiles.h"
+
+namespace tpmlp {
+
+constexpr int SK_THREADS = 256;
+constexpr int SK_COLS = 256;  // columns per block
+constexpr int SK_STAGES = 4;
+constexpr int SK_BK = 64;
+
+template <int MB, int NMAT>
+__global__ void __launch_bounds__(SK_THREADS)
+skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_bytes, const uint16_t* W0,
+               const uint16_t* W1, uint32_t w_bytes, int K, int ncols, int strips, int kt_per_split,
+               float* __restrict__ part) {
+  constexpr int TM = MB / 16;                // 16-row blocks (all waves)
+  constexpr int TN = 4;                      // 16-column blocks per wave
+  constexpr int W_BYTES = SK_COLS * 128;     // [64 k][256 cols]
+  constexpr int NIX = MB / 32 > 0 ? MB / 32 : 1;  // activation DMA instructions per wave
+  constexpr int X_BYTES = NIX * 4 * 1024;   // [MB rows][64 k], rounded up to whole instructions
+  constexpr int STAGE = W_BYTES + X_BYTES;
+  constexpr int NIW = SK_COLS / 32;          // weight DMA instructions per wave
+  constexpr int NI = NIW + NIX;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SK_STAGES * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.x;
+  const int s = b % strips, rest = b / strips;
+  const int mat = rest % NMAT, q = rest / NMAT;
+  const int col0 = s * SK_COLS;
+  const int nkt = (K + SK_BK - 1) / SK_BK;
+  const int t0 = q * kt_per_split;
+  const int nt = min(nkt, t0 + kt_per_split) - t0;
+  const uint16_t* Wm = (NMAT == 2 && mat == 1) ? W1 : W0;
+
+  // weight tile DMA: [64 k][256 cols] of Wm starting at row k0
+  DmaMN<SK_COLS> dw;
+  dw.init(col0, ncols, ncols, lane, w);
+  const uint32_t ldw2 = (uint32_t)ncols * 2u;
+  // activation tile DMA: instruction i = w + 4j covers rows 8i .. 8i+7, eight
+  // 16-byte chunks per row, chunk c of row r at slot c ^ (r & 7); rows past N
+  // (and the padding instructions when MB = 16) read zeros
+  const int kc = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+  uint32_t xoff[NIX];
+#pragma unroll
+  for (int j = 0; j < NIX; ++j) {
+    const int row = (w + 4 * j) * 8 + (lane >> 3);
+    xoff[j] = (row < N && row < MB) ? (uint32_t)((int64_t)row * ldx * 2) + (uint32_t)kc * 2u : OOB;
+  }
+  auto shifted = [](const uint16_t* p, uint32_t bytes, uint32_t skip) __attribute__((always_inline)) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p) + skip;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(skip < bytes ? bytes - skip : 0u);
+    return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), n);
+  };
+  // DMA of the split's i-th tile into stage slot; tiles past the split read
+  // zeros (keeps the per-wave count of loads in flight uniform)
+  auto issue_tile = [&](int i, uint8_t* st) __attribute__((always_inline)) {
+    const bool live = i < nt;
+    const int k0 = (t0 + i) * SK_BK;
+    const int kvalid = live ? K - k0 : 0;
+    const rsrc_t rw = shifted(Wm, live ? w_bytes : 0u, (uint32_t)k0 * ldw2);
+    static_for<NIW>([&](auto J) __attribute__((always_inline)) { dw.template issue<decltype(J)::value>(rw, st, w); });
+    const rsrc_t rx = shifted(X, live ? x_bytes : 0u, (uint32_t)k0 * 2u);
+#pragma unroll
+    for (int j = 0; j < NIX; ++j) dma16(rx, st + W_BYTES + (w + 4 * j) * 1024, kc < kvalid ? xoff[j] : OOB);
+  };
+
+  // fragment addressing within a stage
+  const uint32_t a_off0 = W_BYTES + kfrag_off(0, 0, lane), a_off1 = W_BYTES + kfrag_off(0, 1, lane);
+  uint32_t b_col[TN];
+  {
+    const uint32_t kb = mn_kbase<SK_COLS>(lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b_col[j] = kb + mn_coloff<SK_COLS>(w * 64, j, lane);
+  }
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t base = lds_addr(smem);
+#pragma unroll
+  for (int p = 0; p < SK_STAGES - 1; ++p) issue_tile(p, smem + p * STAGE);
+
+  for (int i = 0; i < nt; ++i) {
+    const int sl = i % SK_STAGES;
+    // this wave's loads of tile i have landed; after the barrier everyone's
+    // have, and everyone has finished reading tile i-1's slot
+    wait_vmcnt<(SK_STAGES - 2) * NI>();
+    barrier();
+    const int sn = (i + SK_STAGES - 1) % SK_STAGES;
+    issue_tile(i + SK_STAGES - 1, smem + sn * STAGE);
+    const uint32_t sa = base + sl * STAGE;
+    bf16x8 af[2][TM], bf[2][TN];
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      constexpr int ii = decltype(I)::value;
+      af[0][ii] = ld_b128<ii * 2048>(sa + a_off0);
+      af[1][ii] = ld_b128<ii * 2048>(sa + a_off1);
+    });
+    constexpr int RS = SK_COLS * 2;
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      constexpr int jj = decltype(J)::value;
+      bf[0][jj] = ld_tr2<0, 4 * RS>(sa + b_col[jj]);
+      bf[1][jj] = ld_tr2<32 * RS, 36 * RS>(sa + b_col[jj]);
+    });
+    // the fragments are consumed only after this wait: the reads and MFMAs
+    // are volatile asm, so they keep this order
+    wait_lgkm0();
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int ii = 0; ii < TM; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+          asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[ii][jj]) : "v"(bf[st][jj]), "v"(af[st][ii]));
+  }
+  asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // last MFMA results written before they are read
+  wait_vmcnt<0>();  // no DMA may land after the block has left
+
+  // lane holds rows n = 16i + l16, columns col0 + 64w + 16j + 4lq .. +3
+  const int l16 = lane & 15, lq = lane >> 4;
+  float* dst = part + (int64_t)(q * NMAT + mat) * N * ncols;
+#pragma unroll
+  for (int ii = 0; ii < TM; ++ii) {
+    const int n = ii * 16 + l16;
+    if (n >= N) continue;
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) {
+      const int c = col0 + w * 64 + jj * 16 + 4 * lq;
+      if (c < ncols)
+        *reinterpret_cast<float4*>(dst + (int64_t)n * ncols + c) =
+            make_float4(acc[ii][jj][0], acc[ii][jj][1], acc[ii][jj][2], acc[ii][jj][3]);
+    }
+  }
+}
+
+// A[e] = act(sum_q part[q][0][e] (, sum_q part[q][1][e])) for e < n (the
+// flattened [N, F_i]); sums in k-split order.  st0 / st1 as for the decode
+// GEMVs (SwiGLU: gate, up; otherwise st0 = the pre-activation).
+template <int ACT>
+__global__ void __launch_bounds__(256)
+skinny_act(const float* __restrict__ part, int ks, int64_t n, uint16_t* __restrict__ A, uint16_t* __restrict__ st0,
+           uint16_t* __restrict__ st1) {
+  constexpr int NMAT = ACT == ACT_SWIGLU ? 2 : 1;
+  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < n; e += (int64_t)gridDim.x * 256 * 4) {
+    float4 sum[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) sum[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < ks; ++q)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)q * NMAT + m) * n + e);
+        sum[m].x += v.x; sum[m].y += v.y; sum[m].z += v.z; sum[m].w += v.w;
+      }
+    float a[4];
+    const float g[4] = {sum[0].x, sum[0].y, sum[0].z, sum[0].w};
+    const float u[4] = {sum[NMAT - 1].x, sum[NMAT - 1].y, sum[NMAT - 1].z, sum[NMAT - 1].w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = ACT == ACT_SWIGLU ? swiglu_f(g[r], u[r]) : act_f<ACT>(g[r]);
+    *reinterpret_cast<uint2*>(A + e) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+    if (st0) *reinterpret_cast<uint2*>(st0 + e) = make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+    if (ACT == ACT_SWIGLU && st1)
+      *reinterpret_cast<uint2*>(st1 + e) = make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
+  }
+}
+
+SkinnyPlan skinny_plan(int N, int K, int ncols, int nmat, int target_blocks) {
+  SkinnyPlan p;
+  p.rows = N <= 16 ? 16 : (N <= 32 ? 32 : 64);
+  p.strips = (ncols + SK_COLS - 1) / SK_COLS;
+  const int nkt = (K + SK_BK - 1) / SK_BK;
+  int ks = target_blocks / (p.strips * nmat);
+  ks = max(1, min(ks, nkt));
+  p.kt = (nkt + ks - 1) / ks;
+  p.ks = (nkt + p.kt - 1) / p.kt;  // every split non-empty
+  p.part_floats = (size_t)p.ks * nmat * N * ncols;
+  return p;
+}
+
+namespace {
+
+template <int NMAT>
+hipError_t partial_launch(const SkinnyPlan& p, int N, const uint16_t* X, int64_t ldx, const uint16_t* W0,
+                          const uint16_t* W1, int K, int ncols, float* part, hipStream_t st) {
+  const uint32_t x_bytes = (uint32_t)((int64_t)N * ldx * 2);
+  const uint32_t w_bytes = (uint32_t)((int64_t)K * ncols * 2);
+  const dim3 grid(p.strips * NMAT * p.ks), blk(SK_THREADS);
+  if (p.rows == 16)
+    hipLaunchKernelGGL((skinny_partial<16, NMAT>), grid, blk, 0, st, X, N, ldx, x_bytes, W0, W1, w_bytes, K, ncols,
+                       p.strips, p.kt, part);
+  else if (p.rows == 32)
+    hipLaunchKernelGGL((skinny_partial<32, NMAT>), grid, blk, 0, st, X, N, ldx, x_bytes, W0, W1, w_bytes, K, ncols,
+                       p.strips, p.kt, part);
+  else
+    hipLaunchKernelGGL((skinny_partial<64, NMAT>), grid, blk, 0, st, X, N, ldx, x_bytes, W0, W1, w_bytes, K, ncols,
+                       p.strips, p.kt, part);
+  return hipGetLastError();
+}
+
+int act_blocks(int64_t n) {
+  const int64_t b = (n / 4 + 255) / 256;
+  return (int)(b < 1024 ? (b < 1 ? 1 : b) : 1024);
+}
+
+}  // namespace
+
+hipError_t skinny_launch(int act, int N, const uint16_t* X, const uint16_t* Wa, const uint16_t* Wb,
+                         const uint16_t* W2, int h, int Fi, const SkinnyPlan& up, const SkinnyPlan& down,
+                         float* part_up, float* part_down, uint16_t* A, uint16_t* st0, uint16_t* st1, uint16_t* Y,
+                         hipStream_t st) {
+  hipError_t e = act == ACT_SWIGLU ? partial_launch<2>(up, N, X, h, Wa, Wb, h, Fi, part_up, st)
+                                   : partial_launch<1>(up, N, X, h, Wa, Wa, h, Fi, part_up, st);
+  if (e != hipSuccess) return e;
+  const int64_t n_act = (int64_t)N * Fi;
+  const dim3 ga(act_blocks(n_act)), ba(256);
+  if (act == ACT_SWIGLU)
+    hipLaunchKernelGGL(skinny_act<ACT_SWIGLU>, ga, ba, 0, st, part_up, up.ks, n_act, A, st0, st1);
+  else if (act == ACT_RELU)
+    hipLaunchKernelGGL(skinny_act<ACT_RELU>, ga, ba, 0, st, part_up, up.ks, n_act, A, st0, nullptr);
+  else
+    hipLaunchKernelGGL(skinny_act<ACT_GELU>, ga, ba, 0, st, part_up, up.ks, n_act, A, st0, nullptr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = partial_launch<1>(down, N, A, Fi, W2, W2, Fi, h, part_down, st);
+  if (e != hipSuccess) return e;
+  return ksum_launch(part_down, down.ks, (int64_t)N * h, Y, st);
+}
+
+}  // namespace tpmlp

@@ -177,3 +177,18 @@ def test_all_gather_rejects_bad_arguments():
     assert ag(2, bad, 4, 8, FAKE + (2 << 20), None) == INVALID            # misaligned shard
     big = (ctypes.c_void_p * 65)(*([FAKE] * 65))
     assert ag(65, big, 4, 8, FAKE + (2 << 20), None) == UNSUPPORTED
+
+
+def test_small_batch_workspace_sizes():
+    """2 <= N <= 64 uses the split-K small-batch path, which needs float32
+    partials; N == 65 goes to the wide-tile GEMMs, which need none."""
+    prev = 0
+    for N in (2, 16, 17, 32, 33, 64):
+        ws = B.workspace_bytes(B.make_shape(N, 8192, 28672, 4, 0, "swiglu"), False)
+        assert ws > 0 and ws % 256 == 0
+        assert ws >= prev
+        prev = ws
+    assert B.workspace_bytes(B.make_shape(65, 8192, 28672, 4, 0, "swiglu"), False) == 0
+    s = B.make_shape(8, 64, 128, 2, 0, "gelu")
+    assert _fwd(s) == WORKSPACE                                  # small batch needs workspace
+    assert _fwd(s, ws=FAKE, wsb=B.workspace_bytes(s, False) - 1) == WORKSPACE

@@ -22,7 +22,7 @@ import torch
 import oracle
 from megatron_tensor_transformer_rank_amd import binding as B
 from megatron_tensor_transformer_rank_amd import inputs as I
-from tests.helpers import Shard, assert_close, bf16_dev, f64
+from tests.helpers import Shard, assert_close, bf16_dev, f64, run_group
 
 pytestmark = pytest.mark.gpu
 
@@ -31,62 +31,6 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def run_group(wid, N, h, F, t, act, bias, stash=True):
-    """Run all t shards fwd+bwd on the GPU and the oracle on the same bf16
-    inputs; compare everything."""
-    say(f"[group] wid={wid} N={N} h={h} F={F} t={t} act={act} bias={bias}")
-    sw = act == "swiglu"
-    Fi = F // t
-    Xb, dYb = I.gen_x(wid, N, h), I.gen_dy(wid, N, h)
-    W1b, W2b, Wgb = I.gen_full_weights(wid, h, F, t, sw)
-    b2b = I.gen_b2(wid, h) if bias else None
-    X, dY = oracle.bf16_bits_to_f64(Xb), oracle.bf16_bits_to_f64(dYb)
-    W1, W2 = oracle.bf16_bits_to_f64(W1b), oracle.bf16_bits_to_f64(W2b)
-    Wg = oracle.bf16_bits_to_f64(Wgb) if sw else None
-    b2 = oracle.bf16_bits_to_f64(b2b) if bias else None
-    Yref, fr = oracle.tp_forward(act, X, W1, W2, t, Wg=Wg, b2=b2)
-    dXref, db2ref, br = oracle.tp_backward(act, X, W1, W2, dY, t, Wg=Wg)
-
-    Xd, dYd = bf16_dev(Xb), bf16_dev(dYb)
-    shards = []
-    for r in range(t):
-        c = oracle.column_block(r, t, F)
-        s = Shard(N, h, F, t, r, act, Xd, bf16_dev(np.ascontiguousarray(W1b[:, c])),
-                  bf16_dev(np.ascontiguousarray(W2b[c, :])),
-                  bf16_dev(np.ascontiguousarray(Wgb[:, c])) if sw else None, stash=stash)
-        s.forward()
-        s.backward(dYd, db2=(r == 0))
-        shards.append(s)
-    Y = torch.empty(N, h, dtype=torch.bfloat16, device="cuda")
-    B.tp_mlp_reduce_partials_local([s.Y for s in shards], Y, bias=bf16_dev(b2b) if bias else None)
-    dX = torch.empty(N, h, dtype=torch.bfloat16, device="cuda")
-    B.tp_mlp_reduce_partials_local([s.dX for s in shards], dX)
-    torch.cuda.synchronize()
-
-    for r, s in enumerate(shards):
-        f, b = fr[r], br[r]
-        assert_close(f"A[{r}]", f64(s.A), f["A"])
-        if stash:
-            assert_close(f"U[{r}]", f64(s.U), f["U"])
-            if sw:
-                assert_close(f"G[{r}]", f64(s.G), f["G"])
-        assert_close(f"Y_i[{r}]", f64(s.Y), f["Y"])
-        dU = f64(s.dU)
-        if sw:
-            assert_close(f"dG[{r}]", dU[:, :Fi], b["dG"])
-            assert_close(f"dP[{r}]", dU[:, Fi:], b["dU"])
-            assert_close(f"dWg[{r}]", f64(s.dWg), b["dWg"])
-        else:
-            assert_close(f"dU[{r}]", dU, b["dU"])
-        assert_close(f"dW1[{r}]", f64(s.dW1), b["dW1"])
-        assert_close(f"dW2[{r}]", f64(s.dW2), b["dW2"])
-        assert_close(f"dX_i[{r}]", f64(s.dX), b["dX"])
-    assert_close("Y", f64(Y), Yref)
-    assert_close("dX", f64(dX), dXref)
-    assert_close("db2", f64(shards[0].db2), db2ref, rel_fro=1e-5, max_rel=1e-5)
-    return shards, Y, dX
 
 
 # (wid, N, h, F, t, act, bias): several 256-wide tiles plus ragged tails in
