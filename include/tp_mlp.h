@@ -285,6 +285,74 @@ tp_mlp_status tp_mlp_bias_grad(const void* dY, int64_t rows, int64_t cols,
                                size_t workspace_bytes, hipStream_t stream);
 size_t tp_mlp_bias_grad_workspace_bytes(int64_t rows, int64_t cols);
 
+/* ------------------------------------------------------------------------
+ * Attention block projections ("02 -- Tensor Parallelism", section "The
+ * attention pairing"; "Megatron-LM: Tensor Parallelism", section "Attention
+ * Block"; "Tensor and sequence parallelism", closing exercise 1).  The same
+ * pairing as the MLP: the Q, K and V projections are column-parallel by head,
+ * the output projection row-parallel into a full-shape partial sum.  The
+ * attention core between them (scores, softmax, weighted sum) is not part of
+ * this library: the caller passes its output O_i and, backward, its
+ * gradient dQKV_i.
+ *
+ * Heads: rank r owns query heads [r*n_heads/t, (r+1)*n_heads/t) and the
+ * key/value heads of their groups (query head j is in group
+ * j / (n_heads / n_kv_heads)): the block [r*n_kv/t, (r+1)*n_kv/t) when
+ * n_kv_heads >= t, else the single head r*n_kv/t, which is then replicated
+ * on t/n_kv_heads ranks (its weight gradients must be summed over those
+ * replicas).  Head j owns head_dim consecutive columns.  Requires
+ * n_heads % n_kv_heads == 0, n_heads % t == 0, n_kv_heads % t == 0 or
+ * t % n_kv_heads == 0, head_dim % 8 == 0, hidden % 8 == 0, 1 <= t <= 64.
+ *
+ * Widths on rank r: qc = n_heads/t * head_dim; kvc = (n_kv/t or 1) *
+ * head_dim; qkvc = qc + 2*kvc.  Buffers (bf16 unless noted, row-major):
+ *   X       [N, h]        replicated input
+ *   Wqkv_i  [h, qkvc]     [W_q columns of its query heads | W_k columns of
+ *                         its key/value heads | W_v columns of the same]
+ *   QKV_i   [N, qkvc]     out: [Q_i | K_i | V_i]
+ *   O_i     [N, qc]       the attention core's output for the rank's heads
+ *   Wo_i    [qc, h]       the W_o rows of the rank's query heads
+ *   Y_i     [N, h]        out: partial sum (add over ranks; bias once after)
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t n_tokens;   /* N                                      */
+  int64_t hidden;     /* h                                      */
+  int32_t n_heads;    /* query heads                            */
+  int32_t n_kv_heads; /* key/value heads (= n_heads without GQA) */
+  int32_t head_dim;
+  int32_t t;          /* tensor-parallel degree                 */
+  int32_t rank;
+} tp_attn_shape;
+
+/* Column-parallel QKV projection: QKV_i = X @ Wqkv_i (no communication). */
+tp_mlp_status tp_attn_qkv_shard(const tp_attn_shape* s, const void* X,
+                                const void* Wqkv_i, void* QKV_i,
+                                hipStream_t stream);
+
+/* Row-parallel output projection: Y_i = O_i @ Wo_i, the full-shape partial
+ * sum (sum over ranks with tp_mlp_reduce_partials_local, bias once). */
+tp_mlp_status tp_attn_out_shard(const tp_attn_shape* s, const void* O_i,
+                                const void* Wo_i, void* Y_i,
+                                hipStream_t stream);
+
+/* Backward of the output projection for dY [N, h] (the same on every rank):
+ *   dO_i  = dY @ Wo_i^T  -> bf16 [N, qc]  (input of the attention core's
+ *                                          backward)
+ *   dWo_i = O_i^T @ dY   -> fp32 [qc, h]                               */
+tp_mlp_status tp_attn_out_bwd_shard(const tp_attn_shape* s, const void* dY,
+                                    const void* O_i, const void* Wo_i,
+                                    void* dO_i, float* dWo_i,
+                                    hipStream_t stream);
+
+/* Backward of the QKV projection for dQKV_i [N, qkvc] (the attention core's
+ * gradient, laid out like QKV_i):
+ *   dX_partial = dQKV_i @ Wqkv_i^T -> bf16 [N, h]  (sum over ranks)
+ *   dWqkv_i    = X^T @ dQKV_i      -> fp32 [h, qkvc]                    */
+tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X,
+                                    const void* Wqkv_i, const void* dQKV_i,
+                                    float* dWqkv_i, void* dX_partial,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

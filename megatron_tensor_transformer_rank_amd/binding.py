@@ -46,6 +46,29 @@ def make_shape(N: int, h: int, F: int, t: int = 1, rank: int = 0, act: str | int
     return Shape(N, h, F, t, rank, ACTS[act] if isinstance(act, str) else act)
 
 
+class AttnShape(ctypes.Structure):
+    """Mirror of tp_attn_shape."""
+    _fields_ = [("n_tokens", c_int64), ("hidden", c_int64), ("n_heads", c_int32), ("n_kv_heads", c_int32),
+                ("head_dim", c_int32), ("t", c_int32), ("rank", c_int32)]
+
+    @property
+    def q_cols(self) -> int:
+        return self.n_heads // self.t * self.head_dim
+
+    @property
+    def kv_cols(self) -> int:
+        return (self.n_kv_heads // self.t if self.n_kv_heads >= self.t else 1) * self.head_dim
+
+    @property
+    def qkv_cols(self) -> int:
+        return self.q_cols + 2 * self.kv_cols
+
+
+def make_attn_shape(N: int, h: int, n_heads: int, n_kv_heads: int, head_dim: int, t: int = 1,
+                    rank: int = 0) -> AttnShape:
+    return AttnShape(N, h, n_heads, n_kv_heads, head_dim, t, rank)
+
+
 _lib = None
 
 _SIGS = {
@@ -62,6 +85,10 @@ _SIGS = {
     "tp_mlp_up_wgrad_shard": [POINTER(Shape)] + [c_void_p] * 4 + [c_void_p],
     "tp_mlp_up_dgrad_shard": [POINTER(Shape)] + [c_void_p] * 4 + [c_void_p],
     "tp_mlp_bias_grad": [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p],
+    "tp_attn_qkv_shard": [POINTER(AttnShape)] + [c_void_p] * 3 + [c_void_p],
+    "tp_attn_out_shard": [POINTER(AttnShape)] + [c_void_p] * 3 + [c_void_p],
+    "tp_attn_out_bwd_shard": [POINTER(AttnShape)] + [c_void_p] * 5 + [c_void_p],
+    "tp_attn_qkv_bwd_shard": [POINTER(AttnShape)] + [c_void_p] * 5 + [c_void_p],
 }
 
 
@@ -268,3 +295,34 @@ def tp_mlp_bias_grad(dY, db2, workspace, stream=None):
     wp, wb = _ws(workspace, 0)
     _check("tp_mlp_bias_grad", lib().tp_mlp_bias_grad(
         _p(dY, BF16, rows * cols, "dY"), rows, cols, _p(db2, F32, cols, "db2"), wp, wb, _stream(stream)))
+
+
+# ------------------------------------------------------ attention projections
+def tp_attn_qkv_shard(shape: AttnShape, X, Wqkv_i, QKV_i, stream=None):
+    N, h, w = shape.n_tokens, shape.hidden, shape.qkv_cols
+    _check("tp_attn_qkv_shard", lib().tp_attn_qkv_shard(
+        ctypes.byref(shape), _p(X, BF16, N * h, "X"), _p(Wqkv_i, BF16, h * w, "Wqkv_i"),
+        _p(QKV_i, BF16, N * w, "QKV_i"), _stream(stream)))
+
+
+def tp_attn_out_shard(shape: AttnShape, O_i, Wo_i, Y_i, stream=None):
+    N, h, q = shape.n_tokens, shape.hidden, shape.q_cols
+    _check("tp_attn_out_shard", lib().tp_attn_out_shard(
+        ctypes.byref(shape), _p(O_i, BF16, N * q, "O_i"), _p(Wo_i, BF16, q * h, "Wo_i"),
+        _p(Y_i, BF16, N * h, "Y_i"), _stream(stream)))
+
+
+def tp_attn_out_bwd_shard(shape: AttnShape, dY, O_i, Wo_i, dO_i, dWo_i, stream=None):
+    N, h, q = shape.n_tokens, shape.hidden, shape.q_cols
+    _check("tp_attn_out_bwd_shard", lib().tp_attn_out_bwd_shard(
+        ctypes.byref(shape), _p(dY, BF16, N * h, "dY"), _p(O_i, BF16, N * q, "O_i"),
+        _p(Wo_i, BF16, q * h, "Wo_i"), _p(dO_i, BF16, N * q, "dO_i"), _p(dWo_i, F32, q * h, "dWo_i"),
+        _stream(stream)))
+
+
+def tp_attn_qkv_bwd_shard(shape: AttnShape, X, Wqkv_i, dQKV_i, dWqkv_i, dX_partial, stream=None):
+    N, h, w = shape.n_tokens, shape.hidden, shape.qkv_cols
+    _check("tp_attn_qkv_bwd_shard", lib().tp_attn_qkv_bwd_shard(
+        ctypes.byref(shape), _p(X, BF16, N * h, "X"), _p(Wqkv_i, BF16, h * w, "Wqkv_i"),
+        _p(dQKV_i, BF16, N * w, "dQKV_i"), _p(dWqkv_i, F32, h * w, "dWqkv_i"),
+        _p(dX_partial, BF16, N * h, "dX_partial"), _stream(stream)))

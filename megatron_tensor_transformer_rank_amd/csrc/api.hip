@@ -250,6 +250,79 @@ hipError_t run_dgrad_up(const Dims& d, const void* dU, const void* W1, const voi
   return gemm_launch(GEMM_DGRAD, d.act, g, num_cu_current(), st);
 }
 
+// ------------------------------------------------------- attention projections
+struct AttnDims {
+  int64_t N, h;
+  int64_t q_cols, kv_cols, qkv_cols;  // this rank's query / key-value / fused widths
+};
+
+// INVALID_ARG for a malformed shape or head split, UNSUPPORTED for t above
+// MAX_T or an operand too large for one buffer resource.
+tp_mlp_status attn_status(const tp_attn_shape* s, AttnDims& a) {
+  if (s == nullptr) return TP_MLP_ERR_INVALID_ARG;
+  if (s->t < 1 || s->rank < 0 || s->rank >= s->t) return TP_MLP_ERR_INVALID_ARG;
+  if (s->n_tokens < 1 || s->hidden < 8 || s->hidden % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
+  if (s->n_heads < 1 || s->n_kv_heads < 1 || s->head_dim < 8 || s->head_dim % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
+  const int64_t t = s->t, nh = s->n_heads, nkv = s->n_kv_heads, d = s->head_dim;
+  if (nh % nkv != 0 || nh % t != 0) return TP_MLP_ERR_INVALID_ARG;
+  if (nkv >= t ? nkv % t != 0 : t % nkv != 0) return TP_MLP_ERR_INVALID_ARG;
+  if (t > MAX_T) return TP_MLP_ERR_UNSUPPORTED;
+  a.N = s->n_tokens;
+  a.h = s->hidden;
+  a.q_cols = nh / t * d;
+  a.kv_cols = (nkv >= t ? nkv / t : 1) * d;
+  a.qkv_cols = a.q_cols + 2 * a.kv_cols;
+  const int64_t lim = 0x7fffffffLL;
+  if (a.N > lim || a.h > lim || a.qkv_cols > lim) return TP_MLP_ERR_UNSUPPORTED;
+  const uint64_t cap = GEMM_MAX_OPERAND_BYTES / 2;
+  const uint64_t N = (uint64_t)a.N, h = (uint64_t)a.h, w = (uint64_t)a.qkv_cols;
+  if (N * h > cap || N * w > cap || h * w > cap) return TP_MLP_ERR_UNSUPPORTED;
+  return TP_MLP_OK;
+}
+
+// C [M, Nc] = A [M, K] @ B [K, Nc], both row-major, bf16 out.
+hipError_t run_nn(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, void* C, hipStream_t st) {
+  GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
+  g.a[0] = g.a[1] = cu16(A);
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(M, K);
+  g.lda = K;
+  g.b[0] = g.b[1] = cu16(B);
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(K, Nc);
+  g.ldb = Nc;
+  g.c0 = C;
+  g.ldc = Nc;
+  return gemm_launch(GEMM_DOWN, 0, g, num_cu_current(), st);
+}
+
+// C [M, Nc] = A [M, K] @ B^T with B stored [Nc, K], bf16 out.
+hipError_t run_nt(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, void* C, hipStream_t st) {
+  GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
+  g.a[0] = g.a[1] = cu16(A);
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(M, K);
+  g.lda = K;
+  g.b[0] = g.b[1] = cu16(B);
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(Nc, K);
+  g.ldb = K;
+  g.c0 = C;
+  g.ldc = Nc;
+  return gemm_launch(GEMM_DGRAD, 0, g, num_cu_current(), st);
+}
+
+// C [M, Nc] = A^T @ B with A stored [K, M] and B stored [K, Nc], fp32 out.
+hipError_t run_tn(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, float* C, hipStream_t st) {
+  GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
+  g.a[0] = g.a[1] = cu16(A);
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(K, M);
+  g.lda = M;
+  g.b[0] = g.b[1] = cu16(B);
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(K, Nc);
+  g.ldb = Nc;
+  g.c0 = g.c1 = C;
+  g.ldc = Nc;
+  g.c_split = (int)Nc;
+  return gemm_launch(GEMM_WGRAD, 0, g, num_cu_current(), st);
+}
+
 // A host array of t device pointers to bf16 [rows, cols] blocks: INVALID_ARG
 // for a malformed list or shape, UNSUPPORTED for t above MAX_T.
 tp_mlp_status partial_list(int32_t t, const void* const* ptrs, int64_t rows, int64_t cols, PartialPtrs& pp) {
@@ -475,6 +548,42 @@ tp_mlp_status tp_mlp_all_gather_local(int32_t t, const void* const* shards, int6
   for (int r = 0; r < t; ++r)
     if (!disjoint(out, shard_bytes * (uint64_t)t, pp.p[r], shard_bytes)) return TP_MLP_ERR_INVALID_ARG;
   return hip_status(gather_launch(pp, t, shard_rows, cols, u16(out), num_cu_current(), stream));
+}
+
+tp_mlp_status tp_attn_qkv_shard(const tp_attn_shape* s, const void* X, const void* Wqkv_i, void* QKV_i,
+                                hipStream_t stream) {
+  AttnDims a;
+  if (const tp_mlp_status ss = attn_status(s, a)) return ss;
+  if (!req(X) || !req(Wqkv_i) || !req(QKV_i)) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(run_nn(a.N, a.qkv_cols, a.h, X, Wqkv_i, QKV_i, stream));
+}
+
+tp_mlp_status tp_attn_out_shard(const tp_attn_shape* s, const void* O_i, const void* Wo_i, void* Y_i,
+                                hipStream_t stream) {
+  AttnDims a;
+  if (const tp_mlp_status ss = attn_status(s, a)) return ss;
+  if (!req(O_i) || !req(Wo_i) || !req(Y_i)) return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(run_nn(a.N, a.h, a.q_cols, O_i, Wo_i, Y_i, stream));
+}
+
+tp_mlp_status tp_attn_out_bwd_shard(const tp_attn_shape* s, const void* dY, const void* O_i, const void* Wo_i,
+                                    void* dO_i, float* dWo_i, hipStream_t stream) {
+  AttnDims a;
+  if (const tp_mlp_status ss = attn_status(s, a)) return ss;
+  if (!req(dY) || !req(O_i) || !req(Wo_i) || !req(dO_i) || !req(dWo_i)) return TP_MLP_ERR_INVALID_ARG;
+  hipError_t e = run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream);
+  if (e == hipSuccess) e = run_tn(a.q_cols, a.h, a.N, O_i, dY, dWo_i, stream);
+  return hip_status(e);
+}
+
+tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X, const void* Wqkv_i,
+                                    const void* dQKV_i, float* dWqkv_i, void* dX_partial, hipStream_t stream) {
+  AttnDims a;
+  if (const tp_mlp_status ss = attn_status(s, a)) return ss;
+  if (!req(X) || !req(Wqkv_i) || !req(dQKV_i) || !req(dWqkv_i) || !req(dX_partial)) return TP_MLP_ERR_INVALID_ARG;
+  hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV_i, Wqkv_i, dX_partial, stream);
+  if (e == hipSuccess) e = run_tn(a.h, a.qkv_cols, a.N, X, dQKV_i, dWqkv_i, stream);
+  return hip_status(e);
 }
 
 }  // extern "C"

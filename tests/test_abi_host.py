@@ -19,7 +19,7 @@ FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced by validati
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tp_mlp_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tp_(?:mlp|attn)_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -28,7 +28,8 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
-    for required in ("tp_mlp_fwd_shard", "tp_mlp_bwd_shard", "tp_mlp_reduce_partials_local"):
+    for required in ("tp_mlp_fwd_shard", "tp_mlp_bwd_shard", "tp_mlp_reduce_partials_local",
+                     "tp_attn_qkv_shard", "tp_attn_out_shard", "tp_attn_out_bwd_shard", "tp_attn_qkv_bwd_shard"):
         assert required in names
 
 
@@ -192,3 +193,33 @@ def test_small_batch_workspace_sizes():
     s = B.make_shape(8, 64, 128, 2, 0, "gelu")
     assert _fwd(s) == WORKSPACE                                  # small batch needs workspace
     assert _fwd(s, ws=FAKE, wsb=B.workspace_bytes(s, False) - 1) == WORKSPACE
+
+
+@pytest.mark.parametrize("shape,expect", [
+    (B.make_attn_shape(0, 64, 8, 8, 64, 2, 0), INVALID),        # no tokens
+    (B.make_attn_shape(4, 60, 8, 8, 64, 2, 0), INVALID),        # h % 8
+    (B.make_attn_shape(4, 64, 8, 8, 60, 2, 0), INVALID),        # head_dim % 8
+    (B.make_attn_shape(4, 64, 6, 4, 64, 2, 0), INVALID),        # n_heads % n_kv
+    (B.make_attn_shape(4, 64, 12, 6, 64, 4, 0), INVALID),       # 6 kv heads over 4 ranks: neither split nor replicas
+    (B.make_attn_shape(4, 64, 8, 8, 64, 3, 0), INVALID),        # n_heads % t
+    (B.make_attn_shape(4, 64, 8, 8, 64, 2, 2), INVALID),        # rank >= t
+    (B.make_attn_shape(4, 64, 128, 1, 64, 128, 0), UNSUPPORTED),  # t > 64
+])
+def test_attn_rejects_bad_shapes(shape, expect):
+    L = B.lib()
+    r = ctypes.byref(shape)
+    assert L.tp_attn_qkv_shard(r, FAKE, FAKE, FAKE, None) == expect
+    assert L.tp_attn_out_shard(r, FAKE, FAKE, FAKE, None) == expect
+    assert L.tp_attn_out_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, FAKE, None) == expect
+    assert L.tp_attn_qkv_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, FAKE, None) == expect
+
+
+def test_attn_rejects_bad_pointers_and_reports_widths():
+    L = B.lib()
+    s = B.make_attn_shape(4, 64, 8, 2, 64, 4, 1)     # 2 kv heads over 4 ranks: replicated
+    assert (s.q_cols, s.kv_cols, s.qkv_cols) == (128, 64, 256)
+    r = ctypes.byref(s)
+    assert L.tp_attn_qkv_shard(r, None, FAKE, FAKE, None) == INVALID
+    assert L.tp_attn_out_shard(r, FAKE, FAKE + 2, FAKE, None) == INVALID
+    assert L.tp_attn_out_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
+    assert L.tp_attn_qkv_bwd_shard(r, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == INVALID
