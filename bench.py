@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--decode-workload", default="llama3_70b_decode_t4")
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-attn", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=256)
     return p.parse_args()
@@ -173,11 +174,16 @@ def main():
         "copy_probe": copy,
     }
 
-    # ---- decode (one token), HBM bound; weights rotated over copies
+    del X, dY, W1, W2, Wg, others_y, others_dx, A, U, G, dU, dW1, dWg, dW2, dX, Y, Yred, dXred
+    torch.cuda.empty_cache()
+    # ---- decode (one token, and small batches), HBM bound; weights rotated over copies
     if not args.no_decode:
         result["decode"] = bench_decode(args, WORKLOADS[args.decode_workload], B, I, torch, np, to_dev)
-    del X, dY, W1, W2, Wg, others_y, others_dx
-    torch.cuda.empty_cache()
+        torch.cuda.empty_cache()
+    # ---- attention block projections of the same model scale
+    if not args.no_attn:
+        result["attention_projections"] = bench_attn(args, B, I, torch, np, to_dev)
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows, I)
@@ -274,13 +280,77 @@ def bench_decode(args, w, B, I, torch, np, to_dev):
     gbs = wbytes / (us * 1e-6) / 1e9
     traffic = counter_traffic(f"gemv_hbm_traffic_{w.name}.md", GEMV_SOURCES, "decode")
     log(f"[bench] decode: {us:.2f} us/token cold ({gbs:.0f} GB/s), {us_warm:.2f} us warm")
+    # small-batch decode (2 <= N <= 64 takes the split-K MFMA path), same rotated weights
+    small = {}
+    for nb in (8, 32):
+        xb = to_dev(I.normal_bf16([w.wid, 40, nb], (nb, h)))
+        sb = B.make_shape(nb, h, w.F, w.t, 0, w.act)
+        wsb = B.alloc_workspace(B.workspace_bytes(sb, False))
+        Yb = torch.empty(nb, h, dtype=bf, device="cuda")
+        Ab = torch.empty(nb, Fi, dtype=bf, device="cuda")
+        for i in range(10):
+            a, g, b = sets[i % nsets]
+            B.tp_mlp_fwd_shard(sb, xb, a, g, b, Yb, Ab, None, None, wsb)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            a, g, b = sets[i % nsets]
+            B.tp_mlp_fwd_shard(sb, xb, a, g, b, Yb, Ab, None, None, wsb)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        usb = e0.elapsed_time(e1) * 1e3 / n
+        small[str(nb)] = {"us_per_step": round(usb, 3), "GB/s_of_weights": round(wbytes / (usb * 1e-6) / 1e9, 1),
+                          "tokens_per_s": round(nb / (usb * 1e-6), 1)}
+        log(f"[bench] small-batch decode N={nb}: {usb:.2f} us ({wbytes / (usb * 1e-6) / 1e9:.0f} GB/s of weights)")
     return {"workload": w.name, "value": round(gbs, 1), "unit": "GB/s", "us_per_token": round(us, 3),
+            "small_batch": small,
             "bytes_per_token": wbytes, "weight_sets_rotated": nsets,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic["bytes"] if traffic else None,
                          "scope": "whole decode call (gate/up GEMV + down GEMV)"},
             "us_per_token_warm_cache": round(us_warm, 3)}
+
+
+def bench_attn(args, B, I, torch, np, to_dev, N=2048, h=12288, heads=96, kv=96, d=128, t=8):
+    """One rank's attention projections at the GPT-3-scale shape of the MLP
+    workload (t = 8: 12 query heads of 128 per rank): QKV projection, output
+    projection, and both backwards (dO and dW_o; dX and dW_qkv), 6 GEMMs per
+    step.  The attention core between them is not part of this path."""
+    bf, f32 = torch.bfloat16, torch.float32
+    s = B.make_attn_shape(N, h, heads, kv, d, t, 0)
+    qc, wc = s.q_cols, s.qkv_cols
+    sig = I.WEIGHT_SIGMA
+    X, dY = to_dev(I.normal_bf16([900, 0], (N, h))), to_dev(I.normal_bf16([900, 1], (N, h)))
+    Wqkv, Wo = to_dev(I.normal_bf16([900, 2], (h, wc), sig)), to_dev(I.normal_bf16([900, 3], (qc, h), sig))
+    O, dQKV = to_dev(I.normal_bf16([900, 4], (N, qc))), to_dev(I.normal_bf16([900, 5], (N, wc)))
+    QKV, Y, dO = (torch.empty(N, c, dtype=bf, device="cuda") for c in (wc, h, qc))
+    dWo, dWqkv = torch.empty(qc, h, dtype=f32, device="cuda"), torch.empty(h, wc, dtype=f32, device="cuda")
+    dX = torch.empty(N, h, dtype=bf, device="cuda")
+
+    def step():
+        B.tp_attn_qkv_shard(s, X, Wqkv, QKV)
+        B.tp_attn_out_shard(s, O, Wo, Y)
+        B.tp_attn_out_bwd_shard(s, dY, O, Wo, dO, dWo)
+        B.tp_attn_qkv_bwd_shard(s, X, Wqkv, dQKV, dWqkv, dX)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record(stream)
+    for _ in range(n):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 3 * 2 * N * h * (wc + qc)
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] attention projections gpt3 t=8: {ms:.3f} ms/step, {tf:.1f} TFLOP/s")
+    return {"workload": f"gpt3_attn_t{t}: N={N} h={h} heads={heads} head_dim={d} t={t} (qkv {wc}, o {qc} cols/rank)",
+            "ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops_per_step": flops, "step": "QKV fwd, O fwd, O bwd (dO, dW_o), QKV bwd (dX, dW_qkv)"}
 
 
 def cpu_baseline(w, rows, I, target_s=10.0, cap_s=30.0):
