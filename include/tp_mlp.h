@@ -353,6 +353,98 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X,
                                     float* dWqkv_i, void* dX_partial,
                                     hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * LayerNorm of the sequence-parallel region ("Tensor and sequence
+ * parallelism", section "Sequence parallelism" and its check script;
+ * "02 -- Tensor Parallelism", the paragraph on LayerNorm and dropout between
+ * the two all-reduces).  Under sequence parallelism the LayerNorm works on
+ * the rank's own block of rows/t token rows; its output enters the
+ * tensor-parallel region through the all-gather, and the LayerNorm weights,
+ * shared by every block, have their gradients summed over the group.
+ *
+ * Per row of length h = cols:
+ *   mean = sum(x)/h,  var = sum((x - mean)^2)/h (biased),
+ *   rstd = 1/sqrt(var + eps),  y = (x - mean)*rstd*gamma + beta,
+ * computed in float32 from the bf16 row (mean and the centred variance from
+ * registers, two passes), y rounded to bf16 once.  Row statistics and the
+ * weight-gradient column sums are added in a fixed order: results are
+ * deterministic.  Dropout is not part of this path (probability 0).
+ *
+ * Common requirements: rows >= 1, 8 <= cols <= 16384 (larger: UNSUPPORTED),
+ * cols % 8 == 0, eps > 0 and finite, every pointer a 16-byte aligned device
+ * pointer.
+ * ------------------------------------------------------------------------ */
+
+/* y = LayerNorm(x).
+ *   x          bf16 [rows, cols]: the rank's block of token rows
+ *   gamma      bf16 [cols]; beta bf16 [cols] or NULL (no bias)
+ *   y          out bf16 [rows, cols]; may be the rank's block inside the
+ *              all-gather destination; may coincide exactly with x, must not
+ *              otherwise overlap an input
+ *   mean, rstd out float32 [rows] each (the backward's stash), or both NULL
+ *              (inference). */
+tp_mlp_status tp_sp_layernorm_fwd(int64_t rows, int64_t cols, float eps,
+                                  const void* x, const void* gamma,
+                                  const void* beta, void* y, float* mean,
+                                  float* rstd, hipStream_t stream);
+
+/* Leaving the tensor-parallel region into the next LayerNorm, in one pass:
+ * the reduce-scatter of tp_mlp_reduce_scatter_local,
+ *   z = bf16( sum_{k<t} partials[k][rank*rows/t + i][c] + bias[c]
+ *             + residual[i][c] )                (the new residual stream)
+ * then y = LayerNorm(z) of the stored bf16 z, exactly as the two separate
+ * calls would compute it.
+ *   partials, rows, cols, rank, bias, residual: as for
+ *              tp_mlp_reduce_scatter_local (rows % t == 0, 1 <= t <= 64);
+ *   z          out bf16 [rows/t, cols]; the same overlap rules as that
+ *              call's out;
+ *   gamma, beta, y, mean, rstd: as for tp_sp_layernorm_fwd over the
+ *              rows/t rows; y must not overlap z or any input. */
+tp_mlp_status tp_sp_reduce_scatter_layernorm_local(
+    int32_t t, const void* const* partials, int64_t rows, int64_t cols,
+    int32_t rank, const void* bias, const void* residual, void* z, float eps,
+    const void* gamma, const void* beta, void* y, float* mean, float* rstd,
+    hipStream_t stream);
+
+/* Backward of tp_sp_layernorm_fwd for the output gradient dy:
+ *   xhat = (x - mean)*rstd,  g = dy*gamma,
+ *   dx = rstd*(g - sum(g)/h - xhat*sum(g*xhat)/h) + dres,
+ *   dgamma = sum over the rows of dy*xhat,  dbeta = sum over the rows of dy.
+ * dgamma and dbeta cover this block's rows only: the group's gradient is
+ * their sum over the ranks (tp_sp_sum_grads_local).
+ *   x          bf16 [rows, cols]: the forward's input
+ *   gamma      bf16 [cols]
+ *   mean, rstd float32 [rows]: the forward's stash
+ *   dy         bf16 [rows, cols]
+ *   dres       bf16 [rows, cols] or NULL: the gradient arriving along the
+ *              residual branch, added to dx
+ *   dx         out bf16 [rows, cols]; may coincide exactly with dy or dres,
+ *              must not otherwise overlap an input
+ *   dgamma     out float32 [cols]; dbeta out float32 [cols] or NULL
+ *   workspace  tp_sp_layernorm_bwd_workspace_bytes(rows, cols) bytes of
+ *              device scratch (no initial contents needed; smaller:
+ *              TP_MLP_ERR_WORKSPACE). */
+tp_mlp_status tp_sp_layernorm_bwd(int64_t rows, int64_t cols, const void* x,
+                                  const void* gamma, const float* mean,
+                                  const float* rstd, const void* dy,
+                                  const void* dres, void* dx, float* dgamma,
+                                  float* dbeta, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes for tp_sp_layernorm_bwd; 0 for invalid sizes. */
+size_t tp_sp_layernorm_bwd_workspace_bytes(int64_t rows, int64_t cols);
+
+/* The all-reduce of a parameter shared by the sequence blocks (the LayerNorm
+ * weight and bias): out[i] = sum_{k<t} grads[k][i], float32, rank order.
+ *   grads  HOST array of t DEVICE pointers, each float32 [n]
+ *   out    float32 [n]; may coincide exactly with grads[0] (any rank's
+ *          buffer would be read after it is written), must not otherwise
+ *          overlap an input.
+ * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), n >= 4, n % 4 == 0. */
+tp_mlp_status tp_sp_sum_grads_local(int32_t t, const float* const* grads,
+                                    int64_t n, float* out,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_char_p, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
 
 import torch
 
@@ -89,6 +89,11 @@ _SIGS = {
     "tp_attn_out_shard": [POINTER(AttnShape)] + [c_void_p] * 3 + [c_void_p],
     "tp_attn_out_bwd_shard": [POINTER(AttnShape)] + [c_void_p] * 5 + [c_void_p],
     "tp_attn_qkv_bwd_shard": [POINTER(AttnShape)] + [c_void_p] * 5 + [c_void_p],
+    "tp_sp_layernorm_fwd": [c_int64, c_int64, c_float] + [c_void_p] * 6 + [c_void_p],
+    "tp_sp_reduce_scatter_layernorm_local": [c_int32, POINTER(c_void_p), c_int64, c_int64, c_int32, c_void_p,
+                                             c_void_p, c_void_p, c_float] + [c_void_p] * 5 + [c_void_p],
+    "tp_sp_layernorm_bwd": [c_int64, c_int64] + [c_void_p] * 10 + [c_size_t, c_void_p],
+    "tp_sp_sum_grads_local": [c_int32, POINTER(c_void_p), c_int64, c_void_p, c_void_p],
 }
 
 
@@ -108,6 +113,8 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_workspace_bytes.restype = c_size_t
         L.tp_mlp_bias_grad_workspace_bytes.argtypes = [c_int64, c_int64]
         L.tp_mlp_bias_grad_workspace_bytes.restype = c_size_t
+        L.tp_sp_layernorm_bwd_workspace_bytes.argtypes = [c_int64, c_int64]
+        L.tp_sp_layernorm_bwd_workspace_bytes.restype = c_size_t
         L.tp_mlp_status_string.argtypes = [c_int32]
         L.tp_mlp_status_string.restype = c_char_p
         _lib = L
@@ -124,6 +131,10 @@ def workspace_bytes(shape: Shape, backward: bool) -> int:
 
 def bias_grad_workspace_bytes(rows: int, cols: int) -> int:
     return int(lib().tp_mlp_bias_grad_workspace_bytes(rows, cols))
+
+
+def layernorm_bwd_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().tp_sp_layernorm_bwd_workspace_bytes(rows, cols))
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
@@ -326,3 +337,57 @@ def tp_attn_qkv_bwd_shard(shape: AttnShape, X, Wqkv_i, dQKV_i, dWqkv_i, dX_parti
         ctypes.byref(shape), _p(X, BF16, N * h, "X"), _p(Wqkv_i, BF16, h * w, "Wqkv_i"),
         _p(dQKV_i, BF16, N * w, "dQKV_i"), _p(dWqkv_i, F32, h * w, "dWqkv_i"),
         _p(dX_partial, BF16, N * h, "dX_partial"), _stream(stream)))
+
+
+# ------------------------------------------- sequence-parallel LayerNorm
+LN_EPS = 1e-5
+
+
+def tp_sp_layernorm_fwd(x, gamma, y, beta=None, mean=None, rstd=None, eps=LN_EPS, stream=None):
+    """y = LayerNorm(x) over the rank's bf16 [rows, cols] block; mean / rstd
+    float32 [rows] (both or neither) receive the backward's stash."""
+    rows, cols = x.shape
+    _check("tp_sp_layernorm_fwd", lib().tp_sp_layernorm_fwd(
+        rows, cols, eps, _p(x, BF16, rows * cols, "x"), _p(gamma, BF16, cols, "gamma"),
+        _p(beta, BF16, cols, "beta", optional=True), _p(y, BF16, rows * cols, "y"),
+        _p(mean, F32, rows, "mean", optional=True), _p(rstd, F32, rows, "rstd", optional=True), _stream(stream)))
+
+
+def tp_sp_reduce_scatter_layernorm_local(partials, rank, z, gamma, y, bias=None, residual=None, beta=None,
+                                         mean=None, rstd=None, eps=LN_EPS, stream=None):
+    """z = rank's block of sum(partials) + bias + residual (bf16), then
+    y = LayerNorm(z); z, y, residual are [rows / t, cols]."""
+    t, rows, cols, ptrs = _ptr_list(partials, "partials")
+    n = rows // t
+    _check("tp_sp_reduce_scatter_layernorm_local", lib().tp_sp_reduce_scatter_layernorm_local(
+        t, ptrs, rows, cols, rank, _p(bias, BF16, cols, "bias", optional=True),
+        _p(residual, BF16, n * cols, "residual", optional=True), _p(z, BF16, n * cols, "z"), eps,
+        _p(gamma, BF16, cols, "gamma"), _p(beta, BF16, cols, "beta", optional=True), _p(y, BF16, n * cols, "y"),
+        _p(mean, F32, n, "mean", optional=True), _p(rstd, F32, n, "rstd", optional=True), _stream(stream)))
+
+
+def tp_sp_layernorm_bwd(x, gamma, mean, rstd, dy, dx, dgamma, dbeta=None, dres=None, workspace=None, stream=None):
+    """dx = LayerNorm backward of dy (+ dres); dgamma / dbeta: float32 [cols]
+    sums over this block's rows."""
+    rows, cols = x.shape
+    wp, wb = _ws(workspace, 0)
+    _check("tp_sp_layernorm_bwd", lib().tp_sp_layernorm_bwd(
+        rows, cols, _p(x, BF16, rows * cols, "x"), _p(gamma, BF16, cols, "gamma"), _p(mean, F32, rows, "mean"),
+        _p(rstd, F32, rows, "rstd"), _p(dy, BF16, rows * cols, "dy"),
+        _p(dres, BF16, rows * cols, "dres", optional=True), _p(dx, BF16, rows * cols, "dx"),
+        _p(dgamma, F32, cols, "dgamma"), _p(dbeta, F32, cols, "dbeta", optional=True), wp, wb, _stream(stream)))
+
+
+def tp_sp_sum_grads_local(grads, out, stream=None):
+    """out = sum of the ranks' float32 gradients of a shared parameter, in
+    rank order (the all-reduce's arithmetic)."""
+    t = len(grads)
+    if t == 0:
+        raise ValueError("need at least one gradient")
+    n = grads[0].numel()
+    for g in grads:
+        if g.numel() != n:
+            raise ValueError("grads must share one size")
+    ptrs = (c_void_p * t)(*[_p(g, F32, n, f"grads[{i}]") for i, g in enumerate(grads)])
+    _check("tp_sp_sum_grads_local", lib().tp_sp_sum_grads_local(t, ptrs, n, _p(out, F32, n, "out"),
+                                                                 _stream(stream)))

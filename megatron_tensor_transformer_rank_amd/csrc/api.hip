@@ -9,6 +9,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "gemv.h"
+#include "norm.h"
 #include "reduce.h"
 #include "skinny.h"
 #include "tp_mlp.h"
@@ -347,6 +348,47 @@ bool same_or_disjoint(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return (a == b && na == nb) || disjoint(a, na, b, nb);
 }
 
+// The reduce-scatter's arguments: rank's block of rows/t rows, out may
+// coincide exactly with the residual or with rank's block of any partial and
+// must not otherwise overlap an input.
+tp_mlp_status rs_status(int32_t t, const void* const* partials, int64_t rows, int64_t cols, int32_t rank,
+                        const void* bias, const void* residual, const void* out, PartialPtrs& pp) {
+  if (const tp_mlp_status ss = partial_list(t, partials, rows, cols, pp)) return ss;
+  if (rows % t != 0 || rank < 0 || rank >= t) return TP_MLP_ERR_INVALID_ARG;
+  if (!req(out) || !opt_aligned(bias) || !opt_aligned(residual)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t out_bytes = (uint64_t)(rows / t) * (uint64_t)cols * 2;
+  const uint64_t block_off = (uint64_t)rank * out_bytes;
+  for (int r = 0; r < t; ++r) {
+    const uint8_t* blk = reinterpret_cast<const uint8_t*>(pp.p[r]) + block_off;
+    if (!same_or_disjoint(out, out_bytes, blk, out_bytes)) return TP_MLP_ERR_INVALID_ARG;
+    if (!disjoint(out, out_bytes, pp.p[r], block_off) ||
+        !disjoint(out, out_bytes, blk + out_bytes, (uint64_t)(t - 1 - rank) * out_bytes))
+      return TP_MLP_ERR_INVALID_ARG;
+  }
+  if (residual && !same_or_disjoint(out, out_bytes, residual, out_bytes)) return TP_MLP_ERR_INVALID_ARG;
+  if (bias && !disjoint(out, out_bytes, bias, (uint64_t)cols * 2)) return TP_MLP_ERR_INVALID_ARG;
+  return TP_MLP_OK;
+}
+
+// LayerNorm sizes and parameters shared by the sequence-parallel entry points.
+tp_mlp_status ln_status(int64_t rows, int64_t cols, float eps, const void* gamma, const void* beta) {
+  if (rows < 1 || rows >= (int64_t)1 << 31 || cols < 8 || cols % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
+  if (!(eps > 0.0f) || !(eps < 3.0e38f)) return TP_MLP_ERR_INVALID_ARG;
+  if (!req(gamma) || !opt_aligned(beta)) return TP_MLP_ERR_INVALID_ARG;
+  if (cols > LN_MAX_COLS) return TP_MLP_ERR_UNSUPPORTED;
+  return TP_MLP_OK;
+}
+
+// The LayerNorm stash: both float32 [rows] or both NULL; disjoint from y and
+// from each other.
+bool stash_ok(const float* mean, const float* rstd, int64_t rows, const void* y, uint64_t y_bytes) {
+  if ((mean == nullptr) != (rstd == nullptr)) return false;
+  if (!mean) return true;
+  const uint64_t sb = (uint64_t)rows * 4;
+  return req(mean) && req(rstd) && disjoint(mean, sb, rstd, sb) && disjoint(mean, sb, y, y_bytes) &&
+         disjoint(rstd, sb, y, y_bytes);
+}
+
 }  // namespace
 
 extern "C" {
@@ -519,22 +561,8 @@ tp_mlp_status tp_mlp_reduce_scatter_local(int32_t t, const void* const* partials
                                           int32_t rank, const void* bias, const void* residual, void* out,
                                           hipStream_t stream) {
   PartialPtrs pp = {};
-  if (const tp_mlp_status ss = partial_list(t, partials, rows, cols, pp)) return ss;
-  if (rows % t != 0 || rank < 0 || rank >= t) return TP_MLP_ERR_INVALID_ARG;
-  if (!req(out) || !opt_aligned(bias) || !opt_aligned(residual)) return TP_MLP_ERR_INVALID_ARG;
+  if (const tp_mlp_status ss = rs_status(t, partials, rows, cols, rank, bias, residual, out, pp)) return ss;
   const int64_t shard = rows / t;
-  const uint64_t out_bytes = (uint64_t)shard * (uint64_t)cols * 2;
-  const uint64_t block_off = (uint64_t)rank * out_bytes;
-  // out may coincide with the rank's block of a partial or with the residual;
-  // it must not otherwise overlap any input
-  for (int r = 0; r < t; ++r) {
-    const uint8_t* blk = reinterpret_cast<const uint8_t*>(pp.p[r]) + block_off;
-    if (!same_or_disjoint(out, out_bytes, blk, out_bytes)) return TP_MLP_ERR_INVALID_ARG;
-    if (!disjoint(out, out_bytes, pp.p[r], block_off) ||
-        !disjoint(out, out_bytes, blk + out_bytes, (uint64_t)(t - 1 - rank) * out_bytes))
-      return TP_MLP_ERR_INVALID_ARG;
-  }
-  if (residual && !same_or_disjoint(out, out_bytes, residual, out_bytes)) return TP_MLP_ERR_INVALID_ARG;
   return hip_status(reduce_partials_launch(pp, t, shard, cols, (int64_t)rank * shard, cu16(bias), cu16(residual),
                                            u16(out), num_cu_current(), stream));
 }
@@ -584,6 +612,84 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X, const
   hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV_i, Wqkv_i, dX_partial, stream);
   if (e == hipSuccess) e = run_tn(a.h, a.qkv_cols, a.N, X, dQKV_i, dWqkv_i, stream);
   return hip_status(e);
+}
+
+tp_mlp_status tp_sp_layernorm_fwd(int64_t rows, int64_t cols, float eps, const void* x, const void* gamma,
+                                  const void* beta, void* y, float* mean, float* rstd, hipStream_t stream) {
+  if (const tp_mlp_status ss = ln_status(rows, cols, eps, gamma, beta)) return ss;
+  if (!req(x) || !req(y)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t nb = (uint64_t)rows * (uint64_t)cols * 2;
+  if (!same_or_disjoint(y, nb, x, nb) || !disjoint(y, nb, gamma, (uint64_t)cols * 2) ||
+      (beta && !disjoint(y, nb, beta, (uint64_t)cols * 2)) || !stash_ok(mean, rstd, rows, y, nb) ||
+      (mean && (!disjoint(mean, (uint64_t)rows * 4, x, nb) || !disjoint(rstd, (uint64_t)rows * 4, x, nb))))
+    return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(ln_fwd_launch(cu16(x), rows, cols, eps, cu16(gamma), cu16(beta), u16(y), mean, rstd, stream));
+}
+
+tp_mlp_status tp_sp_reduce_scatter_layernorm_local(int32_t t, const void* const* partials, int64_t rows,
+                                                   int64_t cols, int32_t rank, const void* bias,
+                                                   const void* residual, void* z, float eps, const void* gamma,
+                                                   const void* beta, void* y, float* mean, float* rstd,
+                                                   hipStream_t stream) {
+  PartialPtrs pp = {};
+  if (const tp_mlp_status ss = rs_status(t, partials, rows, cols, rank, bias, residual, z, pp)) return ss;
+  const int64_t shard = rows / t;
+  if (const tp_mlp_status ss = ln_status(shard, cols, eps, gamma, beta)) return ss;
+  if (!req(y)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t nb = (uint64_t)shard * (uint64_t)cols * 2, full = (uint64_t)rows * (uint64_t)cols * 2;
+  for (int r = 0; r < t; ++r)
+    if (!disjoint(y, nb, pp.p[r], full)) return TP_MLP_ERR_INVALID_ARG;
+  if (!disjoint(y, nb, z, nb) || (residual && !disjoint(y, nb, residual, nb)) ||
+      (bias && !disjoint(y, nb, bias, (uint64_t)cols * 2)) || !disjoint(y, nb, gamma, (uint64_t)cols * 2) ||
+      (beta && !disjoint(y, nb, beta, (uint64_t)cols * 2)) || !stash_ok(mean, rstd, shard, y, nb) ||
+      (mean && (!disjoint(mean, (uint64_t)shard * 4, z, nb) || !disjoint(rstd, (uint64_t)shard * 4, z, nb))))
+    return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(ln_fwd_fused_launch(pp, t, shard, cols, (int64_t)rank * shard, cu16(bias), cu16(residual),
+                                        u16(z), eps, cu16(gamma), cu16(beta), u16(y), mean, rstd, stream));
+}
+
+size_t tp_sp_layernorm_bwd_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 1 || rows >= (int64_t)1 << 31 || cols < 8 || cols % 8 != 0 || cols > LN_MAX_COLS) return 0;
+  return ln_bwd_workspace_bytes(rows, cols);
+}
+
+tp_mlp_status tp_sp_layernorm_bwd(int64_t rows, int64_t cols, const void* x, const void* gamma, const float* mean,
+                                  const float* rstd, const void* dy, const void* dres, void* dx, float* dgamma,
+                                  float* dbeta, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (const tp_mlp_status ss = ln_status(rows, cols, 1.0f, gamma, nullptr)) return ss;
+  if (!req(x) || !req(mean) || !req(rstd) || !req(dy) || !opt_aligned(dres) || !req(dx) || !req(dgamma) ||
+      !opt_aligned(dbeta))
+    return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t nb = (uint64_t)rows * (uint64_t)cols * 2, gb = (uint64_t)cols * 4;
+  const size_t need = ln_bwd_workspace_bytes(rows, cols);
+  if (!disjoint(dx, nb, x, nb) || !same_or_disjoint(dx, nb, dy, nb) || (dres && !same_or_disjoint(dx, nb, dres, nb)) ||
+      !disjoint(dx, nb, gamma, (uint64_t)cols * 2) || !disjoint(dx, nb, mean, (uint64_t)rows * 4) ||
+      !disjoint(dx, nb, rstd, (uint64_t)rows * 4) || !disjoint(dgamma, gb, dx, nb) ||
+      (dbeta && (!disjoint(dbeta, gb, dx, nb) || !disjoint(dbeta, gb, dgamma, gb))))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return TP_MLP_ERR_WORKSPACE;
+  if (!disjoint(workspace, need, dx, nb) || !disjoint(workspace, need, dgamma, gb) ||
+      (dbeta && !disjoint(workspace, need, dbeta, gb)) || !disjoint(workspace, need, x, nb) ||
+      !disjoint(workspace, need, dy, nb))
+    return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(ln_bwd_launch(cu16(x), cu16(gamma), mean, rstd, cu16(dy), cu16(dres), u16(dx), rows, cols,
+                                  dgamma, dbeta, static_cast<float*>(workspace), stream));
+}
+
+tp_mlp_status tp_sp_sum_grads_local(int32_t t, const float* const* grads, int64_t n, float* out,
+                                    hipStream_t stream) {
+  if (grads == nullptr || t < 1) return TP_MLP_ERR_INVALID_ARG;
+  if (t > MAX_T) return TP_MLP_ERR_UNSUPPORTED;
+  if (n < 4 || n % 4 != 0 || n > (int64_t)1 << 40 || !req(out)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t nb = (uint64_t)n * 4;
+  GradPtrs g = {};
+  for (int r = 0; r < t; ++r) {
+    if (!req(grads[r])) return TP_MLP_ERR_INVALID_ARG;
+    if (r == 0 ? !same_or_disjoint(out, nb, grads[r], nb) : !disjoint(out, nb, grads[r], nb))
+      return TP_MLP_ERR_INVALID_ARG;
+    g.p[r] = grads[r];
+  }
+  return hip_status(sum_f32_launch(g, t, n, out, stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,421 @@
+// LayerNorm of the sequence-parallel region for gfx950: forward (optionally
+// fused with the reduce-scatter that leaves the tensor-parallel region, its
+// output bias and the residual addition), backward (with the residual
+// branch's gradient added), and the sum over ranks of the LayerNorm weight's
+// gradient ("Tensor and sequence parallelism", section "Sequence
+// parallelism": the LayerNorms, dropouts and residual additions work on the
+// rank's s/t token rows, and the weights shared by those blocks need their
+// gradients summed over the group).
+//
+// All HBM-bound streams of 16-byte chunks.  A 256-thread block owns a whole
+// row (LayerNorm needs the row's statistics): thread i holds chunks
+// i, i + 256, ... of the row in registers, so every element is read once and
+// the statistics come from registers in two passes (mean, then the biased
+// variance of the centred values).  Block sums: a butterfly over the 64 lanes
+// (every lane ends with the same bits), then the 4 waves in wave order, so
+// results are deterministic.  The fused forward adds the t partial sums in
+// float32 in rank order, then the bias, then the residual, rounds z to bf16,
+// stores it, and normalises that stored value: bit for bit what a separate
+// reduce-scatter followed by a LayerNorm of z computes.
+//
+// The backward's column sums (dgamma, dbeta) are per-block partial rows over
+// a slab of rows, then a second kernel adds the slabs in slab order.
+#include "common.h"
+#include "norm.h"
+
+namespace tpmlp {
+
+constexpr int LN_THREADS = 256;
+constexpr int LN_WAVES = LN_THREADS / 64;
+constexpr int LN_BATCH = 4;  // ranks loaded before they are added
+constexpr int SS_GROUPS = 16;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__device__ __forceinline__ u32x4 ld_nt(const uint16_t* p, int64_t chunk) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + chunk);
+}
+__device__ __forceinline__ u32x4 ld_c(const uint16_t* p, int64_t chunk) {
+  return reinterpret_cast<const u32x4*>(p)[chunk];
+}
+__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
+  f[0] = bf16lo(v.x); f[1] = bf16hi(v.x);
+  f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
+  f[4] = bf16lo(v.z); f[5] = bf16hi(v.z);
+  f[6] = bf16lo(v.w); f[7] = bf16hi(v.w);
+}
+__device__ __forceinline__ void add8(float (&s)[8], u32x4 v) {
+  s[0] += bf16lo(v.x); s[1] += bf16hi(v.x);
+  s[2] += bf16lo(v.y); s[3] += bf16hi(v.y);
+  s[4] += bf16lo(v.z); s[5] += bf16hi(v.z);
+  s[6] += bf16lo(v.w); s[7] += bf16hi(v.w);
+}
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Sum of v over the block; red is LN_WAVES floats of LDS used by this call
+// only.  Every thread returns the same value.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = red[0];
+#pragma unroll
+  for (int w = 1; w < LN_WAVES; ++w) s += red[w];
+  return s;
+}
+
+}  // namespace
+
+// One row per block.  FUSED: the row is row0 + blockIdx.x of the partial sums
+// (plus bias and residual), stored to z; otherwise it is row blockIdx.x of x.
+template <int J, bool FUSED>
+__global__ void __launch_bounds__(LN_THREADS)
+ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ bias, const uint16_t* residual,
+              uint16_t* z, const uint16_t* x, int cols8, int cols, float eps, const uint16_t* __restrict__ gamma,
+              const uint16_t* __restrict__ beta, uint16_t* y, float* __restrict__ mean_out,
+              float* __restrict__ rstd_out) {
+  __shared__ float red[2][LN_WAVES];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t base = row * cols8;
+  float v[J][8];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+
+  if constexpr (FUSED) {
+    const int64_t in_base = (row0 + row) * cols8;
+    for (int r0 = 0; r0 < t; r0 += LN_BATCH) {
+      u32x4 c[J][LN_BATCH];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int q = tid + j * LN_THREADS;
+#pragma unroll
+        for (int b = 0; b < LN_BATCH; ++b)
+          c[j][b] = (r0 + b < t && q < cols8) ? ld_nt(pp.p[r0 + b], in_base + q) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int b = 0; b < LN_BATCH; ++b)
+          if (r0 + b < t) add8(v[j], c[j][b]);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = tid + j * LN_THREADS;
+      if (q < cols8) {
+        if (bias) add8(v[j], ld_c(bias, q));
+        if (residual) add8(v[j], ld_nt(residual, base + q));
+        const u32x4 o = pack8(v[j]);
+        reinterpret_cast<u32x4*>(z)[base + q] = o;
+        unpack8(o, v[j]);  // the LayerNorm reads z as stored
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = tid + j * LN_THREADS;
+      if (q < cols8) unpack8(ld_nt(x, base + q), v[j]);
+    }
+  }
+
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += v[j][e];
+  const float mean = block_sum(s, red[0]) / (float)cols;
+  float d = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (tid + j * LN_THREADS < cols8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float c = v[j][e] - mean;
+        d += c * c;
+      }
+    }
+  }
+  const float var = block_sum(d, red[1]) / (float)cols;
+  const float rstd = 1.0f / sqrtf(var + eps);
+
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int q = tid + j * LN_THREADS;
+    if (q < cols8) {
+      float g[8], b[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, o[8];
+      unpack8(ld_c(gamma, q), g);
+      if (beta) unpack8(ld_c(beta, q), b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (v[j][e] - mean) * rstd * g[e] + b[e];
+      reinterpret_cast<u32x4*>(y)[base + q] = pack8(o);
+    }
+  }
+  if (tid == 0 && mean_out) {
+    mean_out[row] = mean;
+    rstd_out[row] = rstd;
+  }
+}
+
+// Block b owns rows [b * rpb, min(rows, (b + 1) * rpb)), one after another.
+// Per row: xhat = (x - mean) * rstd, g = dy * gamma,
+// dx = rstd * (g - sum(g)/h - xhat * sum(g * xhat)/h) (+ dres); the block's
+// dgamma = sum dy * xhat and dbeta = sum dy go to its partial rows.
+template <int J>
+__global__ void __launch_bounds__(LN_THREADS)
+ln_bwd_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
+              const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int64_t rows,
+              int cols8, int cols, int64_t rpb, float* __restrict__ part_g, float* __restrict__ part_b) {
+  __shared__ float red[2][2][LN_WAVES];  // [row parity][sum][wave]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * rpb;
+  const int64_t r1 = r0 + rpb < rows ? r0 + rpb : rows;
+  float ag[J][8], ab[J][8];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[j][e] = ab[j][e] = 0.f;
+
+  for (int64_t r = r0; r < r1; ++r) {
+    const int par = (int)(r & 1);
+    const float mu = mean[r], rs = rstd[r];
+    const int64_t base = r * cols8;
+    u32x4 xv[J], dv[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = tid + j * LN_THREADS;
+      xv[j] = q < cols8 ? ld_nt(x, base + q) : u32x4{0u, 0u, 0u, 0u};
+      dv[j] = q < cols8 ? ld_nt(dy, base + q) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // xhat and g are recomputed from the packed row in the output loop
+    // (fewer registers than keeping them as floats)
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = tid + j * LN_THREADS;
+      if (q < cols8) {
+        float xf[8], df[8], gm[8];
+        unpack8(xv[j], xf);
+        unpack8(dv[j], df);
+        unpack8(ld_c(gamma, q), gm);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xh = (xf[e] - mu) * rs, g = df[e] * gm[e];
+          s1 += g;
+          s2 += g * xh;
+          ag[j][e] += df[e] * xh;
+          ab[j][e] += df[e];
+        }
+      }
+    }
+    // both row sums with one barrier: the buffers alternate with the row's
+    // parity, and a buffer is written again only after the next row's
+    // barrier, which every thread passes after its reads of this one
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    if (lane == 0) {
+      red[par][0][w] = s1;
+      red[par][1][w] = s2;
+    }
+    __syncthreads();
+    float S1 = red[par][0][0], S2 = red[par][1][0];
+#pragma unroll
+    for (int q = 1; q < LN_WAVES; ++q) {
+      S1 += red[par][0][q];
+      S2 += red[par][1][q];
+    }
+    const float m1 = S1 / (float)cols, m2 = S2 / (float)cols;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = tid + j * LN_THREADS;
+      if (q < cols8) {
+        float xf[8], df[8], gm[8], o[8];
+        unpack8(xv[j], xf);
+        unpack8(dv[j], df);
+        unpack8(ld_c(gamma, q), gm);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = rs * (df[e] * gm[e] - m1 - (xf[e] - mu) * rs * m2);
+        if (dres) add8(o, ld_nt(dres, base + q));
+        reinterpret_cast<u32x4*>(dx)[base + q] = pack8(o);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int q = tid + j * LN_THREADS;
+    if (q < cols8) {
+      float4* pg = reinterpret_cast<float4*>(part_g + (int64_t)blockIdx.x * cols + (int64_t)q * 8);
+      pg[0] = make_float4(ag[j][0], ag[j][1], ag[j][2], ag[j][3]);
+      pg[1] = make_float4(ag[j][4], ag[j][5], ag[j][6], ag[j][7]);
+      if (part_b) {
+        float4* pb = reinterpret_cast<float4*>(part_b + (int64_t)blockIdx.x * cols + (int64_t)q * 8);
+        pb[0] = make_float4(ab[j][0], ab[j][1], ab[j][2], ab[j][3]);
+        pb[1] = make_float4(ab[j][4], ab[j][5], ab[j][6], ab[j][7]);
+      }
+    }
+  }
+}
+
+// out[c] = sum_{q<slabs} part[q][c].  A block owns 64 columns (16 float4
+// lanes); its 16 groups each add every 16th slab in increasing order, then the
+// group sums are added in group order.
+__global__ void __launch_bounds__(LN_THREADS)
+slab_sum_kernel(const float* __restrict__ part, int slabs, int64_t cols, float* __restrict__ out) {
+  __shared__ float4 red[SS_GROUPS][16];
+  const int c4 = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int64_t c = (int64_t)blockIdx.x * 64 + c4 * 4;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < cols) {
+    for (int q = grp; q < slabs; q += SS_GROUPS) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)q * cols + c);
+      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+  }
+  red[grp][c4] = a;
+  __syncthreads();
+  if (grp == 0 && c < cols) {
+    float4 r = red[0][c4];
+#pragma unroll
+    for (int q = 1; q < SS_GROUPS; ++q) {
+      const float4 o = red[q][c4];
+      r.x += o.x; r.y += o.y; r.z += o.z; r.w += o.w;
+    }
+    *reinterpret_cast<float4*>(out + c) = r;
+  }
+}
+
+// out[i] = sum_{k<t} g.p[k][i], float4 per thread, rank order.
+__global__ void __launch_bounds__(LN_THREADS)
+sum_f32_kernel(GradPtrs g, int t, int64_t n4, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * LN_THREADS + threadIdx.x; i < n4; i += (int64_t)gridDim.x * LN_THREADS) {
+    float4 s = reinterpret_cast<const float4*>(g.p[0])[i];
+    for (int k = 1; k < t; ++k) {
+      const float4 v = reinterpret_cast<const float4*>(g.p[k])[i];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    reinterpret_cast<float4*>(out)[i] = s;
+  }
+}
+
+namespace {
+
+// chunks per thread, the smallest instantiated J >= cols8 / 256
+int ln_j(int64_t cols) {
+  const int64_t need = (cols / 8 + LN_THREADS - 1) / LN_THREADS;
+  static const int js[] = {1, 2, 3, 4, 6, 8};
+  for (int j : js)
+    if (j >= need) return j;
+  return 0;
+}
+
+void bwd_slabs(int64_t rows, int& slabs, int64_t& rpb) {
+  int64_t nb = rows < LN_MAX_SLABS ? rows : LN_MAX_SLABS;
+  if (nb < 1) nb = 1;
+  rpb = (rows + nb - 1) / nb;
+  slabs = (int)((rows + rpb - 1) / rpb);
+}
+
+template <bool FUSED>
+hipError_t fwd_dispatch(const PartialPtrs& pp, int t, int64_t rows, int64_t cols, int64_t row0,
+                        const uint16_t* bias, const uint16_t* residual, uint16_t* z, const uint16_t* x, float eps,
+                        const uint16_t* gamma, const uint16_t* beta, uint16_t* y, float* mean, float* rstd,
+                        hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int cols8 = (int)(cols / 8);
+  const dim3 grid((unsigned)rows), blk(LN_THREADS);
+#define LN_FWD(J)                                                                                              \
+  hipLaunchKernelGGL((ln_fwd_kernel<J, FUSED>), grid, blk, 0, st, pp, t, row0, bias, residual, z, x, cols8,   \
+                     (int)cols, eps, gamma, beta, y, mean, rstd)
+  switch (ln_j(cols)) {
+    case 1: LN_FWD(1); break;
+    case 2: LN_FWD(2); break;
+    case 3: LN_FWD(3); break;
+    case 4: LN_FWD(4); break;
+    case 6: LN_FWD(6); break;
+    case 8: LN_FWD(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef LN_FWD
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t ln_fwd_launch(const uint16_t* x, int64_t rows, int64_t cols, float eps, const uint16_t* gamma,
+                         const uint16_t* beta, uint16_t* y, float* mean, float* rstd, hipStream_t st) {
+  const PartialPtrs none = {};
+  return fwd_dispatch<false>(none, 0, rows, cols, 0, nullptr, nullptr, nullptr, x, eps, gamma, beta, y, mean, rstd,
+                             st);
+}
+
+hipError_t ln_fwd_fused_launch(const PartialPtrs& pp, int t, int64_t rows, int64_t cols, int64_t row0,
+                               const uint16_t* bias, const uint16_t* residual, uint16_t* z, float eps,
+                               const uint16_t* gamma, const uint16_t* beta, uint16_t* y, float* mean, float* rstd,
+                               hipStream_t st) {
+  return fwd_dispatch<true>(pp, t, rows, cols, row0, bias, residual, z, nullptr, eps, gamma, beta, y, mean, rstd, st);
+}
+
+size_t ln_bwd_workspace_bytes(int64_t rows, int64_t cols) {
+  int slabs;
+  int64_t rpb;
+  bwd_slabs(rows, slabs, rpb);
+  return (size_t)2 * (size_t)slabs * (size_t)cols * sizeof(float);
+}
+
+hipError_t ln_bwd_launch(const uint16_t* x, const uint16_t* gamma, const float* mean, const float* rstd,
+                         const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int64_t rows, int64_t cols,
+                         float* dgamma, float* dbeta, float* part, hipStream_t st) {
+  int slabs;
+  int64_t rpb;
+  bwd_slabs(rows, slabs, rpb);
+  float* part_g = part;
+  float* part_b = dbeta ? part + (int64_t)slabs * cols : nullptr;
+  const int cols8 = (int)(cols / 8);
+  const dim3 grid((unsigned)slabs), blk(LN_THREADS);
+#define LN_BWD(J)                                                                                                \
+  hipLaunchKernelGGL((ln_bwd_kernel<J>), grid, blk, 0, st, x, gamma, mean, rstd, dy, dres, dx, rows, cols8,     \
+                     (int)cols, rpb, part_g, part_b)
+  switch (ln_j(cols)) {
+    case 1: LN_BWD(1); break;
+    case 2: LN_BWD(2); break;
+    case 3: LN_BWD(3); break;
+    case 4: LN_BWD(4); break;
+    case 6: LN_BWD(6); break;
+    case 8: LN_BWD(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef LN_BWD
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 sgrid((unsigned)((cols + 63) / 64));
+  hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, slabs, cols, dgamma);
+  e = hipGetLastError();
+  if (e != hipSuccess || !dbeta) return e;
+  hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_b, slabs, cols, dbeta);
+  return hipGetLastError();
+}
+
+hipError_t sum_f32_launch(const GradPtrs& g, int t, int64_t n, float* out, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  int64_t blocks = (n4 + LN_THREADS - 1) / LN_THREADS;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(sum_f32_kernel, dim3((unsigned)blocks), dim3(LN_THREADS), 0, st, g, t, n4, out);
+  return hipGetLastError();
+}
+
+}  // namespace tpmlp

@@ -11,7 +11,9 @@ Recipe (the shapes come from the workload table in ``configs.py``):
 * Generator: numpy PCG64 seeded with ``[workload_id, tensor_id, block]``,
   ``standard_normal(dtype=float32) * sigma``, then RNE to bf16.
 * tensor ids: X = 0, W_up (W1) = 1, W_gate = 2, W_down (W2) = 3, dY = 4,
-  b2 = 5.
+  b2 = 5, LayerNorm weight = 6, LayerNorm bias = 7.
+* LayerNorm parameters: weight ~ 1 + N(0, 0.1), bias ~ N(0, 0.02) (a
+  trained-looking spread around the initial 1 and 0).
 * Weights are generated one rank block at a time (block = rank): W1 and
   W_gate column blocks [h, F/t], W2 row blocks [F/t, h].  The full matrix is
   the concatenation of the blocks in rank order, so a rank's shard can be
@@ -21,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-X_ID, WUP_ID, WGATE_ID, WDOWN_ID, DY_ID, B2_ID = 0, 1, 2, 3, 4, 5
+X_ID, WUP_ID, WGATE_ID, WDOWN_ID, DY_ID, B2_ID, LNW_ID, LNB_ID = 0, 1, 2, 3, 4, 5, 6, 7
 WEIGHT_SIGMA = 0.02
 
 
@@ -56,6 +58,16 @@ def gen_dy(wid: int, N: int, h: int) -> np.ndarray:
 
 def gen_b2(wid: int, h: int) -> np.ndarray:
     return normal_bf16([wid, B2_ID, 0], (h,), WEIGHT_SIGMA)
+
+
+def gen_ln_weight(wid: int, h: int) -> np.ndarray:
+    """LayerNorm weight [h]: bf16 of 1 + 0.1 * N(0, 1)."""
+    rng = np.random.default_rng([wid, LNW_ID, 0])
+    return f32_to_bf16_bits(np.float32(1.0) + np.float32(0.1) * rng.standard_normal(size=(h,), dtype=np.float32))
+
+
+def gen_ln_bias(wid: int, h: int) -> np.ndarray:
+    return normal_bf16([wid, LNB_ID, 0], (h,), WEIGHT_SIGMA)
 
 
 def gen_w_up_shard(wid: int, h: int, Fi: int, rank: int) -> np.ndarray:

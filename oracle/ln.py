@@ -25,7 +25,9 @@ rounding:
 * the all-reduce of a shared parameter's gradient: the ranks' contributions
   added in rank order;
 * the pages' TP+SP block: LayerNorm on each rank's block, all-gather, the
-  MLP shard of every rank, reduce-scatter (oracle/mlp.py), and its backward.
+  MLP shard of every rank, reduce-scatter (oracle/mlp.py), and its backward;
+  optionally with the gathered activations rounded to bfloat16, the format
+  in which they travel (round_bf16, the format's definition).
 Dropout is not modelled (probability 0, as in the pages' check).
 
 Every function here is pinned in ``tests/test_oracle_ln_pins.py``.
@@ -95,6 +97,17 @@ def layer_norm_backward(dy, x, gamma, eps: float = EPS, dres=None):
     return dx, dgamma, dbeta
 
 
+def round_bf16(a):
+    """Nearest bfloat16 value of each float64 (ties to even): the storage
+    format of the activations that cross the all-gather.  bfloat16 keeps 8
+    significant bits (7 stored) and float32's exponent range; values are
+    finite and within that range here."""
+    a = _f64(a)
+    m, e = np.frexp(a)              # a = m * 2^e, 0.5 <= |m| < 1
+    scaled = m * 256.0               # 8 significant bits -> an integer part
+    return np.ldexp(np.round(scaled), e - 8)   # np.round: half to even
+
+
 def sum_shared_grads(grads):
     """The all-reduce of a parameter shared by the sequence blocks (the
     LayerNorm weight and bias): the ranks' gradients added in rank order."""
@@ -104,18 +117,25 @@ def sum_shared_grads(grads):
     return out
 
 
-def sp_block_forward(act, x, gamma, W1, W2, t, Wg=None, beta=None, b2=None, residual=None, eps: float = EPS):
+def sp_block_forward(act, x, gamma, W1, W2, t, Wg=None, beta=None, b2=None, residual=None, eps: float = EPS,
+                     payload_bf16: bool = False):
     """The pages' TP+SP block for the whole group: rank r normalises its
     block x[r*N/t:(r+1)*N/t] of x [N, h]; the blocks are all-gathered; every
     rank runs its MLP shard on the gathered rows; the partial sums are
     reduce-scattered, with the output bias added once and the rank's block of
     ``residual`` [N, h] added.  Returns (outs, ln), both lists of the ranks'
-    [N/t, h] blocks (the block outputs and the LayerNorm outputs)."""
+    [N/t, h] blocks (the block outputs and the LayerNorm outputs).
+
+    payload_bf16: the LayerNorm outputs are rounded to bfloat16 before the
+    all-gather, the format in which they travel; the default keeps them in
+    float64 (no intermediate rounding).  With ReLU the backward's derivative
+    is a decision (U > 0) taken on the gathered activations, so a comparison
+    with a path that gathers bf16 activations takes it on the same values."""
     x = _f64(x)
     N, F = x.shape[0], _f64(W1).shape[1]
     blocks = [mlp.sequence_block(r, t, N) for r in range(t)]
     ln = [layer_norm_forward(x[b], gamma, beta, eps)[0] for b in blocks]
-    X = mlp.all_gather(ln)
+    X = mlp.all_gather([round_bf16(a) for a in ln] if payload_bf16 else ln)
     partials = []
     for r in range(t):
         c = mlp.column_block(r, t, F)
@@ -126,7 +146,8 @@ def sp_block_forward(act, x, gamma, W1, W2, t, Wg=None, beta=None, b2=None, resi
     return outs, ln
 
 
-def sp_block_backward(act, x, gamma, W1, W2, douts, t, Wg=None, beta=None, eps: float = EPS, dres=None):
+def sp_block_backward(act, x, gamma, W1, W2, douts, t, Wg=None, beta=None, eps: float = EPS, dres=None,
+                      payload_bf16: bool = False):
     """Backward of sp_block_forward for the ranks' output-gradient blocks
     ``douts`` (list of t [N/t, h]).  The reduce-scatter's backward is an
     all-gather of douts (the MLP's dY, the same on every rank); each rank's
@@ -134,12 +155,14 @@ def sp_block_backward(act, x, gamma, W1, W2, douts, t, Wg=None, beta=None, eps: 
     all-gather's backward reduce-scatters those into the rank's rows; the
     LayerNorm backward of the rank's block follows (``dres``: list of t
     residual-branch gradients or None), and the LayerNorm weight's gradient is
-    summed over the ranks.  Returns dict(dx=[t blocks], dgamma, dbeta,
-    dgamma_r=[t], dbeta_r=[t], shard=[t shard_backward results])."""
+    summed over the ranks.  payload_bf16 as for sp_block_forward.  Returns
+    dict(dx=[t blocks], dgamma, dbeta, dgamma_r=[t], dbeta_r=[t],
+    shard=[t shard_backward results])."""
     x = _f64(x)
     N, F = x.shape[0], _f64(W1).shape[1]
     blocks = [mlp.sequence_block(r, t, N) for r in range(t)]
-    X = mlp.all_gather([layer_norm_forward(x[b], gamma, beta, eps)[0] for b in blocks])
+    ln = [layer_norm_forward(x[b], gamma, beta, eps)[0] for b in blocks]
+    X = mlp.all_gather([round_bf16(a) for a in ln] if payload_bf16 else ln)
     dY = mlp.all_gather(douts)
     shard = []
     for r in range(t):

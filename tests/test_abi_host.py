@@ -19,7 +19,7 @@ FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced by validati
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tp_(?:mlp|attn)_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tp_(?:mlp|attn|sp)_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -29,7 +29,9 @@ def test_library_exports_every_declared_symbol():
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     for required in ("tp_mlp_fwd_shard", "tp_mlp_bwd_shard", "tp_mlp_reduce_partials_local",
-                     "tp_attn_qkv_shard", "tp_attn_out_shard", "tp_attn_out_bwd_shard", "tp_attn_qkv_bwd_shard"):
+                     "tp_attn_qkv_shard", "tp_attn_out_shard", "tp_attn_out_bwd_shard", "tp_attn_qkv_bwd_shard",
+                     "tp_sp_layernorm_fwd", "tp_sp_reduce_scatter_layernorm_local", "tp_sp_layernorm_bwd",
+                     "tp_sp_layernorm_bwd_workspace_bytes", "tp_sp_sum_grads_local"):
         assert required in names
 
 
@@ -223,3 +225,106 @@ def test_attn_rejects_bad_pointers_and_reports_widths():
     assert L.tp_attn_out_shard(r, FAKE, FAKE + 2, FAKE, None) == INVALID
     assert L.tp_attn_out_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
     assert L.tp_attn_qkv_bwd_shard(r, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == INVALID
+
+
+# ------------------------------------------- sequence-parallel LayerNorm
+MB = 1 << 20
+
+
+def test_layernorm_fwd_rejects_bad_arguments():
+    f = B.lib().tp_sp_layernorm_fwd
+    x, g, y, m, r = FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 3 * MB, FAKE + 4 * MB
+    assert f(0, 16, 1e-5, x, g, None, y, m, r, None) == INVALID            # no rows
+    assert f(4, 12, 1e-5, x, g, None, y, m, r, None) == INVALID            # cols % 8
+    assert f(4, 16, 0.0, x, g, None, y, m, r, None) == INVALID             # eps must be > 0
+    assert f(4, 16, -1.0, x, g, None, y, m, r, None) == INVALID
+    assert f(4, 16, float("nan"), x, g, None, y, m, r, None) == INVALID
+    assert f(4, 16, float("inf"), x, g, None, y, m, r, None) == INVALID
+    assert f(4, 16, 1e-5, None, g, None, y, m, r, None) == INVALID
+    assert f(4, 16, 1e-5, x, None, None, y, m, r, None) == INVALID         # gamma required
+    assert f(4, 16, 1e-5, x, g, FAKE + 8, y, m, r, None) == INVALID        # misaligned beta
+    assert f(4, 16, 1e-5, x, g, None, y, m, None, None) == INVALID         # mean without rstd
+    assert f(4, 16, 1e-5, x, g, None, y, None, r, None) == INVALID
+    assert f(4, 16, 1e-5, x, g, None, x + 16, m, r, None) == INVALID       # y straddles x
+    assert f(4, 16, 1e-5, x, g, None, g, m, r, None) == INVALID            # y on gamma
+    assert f(4, 16, 1e-5, x, g, None, y, y, r, None) == INVALID            # stash on y
+    assert f(4, 16, 1e-5, x, g, None, y, m, m, None) == INVALID            # mean == rstd
+    assert f(4, 16400, 1e-5, x, g, None, y, m, r, None) == UNSUPPORTED     # more than 16384 columns
+
+
+def test_layernorm_fused_rejects_bad_arguments():
+    f = B.lib().tp_sp_reduce_scatter_layernorm_local
+    p0, p1 = FAKE, FAKE + MB
+    z, g, y, m, r = FAKE + 2 * MB, FAKE + 3 * MB, FAKE + 4 * MB, FAKE + 5 * MB, FAKE + 6 * MB
+    ptrs = (ctypes.c_void_p * 2)(p0, p1)
+
+    def call(**o):
+        a = dict(t=2, ptrs=ptrs, rows=4, cols=16, rank=0, bias=None, res=None, z=z, eps=1e-5, g=g, beta=None,
+                 y=y, m=m, r=r)
+        a.update(o)
+        return f(a["t"], a["ptrs"], a["rows"], a["cols"], a["rank"], a["bias"], a["res"], a["z"], a["eps"],
+                 a["g"], a["beta"], a["y"], a["m"], a["r"], None)
+
+    assert call(rows=5) == INVALID                    # rows % t
+    assert call(rank=2) == INVALID
+    assert call(eps=0.0) == INVALID
+    assert call(g=None) == INVALID
+    assert call(y=p0) == INVALID                      # y on a partial
+    assert call(y=z) == INVALID                       # y on z
+    assert call(res=FAKE + 7 * MB, y=FAKE + 7 * MB) == INVALID   # y on the residual
+    assert call(z=p1 + 16) == INVALID                 # z straddles rank 0's block of a partial
+    assert call(m=z) == INVALID                       # stash on z
+    assert call(cols=16400) == UNSUPPORTED
+    big = (ctypes.c_void_p * 65)(*([FAKE] * 65))
+    assert call(t=65, ptrs=big, rows=65) == UNSUPPORTED
+
+
+def test_layernorm_bwd_workspace_and_arguments():
+    ws = B.layernorm_bwd_workspace_bytes
+    # one slab per row up to 256 rows, then 256 slabs; dgamma and dbeta partials
+    assert ws(1, 8) == 2 * 1 * 8 * 4
+    assert ws(256, 12288) == 2 * 256 * 12288 * 4
+    assert ws(4096, 8192) == 2 * 256 * 8192 * 4
+    assert ws(1000, 16) == 2 * 250 * 16 * 4         # 4 rows per slab
+    assert ws(0, 16) == 0 and ws(4, 12) == 0 and ws(4, 16392) == 0
+    f = B.lib().tp_sp_layernorm_bwd
+    x, g, m, r, dy, dx, dg, db, w = (FAKE + i * MB for i in range(9))
+    need = ws(4, 16)
+
+    def call(**o):
+        a = dict(rows=4, cols=16, x=x, g=g, m=m, r=r, dy=dy, dres=None, dx=dx, dg=dg, db=db, w=w, wb=need)
+        a.update(o)
+        return f(a["rows"], a["cols"], a["x"], a["g"], a["m"], a["r"], a["dy"], a["dres"], a["dx"], a["dg"],
+                 a["db"], a["w"], a["wb"], None)
+
+    assert call(w=None) == WORKSPACE
+    assert call(wb=need - 1) == WORKSPACE
+    assert call(w=w + 8) == WORKSPACE                 # misaligned workspace
+    assert call(m=None) == INVALID                    # the stash is required
+    assert call(dg=None) == INVALID
+    assert call(dx=x) == INVALID                      # dx on the forward input
+    assert call(dx=dy + 16) == INVALID                # dx straddles dy
+    assert call(dres=dx + 16) == INVALID              # dx straddles dres
+    assert call(db=dg) == INVALID                     # dbeta on dgamma
+    assert call(w=dx) == INVALID                      # workspace on dx
+    assert call(cols=12) == INVALID
+    assert call(rows=0) == INVALID
+    assert call(cols=16400, wb=1 << 30) == UNSUPPORTED
+
+
+def test_sum_grads_rejects_bad_arguments():
+    f = B.lib().tp_sp_sum_grads_local
+    g0, g1, out = FAKE, FAKE + MB, FAKE + 2 * MB
+    ptrs = (ctypes.c_void_p * 2)(g0, g1)
+    assert f(2, ptrs, 6, out, None) == INVALID        # n % 4
+    assert f(2, ptrs, 0, out, None) == INVALID
+    assert f(0, ptrs, 8, out, None) == INVALID
+    assert f(2, None, 8, out, None) == INVALID
+    assert f(2, ptrs, 8, None, None) == INVALID
+    assert f(2, ptrs, 8, g1, None) == INVALID         # out on a later rank's gradient
+    assert f(2, ptrs, 8, g0 + 16, None) == INVALID    # out straddles rank 0's
+    bad = (ctypes.c_void_p * 2)(g0, g1 + 4)
+    assert f(2, bad, 8, out, None) == INVALID
+    big = (ctypes.c_void_p * 65)(*([FAKE] * 65))
+    assert f(65, big, 8, out, None) == UNSUPPORTED
+

@@ -1,0 +1,381 @@
+"""GPU parity of the sequence-parallel LayerNorm against the fp64 oracle
+(oracle/ln.py), through the C ABI.
+
+Checked:
+
+* tp_sp_layernorm_fwd / tp_sp_layernorm_bwd on one rank's block at widths
+  on both sides of every per-thread chunk count (8 ... 16384 columns, ragged
+  tails), 1 to 300 rows, with and without the bias, the stash, dbeta and the
+  residual branch's gradient; constant rows (zero variance) and rows with a
+  large mean;
+* the fused reduce-scatter + LayerNorm: z and y against the oracle, and bit
+  for bit equal to the separate reduce-scatter followed by the LayerNorm;
+* tp_sp_sum_grads_local: bit for bit the float32 rank-order sum;
+* the whole TP+SP block of "Tensor and sequence parallelism" (LayerNorm on
+  each rank's rows written into the all-gather destination, every rank's
+  MLP shard, reduce-scatter; and its backward, with the LayerNorm weight's
+  gradient summed over the ranks) against the oracle's composition;
+* the GPT-3-scale (2048 tokens, h = 12288, t = 8) and 70B-prefill-scale
+  (16384 tokens, h = 8192, t = 4) per-rank blocks at full size: sampled rows
+  for the row-local outputs, every column of dgamma and dbeta;
+* determinism: two calls, the second on a dirtied workspace, bitwise equal.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import ln
+from megatron_tensor_transformer_rank_amd import binding as B
+from megatron_tensor_transformer_rank_amd import inputs as I
+from tests.helpers import assert_close, bf16_dev, f64
+
+pytestmark = pytest.mark.gpu
+f = oracle.bf16_bits_to_f64
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+
+
+def run_ln(wid, rows, cols, with_beta=True, stash=True, with_dres=False, with_dbeta=True, shift=0.0):
+    say(f"[ln] wid={wid} rows={rows} cols={cols} beta={with_beta} dres={with_dres} shift={shift}")
+    if shift:
+        rng = np.random.default_rng([wid, 99])
+        xb = I.f32_to_bf16_bits(rng.standard_normal((rows, cols), dtype=np.float32) + np.float32(shift))
+    else:
+        xb = I.gen_x(wid, rows, cols)
+    gb, bb = I.gen_ln_weight(wid, cols), I.gen_ln_bias(wid, cols)
+    dyb = I.gen_dy(wid, rows, cols)
+    drb = I.normal_bf16([wid, 20], (rows, cols))
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    x, g, b, dy = bf16_dev(xb), bf16_dev(gb), bf16_dev(bb) if with_beta else None, bf16_dev(dyb)
+    y = torch.empty(rows, cols, **bf)
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    B.tp_sp_layernorm_fwd(x, g, y, beta=b, mean=mean if stash else None, rstd=rstd if stash else None)
+    yref, mref, rref = ln.layer_norm_forward(f(xb), f(gb), f(bb) if with_beta else None)
+    torch.cuda.synchronize()
+    assert_close("y", f64(y), yref)
+    if not stash:
+        return
+    np.testing.assert_allclose(f64(mean), mref, rtol=1e-5, atol=1e-5 * (1 + abs(shift)))
+    np.testing.assert_allclose(f64(rstd), rref, rtol=2e-5)
+    dx = torch.empty(rows, cols, **bf)
+    dg = torch.empty(cols, dtype=torch.float32, device="cuda")
+    db = torch.empty(cols, dtype=torch.float32, device="cuda") if with_dbeta else None
+    ws = B.alloc_workspace(B.layernorm_bwd_workspace_bytes(rows, cols))
+    B.tp_sp_layernorm_bwd(x, g, mean, rstd, dy, dx, dg, dbeta=db, dres=bf16_dev(drb) if with_dres else None,
+                          workspace=ws)
+    dxr, dgr, dbr = ln.layer_norm_backward(f(dyb), f(xb), f(gb), dres=f(drb) if with_dres else None)
+    torch.cuda.synchronize()
+    assert_close("dx", f64(dx), dxr)
+    assert_close("dgamma", f64(dg), dgr)
+    if with_dbeta:
+        assert_close("dbeta", f64(db), dbr, rel_fro=1e-5, max_rel=1e-5)
+
+
+# (wid, rows, cols): column counts on both sides of the 256-thread chunk
+# boundaries (2048, 4096, 6144, 8192, 12288 columns) and ragged tails
+SHAPES = [(901, 1, 8), (902, 3, 24), (903, 17, 264), (904, 64, 1032), (905, 5, 2048), (906, 7, 2056),
+          (907, 33, 4104), (908, 9, 6152), (909, 300, 1024), (910, 6, 8200), (911, 4, 12288), (912, 3, 16384),
+          (913, 260, 520)]
+
+
+@pytest.mark.parametrize("case", SHAPES, ids=[f"r{c[1]}_c{c[2]}" for c in SHAPES])
+def test_layernorm_matches_oracle(case):
+    run_ln(*case)
+
+
+@pytest.mark.parametrize("with_beta,stash,with_dres,with_dbeta", [(False, True, True, False), (True, False, False, True),
+                                                                  (False, True, False, True)])
+def test_layernorm_options(with_beta, stash, with_dres, with_dbeta):
+    run_ln(920, 37, 3080, with_beta=with_beta, stash=stash, with_dres=with_dres, with_dbeta=with_dbeta)
+
+
+def test_layernorm_large_mean_rows():
+    run_ln(921, 20, 1536, shift=40.0)
+
+
+def test_layernorm_constant_rows():
+    """Zero variance: rstd = 1/sqrt(eps), y = beta exactly; the backward is
+    rstd * (g - mean(g)) with xhat = 0."""
+    rows, cols = 4, 64
+    xb = np.repeat(I.f32_to_bf16_bits(np.array([3.0, -1.5, 0.0, 7.25], dtype=np.float32))[:, None], cols, axis=1)
+    gb, bb, dyb = I.gen_ln_weight(930, cols), I.gen_ln_bias(930, cols), I.gen_dy(930, rows, cols)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    x, g, b = bf16_dev(xb), bf16_dev(gb), bf16_dev(bb)
+    y = torch.empty(rows, cols, **bf)
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    B.tp_sp_layernorm_fwd(x, g, y, beta=b, mean=mean, rstd=rstd)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), np.tile(bb, (rows, 1)))
+    np.testing.assert_allclose(f64(rstd), 1.0 / np.sqrt(1e-5), rtol=1e-6)
+    dx = torch.empty(rows, cols, **bf)
+    dg = torch.empty(cols, dtype=torch.float32, device="cuda")
+    B.tp_sp_layernorm_bwd(x, g, mean, rstd, bf16_dev(dyb), dx, dg,
+                          workspace=B.alloc_workspace(B.layernorm_bwd_workspace_bytes(rows, cols)))
+    dxr, dgr, _ = ln.layer_norm_backward(f(dyb), f(xb), f(gb))
+    torch.cuda.synchronize()
+    assert_close("dx", f64(dx), dxr)
+    assert np.all(f64(dg) == 0.0)
+
+
+# (wid, t, rows, cols, bias, residual)
+FUSED = [(940, 2, 8, 264, True, True), (941, 4, 12, 2056, False, True), (942, 8, 64, 1024, True, False),
+         (943, 3, 9, 6152, True, True), (944, 1, 5, 16384, False, False)]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[f"t{c[1]}_r{c[2]}_c{c[3]}" for c in FUSED])
+def test_fused_reduce_scatter_layernorm(case):
+    wid, t, rows, cols, with_bias, with_res = case
+    n = rows // t
+    say(f"[fused rs+ln] wid={wid} t={t} rows={rows} cols={cols}")
+    pb = [I.normal_bf16([wid, 1, k], (rows, cols)) for k in range(t)]
+    biasb = I.gen_b2(wid, cols) if with_bias else None
+    gb, betab = I.gen_ln_weight(wid, cols), I.gen_ln_bias(wid, cols)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    parts = [bf16_dev(p) for p in pb]
+    bias = bf16_dev(biasb) if with_bias else None
+    g, beta = bf16_dev(gb), bf16_dev(betab)
+    for rank in range(t):
+        resb = I.normal_bf16([wid, 2, rank], (n, cols)) if with_res else None
+        res = bf16_dev(resb) if with_res else None
+        z, y = torch.empty(n, cols, **bf), torch.empty(n, cols, **bf)
+        mean = torch.empty(n, dtype=torch.float32, device="cuda")
+        rstd = torch.empty(n, dtype=torch.float32, device="cuda")
+        B.tp_sp_reduce_scatter_layernorm_local(parts, rank, z, g, y, bias=bias, residual=res, beta=beta, mean=mean,
+                                               rstd=rstd)
+        # the two separate calls
+        z2, y2 = torch.empty(n, cols, **bf), torch.empty(n, cols, **bf)
+        mean2 = torch.empty(n, dtype=torch.float32, device="cuda")
+        rstd2 = torch.empty(n, dtype=torch.float32, device="cuda")
+        B.tp_mlp_reduce_scatter_local(parts, z2, rank, bias=bias, residual=res)
+        B.tp_sp_layernorm_fwd(z2, g, y2, beta=beta, mean=mean2, rstd=rstd2)
+        torch.cuda.synchronize()
+        zref = oracle.reduce_scatter([f(p) for p in pb], rank, f(biasb) if with_bias else None,
+                                     f(resb) if with_res else None)
+        yref, _, _ = ln.layer_norm_forward(zref, f(gb), f(betab))
+        assert_close(f"z[{rank}]", f64(z), zref)
+        assert_close(f"y[{rank}]", f64(y), yref)
+        assert torch.equal(z.view(torch.int16), z2.view(torch.int16))
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+        assert torch.equal(mean, mean2) and torch.equal(rstd, rstd2)
+
+
+def test_fused_in_place_on_the_residual():
+    """z may be the residual buffer itself (the residual stream updated in
+    place)."""
+    t, rows, cols, rank = 2, 6, 520, 1
+    n = rows // t
+    pb = [I.normal_bf16([950, 1, k], (rows, cols)) for k in range(t)]
+    resb = I.normal_bf16([950, 2], (n, cols))
+    gb = I.gen_ln_weight(950, cols)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    res = bf16_dev(resb)
+    y = torch.empty(n, cols, **bf)
+    B.tp_sp_reduce_scatter_layernorm_local([bf16_dev(p) for p in pb], rank, res, bf16_dev(gb), y, residual=res)
+    torch.cuda.synchronize()
+    zref = oracle.reduce_scatter([f(p) for p in pb], rank, None, f(resb))
+    assert_close("z", f64(res), zref)
+    assert_close("y", f64(y), ln.layer_norm_forward(zref, f(gb))[0])
+
+
+@pytest.mark.parametrize("t,n", [(1, 8), (2, 12288), (4, 8192), (8, 1000)])
+def test_sum_grads_is_the_rank_order_float32_sum(t, n):
+    rng = np.random.default_rng(t * 100 + n)
+    gs = [rng.standard_normal(n).astype(np.float32) * (10.0 ** k) for k in range(t)]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    B.tp_sp_sum_grads_local([dev_f32(a) for a in gs], out)
+    torch.cuda.synchronize()
+    want = gs[0].copy()
+    for a in gs[1:]:
+        want = want + a        # float32, rank order
+    assert np.array_equal(out.cpu().numpy(), want)
+    np.testing.assert_allclose(f64(out), ln.sum_shared_grads(gs), rtol=1e-6, atol=1e-6 * 10.0 ** (t - 1))
+
+
+def test_sum_grads_in_place_on_rank_zero():
+    gs = [dev_f32(np.full(16, float(k + 1))) for k in range(3)]
+    B.tp_sp_sum_grads_local(gs, gs[0])
+    torch.cuda.synchronize()
+    assert np.all(gs[0].cpu().numpy() == 6.0)
+
+
+# (wid, act, N, h, F, t, extras)
+BLOCKS = [(960, "gelu", 64, 264, 4 * 264, 4, False), (961, "swiglu", 48, 520, 2 * 776, 2, True),
+          (962, "relu", 128, 1032, 8 * 264, 8, True)]
+
+
+@pytest.mark.parametrize("case", BLOCKS, ids=[f"{c[1]}_N{c[2]}_h{c[3]}_t{c[5]}" for c in BLOCKS])
+def test_sp_block_matches_oracle(case):
+    """The pages' TP+SP block: LayerNorm on each rank's rows (written straight
+    into its block of the all-gather destination), every rank's MLP shard,
+    reduce-scatter (+ bias, + residual); backward: all-gather of the output
+    gradient blocks, every shard's backward, reduce-scatter of the partial
+    input gradients, the LayerNorm backward and the sum of the LayerNorm
+    weight's gradient over the ranks.  The oracle gathers the LayerNorm
+    outputs rounded to bf16, as this path does, so that ReLU's derivative
+    (U > 0) is decided on the same activations."""
+    wid, act, N, h, F, t, extras = case
+    say(f"[sp block] wid={wid} act={act} N={N} h={h} F={F} t={t}")
+    sw = act == "swiglu"
+    Fi, n = F // t, N // t
+    xb, gb = I.gen_x(wid, N, h), I.gen_ln_weight(wid, h)
+    betab = I.gen_ln_bias(wid, h) if extras else None
+    W1b, W2b, Wgb = I.gen_full_weights(wid, h, F, t, sw)
+    b2b = I.gen_b2(wid, h) if extras else None
+    resb = I.normal_bf16([wid, 30], (N, h)) if extras else None
+    doutb = I.gen_dy(wid, N, h)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    x, g = bf16_dev(xb), bf16_dev(gb)
+    beta = bf16_dev(betab) if extras else None
+    blocks = [oracle.sequence_block(r, t, N) for r in range(t)]
+
+    # forward
+    X = torch.empty(N, h, **bf)
+    means = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(t)]
+    rstds = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(t)]
+    for r in range(t):
+        B.tp_sp_layernorm_fwd(x[blocks[r]], g, X[blocks[r]], beta=beta, mean=means[r], rstd=rstds[r])
+    shards = []
+    for r in range(t):
+        c = oracle.column_block(r, t, F)
+        s = B.make_shape(N, h, F, t, r, act)
+        W1, W2 = bf16_dev(np.ascontiguousarray(W1b[:, c])), bf16_dev(np.ascontiguousarray(W2b[c, :]))
+        Wg = bf16_dev(np.ascontiguousarray(Wgb[:, c])) if sw else None
+        Y, A = torch.empty(N, h, **bf), torch.empty(N, Fi, **bf)
+        U = torch.empty(N, Fi, **bf)
+        G = torch.empty(N, Fi, **bf) if sw else None
+        B.tp_mlp_fwd_shard(s, X, W1, Wg, W2, Y, A, U, G, B.alloc_workspace(B.workspace_bytes(s, False)))
+        shards.append(dict(s=s, W1=W1, W2=W2, Wg=Wg, Y=Y, A=A, U=U, G=G))
+    outs = []
+    for r in range(t):
+        o = torch.empty(n, h, **bf)
+        B.tp_mlp_reduce_scatter_local([sh["Y"] for sh in shards], o, r, bias=bf16_dev(b2b) if extras else None,
+                                      residual=bf16_dev(np.ascontiguousarray(resb[blocks[r]])) if extras else None)
+        outs.append(o)
+    # backward
+    dY = torch.empty(N, h, **bf)
+    B.tp_mlp_all_gather_local([bf16_dev(np.ascontiguousarray(doutb[b])) for b in blocks], dY)
+    for sh in shards:
+        s = sh["s"]
+        sh["dU"] = torch.empty(N, s.g * Fi, **bf)
+        sh["dW1"] = torch.empty(h, Fi, dtype=torch.float32, device="cuda")
+        sh["dWg"] = torch.empty(h, Fi, dtype=torch.float32, device="cuda") if sw else None
+        sh["dW2"] = torch.empty(Fi, h, dtype=torch.float32, device="cuda")
+        sh["dX"] = torch.empty(N, h, **bf)
+        B.tp_mlp_bwd_shard(s, X, sh["W1"], sh["Wg"], sh["W2"], dY, sh["A"], sh["U"], sh["G"], sh["dU"], sh["dW1"],
+                           sh["dWg"], sh["dW2"], sh["dX"], None, B.alloc_workspace(B.workspace_bytes(s, True)))
+    dxs, dgs, dbs = [], [], []
+    for r in range(t):
+        dln = torch.empty(n, h, **bf)
+        B.tp_mlp_reduce_scatter_local([sh["dX"] for sh in shards], dln, r)
+        dx = torch.empty(n, h, **bf)
+        dg = torch.empty(h, dtype=torch.float32, device="cuda")
+        db = torch.empty(h, dtype=torch.float32, device="cuda")
+        B.tp_sp_layernorm_bwd(x[blocks[r]], g, means[r], rstds[r], dln, dx, dg, dbeta=db,
+                              workspace=B.alloc_workspace(B.layernorm_bwd_workspace_bytes(n, h)))
+        dxs.append(dx)
+        dgs.append(dg)
+        dbs.append(db)
+    dgamma = torch.empty(h, dtype=torch.float32, device="cuda")
+    dbeta = torch.empty(h, dtype=torch.float32, device="cuda")
+    B.tp_sp_sum_grads_local(dgs, dgamma)
+    B.tp_sp_sum_grads_local(dbs, dbeta)
+    torch.cuda.synchronize()
+
+    Wg64 = f(Wgb) if sw else None
+    ref_outs, ref_ln = ln.sp_block_forward(act, f(xb), f(gb), f(W1b), f(W2b), t, Wg=Wg64,
+                                           beta=f(betab) if extras else None, b2=f(b2b) if extras else None,
+                                           residual=f(resb) if extras else None, payload_bf16=True)
+    bw = ln.sp_block_backward(act, f(xb), f(gb), f(W1b), f(W2b), [f(doutb[b]) for b in blocks], t, Wg=Wg64,
+                              beta=f(betab) if extras else None, payload_bf16=True)
+    assert_close("X (gathered LayerNorm)", f64(X), np.vstack(ref_ln))
+    for r in range(t):
+        assert_close(f"out[{r}]", f64(outs[r]), ref_outs[r])
+        assert_close(f"dx[{r}]", f64(dxs[r]), bw["dx"][r])
+        assert_close(f"dW1[{r}]", f64(shards[r]["dW1"]), bw["shard"][r]["dW1"])
+        assert_close(f"dW2[{r}]", f64(shards[r]["dW2"]), bw["shard"][r]["dW2"])
+        if sw:
+            assert_close(f"dWg[{r}]", f64(shards[r]["dWg"]), bw["shard"][r]["dWg"])
+    assert_close("dgamma", f64(dgamma), bw["dgamma"])
+    assert_close("dbeta", f64(dbeta), bw["dbeta"])
+
+
+@pytest.mark.parametrize("name,N,h,t", [("gpt3_sp_t8", 2048, 12288, 8), ("llama3_70b_prefill_sp_t4", 16384, 8192, 4)])
+def test_layernorm_full_size(name, N, h, t):
+    """One rank's block at the full per-rank size: the fused reduce-scatter +
+    LayerNorm of rank t-1 and the backward of its rows; 48 sampled rows for
+    z, y and dx, every column of dgamma and dbeta (from all rows)."""
+    n, rank = N // t, t - 1
+    wid = 970 + t
+    say(f"[ln full size] {name}: t={t} rows={n} cols={h}")
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    # partials generated on the host per rank block: only rank's rows are needed
+    # by the oracle, but the kernel reads them from the full partials
+    pb = [I.normal_bf16([wid, 1, k], (N, h)) for k in range(t)]
+    resb = I.normal_bf16([wid, 2], (n, h))
+    gb, betab, biasb = I.gen_ln_weight(wid, h), I.gen_ln_bias(wid, h), I.gen_b2(wid, h)
+    dyb = I.gen_dy(wid, n, h)
+    parts = [bf16_dev(p) for p in pb]
+    z, y = torch.empty(n, h, **bf), torch.empty(n, h, **bf)
+    mean = torch.empty(n, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(n, dtype=torch.float32, device="cuda")
+    g = bf16_dev(gb)
+    B.tp_sp_reduce_scatter_layernorm_local(parts, rank, z, g, y, bias=bf16_dev(biasb), residual=bf16_dev(resb),
+                                           beta=bf16_dev(betab), mean=mean, rstd=rstd)
+    dx = torch.empty(n, h, **bf)
+    dg = torch.empty(h, dtype=torch.float32, device="cuda")
+    db = torch.empty(h, dtype=torch.float32, device="cuda")
+    B.tp_sp_layernorm_bwd(z, g, mean, rstd, bf16_dev(dyb), dx, dg, dbeta=db,
+                          workspace=B.alloc_workspace(B.layernorm_bwd_workspace_bytes(n, h)))
+    torch.cuda.synchronize()
+    blk = oracle.sequence_block(rank, t, N)
+    # the reduce-scatter's arithmetic on the rank's block: the partials' rows
+    # added in rank order, the bias once, then the residual
+    zref = oracle.reduce_partials([f(p[blk]) for p in pb], f(biasb)) + f(resb)
+    del pb, parts
+    rows = np.sort(np.random.default_rng(len(name)).choice(n, size=48, replace=False))
+    assert_close("z", f64(z)[rows], zref[rows])
+    yref, _, _ = ln.layer_norm_forward(zref[rows], f(gb), f(betab))
+    assert_close("y", f64(y)[rows], yref)
+    # the backward reads the stored bf16 z: the oracle's input is the same
+    # generator's z (not the GPU's), so compare against the oracle on zref
+    dxr, dgr, dbr = ln.layer_norm_backward(f(dyb), zref, f(gb))
+    assert_close("dx", f64(dx)[rows], dxr[rows])
+    assert_close("dgamma", f64(dg), dgr)
+    assert_close("dbeta", f64(db), dbr, rel_fro=1e-5, max_rel=1e-5)
+
+
+def test_layernorm_deterministic_and_workspace_contents_irrelevant():
+    rows, cols = 300, 2056
+    xb, dyb = I.gen_x(980, rows, cols), I.gen_dy(980, rows, cols)
+    gb = I.gen_ln_weight(980, cols)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    x, dy, g = bf16_dev(xb), bf16_dev(dyb), bf16_dev(gb)
+    ws = B.alloc_workspace(B.layernorm_bwd_workspace_bytes(rows, cols))
+    outs = []
+    for fill in (0, 0x7f):
+        ws.fill_(fill)
+        y = torch.empty(rows, cols, **bf)
+        mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+        rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+        B.tp_sp_layernorm_fwd(x, g, y, mean=mean, rstd=rstd)
+        dx = torch.empty(rows, cols, **bf)
+        dg = torch.empty(cols, dtype=torch.float32, device="cuda")
+        db = torch.empty(cols, dtype=torch.float32, device="cuda")
+        B.tp_sp_layernorm_bwd(x, g, mean, rstd, dy, dx, dg, dbeta=db, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([a.clone() for a in (y, mean, rstd, dx, dg, db)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -213,3 +213,44 @@ def test_residual_gradient_adds_to_dx():
     b = ln.sp_block_backward("gelu", x, gamma, W1, W2, douts, t, dres=dres)
     for r in range(t):
         np.testing.assert_allclose(b["dx"][r] - a["dx"][r], dres[r], rtol=1e-12, atol=1e-12)
+
+
+def test_round_bf16_matches_torch_and_ties_to_even():
+    """Against torch's float32 -> bfloat16 conversion (round to nearest even)
+    on float32 values (exact in float64, so no double rounding), and on
+    hand-made ties."""
+    rng = np.random.default_rng(60)
+    v = np.concatenate([rng.standard_normal(20000), rng.standard_normal(2000) * 1e-30,
+                        rng.standard_normal(2000) * 1e30]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ln.round_bf16(v.astype(np.float64)), want)
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties go to the even 1;
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: goes to 1 + 2^-6;
+    # 1028 = 2^10 (1 + 2^-8) lies halfway between 1024 and 1032: goes to 1024
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1028.0, 0.0])
+    np.testing.assert_array_equal(ln.round_bf16(ties), [1.0, 1 + 2.0 ** -6, -1.0, 1024.0, 0.0])
+    # a value just above a tie rounds up
+    assert ln.round_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -30]))[0] == 1 + 2.0 ** -7
+
+
+def test_sp_block_bf16_payload_is_the_rounded_gather():
+    """With payload_bf16 the MLP sees the bf16-rounded LayerNorm outputs: the
+    block output equals the plain MLP of the rounded gathered rows."""
+    rng = np.random.default_rng(70)
+    t, N, h, F = 2, 6, 16, 32
+    x, gamma = rng.standard_normal((N, h)), rng.standard_normal(h)
+    W1, W2 = rng.standard_normal((h, F)) / 4, rng.standard_normal((F, h)) / 6
+    outs, lnb = ln.sp_block_forward("relu", x, gamma, W1, W2, t, payload_bf16=True)
+    Xr = ln.round_bf16(np.vstack(lnb))
+    assert not np.array_equal(Xr, np.vstack(lnb))
+    full = np.maximum(Xr @ W1, 0.0) @ W2
+    np.testing.assert_allclose(np.vstack(outs), full, rtol=1e-12, atol=1e-12)
+    douts = [rng.standard_normal((N // t, h)) for _ in range(t)]
+    bw = ln.sp_block_backward("relu", x, gamma, W1, W2, douts, t, payload_bf16=True)
+    dA = np.vstack(douts) @ W2.T
+    dXfull = (dA * (Xr @ W1 > 0)) @ W1.T
+    for r in range(t):
+        blk = oracle.sequence_block(r, t, N)
+        np.testing.assert_allclose(bw["dx"][r], ln.layer_norm_backward(dXfull[blk], x[blk], gamma)[0],
+                                   rtol=1e-10, atol=1e-12)
+
