@@ -192,7 +192,7 @@ def main():
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm.h", "tiles.h", "common.h")
-GEMV_SOURCES = ("gemv.hip", "gemv.h", "common.h", "api.hip")
+GEMV_SOURCES = ("gemv.hip", "gemv.h", "common.h")
 
 
 def source_hash(files):

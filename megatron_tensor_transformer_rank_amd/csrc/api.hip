@@ -107,12 +107,6 @@ SkinnyLayout skinny_layout(const Dims& d) {
   return L;
 }
 
-// Blocks per GEMV, measured best for the one-token stream on 256 CUs: the
-// up-projection ~224 (fewer k-splits leave fewer partials for the
-// down-projection's prologue to add), the down-projection ~256 (one per CU).
-constexpr int DECODE_UP_BLOCKS = 224;
-constexpr int DECODE_DOWN_BLOCKS = 256;
-
 DecodeLayout decode_layout(const Dims& d) {
   DecodeLayout L;
   L.up = gemv_plan((int)d.h, (int)d.Fi, d.g, DECODE_UP_BLOCKS);

@@ -9,6 +9,12 @@ namespace tpmlp {
 
 constexpr int GV_MAX_KR = 2048;  // rows of one k-split (LDS copy of x)
 
+// Blocks per GEMV, measured best for the one-token stream on 256 CUs: the
+// up-projection ~224 (fewer k-splits leave fewer partials for the
+// down-projection's prologue to add), the down-projection ~256 (one per CU).
+constexpr int DECODE_UP_BLOCKS = 224;
+constexpr int DECODE_DOWN_BLOCKS = 256;
+
 struct GemvPlan {
   int strips, ks, kr;
   size_t part_floats;
