@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-attn", action="store_true")
+    p.add_argument("--no-ln", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=256)
     return p.parse_args()
@@ -183,6 +184,10 @@ def main():
     # ---- attention block projections of the same model scale
     if not args.no_attn:
         result["attention_projections"] = bench_attn(args, B, I, torch, np, to_dev)
+    if not args.no_ln:
+        result["sp_layernorm"] = {name: bench_ln(B, I, torch, to_dev, name, N, h, t)
+                                  for name, N, h, t in (("gpt3_sp_t8", 2048, 12288, 8),
+                                                        ("llama3_70b_prefill_sp_t4", 16384, 8192, 4))}
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
@@ -351,6 +356,56 @@ def bench_attn(args, B, I, torch, np, to_dev, N=2048, h=12288, heads=96, kv=96, 
     return {"workload": f"gpt3_attn_t{t}: N={N} h={h} heads={heads} head_dim={d} t={t} (qkv {wc}, o {qc} cols/rank)",
             "ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "flops_per_step": flops, "step": "QKV fwd, O fwd, O bwd (dO, dW_o), QKV bwd (dX, dW_qkv)"}
+
+
+def bench_ln(B, I, torch, to_dev, name, N, h, t):
+    """One rank's sequence-parallel LayerNorm: the fused reduce-scatter +
+    bias + residual + LayerNorm forward over its N/t rows (reading its block
+    of all t partial sums), and the LayerNorm backward with the residual
+    branch's gradient, dgamma and dbeta.  GB/s on algorithmic bytes (every
+    operand read once, every output written once)."""
+    bf, f32 = torch.bfloat16, torch.float32
+    n = N // t
+    parts = [to_dev(I.normal_bf16([990, 1, k], (N, h))) for k in range(t)]
+    res, dy, dres = (to_dev(I.normal_bf16([990, j], (n, h))) for j in (2, 3, 4))
+    bias, g, beta = to_dev(I.gen_b2(990, h)), to_dev(I.gen_ln_weight(990, h)), to_dev(I.gen_ln_bias(990, h))
+    z, y, dx = (torch.empty(n, h, dtype=bf, device="cuda") for _ in range(3))
+    mean, rstd = torch.empty(n, dtype=f32, device="cuda"), torch.empty(n, dtype=f32, device="cuda")
+    dg, db = torch.empty(h, dtype=f32, device="cuda"), torch.empty(h, dtype=f32, device="cuda")
+    ws = B.alloc_workspace(B.layernorm_bwd_workspace_bytes(n, h))
+
+    def fwd():
+        B.tp_sp_reduce_scatter_layernorm_local(parts, t - 1, z, g, y, bias=bias, residual=res, beta=beta, mean=mean,
+                                               rstd=rstd)
+
+    def bwd():
+        B.tp_sp_layernorm_bwd(z, g, mean, rstd, dy, dx, dg, dbeta=db, dres=dres, workspace=ws)
+
+    stream = torch.cuda.current_stream()
+    out = {}
+    nbytes = {"fwd": (t + 4) * n * h * 2 + 3 * h * 2 + 8 * n,     # t partial blocks, residual in; z, y out
+              "bwd": 4 * n * h * 2 + h * 2 + 8 * n + 2 * h * 4}   # z, dy, dres in; dx out
+    for key, fn in (("fwd", fwd), ("bwd", bwd)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = nbytes[key] / (us * 1e-6) / 1e9
+        out[key] = {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                    "algorithmic_bytes": nbytes[key]}
+    log(f"[bench] sp layernorm {name}: fused rs+ln fwd {out['fwd']['us']:.1f} us ({out['fwd']['GB/s']:.0f} GB/s), "
+        f"bwd {out['bwd']['us']:.1f} us ({out['bwd']['GB/s']:.0f} GB/s)")
+    out["workload"] = f"{name}: {N} tokens, h={h}, t={t}: {n} rows per rank"
+    out["fwd"]["step"] = "reduce-scatter of t partials + bias + residual -> z, LayerNorm(z) -> y (one kernel)"
+    out["bwd"]["step"] = "LayerNorm backward + residual gradient -> dx; dgamma, dbeta (row kernel + slab sums)"
+    return out
 
 
 def cpu_baseline(w, rows, I, target_s=10.0, cap_s=30.0):

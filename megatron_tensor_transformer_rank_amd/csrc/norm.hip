@@ -18,8 +18,11 @@
 // stores it, and normalises that stored value: bit for bit what a separate
 // reduce-scatter followed by a LayerNorm of z computes.
 //
-// The backward's column sums (dgamma, dbeta) are per-block partial rows over
-// a slab of rows, then a second kernel adds the slabs in slab order.
+// The backward runs as a row kernel (dx, one row per block, like the
+// forward) and a column kernel: dgamma and dbeta over (512-column strip,
+// row slab) tiles, which re-reads x and dy but keeps every CU busy and its
+// partial rows few (at most 64 slabs); a last kernel adds the slabs in slab
+// order.
 #include "common.h"
 #include "norm.h"
 
@@ -96,6 +99,13 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
 
   if constexpr (FUSED) {
     const int64_t in_base = (row0 + row) * cols8;
+    // the residual is loaded with the first batch of partials
+    u32x4 rv[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = tid + j * LN_THREADS;
+      rv[j] = (residual && q < cols8) ? ld_nt(residual, base + q) : u32x4{0u, 0u, 0u, 0u};
+    }
     for (int r0 = 0; r0 < t; r0 += LN_BATCH) {
       u32x4 c[J][LN_BATCH];
 #pragma unroll
@@ -116,7 +126,7 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
       const int q = tid + j * LN_THREADS;
       if (q < cols8) {
         if (bias) add8(v[j], ld_c(bias, q));
-        if (residual) add8(v[j], ld_nt(residual, base + q));
+        if (residual) add8(v[j], rv[j]);
         const u32x4 o = pack8(v[j]);
         reinterpret_cast<u32x4*>(z)[base + q] = o;
         unpack8(o, v[j]);  // the LayerNorm reads z as stored
@@ -171,110 +181,134 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
   }
 }
 
-// Block b owns rows [b * rpb, min(rows, (b + 1) * rpb)), one after another.
-// Per row: xhat = (x - mean) * rstd, g = dy * gamma,
-// dx = rstd * (g - sum(g)/h - xhat * sum(g * xhat)/h) (+ dres); the block's
-// dgamma = sum dy * xhat and dbeta = sum dy go to its partial rows.
+// One row per block: xhat = (x - mean) * rstd, g = dy * gamma,
+// dx = rstd * (g - sum(g)/h - xhat * sum(g * xhat)/h) (+ dres).
 template <int J>
 __global__ void __launch_bounds__(LN_THREADS)
-ln_bwd_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
-              const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int64_t rows,
-              int cols8, int cols, int64_t rpb, float* __restrict__ part_g, float* __restrict__ part_b) {
-  __shared__ float red[2][2][LN_WAVES];  // [row parity][sum][wave]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * rpb;
-  const int64_t r1 = r0 + rpb < rows ? r0 + rpb : rows;
-  float ag[J][8], ab[J][8];
+ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
+                 const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int cols8,
+                 int cols) {
+  __shared__ float red[2][LN_WAVES];
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int64_t base = r * cols8;
+  const float mu = mean[r], rs = rstd[r];
+  // dres is loaded with x and dy: one round trip to memory per row
+  u32x4 xv[J], dv[J], rv[J];
 #pragma unroll
-  for (int j = 0; j < J; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ag[j][e] = ab[j][e] = 0.f;
-
-  for (int64_t r = r0; r < r1; ++r) {
-    const int par = (int)(r & 1);
-    const float mu = mean[r], rs = rstd[r];
-    const int64_t base = r * cols8;
-    u32x4 xv[J], dv[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int q = tid + j * LN_THREADS;
-      xv[j] = q < cols8 ? ld_nt(x, base + q) : u32x4{0u, 0u, 0u, 0u};
-      dv[j] = q < cols8 ? ld_nt(dy, base + q) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // xhat and g are recomputed from the packed row in the output loop
-    // (fewer registers than keeping them as floats)
-    float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int q = tid + j * LN_THREADS;
-      if (q < cols8) {
-        float xf[8], df[8], gm[8];
-        unpack8(xv[j], xf);
-        unpack8(dv[j], df);
-        unpack8(ld_c(gamma, q), gm);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xh = (xf[e] - mu) * rs, g = df[e] * gm[e];
-          s1 += g;
-          s2 += g * xh;
-          ag[j][e] += df[e] * xh;
-          ab[j][e] += df[e];
-        }
-      }
-    }
-    // both row sums with one barrier: the buffers alternate with the row's
-    // parity, and a buffer is written again only after the next row's
-    // barrier, which every thread passes after its reads of this one
-    s1 = wave_sum(s1);
-    s2 = wave_sum(s2);
-    if (lane == 0) {
-      red[par][0][w] = s1;
-      red[par][1][w] = s2;
-    }
-    __syncthreads();
-    float S1 = red[par][0][0], S2 = red[par][1][0];
-#pragma unroll
-    for (int q = 1; q < LN_WAVES; ++q) {
-      S1 += red[par][0][q];
-      S2 += red[par][1][q];
-    }
-    const float m1 = S1 / (float)cols, m2 = S2 / (float)cols;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int q = tid + j * LN_THREADS;
-      if (q < cols8) {
-        float xf[8], df[8], gm[8], o[8];
-        unpack8(xv[j], xf);
-        unpack8(dv[j], df);
-        unpack8(ld_c(gamma, q), gm);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = rs * (df[e] * gm[e] - m1 - (xf[e] - mu) * rs * m2);
-        if (dres) add8(o, ld_nt(dres, base + q));
-        reinterpret_cast<u32x4*>(dx)[base + q] = pack8(o);
-      }
-    }
+  for (int j = 0; j < J; ++j) {
+    const int q = tid + j * LN_THREADS;
+    xv[j] = q < cols8 ? ld_nt(x, base + q) : u32x4{0u, 0u, 0u, 0u};
+    dv[j] = q < cols8 ? ld_nt(dy, base + q) : u32x4{0u, 0u, 0u, 0u};
+    rv[j] = (dres && q < cols8) ? ld_nt(dres, base + q) : u32x4{0u, 0u, 0u, 0u};
   }
+  float s1 = 0.f, s2 = 0.f;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int q = tid + j * LN_THREADS;
     if (q < cols8) {
-      float4* pg = reinterpret_cast<float4*>(part_g + (int64_t)blockIdx.x * cols + (int64_t)q * 8);
-      pg[0] = make_float4(ag[j][0], ag[j][1], ag[j][2], ag[j][3]);
-      pg[1] = make_float4(ag[j][4], ag[j][5], ag[j][6], ag[j][7]);
-      if (part_b) {
-        float4* pb = reinterpret_cast<float4*>(part_b + (int64_t)blockIdx.x * cols + (int64_t)q * 8);
-        pb[0] = make_float4(ab[j][0], ab[j][1], ab[j][2], ab[j][3]);
-        pb[1] = make_float4(ab[j][4], ab[j][5], ab[j][6], ab[j][7]);
+      float xf[8], df[8], gm[8];
+      unpack8(xv[j], xf);
+      unpack8(dv[j], df);
+      unpack8(ld_c(gamma, q), gm);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float g = df[e] * gm[e];
+        s1 += g;
+        s2 += g * ((xf[e] - mu) * rs);
       }
+    }
+  }
+  const float m1 = block_sum(s1, red[0]) / (float)cols;
+  const float m2 = block_sum(s2, red[1]) / (float)cols;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int q = tid + j * LN_THREADS;
+    if (q < cols8) {
+      float xf[8], df[8], gm[8], o[8];
+      unpack8(xv[j], xf);
+      unpack8(dv[j], df);
+      unpack8(ld_c(gamma, q), gm);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = rs * (df[e] * gm[e] - m1 - (xf[e] - mu) * rs * m2);
+      if (dres) add8(o, rv[j]);
+      reinterpret_cast<u32x4*>(dx)[base + q] = pack8(o);
     }
   }
 }
 
-// out[c] = sum_{q<slabs} part[q][c].  A block owns 64 columns (16 float4
-// lanes); its 16 groups each add every 16th slab in increasing order, then the
-// group sums are added in group order.
+// dgamma / dbeta partial rows of one (column strip, row slab) tile: a lane
+// owns 8 adjacent columns (16-byte loads, a wave covers 512 columns), the 4
+// waves take interleaved rows of the slab, LN_DG_UNROLL rows of loads in
+// flight, and their sums meet in LDS in wave order.
+constexpr int LN_DG_STRIP = 512;
+constexpr int LN_DG_UNROLL = 4;
+
 __global__ void __launch_bounds__(LN_THREADS)
-slab_sum_kernel(const float* __restrict__ part, int slabs, int64_t cols, float* __restrict__ out) {
+ln_bwd_dgb_kernel(const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
+                  const uint16_t* __restrict__ dy, int64_t rows, int64_t cols, int64_t rpb,
+                  float* __restrict__ part_g, float* __restrict__ part_b) {
+  __shared__ float red[LN_WAVES][LN_DG_STRIP];
+  const int strips = (int)((cols + LN_DG_STRIP - 1) / LN_DG_STRIP);
+  const int strip = blockIdx.x % strips, slab = blockIdx.x / strips;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t r0 = (int64_t)slab * rpb;
+  const int64_t r1 = r0 + rpb < rows ? r0 + rpb : rows;
+  const int64_t c = (int64_t)strip * LN_DG_STRIP + lane * 8;
+  const bool cok = c < cols;
+  float ag[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, ab[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t rb = r0 + w; rb < r1; rb += LN_WAVES * LN_DG_UNROLL) {
+    u32x4 xv[LN_DG_UNROLL], dv[LN_DG_UNROLL];
+#pragma unroll
+    for (int u = 0; u < LN_DG_UNROLL; ++u) {
+      const int64_t r = rb + (int64_t)u * LN_WAVES;
+      const bool ok = cok && r < r1;
+      xv[u] = ok ? ld_nt(x + r * cols + c, 0) : u32x4{0u, 0u, 0u, 0u};
+      dv[u] = ok ? ld_nt(dy + r * cols + c, 0) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < LN_DG_UNROLL; ++u) {
+      const int64_t r = rb + (int64_t)u * LN_WAVES;
+      if (cok && r < r1) {
+        const float mu = mean[r], rs = rstd[r];
+        float xf[8], df[8];
+        unpack8(xv[u], xf);
+        unpack8(dv[u], df);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ag[e] += df[e] * ((xf[e] - mu) * rs);
+          ab[e] += df[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[w][lane * 8 + e] = ag[e];
+  __syncthreads();
+  for (int cc = tid; cc < LN_DG_STRIP; cc += LN_THREADS) {
+    const int64_t gc = (int64_t)strip * LN_DG_STRIP + cc;
+    if (gc < cols) part_g[(int64_t)slab * cols + gc] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
+  }
+  if (!part_b) return;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[w][lane * 8 + e] = ab[e];
+  __syncthreads();
+  for (int cc = tid; cc < LN_DG_STRIP; cc += LN_THREADS) {
+    const int64_t gc = (int64_t)strip * LN_DG_STRIP + cc;
+    if (gc < cols) part_b[(int64_t)slab * cols + gc] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
+  }
+}
+
+// out[c] = sum_{q<slabs} part[q][c], for one or two (part, out) pairs.  A
+// block owns 64 columns (16 float4 lanes); its 16 groups each add every 16th
+// slab in increasing order, then the group sums are added in group order.
+__global__ void __launch_bounds__(LN_THREADS)
+slab_sum_kernel(const float* __restrict__ part0, float* __restrict__ out0, const float* __restrict__ part1,
+                float* __restrict__ out1, int slabs, int64_t cols) {
+  // blockIdx.y: 0 for the first sum, 1 for the second
+  const float* part = blockIdx.y ? part1 : part0;
+  float* out = blockIdx.y ? out1 : out0;
   __shared__ float4 red[SS_GROUPS][16];
   const int c4 = threadIdx.x & 15, grp = threadIdx.x >> 4;
   const int64_t c = (int64_t)blockIdx.x * 64 + c4 * 4;
@@ -322,10 +356,14 @@ int ln_j(int64_t cols) {
   return 0;
 }
 
+// Row slabs of the dgamma / dbeta tiles: at least LN_MIN_SLAB_ROWS rows
+// each, at most LN_MAX_SLABS of them.
 void bwd_slabs(int64_t rows, int& slabs, int64_t& rpb) {
-  int64_t nb = rows < LN_MAX_SLABS ? rows : LN_MAX_SLABS;
+  int64_t nb = (rows + LN_MIN_SLAB_ROWS - 1) / LN_MIN_SLAB_ROWS;
+  if (nb > LN_MAX_SLABS) nb = LN_MAX_SLABS;
   if (nb < 1) nb = 1;
   rpb = (rows + nb - 1) / nb;
+  if (rpb < 1) rpb = 1;
   slabs = (int)((rows + rpb - 1) / rpb);
 }
 
@@ -379,16 +417,12 @@ size_t ln_bwd_workspace_bytes(int64_t rows, int64_t cols) {
 hipError_t ln_bwd_launch(const uint16_t* x, const uint16_t* gamma, const float* mean, const float* rstd,
                          const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int64_t rows, int64_t cols,
                          float* dgamma, float* dbeta, float* part, hipStream_t st) {
-  int slabs;
-  int64_t rpb;
-  bwd_slabs(rows, slabs, rpb);
-  float* part_g = part;
-  float* part_b = dbeta ? part + (int64_t)slabs * cols : nullptr;
+  if (rows == 0) return hipSuccess;
   const int cols8 = (int)(cols / 8);
-  const dim3 grid((unsigned)slabs), blk(LN_THREADS);
+  const dim3 blk(LN_THREADS);
 #define LN_BWD(J)                                                                                                \
-  hipLaunchKernelGGL((ln_bwd_kernel<J>), grid, blk, 0, st, x, gamma, mean, rstd, dy, dres, dx, rows, cols8,     \
-                     (int)cols, rpb, part_g, part_b)
+  hipLaunchKernelGGL((ln_bwd_dx_kernel<J>), dim3((unsigned)rows), blk, 0, st, x, gamma, mean, rstd, dy, dres,   \
+                     dx, cols8, (int)cols)
   switch (ln_j(cols)) {
     case 1: LN_BWD(1); break;
     case 2: LN_BWD(2); break;
@@ -401,11 +435,18 @@ hipError_t ln_bwd_launch(const uint16_t* x, const uint16_t* gamma, const float* 
 #undef LN_BWD
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 sgrid((unsigned)((cols + 63) / 64));
-  hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, slabs, cols, dgamma);
+  int slabs;
+  int64_t rpb;
+  bwd_slabs(rows, slabs, rpb);
+  float* part_g = part;
+  float* part_b = dbeta ? part + (int64_t)slabs * cols : nullptr;
+  const int64_t strips = (cols + LN_DG_STRIP - 1) / LN_DG_STRIP;
+  hipLaunchKernelGGL(ln_bwd_dgb_kernel, dim3((unsigned)(strips * slabs)), blk, 0, st, x, mean, rstd, dy, rows, cols,
+                     rpb, part_g, part_b);
   e = hipGetLastError();
-  if (e != hipSuccess || !dbeta) return e;
-  hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_b, slabs, cols, dbeta);
+  if (e != hipSuccess) return e;
+  const dim3 sgrid((unsigned)((cols + 63) / 64), dbeta ? 2u : 1u);
+  hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, dgamma, part_b, dbeta, slabs, cols);
   return hipGetLastError();
 }
 
