@@ -49,36 +49,24 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-attn", action="store_true")
     p.add_argument("--no-ln", action="store_true")
+    p.add_argument("--no-other", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=256)
     return p.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs one tensor-parallel rank's shard on a single "
-              f"MI355X (the t shards of a group are run one after another on it); --gpus {args.gpus} "
-              f"is not supported.", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    from megatron_tensor_transformer_rank_amd import binding as B
-    from megatron_tensor_transformer_rank_amd import inputs as I
-    from megatron_tensor_transformer_rank_amd.configs import WORKLOADS
-
-    B.lib()  # raises if libtpmlp.so is missing: there is no other path
-    w = WORKLOADS[args.workload]
+def train_step(w, steps, warmup, B, I, torch, np, to_dev):
+    """Time `steps` passes of rank 0's whole hot path for workload w: forward,
+    reduce of the t partial sums (+ bias), backward (+ bias gradient), reduce
+    of the t dX partials, launched through the one-kernel entry points (the
+    composite entry points launch exactly these kernels in this order).  A HIP
+    event on the launch stream after every kernel gives per-kernel durations
+    measured inside the timed region itself.  The buffers are freed on
+    return."""
     dev = "cuda"
     bf, f32 = torch.bfloat16, torch.float32
     sw = w.act == "swiglu"
     N, h, Fi, t = w.N, w.h, w.Fi, w.t
-
-    def to_dev(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(bf).to(dev)
-
     log(f"[bench] generating inputs for {w.name}: N={N} h={h} F_i={Fi} t={t} act={w.act}")
     X, dY = to_dev(I.gen_x(w.wid, N, h)), to_dev(I.gen_dy(w.wid, N, h))
     W1 = to_dev(I.gen_w_up_shard(w.wid, h, Fi, 0))
@@ -107,10 +95,6 @@ def main():
     others_dx = [dX.clone() for _ in range(t - 1)]
     torch.cuda.synchronize()
 
-    # one step = the whole hot path through the one-kernel entry points (the
-    # composite entry points launch exactly these kernels in this order); a HIP
-    # event on the launch stream after every kernel gives per-kernel durations
-    # measured inside the timed region itself
     ws_db = B.alloc_workspace(B.bias_grad_workspace_bytes(N, h)) if w.bias else None
     kernels = [
         ("up_act", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_act_shard(shape, X, W1, Wg, A, U, G)),
@@ -125,28 +109,55 @@ def main():
         kernels.append(("bias_grad", 0, lambda: B.tp_mlp_bias_grad(dY, db2, ws_db)))
     kernels.append(("reduce_dx", 0, lambda: B.tp_mlp_reduce_partials_local([dX] + others_dx, dXred)))
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         for _, _, fn in kernels:
             fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     nk = len(kernels)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * nk + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps * nk + 1)]
     t_wall = time.perf_counter()
     evs[0].record(stream)
-    for s in range(args.steps):
+    for s in range(steps):
         for j, (_, _, fn) in enumerate(kernels):
             fn()
             evs[s * nk + j + 1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / steps
     flops = w.flops_train()
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] {w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
-    kern_ms = {name: float(np.mean([evs[s * nk + j].elapsed_time(evs[s * nk + j + 1]) for s in range(args.steps)]))
+    log(f"[bench] {w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {t_wall * 1e3 / steps:.3f} ms/step)")
+    kern_ms = {name: float(np.mean([evs[s * nk + j].elapsed_time(evs[s * nk + j + 1]) for s in range(steps)]))
                for j, (name, _, _) in enumerate(kernels)}
-    gemms = [(n, fl) for n, fl, _ in kernels if fl > 0]
+    return {"ms": ms, "tflops": tflops, "kern_ms": kern_ms, "flops": flops,
+            "gemms": [(n, fl) for n, fl, _ in kernels if fl > 0]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs one tensor-parallel rank's shard on a single "
+              f"MI355X (the t shards of a group are run one after another on it); --gpus {args.gpus} "
+              f"is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from megatron_tensor_transformer_rank_amd import binding as B
+    from megatron_tensor_transformer_rank_amd import inputs as I
+    from megatron_tensor_transformer_rank_amd.configs import WORKLOADS
+
+    B.lib()  # raises if libtpmlp.so is missing: there is no other path
+    w = WORKLOADS[args.workload]
+    N, h, Fi, t = w.N, w.h, w.Fi, w.t
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    st = train_step(w, args.steps, args.warmup, B, I, torch, np, to_dev)
+    ms, tflops, kern_ms, gemms, flops = st["ms"], st["tflops"], st["kern_ms"], st["gemms"], st["flops"]
     dom, dom_fl = max(gemms, key=lambda x: kern_ms[x[0]])
     achieved = dom_fl / (kern_ms[dom] * 1e-3) / 1e12
     traffic = counter_traffic(f"gemm_hbm_traffic_{w.name}.md", GEMM_SOURCES, dom)
@@ -175,8 +186,21 @@ def main():
         "copy_probe": copy,
     }
 
-    del X, dY, W1, W2, Wg, others_y, others_dx, A, U, G, dU, dW1, dWg, dW2, dX, Y, Yred, dXred
     torch.cuda.empty_cache()
+    # ---- the other training configurations, same step, reported beside the headline
+    if not args.no_other:
+        other = {}
+        for name in ("mlp128_h1024_gelu_t2", "llama_7b_train_t2", "llama3_70b_prefill_t4"):
+            if name == w.name:
+                continue
+            o = train_step(WORKLOADS[name], 10, 3, B, I, torch, np, to_dev)
+            ow = WORKLOADS[name]
+            other[name] = {"ms_per_step": round(o["ms"], 4), "TFLOP/s": round(o["tflops"], 1),
+                           "frac_of_bf16_peak": round(o["tflops"] / PEAK_BF16_TFLOPS, 4),
+                           "tokens_per_s": round(ow.N / (o["ms"] * 1e-3), 1), "flops_per_step": o["flops"],
+                           "kernels_ms": {k: round(v, 4) for k, v in o["kern_ms"].items()}}
+            torch.cuda.empty_cache()
+        result["other_configs"] = other
     # ---- decode (one token, and small batches), HBM bound; weights rotated over copies
     if not args.no_decode:
         result["decode"] = bench_decode(args, WORKLOADS[args.decode_workload], B, I, torch, np, to_dev)
