@@ -358,7 +358,7 @@ def bench_attn(args, B, I, torch, np, to_dev, N=2048, h=12288, heads=96, kv=96, 
     dX = torch.empty(N, h, dtype=bf, device="cuda")
 
     def step():
-        B.tp_attn_qkv_shard(s, X, Wqkv, QKV)
+        B.tp_attn_qkv_shard(s, X, Wqkv, QKV)       # N > 64: no workspace
         B.tp_attn_out_shard(s, O, Wo, Y)
         B.tp_attn_out_bwd_shard(s, dY, O, Wo, dO, dWo)
         B.tp_attn_qkv_bwd_shard(s, X, Wqkv, dQKV, dWqkv, dX)
@@ -377,9 +377,53 @@ def bench_attn(args, B, I, torch, np, to_dev, N=2048, h=12288, heads=96, kv=96, 
     flops = 3 * 2 * N * h * (wc + qc)
     tf = flops / (ms * 1e-3) / 1e12
     log(f"[bench] attention projections gpt3 t=8: {ms:.3f} ms/step, {tf:.1f} TFLOP/s")
-    return {"workload": f"gpt3_attn_t{t}: N={N} h={h} heads={heads} head_dim={d} t={t} (qkv {wc}, o {qc} cols/rank)",
+    small = bench_attn_small(B, I, torch, to_dev)
+    return {"small_batch_llama3_70b_t4": small,"workload": f"gpt3_attn_t{t}: N={N} h={h} heads={heads} head_dim={d} t={t} (qkv {wc}, o {qc} cols/rank)",
             "ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "flops_per_step": flops, "step": "QKV fwd, O fwd, O bwd (dO, dW_o), QKV bwd (dX, dW_qkv)"}
+
+
+def bench_attn_small(B, I, torch, to_dev, h=8192, heads=64, kv=8, d=128, t=4):
+    """The forward attention projections (QKV and output) of one rank of the
+    70B block at decode batches of 8 and 32 tokens: the small-batch path,
+    HBM bound on the weights (Wqkv_i + Wo_i), rotated over 5 copies so no
+    cache holds them.  GB/s of weights."""
+    bf = torch.bfloat16
+    s0 = B.make_attn_shape(8, h, heads, kv, d, t, 0)
+    qc, wc = s0.q_cols, s0.qkv_cols
+    sig = I.WEIGHT_SIGMA
+    Wqkv = to_dev(I.normal_bf16([901, 2], (h, wc), sig))
+    Wo = to_dev(I.normal_bf16([901, 3], (qc, h), sig))
+    sets = [(Wqkv, Wo)] + [(Wqkv.clone(), Wo.clone()) for _ in range(4)]
+    wbytes = (h * wc + qc * h) * 2
+    out = {}
+    for N in (8, 32):
+        s = B.make_attn_shape(N, h, heads, kv, d, t, 0)
+        X, O = to_dev(I.normal_bf16([901, 0, N], (N, h))), to_dev(I.normal_bf16([901, 4, N], (N, qc)))
+        QKV, Y = torch.empty(N, wc, dtype=bf, device="cuda"), torch.empty(N, h, dtype=bf, device="cuda")
+        ws = B.alloc_workspace(B.attn_workspace_bytes(s))
+
+        def step(i):
+            a, b = sets[i % len(sets)]
+            B.tp_attn_qkv_shard(s, X, a, QKV, workspace=ws)
+            B.tp_attn_out_shard(s, O, b, Y, workspace=ws)
+        for i in range(10):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 100
+        e0.record(torch.cuda.current_stream())
+        for i in range(n):
+            step(i)
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        out[str(N)] = {"us_per_step": round(us, 2), "GB/s_of_weights": round(wbytes / (us * 1e-6) / 1e9, 1),
+                       "frac_of_hbm_peak": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] attention projections 70b t=4, N={N}: {us:.1f} us ({wbytes / (us * 1e-6) / 1e9:.0f} GB/s of weights)")
+    out["weight_bytes"] = wbytes
+    out["step"] = "QKV projection + output projection forward (small-batch path), weights rotated over 5 copies"
+    return out
 
 
 def bench_ln(B, I, torch, to_dev, name, N, h, t):

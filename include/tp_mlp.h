@@ -324,15 +324,28 @@ typedef struct {
   int32_t rank;
 } tp_attn_shape;
 
-/* Column-parallel QKV projection: QKV_i = X @ Wqkv_i (no communication). */
+/* Workspace bytes the forward projections need for shape s: nonzero only
+ * when 1 <= n_tokens <= 64, where tp_attn_qkv_shard and tp_attn_out_shard
+ * take the small-batch path (split-K products that stream each weight once,
+ * then a fixed-order sum of the k-splits, the arithmetic of the MLP's
+ * small-batch path); 0 for larger N or an invalid shape. */
+size_t tp_attn_workspace_bytes(const tp_attn_shape* s);
+
+/* Column-parallel QKV projection: QKV_i = X @ Wqkv_i (no communication).
+ *   workspace  tp_attn_workspace_bytes(s) bytes of device scratch (no
+ *              initial contents needed; NULL when that is 0); missing or
+ *              smaller: TP_MLP_ERR_WORKSPACE. */
 tp_mlp_status tp_attn_qkv_shard(const tp_attn_shape* s, const void* X,
                                 const void* Wqkv_i, void* QKV_i,
+                                void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
 /* Row-parallel output projection: Y_i = O_i @ Wo_i, the full-shape partial
- * sum (sum over ranks with tp_mlp_reduce_partials_local, bias once). */
+ * sum (sum over ranks with tp_mlp_reduce_partials_local, bias once).
+ *   workspace  as for tp_attn_qkv_shard. */
 tp_mlp_status tp_attn_out_shard(const tp_attn_shape* s, const void* O_i,
                                 const void* Wo_i, void* Y_i,
+                                void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
 /* Backward of the output projection for dY [N, h] (the same on every rank):

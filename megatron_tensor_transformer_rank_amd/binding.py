@@ -85,8 +85,8 @@ _SIGS = {
     "tp_mlp_up_wgrad_shard": [POINTER(Shape)] + [c_void_p] * 4 + [c_void_p],
     "tp_mlp_up_dgrad_shard": [POINTER(Shape)] + [c_void_p] * 4 + [c_void_p],
     "tp_mlp_bias_grad": [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p],
-    "tp_attn_qkv_shard": [POINTER(AttnShape)] + [c_void_p] * 3 + [c_void_p],
-    "tp_attn_out_shard": [POINTER(AttnShape)] + [c_void_p] * 3 + [c_void_p],
+    "tp_attn_qkv_shard": [POINTER(AttnShape)] + [c_void_p] * 4 + [c_size_t, c_void_p],
+    "tp_attn_out_shard": [POINTER(AttnShape)] + [c_void_p] * 4 + [c_size_t, c_void_p],
     "tp_attn_out_bwd_shard": [POINTER(AttnShape)] + [c_void_p] * 5 + [c_void_p],
     "tp_attn_qkv_bwd_shard": [POINTER(AttnShape)] + [c_void_p] * 5 + [c_void_p],
     "tp_sp_layernorm_fwd": [c_int64, c_int64, c_float] + [c_void_p] * 6 + [c_void_p],
@@ -113,6 +113,8 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_workspace_bytes.restype = c_size_t
         L.tp_mlp_bias_grad_workspace_bytes.argtypes = [c_int64, c_int64]
         L.tp_mlp_bias_grad_workspace_bytes.restype = c_size_t
+        L.tp_attn_workspace_bytes.argtypes = [POINTER(AttnShape)]
+        L.tp_attn_workspace_bytes.restype = c_size_t
         L.tp_sp_layernorm_bwd_workspace_bytes.argtypes = [c_int64, c_int64]
         L.tp_sp_layernorm_bwd_workspace_bytes.restype = c_size_t
         L.tp_mlp_status_string.argtypes = [c_int32]
@@ -131,6 +133,10 @@ def workspace_bytes(shape: Shape, backward: bool) -> int:
 
 def bias_grad_workspace_bytes(rows: int, cols: int) -> int:
     return int(lib().tp_mlp_bias_grad_workspace_bytes(rows, cols))
+
+
+def attn_workspace_bytes(shape: AttnShape) -> int:
+    return int(lib().tp_attn_workspace_bytes(ctypes.byref(shape)))
 
 
 def layernorm_bwd_workspace_bytes(rows: int, cols: int) -> int:
@@ -309,18 +315,23 @@ def tp_mlp_bias_grad(dY, db2, workspace, stream=None):
 
 
 # ------------------------------------------------------ attention projections
-def tp_attn_qkv_shard(shape: AttnShape, X, Wqkv_i, QKV_i, stream=None):
+def tp_attn_qkv_shard(shape: AttnShape, X, Wqkv_i, QKV_i, workspace=None, stream=None):
+    """QKV_i = X @ Wqkv_i; workspace: attn_workspace_bytes(shape) bytes (needed
+    only for 1 <= N <= 64)."""
     N, h, w = shape.n_tokens, shape.hidden, shape.qkv_cols
+    wp, wb = _ws(workspace, 0)
     _check("tp_attn_qkv_shard", lib().tp_attn_qkv_shard(
         ctypes.byref(shape), _p(X, BF16, N * h, "X"), _p(Wqkv_i, BF16, h * w, "Wqkv_i"),
-        _p(QKV_i, BF16, N * w, "QKV_i"), _stream(stream)))
+        _p(QKV_i, BF16, N * w, "QKV_i"), wp, wb, _stream(stream)))
 
 
-def tp_attn_out_shard(shape: AttnShape, O_i, Wo_i, Y_i, stream=None):
+def tp_attn_out_shard(shape: AttnShape, O_i, Wo_i, Y_i, workspace=None, stream=None):
+    """Y_i = O_i @ Wo_i (partial sum); workspace as for tp_attn_qkv_shard."""
     N, h, q = shape.n_tokens, shape.hidden, shape.q_cols
+    wp, wb = _ws(workspace, 0)
     _check("tp_attn_out_shard", lib().tp_attn_out_shard(
         ctypes.byref(shape), _p(O_i, BF16, N * q, "O_i"), _p(Wo_i, BF16, q * h, "Wo_i"),
-        _p(Y_i, BF16, N * h, "Y_i"), _stream(stream)))
+        _p(Y_i, BF16, N * h, "Y_i"), wp, wb, _stream(stream)))
 
 
 def tp_attn_out_bwd_shard(shape: AttnShape, dY, O_i, Wo_i, dO_i, dWo_i, stream=None):

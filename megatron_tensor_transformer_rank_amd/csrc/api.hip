@@ -275,6 +275,33 @@ tp_mlp_status attn_status(const tp_attn_shape* s, AttnDims& a) {
   return TP_MLP_OK;
 }
 
+// 1 <= N <= SK_MAX_N tokens: the forward projections stream their weights
+// once through the split-K small-batch product instead of wide tiles.
+bool attn_small(const AttnDims& a) { return a.N <= SK_MAX_N; }
+SkinnyPlan attn_qkv_plan(const AttnDims& a) {
+  return skinny_plan((int)a.N, (int)a.h, (int)a.qkv_cols, 1, SKINNY_TARGET_BLOCKS);
+}
+SkinnyPlan attn_out_plan(const AttnDims& a) {
+  return skinny_plan((int)a.N, (int)a.q_cols, (int)a.h, 1, SKINNY_TARGET_BLOCKS);
+}
+size_t attn_workspace(const AttnDims& a) {
+  if (!attn_small(a)) return 0;
+  const size_t q = attn_qkv_plan(a).part_floats, o = attn_out_plan(a).part_floats;
+  return round256((q > o ? q : o) * sizeof(float));
+}
+bool disjoint(const void* a, uint64_t na, const void* b, uint64_t nb);
+
+// The small-batch path's workspace: present, large enough, aligned, and
+// disjoint from the output.
+tp_mlp_status attn_ws_status(const AttnDims& a, void* workspace, size_t workspace_bytes, const void* out,
+                             uint64_t out_bytes) {
+  const size_t need = attn_workspace(a);
+  if (need == 0) return TP_MLP_OK;
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return TP_MLP_ERR_WORKSPACE;
+  if (!disjoint(workspace, need, out, out_bytes)) return TP_MLP_ERR_INVALID_ARG;
+  return TP_MLP_OK;
+}
+
 // C [M, Nc] = A [M, K] @ B [K, Nc], both row-major, bf16 out.
 hipError_t run_nn(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, void* C, hipStream_t st) {
   GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
@@ -572,19 +599,34 @@ tp_mlp_status tp_mlp_all_gather_local(int32_t t, const void* const* shards, int6
   return hip_status(gather_launch(pp, t, shard_rows, cols, u16(out), num_cu_current(), stream));
 }
 
+size_t tp_attn_workspace_bytes(const tp_attn_shape* s) {
+  AttnDims a;
+  if (attn_status(s, a) != TP_MLP_OK) return 0;
+  return attn_workspace(a);
+}
+
 tp_mlp_status tp_attn_qkv_shard(const tp_attn_shape* s, const void* X, const void* Wqkv_i, void* QKV_i,
-                                hipStream_t stream) {
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   AttnDims a;
   if (const tp_mlp_status ss = attn_status(s, a)) return ss;
   if (!req(X) || !req(Wqkv_i) || !req(QKV_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (const tp_mlp_status ss = attn_ws_status(a, workspace, workspace_bytes, QKV_i, nbytes(a.N, a.qkv_cols)))
+    return ss;
+  if (attn_small(a))
+    return hip_status(skinny_product_launch((int)a.N, cu16(X), cu16(Wqkv_i), (int)a.h, (int)a.qkv_cols,
+                                            attn_qkv_plan(a), static_cast<float*>(workspace), u16(QKV_i), stream));
   return hip_status(run_nn(a.N, a.qkv_cols, a.h, X, Wqkv_i, QKV_i, stream));
 }
 
 tp_mlp_status tp_attn_out_shard(const tp_attn_shape* s, const void* O_i, const void* Wo_i, void* Y_i,
-                                hipStream_t stream) {
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   AttnDims a;
   if (const tp_mlp_status ss = attn_status(s, a)) return ss;
   if (!req(O_i) || !req(Wo_i) || !req(Y_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (const tp_mlp_status ss = attn_ws_status(a, workspace, workspace_bytes, Y_i, nbytes(a.N, a.h))) return ss;
+  if (attn_small(a))
+    return hip_status(skinny_product_launch((int)a.N, cu16(O_i), cu16(Wo_i), (int)a.q_cols, (int)a.h,
+                                            attn_out_plan(a), static_cast<float*>(workspace), u16(Y_i), stream));
   return hip_status(run_nn(a.N, a.h, a.q_cols, O_i, Wo_i, Y_i, stream));
 }
 

@@ -32,4 +32,10 @@ hipError_t skinny_launch(int act, int N, const uint16_t* X, const uint16_t* Wa, 
                          float* part_up, float* part_down, uint16_t* A, uint16_t* st0, uint16_t* st1, uint16_t* Y,
                          hipStream_t st);
 
+// Y [N, ncols] (bf16) = X [N, K] @ W [K, ncols] for 1 <= N <= SK_MAX_N:
+// split-K partials (plan p from skinny_plan(N, K, ncols, 1, ...)), then their
+// sum in k-split order with one rounding.  part holds p.part_floats floats.
+hipError_t skinny_product_launch(int N, const uint16_t* X, const uint16_t* W, int K, int ncols, const SkinnyPlan& p,
+                                 float* part, uint16_t* Y, hipStream_t st);
+
 }  // namespace tpmlp

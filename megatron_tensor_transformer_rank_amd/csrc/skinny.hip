@@ -260,4 +260,11 @@ hipError_t skinny_launch(int act, int N, const uint16_t* X, const uint16_t* Wa, 
   return ksum_launch(part_down, down.ks, (int64_t)N * h, Y, st);
 }
 
+hipError_t skinny_product_launch(int N, const uint16_t* X, const uint16_t* W, int K, int ncols, const SkinnyPlan& p,
+                                 float* part, uint16_t* Y, hipStream_t st) {
+  const hipError_t e = partial_launch<1>(p, N, X, K, W, W, K, ncols, part, st);
+  if (e != hipSuccess) return e;
+  return ksum_launch(part, p.ks, (int64_t)N * ncols, Y, st);
+}
+
 }  // namespace tpmlp

@@ -210,8 +210,9 @@ def test_small_batch_workspace_sizes():
 def test_attn_rejects_bad_shapes(shape, expect):
     L = B.lib()
     r = ctypes.byref(shape)
-    assert L.tp_attn_qkv_shard(r, FAKE, FAKE, FAKE, None) == expect
-    assert L.tp_attn_out_shard(r, FAKE, FAKE, FAKE, None) == expect
+    assert L.tp_attn_qkv_shard(r, FAKE, FAKE, FAKE, None, 0, None) == expect
+    assert L.tp_attn_out_shard(r, FAKE, FAKE, FAKE, None, 0, None) == expect
+    assert B.attn_workspace_bytes(shape) == 0
     assert L.tp_attn_out_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, FAKE, None) == expect
     assert L.tp_attn_qkv_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, FAKE, None) == expect
 
@@ -221,10 +222,29 @@ def test_attn_rejects_bad_pointers_and_reports_widths():
     s = B.make_attn_shape(4, 64, 8, 2, 64, 4, 1)     # 2 kv heads over 4 ranks: replicated
     assert (s.q_cols, s.kv_cols, s.qkv_cols) == (128, 64, 256)
     r = ctypes.byref(s)
-    assert L.tp_attn_qkv_shard(r, None, FAKE, FAKE, None) == INVALID
-    assert L.tp_attn_out_shard(r, FAKE, FAKE + 2, FAKE, None) == INVALID
+    assert L.tp_attn_qkv_shard(r, None, FAKE, FAKE, None, 0, None) == INVALID
+    assert L.tp_attn_out_shard(r, FAKE, FAKE + 2, FAKE, None, 0, None) == INVALID
     assert L.tp_attn_out_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
     assert L.tp_attn_qkv_bwd_shard(r, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == INVALID
+
+
+def test_attn_small_batch_workspace():
+    """1 <= N <= 64 tokens take the small-batch path, which needs float32
+    k-split partials; N = 65 goes to the wide tiles, which need none."""
+    L = B.lib()
+    for N in (1, 2, 17, 64):
+        s = B.make_attn_shape(N, 8192, 64, 8, 128, 4, 0)     # 70B heads, t = 4
+        need = B.attn_workspace_bytes(s)
+        assert need > 0 and need % 256 == 0
+        # the larger of the two projections' partials: ks * N * cols floats
+        assert need >= N * max(s.qkv_cols, 8192) * 4
+        r = ctypes.byref(s)
+        assert L.tp_attn_qkv_shard(r, FAKE, FAKE, FAKE + (1 << 30), None, 0, None) == WORKSPACE
+        assert L.tp_attn_out_shard(r, FAKE, FAKE, FAKE + (1 << 30), FAKE, need - 1, None) == WORKSPACE
+        assert L.tp_attn_out_shard(r, FAKE, FAKE, FAKE + (1 << 30), FAKE + 8, need, None) == WORKSPACE  # alignment
+        # workspace on the output
+        assert L.tp_attn_qkv_shard(r, FAKE, FAKE, FAKE + (1 << 30), FAKE + (1 << 30), need, None) == INVALID
+    assert B.attn_workspace_bytes(B.make_attn_shape(65, 8192, 64, 8, 128, 4, 0)) == 0
 
 
 # ------------------------------------------- sequence-parallel LayerNorm

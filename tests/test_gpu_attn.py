@@ -9,7 +9,10 @@ rank: QKV_i, Y_i, dO_i, dWo_i, dX_i, dWqkv_i; summed over ranks: Y and dX
 key/value head's gradient summed over its replicas).  Shapes cover plain
 multi-head, grouped-query with key/value heads split across ranks and
 replicated on several ranks, ragged token counts, and the GPT-3-scale and
-Llama-3-70B-scale per-rank widths with sampled rows and columns.
+Llama-3-70B-scale per-rank widths with sampled rows and columns.  With
+1 <= N <= 64 tokens the forward projections take the small-batch path
+(split-K products streaming each weight once); those token counts are
+covered for several head layouts and at the 70B per-rank widths.
 """
 from __future__ import annotations
 
@@ -68,8 +71,9 @@ def run_attn_group(wid, N, h, nh, nkv, d, t, rows=None, ncols=None):
         dWo = torch.empty(s.q_cols, h, dtype=torch.float32, device="cuda")
         dWqkv = torch.empty(h, s.qkv_cols, dtype=torch.float32, device="cuda")
         dX = torch.empty(N, h, **bf)
-        B.tp_attn_qkv_shard(s, Xd, Wqkv, QKV)
-        B.tp_attn_out_shard(s, bf16_dev(O_b), Wo, Y)
+        ws = B.alloc_workspace(B.attn_workspace_bytes(s))   # 1 <= N <= 64: small-batch path
+        B.tp_attn_qkv_shard(s, Xd, Wqkv, QKV, workspace=ws)
+        B.tp_attn_out_shard(s, bf16_dev(O_b), Wo, Y, workspace=ws)
         B.tp_attn_out_bwd_shard(s, dYd, bf16_dev(O_b), Wo, dO, dWo)
         B.tp_attn_qkv_bwd_shard(s, Xd, Wqkv, bf16_dev(dQKV_b), dWqkv, dX)
         Yparts.append(Y)
@@ -145,3 +149,29 @@ def test_attn_projections_full_size_sampled(name, N, h, nh, nkv, d, t):
     rng = np.random.default_rng(len(name))
     rows = np.sort(rng.choice(N, size=32, replace=False))
     run_attn_group(800 + t, N, h, nh, nkv, d, t, rows=rows, ncols=48)
+
+
+# small batches: the forward projections on the split-K path, the backward on
+# the wide tiles; (wid, N, h, n_heads, n_kv, head_dim, t)
+SMALL = [
+    (711, 1, 1032, 8, 8, 64, 2),       # one token
+    (712, 2, 264, 8, 2, 64, 4),        # replicated key/value heads
+    (713, 16, 520, 16, 8, 32, 4),
+    (714, 33, 1544, 16, 4, 128, 8),    # ragged: 33 rows, h tail past 256-column strips
+    (715, 64, 136, 4, 1, 64, 1),       # multi-query, the path's largest N
+    (716, 65, 264, 8, 8, 64, 2),       # just past it: wide tiles
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"N{c[1]}_h{c[2]}_H{c[3]}_kv{c[4]}_t{c[6]}" for c in SMALL])
+def test_attn_small_batch_matches_oracle(case):
+    run_attn_group(*case)
+
+
+@pytest.mark.parametrize("N", [8, 32])
+def test_attn_small_batch_llama3_70b_widths(N):
+    """Every rank of the 70B attention block (t = 4: 16 query heads and 2
+    key/value heads of 128 per rank) at a decode batch of N tokens; all rows,
+    48 sampled weight-gradient columns."""
+    run_attn_group(820 + N, N, 8192, 64, 8, 128, 4, ncols=48)
+
