@@ -675,6 +675,8 @@ tp_mlp_status tp_sp_reduce_scatter_layernorm_local(int32_t t, const void* const*
   const uint64_t nb = (uint64_t)shard * (uint64_t)cols * 2, full = (uint64_t)rows * (uint64_t)cols * 2;
   for (int r = 0; r < t; ++r)
     if (!disjoint(y, nb, pp.p[r], full)) return TP_MLP_ERR_INVALID_ARG;
+  if (!disjoint(z, nb, gamma, (uint64_t)cols * 2) || (beta && !disjoint(z, nb, beta, (uint64_t)cols * 2)))
+    return TP_MLP_ERR_INVALID_ARG;
   if (!disjoint(y, nb, z, nb) || (residual && !disjoint(y, nb, residual, nb)) ||
       (bias && !disjoint(y, nb, bias, (uint64_t)cols * 2)) || !disjoint(y, nb, gamma, (uint64_t)cols * 2) ||
       (beta && !disjoint(y, nb, beta, (uint64_t)cols * 2)) || !stash_ok(mean, rstd, shard, y, nb) ||
@@ -700,13 +702,24 @@ tp_mlp_status tp_sp_layernorm_bwd(int64_t rows, int64_t cols, const void* x, con
   const size_t need = ln_bwd_workspace_bytes(rows, cols);
   if (!disjoint(dx, nb, x, nb) || !same_or_disjoint(dx, nb, dy, nb) || (dres && !same_or_disjoint(dx, nb, dres, nb)) ||
       !disjoint(dx, nb, gamma, (uint64_t)cols * 2) || !disjoint(dx, nb, mean, (uint64_t)rows * 4) ||
-      !disjoint(dx, nb, rstd, (uint64_t)rows * 4) || !disjoint(dgamma, gb, dx, nb) ||
-      (dbeta && (!disjoint(dbeta, gb, dx, nb) || !disjoint(dbeta, gb, dgamma, gb))))
+      !disjoint(dx, nb, rstd, (uint64_t)rows * 4))
     return TP_MLP_ERR_INVALID_ARG;
+  // dgamma and dbeta: disjoint from every input, dx and each other
+  const float* grads[2] = {dgamma, dbeta};
+  for (const float* g : grads) {
+    if (!g) continue;
+    if (!disjoint(g, gb, dx, nb) || !disjoint(g, gb, x, nb) || !disjoint(g, gb, dy, nb) ||
+        (dres && !disjoint(g, gb, dres, nb)) || !disjoint(g, gb, gamma, (uint64_t)cols * 2) ||
+        !disjoint(g, gb, mean, (uint64_t)rows * 4) || !disjoint(g, gb, rstd, (uint64_t)rows * 4))
+      return TP_MLP_ERR_INVALID_ARG;
+  }
+  if (dbeta && !disjoint(dbeta, gb, dgamma, gb)) return TP_MLP_ERR_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return TP_MLP_ERR_WORKSPACE;
   if (!disjoint(workspace, need, dx, nb) || !disjoint(workspace, need, dgamma, gb) ||
       (dbeta && !disjoint(workspace, need, dbeta, gb)) || !disjoint(workspace, need, x, nb) ||
-      !disjoint(workspace, need, dy, nb))
+      !disjoint(workspace, need, dy, nb) || (dres && !disjoint(workspace, need, dres, nb)) ||
+      !disjoint(workspace, need, gamma, (uint64_t)cols * 2) || !disjoint(workspace, need, mean, (uint64_t)rows * 4) ||
+      !disjoint(workspace, need, rstd, (uint64_t)rows * 4))
     return TP_MLP_ERR_INVALID_ARG;
   return hip_status(ln_bwd_launch(cu16(x), cu16(gamma), mean, rstd, cu16(dy), cu16(dres), u16(dx), rows, cols,
                                   dgamma, dbeta, static_cast<float*>(workspace), stream));

@@ -18,11 +18,11 @@
 // stores it, and normalises that stored value: bit for bit what a separate
 // reduce-scatter followed by a LayerNorm of z computes.
 //
-// The backward runs as a row kernel (dx, one row per block, like the
-// forward) and a column kernel: dgamma and dbeta over (512-column strip,
-// row slab) tiles, which re-reads x and dy but keeps every CU busy and its
-// partial rows few (at most 64 slabs); a last kernel adds the slabs in slab
-// order.
+// The backward runs as a column kernel, dgamma and dbeta over (512-column
+// strip, row slab) tiles with at most 64 slabs of partial rows, a kernel
+// that adds the slabs in slab order, and then the row kernel (dx, one row
+// per block, like the forward), last because dx may overwrite dy in place.
+// The column kernel re-reads x and dy but keeps every CU busy.
 #include "common.h"
 #include "norm.h"
 
@@ -418,8 +418,23 @@ hipError_t ln_bwd_launch(const uint16_t* x, const uint16_t* gamma, const float* 
                          const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int64_t rows, int64_t cols,
                          float* dgamma, float* dbeta, float* part, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  const int cols8 = (int)(cols / 8);
   const dim3 blk(LN_THREADS);
+  // the column sums first: they read dy, which dx may overwrite in place
+  int slabs;
+  int64_t rpb;
+  bwd_slabs(rows, slabs, rpb);
+  float* part_g = part;
+  float* part_b = dbeta ? part + (int64_t)slabs * cols : nullptr;
+  const int64_t strips = (cols + LN_DG_STRIP - 1) / LN_DG_STRIP;
+  hipLaunchKernelGGL(ln_bwd_dgb_kernel, dim3((unsigned)(strips * slabs)), blk, 0, st, x, mean, rstd, dy, rows, cols,
+                     rpb, part_g, part_b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 sgrid((unsigned)((cols + 63) / 64), dbeta ? 2u : 1u);
+  hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, dgamma, part_b, dbeta, slabs, cols);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int cols8 = (int)(cols / 8);
 #define LN_BWD(J)                                                                                                \
   hipLaunchKernelGGL((ln_bwd_dx_kernel<J>), dim3((unsigned)rows), blk, 0, st, x, gamma, mean, rstd, dy, dres,   \
                      dx, cols8, (int)cols)
@@ -433,20 +448,6 @@ hipError_t ln_bwd_launch(const uint16_t* x, const uint16_t* gamma, const float* 
     default: return hipErrorInvalidValue;
   }
 #undef LN_BWD
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  int slabs;
-  int64_t rpb;
-  bwd_slabs(rows, slabs, rpb);
-  float* part_g = part;
-  float* part_b = dbeta ? part + (int64_t)slabs * cols : nullptr;
-  const int64_t strips = (cols + LN_DG_STRIP - 1) / LN_DG_STRIP;
-  hipLaunchKernelGGL(ln_bwd_dgb_kernel, dim3((unsigned)(strips * slabs)), blk, 0, st, x, mean, rstd, dy, rows, cols,
-                     rpb, part_g, part_b);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 sgrid((unsigned)((cols + 63) / 64), dbeta ? 2u : 1u);
-  hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, dgamma, part_b, dbeta, slabs, cols);
   return hipGetLastError();
 }
 

@@ -294,6 +294,8 @@ def test_layernorm_fused_rejects_bad_arguments():
     assert call(res=FAKE + 7 * MB, y=FAKE + 7 * MB) == INVALID   # y on the residual
     assert call(z=p1 + 16) == INVALID                 # z straddles rank 0's block of a partial
     assert call(m=z) == INVALID                       # stash on z
+    assert call(z=g) == INVALID                       # z on gamma
+    assert call(beta=FAKE + 7 * MB, z=FAKE + 7 * MB) == INVALID   # z on beta
     assert call(cols=16400) == UNSUPPORTED
     big = (ctypes.c_void_p * 65)(*([FAKE] * 65))
     assert call(t=65, ptrs=big, rows=65) == UNSUPPORTED
@@ -328,6 +330,11 @@ def test_layernorm_bwd_workspace_and_arguments():
     assert call(dres=dx + 16) == INVALID              # dx straddles dres
     assert call(db=dg) == INVALID                     # dbeta on dgamma
     assert call(w=dx) == INVALID                      # workspace on dx
+    assert call(w=g) == INVALID                       # workspace on gamma
+    assert call(dg=x) == INVALID                      # dgamma on x
+    assert call(dg=dy + 16) == INVALID                # dgamma inside dy
+    assert call(db=m) == INVALID                      # dbeta on the stash
+    assert call(dres=FAKE + 10 * MB, dg=FAKE + 10 * MB) == INVALID   # dgamma on dres
     assert call(cols=12) == INVALID
     assert call(rows=0) == INVALID
     assert call(cols=16400, wb=1 << 30) == UNSUPPORTED

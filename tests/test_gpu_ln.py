@@ -379,3 +379,33 @@ def test_layernorm_deterministic_and_workspace_contents_irrelevant():
         outs.append([a.clone() for a in (y, mean, rstd, dx, dg, db)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("alias", ["dy", "dres"])
+def test_layernorm_backward_in_place(alias):
+    """dx may be the dy or the dres buffer itself: the result (dx, dgamma,
+    dbeta) is bitwise the out-of-place one."""
+    rows, cols = 40, 1544
+    xb, dyb, drb = I.gen_x(985, rows, cols), I.gen_dy(985, rows, cols), I.normal_bf16([985, 3], (rows, cols))
+    gb = I.gen_ln_weight(985, cols)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    x, g = bf16_dev(xb), bf16_dev(gb)
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    B.tp_sp_layernorm_fwd(x, g, torch.empty(rows, cols, **bf), mean=mean, rstd=rstd)
+    ws = B.alloc_workspace(B.layernorm_bwd_workspace_bytes(rows, cols))
+    res = []
+    for in_place in (False, True):
+        dy, dres = bf16_dev(dyb), bf16_dev(drb)
+        dx = (dy if alias == "dy" else dres) if in_place else torch.empty(rows, cols, **bf)
+        dg = torch.empty(cols, dtype=torch.float32, device="cuda")
+        db = torch.empty(cols, dtype=torch.float32, device="cuda")
+        B.tp_sp_layernorm_bwd(x, g, mean, rstd, dy, dx, dg, dbeta=db, dres=dres, workspace=ws)
+        torch.cuda.synchronize()
+        res.append((dx.clone(), dg.clone(), db.clone()))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+    dxr, dgr, _ = ln.layer_norm_backward(f(dyb), f(xb), f(gb), dres=f(drb))
+    assert_close("dx", f64(res[1][0]), dxr)
+    assert_close("dgamma", f64(res[1][1]), dgr)
+
