@@ -4,6 +4,7 @@
 // Every check runs before the first launch, so an invalid call enqueues
 // nothing.  No exception crosses the ABI; nothing is printed.
 #include <atomic>
+#include <initializer_list>
 #include <new>
 
 #include "common.h"
@@ -369,6 +370,23 @@ bool same_or_disjoint(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return (a == b && na == nb) || disjoint(a, na, b, nb);
 }
 
+// A device buffer of n bytes (p may be NULL: an absent optional buffer).
+struct Span {
+  const void* p;
+  uint64_t n;
+};
+// The outputs are pairwise disjoint and disjoint from every input.
+bool spans_ok(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    if (!o->p) continue;
+    for (auto q = o + 1; q != outs.end(); ++q)
+      if (q->p && !disjoint(o->p, o->n, q->p, q->n)) return false;
+    for (const Span& i : ins)
+      if (i.p && !disjoint(o->p, o->n, i.p, i.n)) return false;
+  }
+  return true;
+}
+
 // The reduce-scatter's arguments: rank's block of rows/t rows, out may
 // coincide exactly with the residual or with rank's block of any partial and
 // must not otherwise overlap an input.
@@ -448,6 +466,8 @@ tp_mlp_status tp_mlp_up_act_shard(const tp_mlp_shape* s, const void* X, const vo
   if (sw != (Wg_i != nullptr) || !opt_aligned(Wg_i)) return TP_MLP_ERR_INVALID_ARG;
   if (!sw && G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
   if (sw && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
+  if (!spans_ok({{A_i, a}, {U_i, a}, {G_i, a}}, {{X, x}, {W1_i, w}, {Wg_i, w}})) return TP_MLP_ERR_INVALID_ARG;
   return hip_status(run_up_act(d, X, W1_i, Wg_i, A_i, U_i, G_i, stream));
 }
 
@@ -456,6 +476,8 @@ tp_mlp_status tp_mlp_down_shard(const tp_mlp_shape* s, const void* A_i, const vo
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   if (!req(A_i) || !req(W2_i) || !req(Y_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{Y_i, (uint64_t)d.N * d.h * 2}}, {{A_i, (uint64_t)d.N * d.Fi * 2}, {W2_i, (uint64_t)d.Fi * d.h * 2}}))
+    return TP_MLP_ERR_INVALID_ARG;
   return hip_status(run_down(d, A_i, W2_i, Y_i, stream));
 }
 
@@ -471,6 +493,13 @@ tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X, const void*
   if (sw != (Wg_i != nullptr)) return TP_MLP_ERR_INVALID_ARG;
   if (!sw && G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
   if (sw && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
+  {
+    const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
+    const uint64_t ws_used = d.N == 1 ? decode_layout(d).total : (small_batch(d) ? skinny_layout(d).total : 0);
+    if (!spans_ok({{Y_i, x}, {A_i, a}, {U_i, a}, {G_i, a}, {ws_used ? workspace : nullptr, ws_used}},
+                  {{X, x}, {W1_i, w}, {Wg_i, w}, {W2_i, w}}))
+      return TP_MLP_ERR_INVALID_ARG;
+  }
 
   if (d.N == 1) {
     const DecodeLayout L = decode_layout(d);
@@ -503,6 +532,10 @@ tp_mlp_status tp_mlp_down_dgrad_act_shard(const tp_mlp_shape* s, const void* dY,
   const bool sw = d.act == ACT_SWIGLU;
   if (!req(dY) || !req(W2_i) || !req(U_i) || !req(dU_i)) return TP_MLP_ERR_INVALID_ARG;
   if (sw ? !req(G_i) : G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t a = (uint64_t)d.N * d.Fi * 2;
+  if (!spans_ok({{dU_i, a * d.g}}, {{dY, (uint64_t)d.N * d.h * 2}, {W2_i, (uint64_t)d.Fi * d.h * 2}, {U_i, a},
+                                   {G_i, a}}))
+    return TP_MLP_ERR_INVALID_ARG;
   return hip_status(run_dgrad_act(d, dY, W2_i, U_i, G_i, dU_i, stream));
 }
 
@@ -511,6 +544,8 @@ tp_mlp_status tp_mlp_down_wgrad_shard(const tp_mlp_shape* s, const void* A_i, co
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   if (!req(A_i) || !req(dY) || !req(dW2_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dW2_i, (uint64_t)d.Fi * d.h * 4}}, {{A_i, (uint64_t)d.N * d.Fi * 2}, {dY, (uint64_t)d.N * d.h * 2}}))
+    return TP_MLP_ERR_INVALID_ARG;
   return hip_status(run_wgrad_down(d, A_i, dY, dW2_i, stream));
 }
 
@@ -521,6 +556,9 @@ tp_mlp_status tp_mlp_up_wgrad_shard(const tp_mlp_shape* s, const void* X, const 
   const bool sw = d.act == ACT_SWIGLU;
   if (!req(X) || !req(dU_i) || !req(dW1_i)) return TP_MLP_ERR_INVALID_ARG;
   if (sw ? !req(dWg_i) : dWg_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t w4 = (uint64_t)d.h * d.Fi * 4;
+  if (!spans_ok({{dW1_i, w4}, {dWg_i, w4}}, {{X, (uint64_t)d.N * d.h * 2}, {dU_i, (uint64_t)d.N * d.g * d.Fi * 2}}))
+    return TP_MLP_ERR_INVALID_ARG;
   return hip_status(run_wgrad_up(d, X, dU_i, dW1_i, dWg_i, stream));
 }
 
@@ -531,6 +569,10 @@ tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i, con
   const bool sw = d.act == ACT_SWIGLU;
   if (!req(dU_i) || !req(W1_i) || !req(dX_partial)) return TP_MLP_ERR_INVALID_ARG;
   if (sw ? !req(Wg_i) : Wg_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t w = (uint64_t)d.h * d.Fi * 2;
+  if (!spans_ok({{dX_partial, (uint64_t)d.N * d.h * 2}},
+                {{dU_i, (uint64_t)d.N * d.g * d.Fi * 2}, {W1_i, w}, {Wg_i, w}}))
+    return TP_MLP_ERR_INVALID_ARG;
   return hip_status(run_dgrad_up(d, dU_i, W1_i, Wg_i, dX_partial, stream));
 }
 
@@ -539,6 +581,9 @@ tp_mlp_status tp_mlp_bias_grad(const void* dY, int64_t rows, int64_t cols, float
   if (rows < 1 || cols < 8 || cols % 8 != 0 || !req(dY) || !req(db2) || !opt_aligned(workspace))
     return TP_MLP_ERR_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < col_sum_workspace_bytes(rows, cols)) return TP_MLP_ERR_WORKSPACE;
+  if (!spans_ok({{db2, (uint64_t)cols * 4}, {workspace, col_sum_workspace_bytes(rows, cols)}},
+                {{dY, (uint64_t)rows * cols * 2}}))
+    return TP_MLP_ERR_INVALID_ARG;
   return hip_status(col_sum_launch(cu16(dY), rows, cols, db2, static_cast<float*>(workspace), stream));
 }
 
@@ -556,6 +601,14 @@ tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X, const void*
     return TP_MLP_ERR_INVALID_ARG;
   if (db2 != nullptr && (workspace == nullptr || workspace_bytes < col_sum_workspace_bytes(d.N, d.h)))
     return TP_MLP_ERR_WORKSPACE;
+  {
+    const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
+    const uint64_t ws_used = db2 ? col_sum_workspace_bytes(d.N, d.h) : 0;
+    if (!spans_ok({{dU_i, a * d.g}, {dW1_i, w * 2}, {dWg_i, w * 2}, {dW2_i, w * 2}, {dX_partial, x},
+                   {db2, (uint64_t)d.h * 4}, {ws_used ? workspace : nullptr, ws_used}},
+                  {{X, x}, {W1_i, w}, {Wg_i, w}, {W2_i, w}, {dY, x}, {A_i, a}, {U_i, a}, {G_i, a}}))
+      return TP_MLP_ERR_INVALID_ARG;
+  }
 
   hipError_t e = run_dgrad_act(d, dY, W2_i, U_i, G_i, dU_i, stream);
   if (e == hipSuccess) e = run_wgrad_down(d, A_i, dY, dW2_i, stream);
@@ -612,6 +665,10 @@ tp_mlp_status tp_attn_qkv_shard(const tp_attn_shape* s, const void* X, const voi
   if (!req(X) || !req(Wqkv_i) || !req(QKV_i)) return TP_MLP_ERR_INVALID_ARG;
   if (const tp_mlp_status ss = attn_ws_status(a, workspace, workspace_bytes, QKV_i, nbytes(a.N, a.qkv_cols)))
     return ss;
+  const size_t wsu = attn_workspace(a);
+  if (!spans_ok({{QKV_i, nbytes(a.N, a.qkv_cols)}, {wsu ? workspace : nullptr, wsu}},
+                {{X, nbytes(a.N, a.h)}, {Wqkv_i, nbytes(a.h, a.qkv_cols)}}))
+    return TP_MLP_ERR_INVALID_ARG;
   if (attn_small(a))
     return hip_status(skinny_product_launch((int)a.N, cu16(X), cu16(Wqkv_i), (int)a.h, (int)a.qkv_cols,
                                             attn_qkv_plan(a), static_cast<float*>(workspace), u16(QKV_i), stream));
@@ -624,6 +681,10 @@ tp_mlp_status tp_attn_out_shard(const tp_attn_shape* s, const void* O_i, const v
   if (const tp_mlp_status ss = attn_status(s, a)) return ss;
   if (!req(O_i) || !req(Wo_i) || !req(Y_i)) return TP_MLP_ERR_INVALID_ARG;
   if (const tp_mlp_status ss = attn_ws_status(a, workspace, workspace_bytes, Y_i, nbytes(a.N, a.h))) return ss;
+  const size_t wsu = attn_workspace(a);
+  if (!spans_ok({{Y_i, nbytes(a.N, a.h)}, {wsu ? workspace : nullptr, wsu}},
+                {{O_i, nbytes(a.N, a.q_cols)}, {Wo_i, nbytes(a.q_cols, a.h)}}))
+    return TP_MLP_ERR_INVALID_ARG;
   if (attn_small(a))
     return hip_status(skinny_product_launch((int)a.N, cu16(O_i), cu16(Wo_i), (int)a.q_cols, (int)a.h,
                                             attn_out_plan(a), static_cast<float*>(workspace), u16(Y_i), stream));
@@ -635,6 +696,9 @@ tp_mlp_status tp_attn_out_bwd_shard(const tp_attn_shape* s, const void* dY, cons
   AttnDims a;
   if (const tp_mlp_status ss = attn_status(s, a)) return ss;
   if (!req(dY) || !req(O_i) || !req(Wo_i) || !req(dO_i) || !req(dWo_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dO_i, nbytes(a.N, a.q_cols)}, {dWo_i, (uint64_t)a.q_cols * a.h * 4}},
+                {{dY, nbytes(a.N, a.h)}, {O_i, nbytes(a.N, a.q_cols)}, {Wo_i, nbytes(a.q_cols, a.h)}}))
+    return TP_MLP_ERR_INVALID_ARG;
   hipError_t e = run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream);
   if (e == hipSuccess) e = run_tn(a.q_cols, a.h, a.N, O_i, dY, dWo_i, stream);
   return hip_status(e);
@@ -645,6 +709,9 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X, const
   AttnDims a;
   if (const tp_mlp_status ss = attn_status(s, a)) return ss;
   if (!req(X) || !req(Wqkv_i) || !req(dQKV_i) || !req(dWqkv_i) || !req(dX_partial)) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dWqkv_i, (uint64_t)a.h * a.qkv_cols * 4}, {dX_partial, nbytes(a.N, a.h)}},
+                {{X, nbytes(a.N, a.h)}, {Wqkv_i, nbytes(a.h, a.qkv_cols)}, {dQKV_i, nbytes(a.N, a.qkv_cols)}}))
+    return TP_MLP_ERR_INVALID_ARG;
   hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV_i, Wqkv_i, dX_partial, stream);
   if (e == hipSuccess) e = run_tn(a.h, a.qkv_cols, a.N, X, dQKV_i, dWqkv_i, stream);
   return hip_status(e);

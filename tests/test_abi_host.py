@@ -16,6 +16,12 @@ OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced by validation
 
 
+def P(k):
+    """The k-th fake device buffer: 1 GiB apart, so distinct buffers never
+    overlap and each check below fails for the reason it names."""
+    return FAKE + k * (1 << 30)
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -52,7 +58,7 @@ def test_workspace_sizes():
 
 
 def _fwd(shape, **over):
-    a = dict(X=FAKE, W1=FAKE, Wg=None, W2=FAKE, Y=FAKE, A=FAKE, U=None, G=None, ws=None, wsb=0)
+    a = dict(X=P(0), W1=P(1), Wg=None, W2=P(3), Y=P(4), A=P(5), U=None, G=None, ws=None, wsb=0)
     a.update(over)
     return B.lib().tp_mlp_fwd_shard(ctypes.byref(shape), a["X"], a["W1"], a["Wg"], a["W2"], a["Y"],
                                     a["A"], a["U"], a["G"], a["ws"], a["wsb"], None)
@@ -76,20 +82,34 @@ def test_fwd_rejects_bad_pointers():
     s = B.make_shape(4, 64, 128, 2, 0, "gelu")
     assert _fwd(s, X=None) == INVALID
     assert _fwd(s, W2=None) == INVALID
-    assert _fwd(s, Y=FAKE + 2) == INVALID                       # misaligned
-    assert _fwd(s, Wg=FAKE) == INVALID                          # gate weight given without SwiGLU
-    assert _fwd(s, G=FAKE) == INVALID                           # gate stash without SwiGLU
+    assert _fwd(s, Y=P(4) + 2) == INVALID                       # misaligned
+    assert _fwd(s, Wg=P(2)) == INVALID                          # gate weight given without SwiGLU
+    assert _fwd(s, G=P(7)) == INVALID                           # gate stash without SwiGLU
     sw = B.make_shape(4, 64, 128, 2, 0, "swiglu")
     assert _fwd(sw) == INVALID                                  # SwiGLU needs the gate shard
-    assert _fwd(sw, Wg=FAKE, U=FAKE) == INVALID                 # U and G stashes come together
+    assert _fwd(sw, Wg=P(2), U=P(6)) == INVALID                 # U and G stashes come together
     dec = B.make_shape(1, 64, 128, 2, 0, "gelu")
     assert _fwd(dec) == WORKSPACE                               # decode path needs workspace
-    assert _fwd(dec, ws=FAKE, wsb=16) == WORKSPACE
+    assert _fwd(dec, ws=P(8), wsb=16) == WORKSPACE
+
+
+def test_fwd_rejects_overlaps():
+    """Outputs may not overlap each other, an input or the workspace in use
+    (N = 4, h = 64, F_i = 64: Y and X 512 B, A 512 B, weights 8 KiB)."""
+    s = B.make_shape(4, 64, 128, 2, 0, "gelu")
+    assert _fwd(s, Y=P(0)) == INVALID                           # Y on X
+    assert _fwd(s, A=P(4) + 256) == INVALID                     # A inside Y
+    assert _fwd(s, Y=P(1) + 4096) == INVALID                    # Y inside W1
+    assert _fwd(s, U=P(5)) == INVALID                           # the stash on A
+    dec = B.make_shape(1, 64, 128, 2, 0, "gelu")
+    need = B.workspace_bytes(dec, False)
+    assert _fwd(dec, ws=P(3), wsb=need) == INVALID              # workspace on W2
+    assert _fwd(dec, ws=P(4), wsb=need) == INVALID              # workspace on Y
 
 
 def test_bwd_rejects_bad_arguments():
     s = B.make_shape(4, 64, 128, 2, 0, "gelu")
-    args = [FAKE] * 13 + [None, None, 0, None]
+    args = [P(k) for k in range(13)] + [None, None, 0, None]
     base = dict(zip(["X", "W1", "Wg", "W2", "dY", "A", "U", "G", "dU", "dW1", "dWg", "dW2", "dX",
                      "db2", "ws", "wsb", "st"], args))
     base.update(Wg=None, G=None, dWg=None)
@@ -100,9 +120,14 @@ def test_bwd_rejects_bad_arguments():
         return B.lib().tp_mlp_bwd_shard(ctypes.byref(s), *a.values())
 
     assert call(U=None) == INVALID
-    assert call(dW2=FAKE + 4) == INVALID
-    assert call(dWg=FAKE) == INVALID
-    assert call(db2=FAKE) == WORKSPACE
+    assert call(dW2=P(11) + 4) == INVALID
+    assert call(dWg=P(10)) == INVALID
+    assert call(db2=P(13)) == WORKSPACE
+    # overlaps: outputs against inputs and each other, the workspace in use
+    assert call(dX=P(4)) == INVALID                             # dX on dY
+    assert call(dU=P(5)) == INVALID                             # dU on A
+    assert call(dW1=P(11) + 1024) == INVALID                    # dW1 inside dW2
+    assert call(db2=P(13), ws=P(12), wsb=1 << 20) == INVALID    # workspace on dX
 
 
 def test_reduce_rejects_bad_arguments():
@@ -123,14 +148,22 @@ def test_step_entry_points_validate():
     L = B.lib()
     s = B.make_shape(4, 64, 128, 2, 0, "swiglu")
     r = ctypes.byref(s)
-    assert L.tp_mlp_up_act_shard(r, FAKE, FAKE, None, FAKE, None, None, None) == INVALID
-    assert L.tp_mlp_down_shard(r, FAKE, None, FAKE, None) == INVALID
-    assert L.tp_mlp_down_dgrad_act_shard(r, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
-    assert L.tp_mlp_down_wgrad_shard(r, FAKE, FAKE, FAKE + 1, None) == INVALID
-    assert L.tp_mlp_up_wgrad_shard(r, FAKE, FAKE, FAKE, None, None) == INVALID
-    assert L.tp_mlp_up_dgrad_shard(r, FAKE, FAKE, None, FAKE, None) == INVALID
-    assert L.tp_mlp_bias_grad(FAKE, 4, 12, FAKE, FAKE, 1 << 20, None) == INVALID
-    assert L.tp_mlp_bias_grad(FAKE, 4, 8, FAKE, None, 0, None) == WORKSPACE
+    assert L.tp_mlp_up_act_shard(r, P(0), P(1), None, P(2), None, None, None) == INVALID    # SwiGLU: no gate
+    assert L.tp_mlp_down_shard(r, P(0), None, P(2), None) == INVALID
+    assert L.tp_mlp_down_dgrad_act_shard(r, P(0), P(1), P(2), None, P(3), None) == INVALID  # no gate stash
+    assert L.tp_mlp_down_wgrad_shard(r, P(0), P(1), P(2) + 1, None) == INVALID
+    assert L.tp_mlp_up_wgrad_shard(r, P(0), P(1), P(2), None, None) == INVALID             # no dWg
+    assert L.tp_mlp_up_dgrad_shard(r, P(0), P(1), None, P(2), None) == INVALID             # no Wg
+    assert L.tp_mlp_bias_grad(P(0), 4, 12, P(1), P(2), 1 << 20, None) == INVALID
+    assert L.tp_mlp_bias_grad(P(0), 4, 8, P(1), None, 0, None) == WORKSPACE
+    # overlaps of each step's output with its inputs
+    assert L.tp_mlp_up_act_shard(r, P(0), P(1), P(2), P(0), P(4), P(5), None) == INVALID   # A on X
+    assert L.tp_mlp_down_shard(r, P(0), P(1), P(1), None) == INVALID                       # Y on W2
+    assert L.tp_mlp_down_dgrad_act_shard(r, P(0), P(1), P(2), P(3), P(3), None) == INVALID  # dU on G
+    assert L.tp_mlp_down_wgrad_shard(r, P(0), P(1), P(0), None) == INVALID                 # dW2 on A
+    assert L.tp_mlp_up_wgrad_shard(r, P(0), P(1), P(2), P(2) + 64, None) == INVALID        # dWg inside dW1
+    assert L.tp_mlp_up_dgrad_shard(r, P(0), P(1), P(2), P(2), None) == INVALID             # dX on Wg
+    assert L.tp_mlp_bias_grad(P(0), 4, 8, P(1), P(0), 1 << 20, None) == INVALID            # workspace on dY
 
 
 def test_reduce_rejects_partial_overlap():
@@ -194,7 +227,7 @@ def test_small_batch_workspace_sizes():
     assert B.workspace_bytes(B.make_shape(65, 8192, 28672, 4, 0, "swiglu"), False) == 0
     s = B.make_shape(8, 64, 128, 2, 0, "gelu")
     assert _fwd(s) == WORKSPACE                                  # small batch needs workspace
-    assert _fwd(s, ws=FAKE, wsb=B.workspace_bytes(s, False) - 1) == WORKSPACE
+    assert _fwd(s, ws=P(8), wsb=B.workspace_bytes(s, False) - 1) == WORKSPACE
 
 
 @pytest.mark.parametrize("shape,expect", [
@@ -210,11 +243,11 @@ def test_small_batch_workspace_sizes():
 def test_attn_rejects_bad_shapes(shape, expect):
     L = B.lib()
     r = ctypes.byref(shape)
-    assert L.tp_attn_qkv_shard(r, FAKE, FAKE, FAKE, None, 0, None) == expect
-    assert L.tp_attn_out_shard(r, FAKE, FAKE, FAKE, None, 0, None) == expect
+    assert L.tp_attn_qkv_shard(r, P(0), P(1), P(2), None, 0, None) == expect
+    assert L.tp_attn_out_shard(r, P(0), P(1), P(2), None, 0, None) == expect
     assert B.attn_workspace_bytes(shape) == 0
-    assert L.tp_attn_out_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, FAKE, None) == expect
-    assert L.tp_attn_qkv_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, FAKE, None) == expect
+    assert L.tp_attn_out_bwd_shard(r, P(0), P(1), P(2), P(3), P(4), None) == expect
+    assert L.tp_attn_qkv_bwd_shard(r, P(0), P(1), P(2), P(3), P(4), None) == expect
 
 
 def test_attn_rejects_bad_pointers_and_reports_widths():
@@ -222,10 +255,17 @@ def test_attn_rejects_bad_pointers_and_reports_widths():
     s = B.make_attn_shape(4, 64, 8, 2, 64, 4, 1)     # 2 kv heads over 4 ranks: replicated
     assert (s.q_cols, s.kv_cols, s.qkv_cols) == (128, 64, 256)
     r = ctypes.byref(s)
-    assert L.tp_attn_qkv_shard(r, None, FAKE, FAKE, None, 0, None) == INVALID
-    assert L.tp_attn_out_shard(r, FAKE, FAKE + 2, FAKE, None, 0, None) == INVALID
-    assert L.tp_attn_out_bwd_shard(r, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
-    assert L.tp_attn_qkv_bwd_shard(r, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == INVALID
+    assert L.tp_attn_qkv_shard(r, None, P(1), P(2), None, 0, None) == INVALID
+    assert L.tp_attn_out_shard(r, P(0), P(1) + 2, P(2), None, 0, None) == INVALID
+    assert L.tp_attn_out_bwd_shard(r, P(0), P(1), P(2), P(3), None, None) == INVALID
+    assert L.tp_attn_qkv_bwd_shard(r, P(0), P(1), P(2), P(3) + 4, P(4), None) == INVALID
+    # overlaps (N = 65 here: the wide-tile path, no workspace)
+    s65 = B.make_attn_shape(65, 64, 8, 2, 64, 4, 1)
+    r65 = ctypes.byref(s65)
+    assert L.tp_attn_qkv_shard(r65, P(0), P(1), P(0), None, 0, None) == INVALID        # QKV on X
+    assert L.tp_attn_out_shard(r65, P(0), P(1), P(1), None, 0, None) == INVALID        # Y on Wo
+    assert L.tp_attn_out_bwd_shard(r65, P(0), P(1), P(2), P(0), P(4), None) == INVALID  # dO on dY
+    assert L.tp_attn_qkv_bwd_shard(r65, P(0), P(1), P(2), P(3), P(3), None) == INVALID  # dX on dWqkv
 
 
 def test_attn_small_batch_workspace():
@@ -239,11 +279,11 @@ def test_attn_small_batch_workspace():
         # the larger of the two projections' partials: ks * N * cols floats
         assert need >= N * max(s.qkv_cols, 8192) * 4
         r = ctypes.byref(s)
-        assert L.tp_attn_qkv_shard(r, FAKE, FAKE, FAKE + (1 << 30), None, 0, None) == WORKSPACE
-        assert L.tp_attn_out_shard(r, FAKE, FAKE, FAKE + (1 << 30), FAKE, need - 1, None) == WORKSPACE
-        assert L.tp_attn_out_shard(r, FAKE, FAKE, FAKE + (1 << 30), FAKE + 8, need, None) == WORKSPACE  # alignment
-        # workspace on the output
-        assert L.tp_attn_qkv_shard(r, FAKE, FAKE, FAKE + (1 << 30), FAKE + (1 << 30), need, None) == INVALID
+        assert L.tp_attn_qkv_shard(r, P(0), P(1), P(2), None, 0, None) == WORKSPACE
+        assert L.tp_attn_out_shard(r, P(0), P(1), P(2), P(3), need - 1, None) == WORKSPACE
+        assert L.tp_attn_out_shard(r, P(0), P(1), P(2), P(3) + 8, need, None) == WORKSPACE  # alignment
+        assert L.tp_attn_qkv_shard(r, P(0), P(1), P(2), P(2), need, None) == INVALID      # workspace on the output
+        assert L.tp_attn_qkv_shard(r, P(0), P(1), P(2), P(1), need, None) == INVALID      # workspace on the weight
     assert B.attn_workspace_bytes(B.make_attn_shape(65, 8192, 64, 8, 128, 4, 0)) == 0
 
 
