@@ -101,8 +101,7 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev):
         ("down", 2 * N * h * Fi, lambda: B.tp_mlp_down_shard(shape, A, W2, Y)),
         ("reduce_y", 0, lambda: B.tp_mlp_reduce_partials_local([Y] + others_y, Yred, bias=b2)),
         ("down_dgrad_act", 2 * N * h * Fi, lambda: B.tp_mlp_down_dgrad_act_shard(shape, dY, W2, U, G, dU)),
-        ("down_wgrad", 2 * N * h * Fi, lambda: B.tp_mlp_down_wgrad_shard(shape, A, dY, dW2)),
-        ("up_wgrad", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_wgrad_shard(shape, X, dU, dW1, dWg)),
+        ("wgrad", 2 * N * h * Fi * (1 + w.g), lambda: B.tp_mlp_wgrad_shard(shape, X, A, dY, dU, dW1, dW2, dWg)),
         ("up_dgrad", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_dgrad_shard(shape, dU, W1, Wg, dX)),
     ]
     if w.bias:

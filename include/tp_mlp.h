@@ -269,6 +269,16 @@ tp_mlp_status tp_mlp_up_wgrad_shard(const tp_mlp_shape* s, const void* X,
                                     const void* dU_i, float* dW1_i,
                                     float* dWg_i, hipStream_t stream);
 
+/* Both weight gradients in one launch (what tp_mlp_bwd_shard runs): dW2_i
+ * as tp_mlp_down_wgrad_shard and dW1_i (dWg_i) as tp_mlp_up_wgrad_shard,
+ * their tiles sharing the waves of blocks so that neither leaves a partial
+ * last wave on its own.  Each element is summed over the tokens in the same
+ * order as in the separate calls: the results are bitwise the same. */
+tp_mlp_status tp_mlp_wgrad_shard(const tp_mlp_shape* s, const void* X,
+                                 const void* A_i, const void* dY,
+                                 const void* dU_i, float* dW1_i, float* dWg_i,
+                                 float* dW2_i, hipStream_t stream);
+
 /* dgrad through W1: dX_partial = dU_i @ W1_i^T (SwiGLU: [dG | dP] @
  * [Wg_i | W1_i]^T). */
 tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i,

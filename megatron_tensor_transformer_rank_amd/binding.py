@@ -84,6 +84,7 @@ _SIGS = {
     "tp_mlp_down_wgrad_shard": [POINTER(Shape)] + [c_void_p] * 3 + [c_void_p],
     "tp_mlp_up_wgrad_shard": [POINTER(Shape)] + [c_void_p] * 4 + [c_void_p],
     "tp_mlp_up_dgrad_shard": [POINTER(Shape)] + [c_void_p] * 4 + [c_void_p],
+    "tp_mlp_wgrad_shard": [POINTER(Shape)] + [c_void_p] * 7 + [c_void_p],
     "tp_mlp_bias_grad": [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p],
     "tp_attn_qkv_shard": [POINTER(AttnShape)] + [c_void_p] * 4 + [c_size_t, c_void_p],
     "tp_attn_out_shard": [POINTER(AttnShape)] + [c_void_p] * 4 + [c_size_t, c_void_p],
@@ -297,6 +298,15 @@ def tp_mlp_up_wgrad_shard(shape: Shape, X, dU_i, dW1_i, dWg_i=None, stream=None)
     _check("tp_mlp_up_wgrad_shard", lib().tp_mlp_up_wgrad_shard(
         ctypes.byref(shape), _p(X, BF16, N * h, "X"), _p(dU_i, BF16, N * g * Fi, "dU_i"),
         _p(dW1_i, F32, h * Fi, "dW1_i"), _p(dWg_i, F32, h * Fi, "dWg_i", optional=True), _stream(stream)))
+
+
+def tp_mlp_wgrad_shard(shape: Shape, X, A_i, dY, dU_i, dW1_i, dW2_i, dWg_i=None, stream=None):
+    """dW2_i = A_i^T dY and dW1_i (dWg_i) = X^T dU_i in one launch."""
+    N, h, Fi, g = shape.n_tokens, shape.hidden, shape.Fi, shape.g
+    _check("tp_mlp_wgrad_shard", lib().tp_mlp_wgrad_shard(
+        ctypes.byref(shape), _p(X, BF16, N * h, "X"), _p(A_i, BF16, N * Fi, "A_i"), _p(dY, BF16, N * h, "dY"),
+        _p(dU_i, BF16, N * g * Fi, "dU_i"), _p(dW1_i, F32, h * Fi, "dW1_i"),
+        _p(dWg_i, F32, h * Fi, "dWg_i", optional=True), _p(dW2_i, F32, Fi * h, "dW2_i"), _stream(stream)))
 
 
 def tp_mlp_up_dgrad_shard(shape: Shape, dU_i, W1_i, Wg_i, dX_partial, stream=None):

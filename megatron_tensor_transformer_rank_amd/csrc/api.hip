@@ -195,7 +195,7 @@ hipError_t run_dgrad_act(const Dims& d, const void* dY, const void* W2, const vo
   return gemm_launch(GEMM_DGRAD_ACT, d.act, g, num_cu_current(), st);
 }
 
-hipError_t run_wgrad_down(const Dims& d, const void* A, const void* dY, float* dW2, hipStream_t st) {
+GemmArgs wgrad_down_args(const Dims& d, const void* A, const void* dY, float* dW2) {
   GemmArgs g = one_segment((int)d.Fi, (int)d.h, (int)d.N);
   g.a[0] = g.a[1] = cu16(A);  // A_i [N][F_i] is [k][m]
   g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.Fi);
@@ -206,10 +206,10 @@ hipError_t run_wgrad_down(const Dims& d, const void* A, const void* dY, float* d
   g.c0 = g.c1 = dW2;
   g.ldc = d.h;
   g.c_split = (int)d.h;
-  return gemm_launch(GEMM_WGRAD, d.act, g, num_cu_current(), st);
+  return g;
 }
 
-hipError_t run_wgrad_up(const Dims& d, const void* X, const void* dU, float* dW1, float* dWg, hipStream_t st) {
+GemmArgs wgrad_up_args(const Dims& d, const void* X, const void* dU, float* dW1, float* dWg) {
   GemmArgs g = one_segment((int)d.h, (int)(d.g * d.Fi), (int)d.N);
   g.a[0] = g.a[1] = cu16(X);  // X [N][h] is [k][m]
   g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.h);
@@ -221,7 +221,24 @@ hipError_t run_wgrad_up(const Dims& d, const void* X, const void* dU, float* dW1
   g.c1 = dW1;                              // columns [F_i, 2F_i): dP -> dW_up
   g.ldc = d.Fi;
   g.c_split = (int)d.Fi;
-  return gemm_launch(GEMM_WGRAD, d.act, g, num_cu_current(), st);
+  return g;
+}
+
+hipError_t run_wgrad_down(const Dims& d, const void* A, const void* dY, float* dW2, hipStream_t st) {
+  return gemm_launch(GEMM_WGRAD, d.act, wgrad_down_args(d, A, dY, dW2), num_cu_current(), st);
+}
+
+hipError_t run_wgrad_up(const Dims& d, const void* X, const void* dU, float* dW1, float* dWg, hipStream_t st) {
+  return gemm_launch(GEMM_WGRAD, d.act, wgrad_up_args(d, X, dU, dW1, dWg), num_cu_current(), st);
+}
+
+// Both weight gradients in one launch: neither leaves a partial last wave of
+// blocks on its own (each output element is summed over k in the same order
+// as in the separate launches, so the results are bitwise the same).
+hipError_t run_wgrads(const Dims& d, const void* X, const void* A, const void* dY, const void* dU, float* dW1,
+                      float* dWg, float* dW2, hipStream_t st) {
+  return gemm_launch2(GEMM_WGRAD, d.act, wgrad_down_args(d, A, dY, dW2), wgrad_up_args(d, X, dU, dW1, dWg),
+                      num_cu_current(), st);
 }
 
 hipError_t run_dgrad_up(const Dims& d, const void* dU, const void* W1, const void* Wg, void* dX, hipStream_t st) {
@@ -562,6 +579,20 @@ tp_mlp_status tp_mlp_up_wgrad_shard(const tp_mlp_shape* s, const void* X, const 
   return hip_status(run_wgrad_up(d, X, dU_i, dW1_i, dWg_i, stream));
 }
 
+tp_mlp_status tp_mlp_wgrad_shard(const tp_mlp_shape* s, const void* X, const void* A_i, const void* dY,
+                                 const void* dU_i, float* dW1_i, float* dWg_i, float* dW2_i, hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  const bool sw = d.act == ACT_SWIGLU;
+  if (!req(X) || !req(A_i) || !req(dY) || !req(dU_i) || !req(dW1_i) || !req(dW2_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (sw ? !req(dWg_i) : dWg_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t x = (uint64_t)d.N * d.h * 2, w4 = (uint64_t)d.h * d.Fi * 4;
+  if (!spans_ok({{dW1_i, w4}, {dWg_i, w4}, {dW2_i, w4}},
+                {{X, x}, {A_i, (uint64_t)d.N * d.Fi * 2}, {dY, x}, {dU_i, (uint64_t)d.N * d.g * d.Fi * 2}}))
+    return TP_MLP_ERR_INVALID_ARG;
+  return hip_status(run_wgrads(d, X, A_i, dY, dU_i, dW1_i, dWg_i, dW2_i, stream));
+}
+
 tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i, const void* W1_i, const void* Wg_i,
                                     void* dX_partial, hipStream_t stream) {
   Dims d;
@@ -611,8 +642,7 @@ tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X, const void*
   }
 
   hipError_t e = run_dgrad_act(d, dY, W2_i, U_i, G_i, dU_i, stream);
-  if (e == hipSuccess) e = run_wgrad_down(d, A_i, dY, dW2_i, stream);
-  if (e == hipSuccess) e = run_wgrad_up(d, X, dU_i, dW1_i, dWg_i, stream);
+  if (e == hipSuccess) e = run_wgrads(d, X, A_i, dY, dU_i, dW1_i, dWg_i, dW2_i, stream);
   if (e == hipSuccess) e = run_dgrad_up(d, dU_i, W1_i, Wg_i, dX_partial, stream);
   if (e == hipSuccess && db2 != nullptr)
     e = col_sum_launch(cu16(dY), d.N, d.h, db2, static_cast<float*>(workspace), stream);

@@ -58,5 +58,9 @@ struct GemmArgs {
 constexpr uint64_t GEMM_MAX_OPERAND_BYTES = 0xFFFFFF00ull;
 
 hipError_t gemm_launch(GemmKind kind, int act, const GemmArgs& g, int num_cu, hipStream_t st);
+// Two problems of the same kind and activation in one launch (one tile
+// shape, chosen for both): their tiles share the waves, so the partial last
+// wave of each is filled by the other's.
+hipError_t gemm_launch2(GemmKind kind, int act, const GemmArgs& g0, const GemmArgs& g1, int num_cu, hipStream_t st);
 
 }  // namespace tpmlp

@@ -62,10 +62,12 @@ constexpr int GROUP_M = 4;
 // ---------------------------------------------------------------------------
 // Block id -> tile: XCD-contiguous, then grouped along M.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void tile_of(int pid, int nb, int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ int logical_of(int pid, int nb) {
   const int xcd = pid & 7, local = pid >> 3;
   const int per = nb >> 3, rem = nb & 7;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+__device__ __forceinline__ void tile_in(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int group = GROUP_M * tiles_n;
   const int gid = logical / group;
   const int first_m = gid * GROUP_M;
@@ -75,9 +77,13 @@ __device__ __forceinline__ void tile_of(int pid, int nb, int tiles_m, int tiles_
   tn = in_group / gsz;
 }
 
+// One launch may run two problems of the same kind (g0's nb0 tiles, then
+// g1's): the logical tiles of both are laid out over the XCDs together, so
+// neither leaves a partial last wave on its own.  A single problem passes
+// g1 = g0 and nb0 = the grid size.
 template <int BM, int BN, int AK, int BKD, int EPI, int ACT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
-gemm_kernel(const GemmArgs g) {
+gemm_kernel(const GemmArgs g0, const GemmArgs g1, int nb0) {
   constexpr int HM = BM / 2;                 // rows per group
   constexpr int QN = BN / 4;                 // B-region columns per wave
   constexpr int TM = HM / 16, TN = QN / 16;  // 16x16 blocks per wave
@@ -92,8 +98,11 @@ gemm_kernel(const GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = w >> 2, q = w & 3;
+  const int L = logical_of(blockIdx.x, gridDim.x);
+  const bool second = L >= nb0;
+  const GemmArgs g = second ? g1 : g0;
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, g.tiles_m, g.tiles_n, tm, tn);
+  tile_in(second ? L - nb0 : L, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM;
   const int n0 = (BKD == 2) ? tn * (BN / 2) : tn * BN;
 
@@ -436,7 +445,7 @@ struct TileCfg {
 // The 256x192 weight was fitted to timings of both tiles on the weight-
 // gradient, down-projection and up-projection shapes of the 7B-, GPT-3- and
 // 70B-class shards; the smaller tiles' weights are estimates.
-TileCfg choose_tile(int M, int N_cols, bool swiglu_fwd, int num_cu) {
+TileCfg choose_tile(int M, int N_cols, bool swiglu_fwd, int num_cu, int M1 = 0, int N1 = 0) {
   static const TileCfg cands[] = {{256, 256}, {256, 192}, {256, 128}, {128, 256}, {128, 128}};
   static const double eff[] = {1.0, 0.87, 0.72, 0.72, 0.5};
   double best = 1e300;
@@ -445,7 +454,8 @@ TileCfg choose_tile(int M, int N_cols, bool swiglu_fwd, int num_cu) {
     const int bm = cands[c].bm, bn = cands[c].bn;
     if (swiglu_fwd && bn == 192) continue;
     const int cols_per_tile = swiglu_fwd ? bn / 2 : bn;
-    const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N_cols + cols_per_tile - 1) / cols_per_tile);
+    const int64_t tiles = (int64_t)((M + bm - 1) / bm) * ((N_cols + cols_per_tile - 1) / cols_per_tile) +
+                          (int64_t)((M1 + bm - 1) / bm) * ((N1 + cols_per_tile - 1) / cols_per_tile);
     const int64_t waves = (tiles + num_cu - 1) / num_cu;
     const double cost = (double)waves * bm * bn / eff[c];
     if (cost < best * 0.999) {
@@ -456,52 +466,72 @@ TileCfg choose_tile(int M, int N_cols, bool swiglu_fwd, int num_cu) {
   return bc;
 }
 
+// g1 == nullptr: one problem
 template <int BM, int BN, int AK, int BKD, int EPI, int ACT>
-hipError_t launch_cfg(GemmArgs g, hipStream_t st) {
+hipError_t launch_cfg(GemmArgs g0, const GemmArgs* g1p, hipStream_t st) {
   const int cols_per_tile = (BKD == 2) ? BN / 2 : BN;
-  g.tiles_m = (g.M + BM - 1) / BM;
-  g.tiles_n = (g.N + cols_per_tile - 1) / cols_per_tile;
-  const int64_t nb = (int64_t)g.tiles_m * g.tiles_n;
+  auto tiles = [&](GemmArgs& g) {
+    g.tiles_m = (g.M + BM - 1) / BM;
+    g.tiles_n = (g.N + cols_per_tile - 1) / cols_per_tile;
+    return (int64_t)g.tiles_m * g.tiles_n;
+  };
+  GemmArgs g1 = g1p ? *g1p : g0;
+  const int64_t nb0 = tiles(g0);
+  const int64_t nb = g1p ? nb0 + tiles(g1) : nb0;
+  if (!g1p) g1 = g0;
   if (nb <= 0) return hipSuccess;
   if (nb > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BKD, EPI, ACT>), dim3((unsigned)nb), dim3(NT), 0, st, g);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BKD, EPI, ACT>), dim3((unsigned)nb), dim3(NT), 0, st, g0, g1,
+                     (int)nb0);
   return hipGetLastError();
 }
 
 template <int AK, int BKD, int EPI, int ACT>
-hipError_t launch_any(const GemmArgs& g, TileCfg t, hipStream_t st) {
-  if (t.bm == 256 && t.bn == 256) return launch_cfg<256, 256, AK, BKD, EPI, ACT>(g, st);
+hipError_t launch_any(const GemmArgs& g, const GemmArgs* g1, TileCfg t, hipStream_t st) {
+  if (t.bm == 256 && t.bn == 256) return launch_cfg<256, 256, AK, BKD, EPI, ACT>(g, g1, st);
   if constexpr (BKD != 2) {
-    if (t.bm == 256 && t.bn == 192) return launch_cfg<256, 192, AK, BKD, EPI, ACT>(g, st);
+    if (t.bm == 256 && t.bn == 192) return launch_cfg<256, 192, AK, BKD, EPI, ACT>(g, g1, st);
   }
-  if (t.bm == 256 && t.bn == 128) return launch_cfg<256, 128, AK, BKD, EPI, ACT>(g, st);
-  if (t.bm == 128 && t.bn == 256) return launch_cfg<128, 256, AK, BKD, EPI, ACT>(g, st);
-  return launch_cfg<128, 128, AK, BKD, EPI, ACT>(g, st);
+  if (t.bm == 256 && t.bn == 128) return launch_cfg<256, 128, AK, BKD, EPI, ACT>(g, g1, st);
+  if (t.bm == 128 && t.bn == 256) return launch_cfg<128, 256, AK, BKD, EPI, ACT>(g, g1, st);
+  return launch_cfg<128, 128, AK, BKD, EPI, ACT>(g, g1, st);
+}
+
+}  // namespace
+
+namespace {
+
+hipError_t launch_kind(GemmKind kind, int act, const GemmArgs& g, const GemmArgs* g1, TileCfg t, hipStream_t st) {
+  switch (kind) {
+    case GEMM_UP_ACT:
+      return act == ACT_RELU ? launch_any<0, 1, EPI_ACT_FWD, ACT_RELU>(g, g1, t, st)
+                             : launch_any<0, 1, EPI_ACT_FWD, ACT_GELU>(g, g1, t, st);
+    case GEMM_UP_SWIGLU:
+      return launch_any<0, 2, EPI_SWIGLU_FWD, ACT_SWIGLU>(g, g1, t, st);
+    case GEMM_DOWN:
+      return launch_any<0, 1, EPI_STORE_BF16, 0>(g, g1, t, st);
+    case GEMM_DGRAD_ACT:
+      if (act == ACT_SWIGLU) return launch_any<0, 0, EPI_SWIGLU_BWD, ACT_SWIGLU>(g, g1, t, st);
+      return act == ACT_RELU ? launch_any<0, 0, EPI_ACT_BWD, ACT_RELU>(g, g1, t, st)
+                             : launch_any<0, 0, EPI_ACT_BWD, ACT_GELU>(g, g1, t, st);
+    case GEMM_WGRAD:
+      return launch_any<1, 1, EPI_STORE_F32_SPLIT, 0>(g, g1, t, st);
+    case GEMM_DGRAD:
+      return launch_any<0, 0, EPI_STORE_BF16, 0>(g, g1, t, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t gemm_launch(GemmKind kind, int act, const GemmArgs& g, int num_cu, hipStream_t st) {
-  const bool sw = kind == GEMM_UP_SWIGLU;
-  const TileCfg t = choose_tile(g.M, g.N, sw, num_cu);
-  switch (kind) {
-    case GEMM_UP_ACT:
-      return act == ACT_RELU ? launch_any<0, 1, EPI_ACT_FWD, ACT_RELU>(g, t, st)
-                             : launch_any<0, 1, EPI_ACT_FWD, ACT_GELU>(g, t, st);
-    case GEMM_UP_SWIGLU:
-      return launch_any<0, 2, EPI_SWIGLU_FWD, ACT_SWIGLU>(g, t, st);
-    case GEMM_DOWN:
-      return launch_any<0, 1, EPI_STORE_BF16, 0>(g, t, st);
-    case GEMM_DGRAD_ACT:
-      if (act == ACT_SWIGLU) return launch_any<0, 0, EPI_SWIGLU_BWD, ACT_SWIGLU>(g, t, st);
-      return act == ACT_RELU ? launch_any<0, 0, EPI_ACT_BWD, ACT_RELU>(g, t, st)
-                             : launch_any<0, 0, EPI_ACT_BWD, ACT_GELU>(g, t, st);
-    case GEMM_WGRAD:
-      return launch_any<1, 1, EPI_STORE_F32_SPLIT, 0>(g, t, st);
-    case GEMM_DGRAD:
-      return launch_any<0, 0, EPI_STORE_BF16, 0>(g, t, st);
-  }
-  return hipErrorInvalidValue;
+  const TileCfg t = choose_tile(g.M, g.N, kind == GEMM_UP_SWIGLU, num_cu);
+  return launch_kind(kind, act, g, nullptr, t, st);
+}
+
+hipError_t gemm_launch2(GemmKind kind, int act, const GemmArgs& g0, const GemmArgs& g1, int num_cu, hipStream_t st) {
+  const TileCfg t = choose_tile(g0.M, g0.N, kind == GEMM_UP_SWIGLU, num_cu, g1.M, g1.N);
+  return launch_kind(kind, act, g0, &g1, t, st);
 }
 
 }  // namespace tpmlp

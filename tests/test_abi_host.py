@@ -164,6 +164,11 @@ def test_step_entry_points_validate():
     assert L.tp_mlp_up_wgrad_shard(r, P(0), P(1), P(2), P(2) + 64, None) == INVALID        # dWg inside dW1
     assert L.tp_mlp_up_dgrad_shard(r, P(0), P(1), P(2), P(2), None) == INVALID             # dX on Wg
     assert L.tp_mlp_bias_grad(P(0), 4, 8, P(1), P(0), 1 << 20, None) == INVALID            # workspace on dY
+    wg = L.tp_mlp_wgrad_shard                     # (s, X, A, dY, dU, dW1, dWg, dW2)
+    assert wg(r, P(0), P(1), P(2), P(3), P(4), None, P(6), None) == INVALID               # SwiGLU: dWg needed
+    assert wg(r, P(0), P(1), P(2), P(3), P(4), P(5), P(3), None) == INVALID               # dW2 on dU
+    assert wg(r, P(0), P(1), P(2), P(3), P(4), P(4) + 1024, P(6), None) == INVALID        # dWg inside dW1
+    assert wg(r, P(0), None, P(2), P(3), P(4), P(5), P(6), None) == INVALID
 
 
 def test_reduce_rejects_partial_overlap():

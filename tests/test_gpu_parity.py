@@ -243,7 +243,37 @@ def test_step_entry_points_match_composite():
     B.tp_mlp_up_dgrad_shard(sh, dU, s.W1, None, dX)
     ws = B.alloc_workspace(B.bias_grad_workspace_bytes(N, h))
     B.tp_mlp_bias_grad(dYd, db2, ws)
+    # both weight gradients in one launch (what the composite runs)
+    dW1g, dW2g = torch.empty_like(s.dW1), torch.empty_like(s.dW2)
+    B.tp_mlp_wgrad_shard(sh, s.X, A, dYd, dU, dW1g, dW2g)
     torch.cuda.synchronize()
     for a, b, n in [(A, s.A, "A"), (U, s.U, "U"), (Y, s.Y, "Y"), (dU, s.dU, "dU"), (dW1, s.dW1, "dW1"),
-                    (dW2, s.dW2, "dW2"), (dX, s.dX, "dX"), (db2, s.db2, "db2")]:
+                    (dW2, s.dW2, "dW2"), (dX, s.dX, "dX"), (db2, s.db2, "db2"), (dW1g, s.dW1, "dW1 grouped"),
+                    (dW2g, s.dW2, "dW2 grouped")]:
         assert torch.equal(a, b), n
+
+
+@pytest.mark.parametrize("N,h,F,t", [(4096, 4096, 11008, 2), (300, 1032, 2 * 2056, 2)])
+def test_grouped_weight_gradients_bitwise_separate(N, h, F, t):
+    """SwiGLU: the one-launch weight gradients (dW2, dWg, dW_up) equal the two
+    separate launches bitwise (those are checked against the oracle in the
+    group tests), at the 7B shard's shape (the two gradients have 1.4 and 2.7
+    waves of tiles alone) and at a ragged one."""
+    Fi = F // t
+    s = B.make_shape(N, h, F, t, 0, "swiglu")
+    X, dY = bf16_dev(I.gen_x(510, N, h)), bf16_dev(I.gen_dy(510, N, h))
+    A = bf16_dev(I.normal_bf16([510, 7], (N, Fi)))
+    dU = bf16_dev(I.normal_bf16([510, 8], (N, 2 * Fi)))
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = []
+    for grouped in (False, True):
+        dW1, dWg, dW2 = torch.empty(h, Fi, **f32), torch.empty(h, Fi, **f32), torch.empty(Fi, h, **f32)
+        if grouped:
+            B.tp_mlp_wgrad_shard(s, X, A, dY, dU, dW1, dW2, dWg)
+        else:
+            B.tp_mlp_down_wgrad_shard(s, A, dY, dW2)
+            B.tp_mlp_up_wgrad_shard(s, X, dU, dW1, dWg)
+        torch.cuda.synchronize()
+        out.append((dW1, dWg, dW2))
+    for a, b in zip(*out):
+        assert torch.equal(a, b)
