@@ -78,6 +78,31 @@ def test_fwd_rejects_bad_shapes(shape, expect):
     assert _fwd(shape) == expect
 
 
+@pytest.mark.parametrize("shape", [
+    B.make_shape(1 << 18, 8192, 16, 2, 0, "gelu"),           # X: 2^31 elements, past one buffer resource
+    B.make_shape(16, 65536, 2 * 65536, 2, 0, "relu"),        # W1_i: 2^32 elements
+    B.make_shape(1 << 16, 64, 2 * (1 << 15), 2, 0, "swiglu"),  # [dG | dP]: N * 2F_i = 2^32 elements
+], ids=["X", "W1", "dU"])
+def test_operands_past_the_buffer_limit_are_unsupported(shape):
+    """Every bf16 operand a GEMM reads is addressed through one buffer
+    resource (< 4 GiB): larger shapes are UNSUPPORTED for every entry point,
+    before any launch."""
+    L = B.lib()
+    r = ctypes.byref(shape)
+    assert _fwd(shape) == UNSUPPORTED
+    assert L.tp_mlp_bwd_shard(r, *([P(k) for k in range(13)] + [None, None, 0, None])) == UNSUPPORTED
+    assert L.tp_mlp_up_act_shard(r, P(0), P(1), P(2), P(3), P(4), P(5), None) == UNSUPPORTED
+    assert L.tp_mlp_wgrad_shard(r, P(0), P(1), P(2), P(3), P(4), P(5), P(6), None) == UNSUPPORTED
+
+
+def test_attn_operands_past_the_buffer_limit_are_unsupported():
+    s = B.make_attn_shape(1 << 18, 8192, 64, 8, 128, 4, 0)    # X: 2^31 elements
+    r = ctypes.byref(s)
+    assert B.lib().tp_attn_qkv_shard(r, P(0), P(1), P(2), None, 0, None) == UNSUPPORTED
+    assert B.lib().tp_attn_qkv_bwd_shard(r, P(0), P(1), P(2), P(3), P(4), None) == UNSUPPORTED
+    assert B.attn_workspace_bytes(s) == 0
+
+
 def test_fwd_rejects_bad_pointers():
     s = B.make_shape(4, 64, 128, 2, 0, "gelu")
     assert _fwd(s, X=None) == INVALID
