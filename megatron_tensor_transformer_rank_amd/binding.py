@@ -15,7 +15,9 @@ from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_voi
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so")
+# TPMLP_LIB selects another build of the library (e.g. the host-sanitized one
+# of build.py --host-sanitize); by default the in-tree libtpmlp.so.
+LIB_PATH = os.environ.get("TPMLP_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so")
 
 ACTS = {"relu": 0, "gelu": 1, "swiglu": 2}
 STATUS = {0: "TP_MLP_OK", 1: "TP_MLP_ERR_INVALID_ARG", 2: "TP_MLP_ERR_UNSUPPORTED",

@@ -1,10 +1,21 @@
 """Build libtpmlp.so (gfx950) in-tree with hipcc.
 
     python -m megatron_tensor_transformer_rank_amd.build
+    python -m megatron_tensor_transformer_rank_amd.build --host-sanitize
 
 Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
 parallel) and the objects are linked into ``libtpmlp.so`` next to this file.
 hipcc cross-compiles for gfx950, so this runs on a machine without a GPU.
+
+``--host-sanitize`` builds ``_build/host_sanitize/libtpmlp.so`` instead: the
+host code (argument validation, dispatch) instrumented with AddressSanitizer
+and UndefinedBehaviorSanitizer, device code as usual.  It is for the host-only
+ABI tests on a machine without a GPU, with clang's ASan runtime preloaded:
+
+    LD_PRELOAD=$(ls /opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so) \
+    ASAN_OPTIONS=detect_leaks=0:verify_asan_link_order=0 UBSAN_OPTIONS=halt_on_error=1 \
+    TPMLP_LIB=megatron_tensor_transformer_rank_amd/_build/host_sanitize/libtpmlp.so \
+    python -m pytest -s tests/test_abi_host.py
 """
 from __future__ import annotations
 
@@ -33,9 +44,14 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src[:-4] + ".o")
-    cmd = [HIPCC, *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# host-side sanitizers only (each -fsanitize= right after -Xarch_host)
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(out_dir, src[:-4] + ".o")
+    cmd = [HIPCC, *CXXFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -58,6 +74,26 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def build_host_sanitized(verbose: bool = True) -> str:
+    out = os.path.join(BUILD, "host_sanitize")
+    os.makedirs(out, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = list(ex.map(lambda f: _compile(f, out, SANITIZE + ["-O1", "-g"]), srcs))
+    lib = os.path.join(out, "libtpmlp.so")
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libasan", "-o", lib, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {lib} (host code under ASan + UBSan)", flush=True)
+    return lib
+
+
 if __name__ == "__main__":
-    build()
+    if "--host-sanitize" in sys.argv[1:]:
+        build_host_sanitized()
+    else:
+        build()
     sys.exit(0)

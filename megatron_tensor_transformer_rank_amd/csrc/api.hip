@@ -4,6 +4,7 @@
 // Every check runs before the first launch, so an invalid call enqueues
 // nothing.  No exception crosses the ABI; nothing is printed.
 #include <atomic>
+#include <cstring>
 #include <initializer_list>
 #include <new>
 
@@ -450,7 +451,11 @@ bool stash_ok(const float* mean, const float* rstd, int64_t rows, const void* y,
 extern "C" {
 
 const char* tp_mlp_status_string(tp_mlp_status st) {
-  switch (st) {
+  // a C caller may pass any int: read it as one (an out-of-range value of
+  // the enum type would be undefined in C++)
+  int v;
+  std::memcpy(&v, &st, sizeof v);
+  switch (v) {
     case TP_MLP_OK: return "ok";
     case TP_MLP_ERR_INVALID_ARG: return "invalid argument (pointer, shape, alignment, rank or activation)";
     case TP_MLP_ERR_UNSUPPORTED: return "valid but unsupported option";
