@@ -1,0 +1,127 @@
+"""Guard bands around the outputs of the decode, small-batch, LayerNorm,
+attention small-batch and sequence-parallel kernels: every output buffer is
+a view into a larger buffer filled with a canary value, and after two runs
+(whose outputs must be bitwise identical) the canaries must be untouched.
+Shapes have ragged tails (columns past the last full strip or chunk)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_transformer_rank_amd import binding as B
+from megatron_tensor_transformer_rank_amd import inputs as I
+from tests.helpers import bf16_dev
+
+pytestmark = pytest.mark.gpu
+
+PAD = 4096
+CANARY = 7.0
+
+
+class Guards:
+    def __init__(self):
+        self.bufs = {}
+
+    def out(self, name, shape, dtype=torch.bfloat16):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * PAD,), CANARY, dtype=dtype, device="cuda")
+        self.bufs[name] = (buf, n, shape)
+        return buf[PAD:PAD + n].view(*shape)
+
+    def view(self, name):
+        buf, n, shape = self.bufs[name]
+        return buf[PAD:PAD + n].view(*shape)
+
+    def check(self, first):
+        for k, (buf, n, _) in self.bufs.items():
+            assert torch.equal(self.view(k), first[k]), f"{k} differs between runs"
+            assert torch.all(buf[:PAD] == CANARY) and torch.all(buf[-PAD:] == CANARY), f"{k}: write outside buffer"
+
+    def snapshot(self):
+        return {k: self.view(k).clone() for k in self.bufs}
+
+
+def twice(fn, g):
+    fn()
+    torch.cuda.synchronize()
+    first = g.snapshot()
+    fn()
+    torch.cuda.synchronize()
+    g.check(first)
+
+
+@pytest.mark.parametrize("N", [1, 17])
+def test_decode_and_small_batch_guard_bands(N):
+    print(f"[guard] forward N={N}", file=sys.stderr, flush=True)
+    h, F, t = 1032, 2 * 776, 2           # h and F_i past the last 512- / 256-column strip
+    Fi = F // t
+    s = B.make_shape(N, h, F, t, 0, "swiglu")
+    W1b, W2b, Wgb = I.gen_full_weights(600, h, F, t, True)
+    c = oracle.column_block(0, t, F)
+    X = bf16_dev(I.gen_x(600 + N, N, h))
+    W1, W2, Wg = (bf16_dev(np.ascontiguousarray(a)) for a in (W1b[:, c], W2b[c, :], Wgb[:, c]))
+    g = Guards()
+    Y, A, U, G = g.out("Y", (N, h)), g.out("A", (N, Fi)), g.out("U", (N, Fi)), g.out("G", (N, Fi))
+    ws = B.alloc_workspace(B.workspace_bytes(s, False))
+    twice(lambda: B.tp_mlp_fwd_shard(s, X, W1, Wg, W2, Y, A, U, G, ws), g)
+
+
+def test_layernorm_guard_bands():
+    print("[guard] layernorm", file=sys.stderr, flush=True)
+    t, rows, cols = 4, 36, 2056          # 9 rows per rank; 257 chunks of 8: one past 256 threads
+    n = rows // t
+    parts = [bf16_dev(I.normal_bf16([601, k], (rows, cols))) for k in range(t)]
+    gm, bt, bias = bf16_dev(I.gen_ln_weight(601, cols)), bf16_dev(I.gen_ln_bias(601, cols)), bf16_dev(I.gen_b2(601, cols))
+    res, dy, dres = (bf16_dev(I.normal_bf16([601, 10 + j], (n, cols))) for j in range(3))
+    g = Guards()
+    z, y, dx = g.out("z", (n, cols)), g.out("y", (n, cols)), g.out("dx", (n, cols))
+    mean, rstd = g.out("mean", (n,), torch.float32), g.out("rstd", (n,), torch.float32)
+    dg, db = g.out("dgamma", (cols,), torch.float32), g.out("dbeta", (cols,), torch.float32)
+    ws = B.alloc_workspace(B.layernorm_bwd_workspace_bytes(n, cols))
+
+    def run():
+        B.tp_sp_reduce_scatter_layernorm_local(parts, 2, z, gm, y, bias=bias, residual=res, beta=bt, mean=mean,
+                                               rstd=rstd)
+        B.tp_sp_layernorm_bwd(z, gm, mean, rstd, dy, dx, dg, dbeta=db, dres=dres, workspace=ws)
+    twice(run, g)
+    gs = Guards()
+    total = gs.out("sum", (cols,), torch.float32)
+    grads = [torch.randn(cols, device="cuda") for _ in range(3)]
+    twice(lambda: B.tp_sp_sum_grads_local(grads, total), gs)
+
+
+def test_attention_small_batch_guard_bands():
+    print("[guard] attention small batch", file=sys.stderr, flush=True)
+    N, h, nh, nkv, d, t = 33, 1032, 16, 4, 72, 4    # 72-wide heads: qkv columns not a multiple of 256
+    s = B.make_attn_shape(N, h, nh, nkv, d, t, 1)
+    X = bf16_dev(I.normal_bf16([602, 0], (N, h)))
+    Wqkv = bf16_dev(I.normal_bf16([602, 1], (h, s.qkv_cols), 0.02))
+    O = bf16_dev(I.normal_bf16([602, 2], (N, s.q_cols)))
+    Wo = bf16_dev(I.normal_bf16([602, 3], (s.q_cols, h), 0.02))
+    g = Guards()
+    QKV, Y = g.out("QKV", (N, s.qkv_cols)), g.out("Y", (N, h))
+    ws = B.alloc_workspace(B.attn_workspace_bytes(s))
+
+    def run():
+        B.tp_attn_qkv_shard(s, X, Wqkv, QKV, workspace=ws)
+        B.tp_attn_out_shard(s, O, Wo, Y, workspace=ws)
+    twice(run, g)
+
+
+def test_sequence_parallel_boundary_guard_bands():
+    print("[guard] reduce-scatter / all-gather", file=sys.stderr, flush=True)
+    t, rows, cols = 3, 27, 264
+    parts = [bf16_dev(I.normal_bf16([603, k], (rows, cols))) for k in range(t)]
+    g = Guards()
+    rs = g.out("rs", (rows // t, cols))
+    ag = g.out("ag", (rows, cols))
+    shards = [bf16_dev(I.normal_bf16([603, 10 + k], (rows // t, cols))) for k in range(t)]
+
+    def run():
+        B.tp_mlp_reduce_scatter_local(parts, rs, 1, bias=bf16_dev(I.gen_b2(603, cols)))
+        B.tp_mlp_all_gather_local(shards, ag)
+    twice(run, g)
