@@ -7,12 +7,13 @@
 // rank's s/t token rows, and the weights shared by those blocks need their
 // gradients summed over the group).
 //
-// All HBM-bound streams of 16-byte chunks.  A 256-thread block owns a whole
-// row (LayerNorm needs the row's statistics): thread i holds chunks
-// i, i + 256, ... of the row in registers, so every element is read once and
+// All HBM-bound streams of 16-byte chunks.  A block owns a whole row
+// (LayerNorm needs the row's statistics), 256 threads, or 1024 when there are
+// fewer than 1024 rows: thread i holds chunks i, i + NT, ... of the row in
+// registers, so every element is read once and
 // the statistics come from registers in two passes (mean, then the biased
 // variance of the centred values).  Block sums: a butterfly over the 64 lanes
-// (every lane ends with the same bits), then the 4 waves in wave order, so
+// (every lane ends with the same bits), then the waves in wave order, so
 // results are deterministic.  The fused forward adds the t partial sums in
 // float32 in rank order, then the bias, then the residual, rounds z to bf16,
 // stores it, and normalises that stored value: bit for bit what a separate
@@ -65,29 +66,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Sum of v over the block; red is LN_WAVES floats of LDS used by this call
-// only.  Every thread returns the same value.
+// Sum of v over a block of NW waves; red is NW floats of LDS used by this
+// call only.  Every thread returns the same value.
+template <int NW>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float s = red[0];
 #pragma unroll
-  for (int w = 1; w < LN_WAVES; ++w) s += red[w];
+  for (int w = 1; w < NW; ++w) s += red[w];
   return s;
 }
 
 }  // namespace
 
-// One row per block.  FUSED: the row is row0 + blockIdx.x of the partial sums
-// (plus bias and residual), stored to z; otherwise it is row blockIdx.x of x.
-template <int J, bool FUSED>
-__global__ void __launch_bounds__(LN_THREADS)
+// One row per block of NT threads.  FUSED: the row is row0 + blockIdx.x of
+// the partial sums (plus bias and residual), stored to z; otherwise it is row
+// blockIdx.x of x.
+template <int NT, int J, bool FUSED>
+__global__ void __launch_bounds__(NT)
 ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ bias, const uint16_t* residual,
               uint16_t* z, const uint16_t* x, int cols8, int cols, float eps, const uint16_t* __restrict__ gamma,
               const uint16_t* __restrict__ beta, uint16_t* y, float* __restrict__ mean_out,
               float* __restrict__ rstd_out) {
-  __shared__ float red[2][LN_WAVES];
+  __shared__ float red[2][NT / 64];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t base = row * cols8;
@@ -103,14 +106,14 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
     u32x4 rv[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int q = tid + j * LN_THREADS;
+      const int q = tid + j * NT;
       rv[j] = (residual && q < cols8) ? ld_nt(residual, base + q) : u32x4{0u, 0u, 0u, 0u};
     }
     for (int r0 = 0; r0 < t; r0 += LN_BATCH) {
       u32x4 c[J][LN_BATCH];
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int q = tid + j * LN_THREADS;
+        const int q = tid + j * NT;
 #pragma unroll
         for (int b = 0; b < LN_BATCH; ++b)
           c[j][b] = (r0 + b < t && q < cols8) ? ld_nt(pp.p[r0 + b], in_base + q) : u32x4{0u, 0u, 0u, 0u};
@@ -123,7 +126,7 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int q = tid + j * LN_THREADS;
+      const int q = tid + j * NT;
       if (q < cols8) {
         if (bias) add8(v[j], ld_c(bias, q));
         if (residual) add8(v[j], rv[j]);
@@ -138,7 +141,7 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
   } else {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int q = tid + j * LN_THREADS;
+      const int q = tid + j * NT;
       if (q < cols8) unpack8(ld_nt(x, base + q), v[j]);
     }
   }
@@ -148,11 +151,11 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
   for (int j = 0; j < J; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) s += v[j][e];
-  const float mean = block_sum(s, red[0]) / (float)cols;
+  const float mean = block_sum<NT / 64>(s, red[0]) / (float)cols;
   float d = 0.f;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    if (tid + j * LN_THREADS < cols8) {
+    if (tid + j * NT < cols8) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float c = v[j][e] - mean;
@@ -160,12 +163,12 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
       }
     }
   }
-  const float var = block_sum(d, red[1]) / (float)cols;
+  const float var = block_sum<NT / 64>(d, red[1]) / (float)cols;
   const float rstd = 1.0f / sqrtf(var + eps);
 
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int q = tid + j * LN_THREADS;
+    const int q = tid + j * NT;
     if (q < cols8) {
       float g[8], b[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, o[8];
       unpack8(ld_c(gamma, q), g);
@@ -181,14 +184,14 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
   }
 }
 
-// One row per block: xhat = (x - mean) * rstd, g = dy * gamma,
+// One row per block of NT threads: xhat = (x - mean) * rstd, g = dy * gamma,
 // dx = rstd * (g - sum(g)/h - xhat * sum(g * xhat)/h) (+ dres).
-template <int J>
-__global__ void __launch_bounds__(LN_THREADS)
+template <int NT, int J>
+__global__ void __launch_bounds__(NT)
 ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
                  const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int cols8,
                  int cols) {
-  __shared__ float red[2][LN_WAVES];
+  __shared__ float red[2][NT / 64];
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
   const int64_t base = r * cols8;
@@ -197,7 +200,7 @@ ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const fl
   u32x4 xv[J], dv[J], rv[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int q = tid + j * LN_THREADS;
+    const int q = tid + j * NT;
     xv[j] = q < cols8 ? ld_nt(x, base + q) : u32x4{0u, 0u, 0u, 0u};
     dv[j] = q < cols8 ? ld_nt(dy, base + q) : u32x4{0u, 0u, 0u, 0u};
     rv[j] = (dres && q < cols8) ? ld_nt(dres, base + q) : u32x4{0u, 0u, 0u, 0u};
@@ -205,7 +208,7 @@ ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const fl
   float s1 = 0.f, s2 = 0.f;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int q = tid + j * LN_THREADS;
+    const int q = tid + j * NT;
     if (q < cols8) {
       float xf[8], df[8], gm[8];
       unpack8(xv[j], xf);
@@ -219,11 +222,11 @@ ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const fl
       }
     }
   }
-  const float m1 = block_sum(s1, red[0]) / (float)cols;
-  const float m2 = block_sum(s2, red[1]) / (float)cols;
+  const float m1 = block_sum<NT / 64>(s1, red[0]) / (float)cols;
+  const float m2 = block_sum<NT / 64>(s2, red[1]) / (float)cols;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int q = tid + j * LN_THREADS;
+    const int q = tid + j * NT;
     if (q < cols8) {
       float xf[8], df[8], gm[8], o[8];
       unpack8(xv[j], xf);
@@ -347,12 +350,18 @@ sum_f32_kernel(GradPtrs g, int t, int64_t n4, float* __restrict__ out) {
 
 namespace {
 
-// chunks per thread, the smallest instantiated J >= cols8 / 256
-int ln_j(int64_t cols) {
-  const int64_t need = (cols / 8 + LN_THREADS - 1) / LN_THREADS;
+// Threads per row: 1024 (16 waves) when there are few rows, so that every
+// CU still holds enough loads in flight; 256 otherwise.  A function of the
+// row count only, so the fused and the separate forward pick the same.
+constexpr int LN_FEW_ROWS = 1024;
+int ln_nt(int64_t rows) { return rows < LN_FEW_ROWS ? 1024 : LN_THREADS; }
+
+// chunks per thread, the smallest instantiated J >= cols8 / nt
+int ln_j(int64_t cols, int nt) {
+  const int64_t need = (cols / 8 + nt - 1) / nt;
   static const int js[] = {1, 2, 3, 4, 6, 8};
   for (int j : js)
-    if (j >= need) return j;
+    if (j >= need && (nt == LN_THREADS || j <= 2)) return j;
   return 0;
 }
 
@@ -374,18 +383,26 @@ hipError_t fwd_dispatch(const PartialPtrs& pp, int t, int64_t rows, int64_t cols
                         hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int cols8 = (int)(cols / 8);
-  const dim3 grid((unsigned)rows), blk(LN_THREADS);
-#define LN_FWD(J)                                                                                              \
-  hipLaunchKernelGGL((ln_fwd_kernel<J, FUSED>), grid, blk, 0, st, pp, t, row0, bias, residual, z, x, cols8,   \
-                     (int)cols, eps, gamma, beta, y, mean, rstd)
-  switch (ln_j(cols)) {
-    case 1: LN_FWD(1); break;
-    case 2: LN_FWD(2); break;
-    case 3: LN_FWD(3); break;
-    case 4: LN_FWD(4); break;
-    case 6: LN_FWD(6); break;
-    case 8: LN_FWD(8); break;
-    default: return hipErrorInvalidValue;
+  const int nt = ln_nt(rows);
+  const dim3 grid((unsigned)rows), blk(nt);
+#define LN_FWD(NT, J)                                                                                          \
+  hipLaunchKernelGGL((ln_fwd_kernel<NT, J, FUSED>), grid, blk, 0, st, pp, t, row0, bias, residual, z, x,      \
+                     cols8, (int)cols, eps, gamma, beta, y, mean, rstd)
+  const int j = ln_j(cols, nt);
+  if (nt == 1024) {
+    if (j == 1) LN_FWD(1024, 1);
+    else if (j == 2) LN_FWD(1024, 2);
+    else return hipErrorInvalidValue;
+  } else {
+    switch (j) {
+      case 1: LN_FWD(LN_THREADS, 1); break;
+      case 2: LN_FWD(LN_THREADS, 2); break;
+      case 3: LN_FWD(LN_THREADS, 3); break;
+      case 4: LN_FWD(LN_THREADS, 4); break;
+      case 6: LN_FWD(LN_THREADS, 6); break;
+      case 8: LN_FWD(LN_THREADS, 8); break;
+      default: return hipErrorInvalidValue;
+    }
   }
 #undef LN_FWD
   return hipGetLastError();
@@ -435,17 +452,25 @@ hipError_t ln_bwd_launch(const uint16_t* x, const uint16_t* gamma, const float* 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int cols8 = (int)(cols / 8);
-#define LN_BWD(J)                                                                                                \
-  hipLaunchKernelGGL((ln_bwd_dx_kernel<J>), dim3((unsigned)rows), blk, 0, st, x, gamma, mean, rstd, dy, dres,   \
-                     dx, cols8, (int)cols)
-  switch (ln_j(cols)) {
-    case 1: LN_BWD(1); break;
-    case 2: LN_BWD(2); break;
-    case 3: LN_BWD(3); break;
-    case 4: LN_BWD(4); break;
-    case 6: LN_BWD(6); break;
-    case 8: LN_BWD(8); break;
-    default: return hipErrorInvalidValue;
+  const int nt = ln_nt(rows);
+#define LN_BWD(NT, J)                                                                                            \
+  hipLaunchKernelGGL((ln_bwd_dx_kernel<NT, J>), dim3((unsigned)rows), dim3(NT), 0, st, x, gamma, mean, rstd, dy, \
+                     dres, dx, cols8, (int)cols)
+  const int j = ln_j(cols, nt);
+  if (nt == 1024) {
+    if (j == 1) LN_BWD(1024, 1);
+    else if (j == 2) LN_BWD(1024, 2);
+    else return hipErrorInvalidValue;
+  } else {
+    switch (j) {
+      case 1: LN_BWD(LN_THREADS, 1); break;
+      case 2: LN_BWD(LN_THREADS, 2); break;
+      case 3: LN_BWD(LN_THREADS, 3); break;
+      case 4: LN_BWD(LN_THREADS, 4); break;
+      case 6: LN_BWD(LN_THREADS, 6); break;
+      case 8: LN_BWD(LN_THREADS, 8); break;
+      default: return hipErrorInvalidValue;
+    }
   }
 #undef LN_BWD
   return hipGetLastError();

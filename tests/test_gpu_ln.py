@@ -5,7 +5,8 @@ Checked:
 
 * tp_sp_layernorm_fwd / tp_sp_layernorm_bwd on one rank's block at widths
   on both sides of every per-thread chunk count (8 ... 16384 columns, ragged
-  tails), 1 to 300 rows, with and without the bias, the stash, dbeta and the
+  tails), 1 to 1030 rows (both the 1024-thread rows of small blocks and the
+  256-thread rows of 1024 rows and more), with and without the bias, the stash, dbeta and the
   residual branch's gradient; constant rows (zero variance) and rows with a
   large mean;
 * the fused reduce-scatter + LayerNorm: z and y against the oracle, and bit
@@ -87,7 +88,9 @@ def run_ln(wid, rows, cols, with_beta=True, stash=True, with_dres=False, with_db
 # boundaries (2048, 4096, 6144, 8192, 12288 columns) and ragged tails
 SHAPES = [(901, 1, 8), (902, 3, 24), (903, 17, 264), (904, 64, 1032), (905, 5, 2048), (906, 7, 2056),
           (907, 33, 4104), (908, 9, 6152), (909, 300, 1024), (910, 6, 8200), (911, 4, 12288), (912, 3, 16384),
-          (913, 260, 520)]
+          (913, 260, 520),
+          # 1024 rows and more: 256 threads per row (fewer rows use 1024)
+          (914, 1030, 2056), (915, 1024, 12296)]
 
 
 @pytest.mark.parametrize("case", SHAPES, ids=[f"r{c[1]}_c{c[2]}" for c in SHAPES])
