@@ -27,10 +27,16 @@
  *              weight gradients and db2 are float32.  Every product
  *              accumulates in float32; bf16 outputs are rounded to nearest
  *              even once.
- *   Pointers   Every pointer except the host array of
- *              tp_mlp_reduce_partials_local and the shape struct is a DEVICE
- *              pointer, 16-byte aligned.  h and F_i must be multiples of 8.
- *              Buffers must not overlap unless stated.
+ *   Pointers   Every pointer is a DEVICE pointer, 16-byte aligned, except
+ *              the shape structs and the HOST arrays of device pointers that
+ *              the local reductions take (tp_mlp_reduce_partials_local,
+ *              tp_mlp_reduce_scatter_local, tp_mlp_all_gather_local,
+ *              tp_sp_reduce_scatter_layernorm_local, tp_sp_sum_grads_local).
+ *              h and F_i must be multiples of 8.
+ *   Overlap    An output may not overlap another output, an input or the
+ *              workspace in use, except where an entry point states that it
+ *              may coincide exactly with one (in-place forms); such calls
+ *              return TP_MLP_ERR_INVALID_ARG.
  *   Ownership  The caller allocates and owns every buffer.  The library never
  *              allocates, frees or keeps a pointer after returning.
  *   Streams    All work is enqueued on `stream` (0 = the null stream) and is
@@ -39,8 +45,9 @@
  *              caller's next synchronisation.
  *   Outputs    Overwritten, never accumulated into.
  *   Errors     Arguments are validated on the host before any launch; an
- *              invalid call returns TP_MLP_ERR_INVALID_ARG and enqueues
- *              nothing.  A failed launch returns TP_MLP_ERR_HIP.  Nothing is
+ *              invalid call returns TP_MLP_ERR_INVALID_ARG (a valid but
+ *              unsupported one TP_MLP_ERR_UNSUPPORTED, a missing or short
+ *              workspace TP_MLP_ERR_WORKSPACE) and enqueues nothing.  A failed launch returns TP_MLP_ERR_HIP.  Nothing is
  *              printed and no C++ exception crosses the ABI.
  *   Threads    Entry points are reentrant; the only process-wide state is a
  *              once-initialised per-device property cache.
