@@ -1,0 +1,32 @@
+"""CPU checks of bench.py's contract that need no GPU: more than one GPU is
+refused with a message (the build runs one rank's shard on one MI355X), and
+the committed counter summaries parse (their traffic is reported only while
+their source hash matches the kernels)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_more_than_one_gpu_is_refused(n):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_counter_summaries_parse():
+    sys.path.insert(0, ROOT)
+    import bench
+    for summary, files, kernel in (("gemm_hbm_traffic_gpt3_train_t8.md", bench.GEMM_SOURCES, "wgrad"),
+                                   ("gemv_hbm_traffic_llama3_70b_decode_t4.md", bench.GEMV_SOURCES, "decode")):
+        path = os.path.join(ROOT, "profiles", summary)
+        assert os.path.exists(path), summary
+        info = bench.counter_traffic(summary, files, kernel)
+        # None only when the kernels changed after the counters were taken
+        if info is not None:
+            assert info["bytes"] > 0 and info["algorithmic_bytes"] > 0
