@@ -37,6 +37,13 @@
  *              workspace in use, except where an entry point states that it
  *              may coincide exactly with one (in-place forms); such calls
  *              return TP_MLP_ERR_INVALID_ARG.
+ *   Extents    Every bf16 operand of a GEMM (X, a weight shard, A_i, dU_i,
+ *              the attention projections' operands) is at most 4 GiB - 256
+ *              bytes: the kernels address each through a 32-bit buffer
+ *              descriptor.  The streaming entry points (local reductions,
+ *              reduce-scatter, all-gather, bias gradient) take cols <= 2^33
+ *              and rows * cols <= 2^50.  Larger calls return
+ *              TP_MLP_ERR_UNSUPPORTED.
  *   Ownership  The caller allocates and owns every buffer.  The library never
  *              allocates, frees or keeps a pointer after returning.
  *   Streams    All work is enqueued on `stream` (0 = the null stream) and is

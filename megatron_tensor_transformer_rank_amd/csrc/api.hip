@@ -364,13 +364,25 @@ hipError_t run_tn(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B
   return gemm_launch(GEMM_WGRAD, 0, g, num_cu_current(), st);
 }
 
+// Extents of a [rows, cols] block for the streaming kernels (reductions,
+// gather, column sums): cols / 8 is an int there, and byte counts of the
+// block must not overflow 64 bits.  INVALID_ARG for a malformed shape,
+// UNSUPPORTED above these limits.
+constexpr int64_t STREAM_MAX_COLS = (int64_t)1 << 33;
+constexpr int64_t STREAM_MAX_ELEMS = (int64_t)1 << 50;
+tp_mlp_status block_status(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 8 || cols % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
+  if (cols > STREAM_MAX_COLS || rows > STREAM_MAX_ELEMS / cols) return TP_MLP_ERR_UNSUPPORTED;
+  return TP_MLP_OK;
+}
+
 // A host array of t device pointers to bf16 [rows, cols] blocks: INVALID_ARG
-// for a malformed list or shape, UNSUPPORTED for t above MAX_T.
+// for a malformed list or shape, UNSUPPORTED for t above MAX_T or a block
+// beyond the streaming limits.
 tp_mlp_status partial_list(int32_t t, const void* const* ptrs, int64_t rows, int64_t cols, PartialPtrs& pp) {
   if (ptrs == nullptr || t < 1) return TP_MLP_ERR_INVALID_ARG;
   if (t > MAX_T) return TP_MLP_ERR_UNSUPPORTED;
-  if (rows < 1 || cols < 8 || cols % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
-  if (rows > (int64_t)1 << 40 || cols > (int64_t)1 << 40) return TP_MLP_ERR_INVALID_ARG;
+  if (const tp_mlp_status bs = block_status(rows, cols)) return bs;
   for (int r = 0; r < t; ++r) {
     if (!req(ptrs[r])) return TP_MLP_ERR_INVALID_ARG;
     pp.p[r] = cu16(ptrs[r]);
@@ -475,7 +487,7 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_shape* s, int backward) {
 }
 
 size_t tp_mlp_bias_grad_workspace_bytes(int64_t rows, int64_t cols) {
-  if (rows < 1 || cols < 1) return 0;
+  if (block_status(rows, cols) != TP_MLP_OK) return 0;
   return col_sum_workspace_bytes(rows, cols);
 }
 
@@ -614,8 +626,8 @@ tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i, con
 
 tp_mlp_status tp_mlp_bias_grad(const void* dY, int64_t rows, int64_t cols, float* db2, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-  if (rows < 1 || cols < 8 || cols % 8 != 0 || !req(dY) || !req(db2) || !opt_aligned(workspace))
-    return TP_MLP_ERR_INVALID_ARG;
+  if (const tp_mlp_status bs = block_status(rows, cols)) return bs;
+  if (!req(dY) || !req(db2) || !opt_aligned(workspace)) return TP_MLP_ERR_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < col_sum_workspace_bytes(rows, cols)) return TP_MLP_ERR_WORKSPACE;
   if (!spans_ok({{db2, (uint64_t)cols * 4}, {workspace, col_sum_workspace_bytes(rows, cols)}},
                 {{dY, (uint64_t)rows * cols * 2}}))

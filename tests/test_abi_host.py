@@ -196,6 +196,27 @@ def test_step_entry_points_validate():
     assert wg(r, P(0), None, P(2), P(3), P(4), P(5), P(6), None) == INVALID
 
 
+def test_streaming_extents_past_the_limits_are_unsupported():
+    """The streaming kernels index a row by cols / 8 in an int and count a
+    block's bytes in 64 bits: cols above 2^33 or rows * cols above 2^50 are
+    refused before any launch (a [1, 2^34] bf16 block would fit in HBM)."""
+    L = B.lib()
+    ptrs = (ctypes.c_void_p * 2)(P(0), P(1))
+    wide, tall = 1 << 34, (1 << 30, 1 << 21)      # cols over 2^33; rows * cols = 2^51
+    assert L.tp_mlp_reduce_partials_local(2, ptrs, 1, wide, None, P(2), None) == UNSUPPORTED
+    assert L.tp_mlp_reduce_partials_local(2, ptrs, *tall, None, P(2), None) == UNSUPPORTED
+    assert L.tp_mlp_reduce_scatter_local(2, ptrs, 2, wide, 0, None, None, P(2), None) == UNSUPPORTED
+    assert L.tp_mlp_all_gather_local(2, ptrs, 1, wide, P(2), None) == UNSUPPORTED
+    assert L.tp_mlp_all_gather_local(2, ptrs, *tall, P(2), None) == UNSUPPORTED
+    assert L.tp_mlp_bias_grad(P(0), 1, wide, P(1), P(2), 1 << 40, None) == UNSUPPORTED
+    assert L.tp_mlp_bias_grad(P(0), *tall, P(1), P(2), 1 << 40, None) == UNSUPPORTED
+    assert B.bias_grad_workspace_bytes(1, wide) == 0
+    assert B.bias_grad_workspace_bytes(1, 12) == 0                # cols % 8
+    # the limits themselves are accepted by the checks
+    assert B.bias_grad_workspace_bytes(1, 1 << 33) == (1 << 33) * 4
+    assert B.bias_grad_workspace_bytes(1 << 17, 1 << 33) > 0
+
+
 def test_reduce_rejects_partial_overlap():
     L = B.lib()
     p0, p1 = FAKE, FAKE + (1 << 20)
