@@ -186,6 +186,10 @@ def main():
     }
 
     torch.cuda.empty_cache()
+    # ---- decode (one token, and small batches), HBM bound; weights rotated over copies
+    if not args.no_decode:
+        result["decode"] = bench_decode(args, WORKLOADS[args.decode_workload], B, I, torch, np, to_dev)
+        torch.cuda.empty_cache()
     # ---- the other training configurations, same step, reported beside the headline
     if not args.no_other:
         other = {}
@@ -200,10 +204,6 @@ def main():
                            "kernels_ms": {k: round(v, 4) for k, v in o["kern_ms"].items()}}
             torch.cuda.empty_cache()
         result["other_configs"] = other
-    # ---- decode (one token, and small batches), HBM bound; weights rotated over copies
-    if not args.no_decode:
-        result["decode"] = bench_decode(args, WORKLOADS[args.decode_workload], B, I, torch, np, to_dev)
-        torch.cuda.empty_cache()
     # ---- attention block projections of the same model scale
     if not args.no_attn:
         result["attention_projections"] = bench_attn(args, B, I, torch, np, to_dev)
@@ -219,6 +219,7 @@ def main():
 
 
 
+DECODE_WINDOWS = 5
 GEMM_SOURCES = ("gemm.hip", "gemm.h", "tiles.h", "common.h")
 GEMV_SOURCES = ("gemv.hip", "gemv.h", "common.h")
 
@@ -291,13 +292,16 @@ def bench_decode(args, w, B, I, torch, np, to_dev):
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = args.decode_steps
-    e0.record(stream)
-    for i in range(n):
-        a, g, b = sets[i % nsets]
-        B.tp_mlp_fwd_shard(shape, x, a, g, b, Y, A, None, None, ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / n
+    windows = []
+    for _ in range(DECODE_WINDOWS):       # the median window is reported, every window listed
+        e0.record(stream)
+        for i in range(n):
+            a, g, b = sets[i % nsets]
+            B.tp_mlp_fwd_shard(shape, x, a, g, b, Y, A, None, None, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        windows.append(e0.elapsed_time(e1) * 1e3 / n)
+    us = float(np.median(windows))
     # warm (same weights every call) for context
     e0.record(stream)
     for i in range(n):
@@ -332,6 +336,7 @@ def bench_decode(args, w, B, I, torch, np, to_dev):
         log(f"[bench] small-batch decode N={nb}: {usb:.2f} us ({wbytes / (usb * 1e-6) / 1e9:.0f} GB/s of weights)")
     return {"workload": w.name, "value": round(gbs, 1), "unit": "GB/s", "us_per_token": round(us, 3),
             "small_batch": small,
+            "us_per_token_windows": [round(v, 3) for v in windows], "calls_per_window": n,
             "bytes_per_token": wbytes, "weight_sets_rotated": nsets,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
