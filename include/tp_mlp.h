@@ -44,6 +44,12 @@
  *              reduce-scatter, all-gather, bias gradient) take cols <= 2^33
  *              and rows * cols <= 2^50.  Larger calls return
  *              TP_MLP_ERR_UNSUPPORTED.
+ *   Empty      N = 0 tokens (rows = 0, n = 0) is valid.  A buffer whose size
+ *              is then zero may be NULL (the storage of an empty tensor);
+ *              the weights, gamma and the gradient outputs may not.  A
+ *              forward or a reduction launches nothing.  A weight
+ *              gradient, db2, dgamma or dbeta, being a sum over the batch's
+ *              rows, is written as zeros.  No workspace is needed.
  *   Ownership  The caller allocates and owns every buffer.  The library never
  *              allocates, frees or keeps a pointer after returning.
  *   Streams    All work is enqueued on `stream` (0 = the null stream) and is
@@ -93,7 +99,7 @@ typedef enum {
 /* The problem as the pages state it: replicated input X [N, h], the full
  * intermediate width F split over t ranks, this shard's rank (it owns the
  * contiguous hidden columns [rank*F/t, (rank+1)*F/t), rank 0 lowest), and the
- * activation.  Requires N >= 1, h >= 8, F % t == 0, 1 <= t <= 64,
+ * activation.  Requires N >= 0, h >= 8, F % t == 0, 1 <= t <= 64,
  * 0 <= rank < t, h % 8 == 0 and (F / t) % 8 == 0. */
 typedef struct {
   int64_t n_tokens; /* N = b * s                                   */
@@ -182,7 +188,7 @@ tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X,
  *   out       bf16 [rows, cols]; may coincide exactly with any partials[k]
  *             (each output chunk is written after its inputs are read); any
  *             other overlap with a partial is rejected (INVALID_ARG).
- * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), rows >= 1, cols % 8 == 0,
+ * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), rows >= 0, cols % 8 == 0,
  * 16-byte alignment. */
 tp_mlp_status tp_mlp_reduce_partials_local(int32_t t,
                                            const void* const* partials,
@@ -230,7 +236,7 @@ tp_mlp_status tp_mlp_reduce_scatter_local(int32_t t,
  *   shards  HOST array of t DEVICE pointers, each bf16 [shard_rows, cols]
  *   out     bf16 [t*shard_rows, cols]; must not overlap any shard
  *           (INVALID_ARG).
- * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), shard_rows >= 1,
+ * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), shard_rows >= 0,
  * cols % 8 == 0, 16-byte alignment. */
 tp_mlp_status tp_mlp_all_gather_local(int32_t t, const void* const* shards,
                                       int64_t shard_rows, int64_t cols,
@@ -303,7 +309,8 @@ tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i,
  * output bias that is added once after the reduction.  Deterministic
  * (fixed-order float32 sums).  workspace: device scratch of at least
  * tp_mlp_bias_grad_workspace_bytes(rows, cols) bytes, no initial contents
- * required.  Requires rows >= 1, cols % 8 == 0. */
+ * required (none when rows = 0: db2 is then zero).  Requires rows >= 0,
+ * cols % 8 == 0. */
 tp_mlp_status tp_mlp_bias_grad(const void* dY, int64_t rows, int64_t cols,
                                float* db2, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
@@ -407,7 +414,7 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X,
  * weight-gradient column sums are added in a fixed order: results are
  * deterministic.  Dropout is not part of this path (probability 0).
  *
- * Common requirements: rows >= 1, 8 <= cols <= 16384 (larger: UNSUPPORTED),
+ * Common requirements: rows >= 0, 8 <= cols <= 16384 (larger: UNSUPPORTED),
  * cols % 8 == 0, eps > 0 and finite, every pointer a 16-byte aligned device
  * pointer.
  * ------------------------------------------------------------------------ */
@@ -477,7 +484,7 @@ size_t tp_sp_layernorm_bwd_workspace_bytes(int64_t rows, int64_t cols);
  *   out    float32 [n]; may coincide exactly with grads[0] (any rank's
  *          buffer would be read after it is written), must not otherwise
  *          overlap an input.
- * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), n >= 4, n % 4 == 0. */
+ * Requires 1 <= t <= 64 (t > 64: UNSUPPORTED), n >= 0, n % 4 == 0. */
 tp_mlp_status tp_sp_sum_grads_local(int32_t t, const float* const* grads,
                                     int64_t n, float* out,
                                     hipStream_t stream);

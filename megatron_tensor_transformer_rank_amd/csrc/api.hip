@@ -37,6 +37,9 @@ int num_cu_current() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool opt_aligned(const void* p) { return p == nullptr || aligned16(p); }
 bool req(const void* p) { return p != nullptr && aligned16(p); }
+// A required buffer of `bytes` bytes; when it is empty (no tokens or rows)
+// it may be NULL, as the storage of an empty tensor is.
+bool req_n(const void* p, uint64_t bytes) { return bytes == 0 ? opt_aligned(p) : req(p); }
 
 struct Dims {
   int64_t N, h, Fi;
@@ -45,7 +48,7 @@ struct Dims {
 
 bool check_shape(const tp_mlp_shape* s, Dims& d) {
   if (s == nullptr) return false;
-  if (s->n_tokens < 1 || s->hidden < 8 || s->ffn < 1) return false;
+  if (s->n_tokens < 0 || s->hidden < 8 || s->ffn < 1) return false;
   if (s->t < 1 || s->t > MAX_T) return false;  // t > MAX_T: see shape_status
   if (s->rank < 0 || s->rank >= s->t) return false;
   if (s->act != TP_MLP_ACT_RELU && s->act != TP_MLP_ACT_GELU && s->act != TP_MLP_ACT_SWIGLU) return false;
@@ -233,6 +236,16 @@ hipError_t run_wgrad_up(const Dims& d, const void* X, const void* dU, float* dW1
   return gemm_launch(GEMM_WGRAD, d.act, wgrad_up_args(d, X, dU, dW1, dWg), num_cu_current(), st);
 }
 
+// The weight gradients of an empty batch are sums over no tokens: zero.
+hipError_t zero_wgrads(const Dims& d, float* dW1, float* dWg, float* dW2, hipStream_t st) {
+  const int64_t n = d.h * d.Fi;
+  const int cu = num_cu_current();
+  hipError_t e = zero_f32_launch(dW1, n, cu, st);
+  if (e == hipSuccess) e = zero_f32_launch(dWg, n, cu, st);
+  if (e == hipSuccess) e = zero_f32_launch(dW2, n, cu, st);
+  return e;
+}
+
 // Both weight gradients in one launch: neither leaves a partial last wave of
 // blocks on its own (each output element is summed over k in the same order
 // as in the separate launches, so the results are bitwise the same).
@@ -275,7 +288,7 @@ struct AttnDims {
 tp_mlp_status attn_status(const tp_attn_shape* s, AttnDims& a) {
   if (s == nullptr) return TP_MLP_ERR_INVALID_ARG;
   if (s->t < 1 || s->rank < 0 || s->rank >= s->t) return TP_MLP_ERR_INVALID_ARG;
-  if (s->n_tokens < 1 || s->hidden < 8 || s->hidden % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
+  if (s->n_tokens < 0 || s->hidden < 8 || s->hidden % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
   if (s->n_heads < 1 || s->n_kv_heads < 1 || s->head_dim < 8 || s->head_dim % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
   const int64_t t = s->t, nh = s->n_heads, nkv = s->n_kv_heads, d = s->head_dim;
   if (nh % nkv != 0 || nh % t != 0) return TP_MLP_ERR_INVALID_ARG;
@@ -296,7 +309,7 @@ tp_mlp_status attn_status(const tp_attn_shape* s, AttnDims& a) {
 
 // 1 <= N <= SK_MAX_N tokens: the forward projections stream their weights
 // once through the split-K small-batch product instead of wide tiles.
-bool attn_small(const AttnDims& a) { return a.N <= SK_MAX_N; }
+bool attn_small(const AttnDims& a) { return a.N >= 1 && a.N <= SK_MAX_N; }
 SkinnyPlan attn_qkv_plan(const AttnDims& a) {
   return skinny_plan((int)a.N, (int)a.h, (int)a.qkv_cols, 1, SKINNY_TARGET_BLOCKS);
 }
@@ -366,12 +379,12 @@ hipError_t run_tn(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B
 
 // Extents of a [rows, cols] block for the streaming kernels (reductions,
 // gather, column sums): cols / 8 is an int there, and byte counts of the
-// block must not overflow 64 bits.  INVALID_ARG for a malformed shape,
-// UNSUPPORTED above these limits.
+// block must not overflow 64 bits.  rows may be 0 (an empty block).
+// INVALID_ARG for a malformed shape, UNSUPPORTED above these limits.
 constexpr int64_t STREAM_MAX_COLS = (int64_t)1 << 33;
 constexpr int64_t STREAM_MAX_ELEMS = (int64_t)1 << 50;
 tp_mlp_status block_status(int64_t rows, int64_t cols) {
-  if (rows < 1 || cols < 8 || cols % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
+  if (rows < 0 || cols < 8 || cols % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
   if (cols > STREAM_MAX_COLS || rows > STREAM_MAX_ELEMS / cols) return TP_MLP_ERR_UNSUPPORTED;
   return TP_MLP_OK;
 }
@@ -383,8 +396,9 @@ tp_mlp_status partial_list(int32_t t, const void* const* ptrs, int64_t rows, int
   if (ptrs == nullptr || t < 1) return TP_MLP_ERR_INVALID_ARG;
   if (t > MAX_T) return TP_MLP_ERR_UNSUPPORTED;
   if (const tp_mlp_status bs = block_status(rows, cols)) return bs;
+  const uint64_t bytes = (uint64_t)rows * (uint64_t)cols * 2;
   for (int r = 0; r < t; ++r) {
-    if (!req(ptrs[r])) return TP_MLP_ERR_INVALID_ARG;
+    if (!req_n(ptrs[r], bytes)) return TP_MLP_ERR_INVALID_ARG;
     pp.p[r] = cu16(ptrs[r]);
   }
   return TP_MLP_OK;
@@ -424,8 +438,8 @@ tp_mlp_status rs_status(int32_t t, const void* const* partials, int64_t rows, in
                         const void* bias, const void* residual, const void* out, PartialPtrs& pp) {
   if (const tp_mlp_status ss = partial_list(t, partials, rows, cols, pp)) return ss;
   if (rows % t != 0 || rank < 0 || rank >= t) return TP_MLP_ERR_INVALID_ARG;
-  if (!req(out) || !opt_aligned(bias) || !opt_aligned(residual)) return TP_MLP_ERR_INVALID_ARG;
   const uint64_t out_bytes = (uint64_t)(rows / t) * (uint64_t)cols * 2;
+  if (!req_n(out, out_bytes) || !opt_aligned(bias) || !opt_aligned(residual)) return TP_MLP_ERR_INVALID_ARG;
   const uint64_t block_off = (uint64_t)rank * out_bytes;
   for (int r = 0; r < t; ++r) {
     const uint8_t* blk = reinterpret_cast<const uint8_t*>(pp.p[r]) + block_off;
@@ -441,7 +455,7 @@ tp_mlp_status rs_status(int32_t t, const void* const* partials, int64_t rows, in
 
 // LayerNorm sizes and parameters shared by the sequence-parallel entry points.
 tp_mlp_status ln_status(int64_t rows, int64_t cols, float eps, const void* gamma, const void* beta) {
-  if (rows < 1 || rows >= (int64_t)1 << 31 || cols < 8 || cols % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
+  if (rows < 0 || rows >= (int64_t)1 << 31 || cols < 8 || cols % 8 != 0) return TP_MLP_ERR_INVALID_ARG;
   if (!(eps > 0.0f) || !(eps < 3.0e38f)) return TP_MLP_ERR_INVALID_ARG;
   if (!req(gamma) || !opt_aligned(beta)) return TP_MLP_ERR_INVALID_ARG;
   if (cols > LN_MAX_COLS) return TP_MLP_ERR_UNSUPPORTED;
@@ -451,10 +465,11 @@ tp_mlp_status ln_status(int64_t rows, int64_t cols, float eps, const void* gamma
 // The LayerNorm stash: both float32 [rows] or both NULL; disjoint from y and
 // from each other.
 bool stash_ok(const float* mean, const float* rstd, int64_t rows, const void* y, uint64_t y_bytes) {
+  if (rows == 0) return opt_aligned(mean) && opt_aligned(rstd);
   if ((mean == nullptr) != (rstd == nullptr)) return false;
   if (!mean) return true;
   const uint64_t sb = (uint64_t)rows * 4;
-  return req(mean) && req(rstd) && disjoint(mean, sb, rstd, sb) && disjoint(mean, sb, y, y_bytes) &&
+  return req_n(mean, sb) && req_n(rstd, sb) && disjoint(mean, sb, rstd, sb) && disjoint(mean, sb, y, y_bytes) &&
          disjoint(rstd, sb, y, y_bytes);
 }
 
@@ -479,7 +494,7 @@ const char* tp_mlp_status_string(tp_mlp_status st) {
 
 size_t tp_mlp_workspace_bytes(const tp_mlp_shape* s, int backward) {
   Dims d;
-  if (!check_shape(s, d)) return 0;
+  if (!check_shape(s, d) || d.N == 0) return 0;
   if (backward) return col_sum_workspace_bytes(d.N, d.h);
   if (d.N == 1) return decode_layout(d).total;
   if (small_batch(d)) return skinny_layout(d).total;
@@ -487,7 +502,7 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_shape* s, int backward) {
 }
 
 size_t tp_mlp_bias_grad_workspace_bytes(int64_t rows, int64_t cols) {
-  if (block_status(rows, cols) != TP_MLP_OK) return 0;
+  if (block_status(rows, cols) != TP_MLP_OK || rows == 0) return 0;
   return col_sum_workspace_bytes(rows, cols);
 }
 
@@ -496,12 +511,14 @@ tp_mlp_status tp_mlp_up_act_shard(const tp_mlp_shape* s, const void* X, const vo
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   const bool sw = d.act == ACT_SWIGLU;
-  if (!req(X) || !req(W1_i) || !req(A_i) || !opt_aligned(U_i) || !opt_aligned(G_i)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
+  if (!req_n(X, x) || !req(W1_i) || !req_n(A_i, a) || !opt_aligned(U_i) || !opt_aligned(G_i))
+    return TP_MLP_ERR_INVALID_ARG;
   if (sw != (Wg_i != nullptr) || !opt_aligned(Wg_i)) return TP_MLP_ERR_INVALID_ARG;
   if (!sw && G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
-  if (sw && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
-  const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
+  if (sw && d.N > 0 && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
   if (!spans_ok({{A_i, a}, {U_i, a}, {G_i, a}}, {{X, x}, {W1_i, w}, {Wg_i, w}})) return TP_MLP_ERR_INVALID_ARG;
+  if (d.N == 0) return TP_MLP_OK;
   return hip_status(run_up_act(d, X, W1_i, Wg_i, A_i, U_i, G_i, stream));
 }
 
@@ -509,9 +526,10 @@ tp_mlp_status tp_mlp_down_shard(const tp_mlp_shape* s, const void* A_i, const vo
                                 hipStream_t stream) {
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
-  if (!req(A_i) || !req(W2_i) || !req(Y_i)) return TP_MLP_ERR_INVALID_ARG;
-  if (!spans_ok({{Y_i, (uint64_t)d.N * d.h * 2}}, {{A_i, (uint64_t)d.N * d.Fi * 2}, {W2_i, (uint64_t)d.Fi * d.h * 2}}))
-    return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t y = (uint64_t)d.N * d.h * 2, a = (uint64_t)d.N * d.Fi * 2;
+  if (!req_n(A_i, a) || !req(W2_i) || !req_n(Y_i, y)) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{Y_i, y}}, {{A_i, a}, {W2_i, (uint64_t)d.Fi * d.h * 2}})) return TP_MLP_ERR_INVALID_ARG;
+  if (d.N == 0) return TP_MLP_OK;
   return hip_status(run_down(d, A_i, W2_i, Y_i, stream));
 }
 
@@ -521,19 +539,20 @@ tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X, const void*
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   const bool sw = d.act == ACT_SWIGLU;
-  if (!req(X) || !req(W1_i) || !req(W2_i) || !req(Y_i) || !req(A_i)) return TP_MLP_ERR_INVALID_ARG;
-  if (!opt_aligned(U_i) || !opt_aligned(G_i) || !opt_aligned(Wg_i) || !opt_aligned(workspace))
-    return TP_MLP_ERR_INVALID_ARG;
-  if (sw != (Wg_i != nullptr)) return TP_MLP_ERR_INVALID_ARG;
-  if (!sw && G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
-  if (sw && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
   {
     const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
+    if (!req_n(X, x) || !req(W1_i) || !req(W2_i) || !req_n(Y_i, x) || !req_n(A_i, a)) return TP_MLP_ERR_INVALID_ARG;
+    if (!opt_aligned(U_i) || !opt_aligned(G_i) || !opt_aligned(Wg_i) || !opt_aligned(workspace))
+      return TP_MLP_ERR_INVALID_ARG;
+    if (sw != (Wg_i != nullptr)) return TP_MLP_ERR_INVALID_ARG;
+    if (!sw && G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+    if (sw && d.N > 0 && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
     const uint64_t ws_used = d.N == 1 ? decode_layout(d).total : (small_batch(d) ? skinny_layout(d).total : 0);
     if (!spans_ok({{Y_i, x}, {A_i, a}, {U_i, a}, {G_i, a}, {ws_used ? workspace : nullptr, ws_used}},
                   {{X, x}, {W1_i, w}, {Wg_i, w}, {W2_i, w}}))
       return TP_MLP_ERR_INVALID_ARG;
   }
+  if (d.N == 0) return TP_MLP_OK;  // no tokens: nothing to compute
 
   if (d.N == 1) {
     const DecodeLayout L = decode_layout(d);
@@ -564,12 +583,12 @@ tp_mlp_status tp_mlp_down_dgrad_act_shard(const tp_mlp_shape* s, const void* dY,
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   const bool sw = d.act == ACT_SWIGLU;
-  if (!req(dY) || !req(W2_i) || !req(U_i) || !req(dU_i)) return TP_MLP_ERR_INVALID_ARG;
-  if (sw ? !req(G_i) : G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
-  const uint64_t a = (uint64_t)d.N * d.Fi * 2;
-  if (!spans_ok({{dU_i, a * d.g}}, {{dY, (uint64_t)d.N * d.h * 2}, {W2_i, (uint64_t)d.Fi * d.h * 2}, {U_i, a},
-                                   {G_i, a}}))
+  const uint64_t a = (uint64_t)d.N * d.Fi * 2, y = (uint64_t)d.N * d.h * 2;
+  if (!req_n(dY, y) || !req(W2_i) || !req_n(U_i, a) || !req_n(dU_i, a)) return TP_MLP_ERR_INVALID_ARG;
+  if (sw ? !req_n(G_i, a) : G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dU_i, a * d.g}}, {{dY, y}, {W2_i, (uint64_t)d.Fi * d.h * 2}, {U_i, a}, {G_i, a}}))
     return TP_MLP_ERR_INVALID_ARG;
+  if (d.N == 0) return TP_MLP_OK;
   return hip_status(run_dgrad_act(d, dY, W2_i, U_i, G_i, dU_i, stream));
 }
 
@@ -577,9 +596,10 @@ tp_mlp_status tp_mlp_down_wgrad_shard(const tp_mlp_shape* s, const void* A_i, co
                                       hipStream_t stream) {
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
-  if (!req(A_i) || !req(dY) || !req(dW2_i)) return TP_MLP_ERR_INVALID_ARG;
-  if (!spans_ok({{dW2_i, (uint64_t)d.Fi * d.h * 4}}, {{A_i, (uint64_t)d.N * d.Fi * 2}, {dY, (uint64_t)d.N * d.h * 2}}))
-    return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t a = (uint64_t)d.N * d.Fi * 2, y = (uint64_t)d.N * d.h * 2;
+  if (!req_n(A_i, a) || !req_n(dY, y) || !req(dW2_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dW2_i, (uint64_t)d.Fi * d.h * 4}}, {{A_i, a}, {dY, y}})) return TP_MLP_ERR_INVALID_ARG;
+  if (d.N == 0) return hip_status(zero_f32_launch(dW2_i, d.Fi * d.h, num_cu_current(), stream));
   return hip_status(run_wgrad_down(d, A_i, dY, dW2_i, stream));
 }
 
@@ -588,11 +608,12 @@ tp_mlp_status tp_mlp_up_wgrad_shard(const tp_mlp_shape* s, const void* X, const 
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   const bool sw = d.act == ACT_SWIGLU;
-  if (!req(X) || !req(dU_i) || !req(dW1_i)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t x = (uint64_t)d.N * d.h * 2, du = (uint64_t)d.N * d.g * d.Fi * 2;
+  if (!req_n(X, x) || !req_n(dU_i, du) || !req(dW1_i)) return TP_MLP_ERR_INVALID_ARG;
   if (sw ? !req(dWg_i) : dWg_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
   const uint64_t w4 = (uint64_t)d.h * d.Fi * 4;
-  if (!spans_ok({{dW1_i, w4}, {dWg_i, w4}}, {{X, (uint64_t)d.N * d.h * 2}, {dU_i, (uint64_t)d.N * d.g * d.Fi * 2}}))
-    return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dW1_i, w4}, {dWg_i, w4}}, {{X, x}, {dU_i, du}})) return TP_MLP_ERR_INVALID_ARG;
+  if (d.N == 0) return hip_status(zero_wgrads(d, dW1_i, dWg_i, nullptr, stream));
   return hip_status(run_wgrad_up(d, X, dU_i, dW1_i, dWg_i, stream));
 }
 
@@ -601,12 +622,14 @@ tp_mlp_status tp_mlp_wgrad_shard(const tp_mlp_shape* s, const void* X, const voi
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   const bool sw = d.act == ACT_SWIGLU;
-  if (!req(X) || !req(A_i) || !req(dY) || !req(dU_i) || !req(dW1_i) || !req(dW2_i)) return TP_MLP_ERR_INVALID_ARG;
-  if (sw ? !req(dWg_i) : dWg_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
   const uint64_t x = (uint64_t)d.N * d.h * 2, w4 = (uint64_t)d.h * d.Fi * 4;
-  if (!spans_ok({{dW1_i, w4}, {dWg_i, w4}, {dW2_i, w4}},
-                {{X, x}, {A_i, (uint64_t)d.N * d.Fi * 2}, {dY, x}, {dU_i, (uint64_t)d.N * d.g * d.Fi * 2}}))
+  const uint64_t a = (uint64_t)d.N * d.Fi * 2, du = (uint64_t)d.N * d.g * d.Fi * 2;
+  if (!req_n(X, x) || !req_n(A_i, a) || !req_n(dY, x) || !req_n(dU_i, du) || !req(dW1_i) || !req(dW2_i))
     return TP_MLP_ERR_INVALID_ARG;
+  if (sw ? !req(dWg_i) : dWg_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dW1_i, w4}, {dWg_i, w4}, {dW2_i, w4}}, {{X, x}, {A_i, a}, {dY, x}, {dU_i, du}}))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (d.N == 0) return hip_status(zero_wgrads(d, dW1_i, dWg_i, dW2_i, stream));
   return hip_status(run_wgrads(d, X, A_i, dY, dU_i, dW1_i, dWg_i, dW2_i, stream));
 }
 
@@ -615,22 +638,25 @@ tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i, con
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   const bool sw = d.act == ACT_SWIGLU;
-  if (!req(dU_i) || !req(W1_i) || !req(dX_partial)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t w = (uint64_t)d.h * d.Fi * 2, dx = (uint64_t)d.N * d.h * 2, du = (uint64_t)d.N * d.g * d.Fi * 2;
+  if (!req_n(dU_i, du) || !req(W1_i) || !req_n(dX_partial, dx)) return TP_MLP_ERR_INVALID_ARG;
   if (sw ? !req(Wg_i) : Wg_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
-  const uint64_t w = (uint64_t)d.h * d.Fi * 2;
-  if (!spans_ok({{dX_partial, (uint64_t)d.N * d.h * 2}},
-                {{dU_i, (uint64_t)d.N * d.g * d.Fi * 2}, {W1_i, w}, {Wg_i, w}}))
-    return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dX_partial, dx}}, {{dU_i, du}, {W1_i, w}, {Wg_i, w}})) return TP_MLP_ERR_INVALID_ARG;
+  if (d.N == 0) return TP_MLP_OK;
   return hip_status(run_dgrad_up(d, dU_i, W1_i, Wg_i, dX_partial, stream));
 }
 
 tp_mlp_status tp_mlp_bias_grad(const void* dY, int64_t rows, int64_t cols, float* db2, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
   if (const tp_mlp_status bs = block_status(rows, cols)) return bs;
-  if (!req(dY) || !req(db2) || !opt_aligned(workspace)) return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t y = (uint64_t)rows * cols * 2;
+  if (!req_n(dY, y) || !req(db2) || !opt_aligned(workspace)) return TP_MLP_ERR_INVALID_ARG;
+  if (rows == 0) {  // a sum over no rows
+    if (!spans_ok({{db2, (uint64_t)cols * 4}}, {})) return TP_MLP_ERR_INVALID_ARG;
+    return hip_status(zero_f32_launch(db2, cols, num_cu_current(), stream));
+  }
   if (workspace == nullptr || workspace_bytes < col_sum_workspace_bytes(rows, cols)) return TP_MLP_ERR_WORKSPACE;
-  if (!spans_ok({{db2, (uint64_t)cols * 4}, {workspace, col_sum_workspace_bytes(rows, cols)}},
-                {{dY, (uint64_t)rows * cols * 2}}))
+  if (!spans_ok({{db2, (uint64_t)cols * 4}, {workspace, col_sum_workspace_bytes(rows, cols)}}, {{dY, y}}))
     return TP_MLP_ERR_INVALID_ARG;
   return hip_status(col_sum_launch(cu16(dY), rows, cols, db2, static_cast<float*>(workspace), stream));
 }
@@ -642,22 +668,26 @@ tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X, const void*
   Dims d;
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   const bool sw = d.act == ACT_SWIGLU;
-  if (!req(X) || !req(W1_i) || !req(W2_i) || !req(dY) || !req(A_i) || !req(U_i) || !req(dU_i) || !req(dW1_i) ||
-      !req(dW2_i) || !req(dX_partial) || !opt_aligned(db2) || !opt_aligned(workspace))
+  const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
+  if (!req_n(X, x) || !req(W1_i) || !req(W2_i) || !req_n(dY, x) || !req_n(A_i, a) || !req_n(U_i, a) ||
+      !req_n(dU_i, a) || !req(dW1_i) || !req(dW2_i) || !req_n(dX_partial, x) || !opt_aligned(db2) ||
+      !opt_aligned(workspace))
     return TP_MLP_ERR_INVALID_ARG;
-  if (sw ? (!req(Wg_i) || !req(G_i) || !req(dWg_i)) : (Wg_i != nullptr || G_i != nullptr || dWg_i != nullptr))
+  if (sw ? (!req(Wg_i) || !req_n(G_i, a) || !req(dWg_i)) : (Wg_i != nullptr || G_i != nullptr || dWg_i != nullptr))
     return TP_MLP_ERR_INVALID_ARG;
-  if (db2 != nullptr && (workspace == nullptr || workspace_bytes < col_sum_workspace_bytes(d.N, d.h)))
-    return TP_MLP_ERR_WORKSPACE;
-  {
-    const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
-    const uint64_t ws_used = db2 ? col_sum_workspace_bytes(d.N, d.h) : 0;
-    if (!spans_ok({{dU_i, a * d.g}, {dW1_i, w * 2}, {dWg_i, w * 2}, {dW2_i, w * 2}, {dX_partial, x},
-                   {db2, (uint64_t)d.h * 4}, {ws_used ? workspace : nullptr, ws_used}},
-                  {{X, x}, {W1_i, w}, {Wg_i, w}, {W2_i, w}, {dY, x}, {A_i, a}, {U_i, a}, {G_i, a}}))
-      return TP_MLP_ERR_INVALID_ARG;
-  }
+  // the bias gradient needs scratch unless there are no tokens to sum
+  const uint64_t ws_used = db2 && d.N > 0 ? col_sum_workspace_bytes(d.N, d.h) : 0;
+  if (ws_used && (workspace == nullptr || workspace_bytes < ws_used)) return TP_MLP_ERR_WORKSPACE;
+  if (!spans_ok({{dU_i, a * d.g}, {dW1_i, w * 2}, {dWg_i, w * 2}, {dW2_i, w * 2}, {dX_partial, x},
+                 {db2, (uint64_t)d.h * 4}, {ws_used ? workspace : nullptr, ws_used}},
+                {{X, x}, {W1_i, w}, {Wg_i, w}, {W2_i, w}, {dY, x}, {A_i, a}, {U_i, a}, {G_i, a}}))
+    return TP_MLP_ERR_INVALID_ARG;
 
+  if (d.N == 0) {  // no tokens: every gradient is a sum over an empty set
+    hipError_t e = zero_wgrads(d, dW1_i, dWg_i, dW2_i, stream);
+    if (e == hipSuccess) e = zero_f32_launch(db2, d.h, num_cu_current(), stream);
+    return hip_status(e);
+  }
   hipError_t e = run_dgrad_act(d, dY, W2_i, U_i, G_i, dU_i, stream);
   if (e == hipSuccess) e = run_wgrads(d, X, A_i, dY, dU_i, dW1_i, dWg_i, dW2_i, stream);
   if (e == hipSuccess) e = run_dgrad_up(d, dU_i, W1_i, Wg_i, dX_partial, stream);
@@ -670,10 +700,11 @@ tp_mlp_status tp_mlp_reduce_partials_local(int32_t t, const void* const* partial
                                            const void* bias, void* out, hipStream_t stream) {
   PartialPtrs pp = {};
   if (const tp_mlp_status ss = partial_list(t, partials, rows, cols, pp)) return ss;
-  if (!req(out) || !opt_aligned(bias)) return TP_MLP_ERR_INVALID_ARG;
   const uint64_t bytes = (uint64_t)rows * (uint64_t)cols * 2;
+  if (!req_n(out, bytes) || !opt_aligned(bias)) return TP_MLP_ERR_INVALID_ARG;
   for (int r = 0; r < t; ++r)
     if (!same_or_disjoint(out, bytes, pp.p[r], bytes)) return TP_MLP_ERR_INVALID_ARG;
+  if (rows == 0) return TP_MLP_OK;
   return hip_status(
       reduce_partials_launch(pp, t, rows, cols, 0, cu16(bias), nullptr, u16(out), num_cu_current(), stream));
 }
@@ -684,6 +715,7 @@ tp_mlp_status tp_mlp_reduce_scatter_local(int32_t t, const void* const* partials
   PartialPtrs pp = {};
   if (const tp_mlp_status ss = rs_status(t, partials, rows, cols, rank, bias, residual, out, pp)) return ss;
   const int64_t shard = rows / t;
+  if (shard == 0) return TP_MLP_OK;
   return hip_status(reduce_partials_launch(pp, t, shard, cols, (int64_t)rank * shard, cu16(bias), cu16(residual),
                                            u16(out), num_cu_current(), stream));
 }
@@ -692,10 +724,11 @@ tp_mlp_status tp_mlp_all_gather_local(int32_t t, const void* const* shards, int6
                                       void* out, hipStream_t stream) {
   PartialPtrs pp = {};
   if (const tp_mlp_status ss = partial_list(t, shards, shard_rows, cols, pp)) return ss;
-  if (!req(out)) return TP_MLP_ERR_INVALID_ARG;
   const uint64_t shard_bytes = (uint64_t)shard_rows * (uint64_t)cols * 2;
+  if (!req_n(out, shard_bytes)) return TP_MLP_ERR_INVALID_ARG;
   for (int r = 0; r < t; ++r)
     if (!disjoint(out, shard_bytes * (uint64_t)t, pp.p[r], shard_bytes)) return TP_MLP_ERR_INVALID_ARG;
+  if (shard_rows == 0) return TP_MLP_OK;
   return hip_status(gather_launch(pp, t, shard_rows, cols, u16(out), num_cu_current(), stream));
 }
 
@@ -709,13 +742,15 @@ tp_mlp_status tp_attn_qkv_shard(const tp_attn_shape* s, const void* X, const voi
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   AttnDims a;
   if (const tp_mlp_status ss = attn_status(s, a)) return ss;
-  if (!req(X) || !req(Wqkv_i) || !req(QKV_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (!req_n(X, nbytes(a.N, a.h)) || !req(Wqkv_i) || !req_n(QKV_i, nbytes(a.N, a.qkv_cols)))
+    return TP_MLP_ERR_INVALID_ARG;
   if (const tp_mlp_status ss = attn_ws_status(a, workspace, workspace_bytes, QKV_i, nbytes(a.N, a.qkv_cols)))
     return ss;
   const size_t wsu = attn_workspace(a);
   if (!spans_ok({{QKV_i, nbytes(a.N, a.qkv_cols)}, {wsu ? workspace : nullptr, wsu}},
                 {{X, nbytes(a.N, a.h)}, {Wqkv_i, nbytes(a.h, a.qkv_cols)}}))
     return TP_MLP_ERR_INVALID_ARG;
+  if (a.N == 0) return TP_MLP_OK;
   if (attn_small(a))
     return hip_status(skinny_product_launch((int)a.N, cu16(X), cu16(Wqkv_i), (int)a.h, (int)a.qkv_cols,
                                             attn_qkv_plan(a), static_cast<float*>(workspace), u16(QKV_i), stream));
@@ -726,12 +761,13 @@ tp_mlp_status tp_attn_out_shard(const tp_attn_shape* s, const void* O_i, const v
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   AttnDims a;
   if (const tp_mlp_status ss = attn_status(s, a)) return ss;
-  if (!req(O_i) || !req(Wo_i) || !req(Y_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (!req_n(O_i, nbytes(a.N, a.q_cols)) || !req(Wo_i) || !req_n(Y_i, nbytes(a.N, a.h))) return TP_MLP_ERR_INVALID_ARG;
   if (const tp_mlp_status ss = attn_ws_status(a, workspace, workspace_bytes, Y_i, nbytes(a.N, a.h))) return ss;
   const size_t wsu = attn_workspace(a);
   if (!spans_ok({{Y_i, nbytes(a.N, a.h)}, {wsu ? workspace : nullptr, wsu}},
                 {{O_i, nbytes(a.N, a.q_cols)}, {Wo_i, nbytes(a.q_cols, a.h)}}))
     return TP_MLP_ERR_INVALID_ARG;
+  if (a.N == 0) return TP_MLP_OK;
   if (attn_small(a))
     return hip_status(skinny_product_launch((int)a.N, cu16(O_i), cu16(Wo_i), (int)a.q_cols, (int)a.h,
                                             attn_out_plan(a), static_cast<float*>(workspace), u16(Y_i), stream));
@@ -742,10 +778,13 @@ tp_mlp_status tp_attn_out_bwd_shard(const tp_attn_shape* s, const void* dY, cons
                                     void* dO_i, float* dWo_i, hipStream_t stream) {
   AttnDims a;
   if (const tp_mlp_status ss = attn_status(s, a)) return ss;
-  if (!req(dY) || !req(O_i) || !req(Wo_i) || !req(dO_i) || !req(dWo_i)) return TP_MLP_ERR_INVALID_ARG;
+  if (!req_n(dY, nbytes(a.N, a.h)) || !req_n(O_i, nbytes(a.N, a.q_cols)) || !req(Wo_i) ||
+      !req_n(dO_i, nbytes(a.N, a.q_cols)) || !req(dWo_i))
+    return TP_MLP_ERR_INVALID_ARG;
   if (!spans_ok({{dO_i, nbytes(a.N, a.q_cols)}, {dWo_i, (uint64_t)a.q_cols * a.h * 4}},
                 {{dY, nbytes(a.N, a.h)}, {O_i, nbytes(a.N, a.q_cols)}, {Wo_i, nbytes(a.q_cols, a.h)}}))
     return TP_MLP_ERR_INVALID_ARG;
+  if (a.N == 0) return hip_status(zero_f32_launch(dWo_i, a.q_cols * a.h, num_cu_current(), stream));
   hipError_t e = run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream);
   if (e == hipSuccess) e = run_tn(a.q_cols, a.h, a.N, O_i, dY, dWo_i, stream);
   return hip_status(e);
@@ -755,10 +794,13 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X, const
                                     const void* dQKV_i, float* dWqkv_i, void* dX_partial, hipStream_t stream) {
   AttnDims a;
   if (const tp_mlp_status ss = attn_status(s, a)) return ss;
-  if (!req(X) || !req(Wqkv_i) || !req(dQKV_i) || !req(dWqkv_i) || !req(dX_partial)) return TP_MLP_ERR_INVALID_ARG;
+  if (!req_n(X, nbytes(a.N, a.h)) || !req(Wqkv_i) || !req_n(dQKV_i, nbytes(a.N, a.qkv_cols)) || !req(dWqkv_i) ||
+      !req_n(dX_partial, nbytes(a.N, a.h)))
+    return TP_MLP_ERR_INVALID_ARG;
   if (!spans_ok({{dWqkv_i, (uint64_t)a.h * a.qkv_cols * 4}, {dX_partial, nbytes(a.N, a.h)}},
                 {{X, nbytes(a.N, a.h)}, {Wqkv_i, nbytes(a.h, a.qkv_cols)}, {dQKV_i, nbytes(a.N, a.qkv_cols)}}))
     return TP_MLP_ERR_INVALID_ARG;
+  if (a.N == 0) return hip_status(zero_f32_launch(dWqkv_i, a.h * a.qkv_cols, num_cu_current(), stream));
   hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV_i, Wqkv_i, dX_partial, stream);
   if (e == hipSuccess) e = run_tn(a.h, a.qkv_cols, a.N, X, dQKV_i, dWqkv_i, stream);
   return hip_status(e);
@@ -767,12 +809,13 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X, const
 tp_mlp_status tp_sp_layernorm_fwd(int64_t rows, int64_t cols, float eps, const void* x, const void* gamma,
                                   const void* beta, void* y, float* mean, float* rstd, hipStream_t stream) {
   if (const tp_mlp_status ss = ln_status(rows, cols, eps, gamma, beta)) return ss;
-  if (!req(x) || !req(y)) return TP_MLP_ERR_INVALID_ARG;
   const uint64_t nb = (uint64_t)rows * (uint64_t)cols * 2;
+  if (!req_n(x, nb) || !req_n(y, nb)) return TP_MLP_ERR_INVALID_ARG;
   if (!same_or_disjoint(y, nb, x, nb) || !disjoint(y, nb, gamma, (uint64_t)cols * 2) ||
       (beta && !disjoint(y, nb, beta, (uint64_t)cols * 2)) || !stash_ok(mean, rstd, rows, y, nb) ||
       (mean && (!disjoint(mean, (uint64_t)rows * 4, x, nb) || !disjoint(rstd, (uint64_t)rows * 4, x, nb))))
     return TP_MLP_ERR_INVALID_ARG;
+  if (rows == 0) return TP_MLP_OK;
   return hip_status(ln_fwd_launch(cu16(x), rows, cols, eps, cu16(gamma), cu16(beta), u16(y), mean, rstd, stream));
 }
 
@@ -785,8 +828,8 @@ tp_mlp_status tp_sp_reduce_scatter_layernorm_local(int32_t t, const void* const*
   if (const tp_mlp_status ss = rs_status(t, partials, rows, cols, rank, bias, residual, z, pp)) return ss;
   const int64_t shard = rows / t;
   if (const tp_mlp_status ss = ln_status(shard, cols, eps, gamma, beta)) return ss;
-  if (!req(y)) return TP_MLP_ERR_INVALID_ARG;
   const uint64_t nb = (uint64_t)shard * (uint64_t)cols * 2, full = (uint64_t)rows * (uint64_t)cols * 2;
+  if (!req_n(y, nb)) return TP_MLP_ERR_INVALID_ARG;
   for (int r = 0; r < t; ++r)
     if (!disjoint(y, nb, pp.p[r], full)) return TP_MLP_ERR_INVALID_ARG;
   if (!disjoint(z, nb, gamma, (uint64_t)cols * 2) || (beta && !disjoint(z, nb, beta, (uint64_t)cols * 2)))
@@ -796,6 +839,7 @@ tp_mlp_status tp_sp_reduce_scatter_layernorm_local(int32_t t, const void* const*
       (beta && !disjoint(y, nb, beta, (uint64_t)cols * 2)) || !stash_ok(mean, rstd, shard, y, nb) ||
       (mean && (!disjoint(mean, (uint64_t)shard * 4, z, nb) || !disjoint(rstd, (uint64_t)shard * 4, z, nb))))
     return TP_MLP_ERR_INVALID_ARG;
+  if (shard == 0) return TP_MLP_OK;
   return hip_status(ln_fwd_fused_launch(pp, t, shard, cols, (int64_t)rank * shard, cu16(bias), cu16(residual),
                                         u16(z), eps, cu16(gamma), cu16(beta), u16(y), mean, rstd, stream));
 }
@@ -809,10 +853,10 @@ tp_mlp_status tp_sp_layernorm_bwd(int64_t rows, int64_t cols, const void* x, con
                                   const float* rstd, const void* dy, const void* dres, void* dx, float* dgamma,
                                   float* dbeta, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (const tp_mlp_status ss = ln_status(rows, cols, 1.0f, gamma, nullptr)) return ss;
-  if (!req(x) || !req(mean) || !req(rstd) || !req(dy) || !opt_aligned(dres) || !req(dx) || !req(dgamma) ||
-      !opt_aligned(dbeta))
+  const uint64_t nb = (uint64_t)rows * (uint64_t)cols * 2, gb = (uint64_t)cols * 4, sb = (uint64_t)rows * 4;
+  if (!req_n(x, nb) || !req_n(mean, sb) || !req_n(rstd, sb) || !req_n(dy, nb) || !opt_aligned(dres) ||
+      !req_n(dx, nb) || !req(dgamma) || !opt_aligned(dbeta))
     return TP_MLP_ERR_INVALID_ARG;
-  const uint64_t nb = (uint64_t)rows * (uint64_t)cols * 2, gb = (uint64_t)cols * 4;
   const size_t need = ln_bwd_workspace_bytes(rows, cols);
   if (!disjoint(dx, nb, x, nb) || !same_or_disjoint(dx, nb, dy, nb) || (dres && !same_or_disjoint(dx, nb, dres, nb)) ||
       !disjoint(dx, nb, gamma, (uint64_t)cols * 2) || !disjoint(dx, nb, mean, (uint64_t)rows * 4) ||
@@ -828,6 +872,11 @@ tp_mlp_status tp_sp_layernorm_bwd(int64_t rows, int64_t cols, const void* x, con
       return TP_MLP_ERR_INVALID_ARG;
   }
   if (dbeta && !disjoint(dbeta, gb, dgamma, gb)) return TP_MLP_ERR_INVALID_ARG;
+  if (rows == 0) {  // dgamma and dbeta are sums over no rows
+    hipError_t e = zero_f32_launch(dgamma, cols, num_cu_current(), stream);
+    if (e == hipSuccess) e = zero_f32_launch(dbeta, cols, num_cu_current(), stream);
+    return hip_status(e);
+  }
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return TP_MLP_ERR_WORKSPACE;
   if (!disjoint(workspace, need, dx, nb) || !disjoint(workspace, need, dgamma, gb) ||
       (dbeta && !disjoint(workspace, need, dbeta, gb)) || !disjoint(workspace, need, x, nb) ||
@@ -843,15 +892,17 @@ tp_mlp_status tp_sp_sum_grads_local(int32_t t, const float* const* grads, int64_
                                     hipStream_t stream) {
   if (grads == nullptr || t < 1) return TP_MLP_ERR_INVALID_ARG;
   if (t > MAX_T) return TP_MLP_ERR_UNSUPPORTED;
-  if (n < 4 || n % 4 != 0 || n > (int64_t)1 << 40 || !req(out)) return TP_MLP_ERR_INVALID_ARG;
+  if (n < 0 || n % 4 != 0 || n > (int64_t)1 << 40) return TP_MLP_ERR_INVALID_ARG;
   const uint64_t nb = (uint64_t)n * 4;
+  if (!req_n(out, nb)) return TP_MLP_ERR_INVALID_ARG;
   GradPtrs g = {};
   for (int r = 0; r < t; ++r) {
-    if (!req(grads[r])) return TP_MLP_ERR_INVALID_ARG;
+    if (!req_n(grads[r], nb)) return TP_MLP_ERR_INVALID_ARG;
     if (r == 0 ? !same_or_disjoint(out, nb, grads[r], nb) : !disjoint(out, nb, grads[r], nb))
       return TP_MLP_ERR_INVALID_ARG;
     g.p[r] = grads[r];
   }
+  if (n == 0) return TP_MLP_OK;
   return hip_status(sum_f32_launch(g, t, n, out, stream));
 }
 

@@ -24,5 +24,7 @@ hipError_t gather_launch(const PartialPtrs& shards, int t, int64_t shard_rows, i
 // device scratch.
 size_t col_sum_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t col_sum_launch(const uint16_t* dY, int64_t rows, int64_t cols, float* db, float* part, hipStream_t st);
+// p[0, n) = 0 (p 16-byte aligned; NULL or n <= 0: nothing is launched).
+hipError_t zero_f32_launch(float* p, int64_t n, int num_cu, hipStream_t st);
 
 }  // namespace tpmlp

@@ -256,4 +256,23 @@ hipError_t col_sum_launch(const uint16_t* dY, int64_t rows, int64_t cols, float*
   return hipGetLastError();
 }
 
+// p[0, n) = 0: the gradients that are sums over the rows of an empty batch.
+// 16-byte stores for the multiple-of-4 head, single floats for the tail.
+__global__ void __launch_bounds__(RD_THREADS) zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t n4 = n / 4, stride = (int64_t)gridDim.x * RD_THREADS;
+  const int64_t i0 = (int64_t)blockIdx.x * RD_THREADS + threadIdx.x;
+  for (int64_t i = i0; i < n4; i += stride) reinterpret_cast<float4*>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (i0 < n - 4 * n4) p[4 * n4 + i0] = 0.f;
+}
+
+hipError_t zero_f32_launch(float* p, int64_t n, int num_cu, hipStream_t st) {
+  if (p == nullptr || n <= 0) return hipSuccess;
+  int64_t blocks = (n / 4 + RD_THREADS - 1) / RD_THREADS;
+  const int64_t cap = (int64_t)num_cu * 16;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)blocks), dim3(RD_THREADS), 0, st, p, n);
+  return hipGetLastError();
+}
+
 }  // namespace tpmlp

@@ -65,7 +65,7 @@ def _fwd(shape, **over):
 
 
 @pytest.mark.parametrize("shape,expect", [
-    (B.make_shape(0, 64, 128, 1, 0, "gelu"), INVALID),         # N = 0
+    (B.make_shape(-1, 64, 128, 1, 0, "gelu"), INVALID),        # N < 0
     (B.make_shape(4, 60, 128, 1, 0, "gelu"), INVALID),         # h % 8
     (B.make_shape(4, 64, 100, 2, 0, "gelu"), INVALID),         # F_i = 50, not a multiple of 8
     (B.make_shape(4, 64, 130, 4, 0, "gelu"), INVALID),         # F % t
@@ -161,7 +161,7 @@ def test_reduce_rejects_bad_arguments():
     assert L.tp_mlp_reduce_partials_local(0, ptrs, 4, 8, None, FAKE, None) == INVALID
     assert L.tp_mlp_reduce_partials_local(2, None, 4, 8, None, FAKE, None) == INVALID
     assert L.tp_mlp_reduce_partials_local(2, ptrs, 4, 12, None, FAKE, None) == INVALID
-    assert L.tp_mlp_reduce_partials_local(2, ptrs, 0, 8, None, FAKE, None) == INVALID
+    assert L.tp_mlp_reduce_partials_local(2, ptrs, -1, 8, None, FAKE, None) == INVALID
     assert L.tp_mlp_reduce_partials_local(2, ptrs, 4, 8, FAKE + 8, FAKE, None) == INVALID
     bad = (ctypes.c_void_p * 2)(FAKE, None)
     assert L.tp_mlp_reduce_partials_local(2, bad, 4, 8, None, FAKE, None) == INVALID
@@ -217,6 +217,50 @@ def test_streaming_extents_past_the_limits_are_unsupported():
     assert B.bias_grad_workspace_bytes(1 << 17, 1 << 33) > 0
 
 
+def test_empty_batch_calls_that_launch_nothing():
+    """N = 0 tokens (rows = 0) is valid: forwards and reductions return OK
+    without launching anything (so this runs without a GPU), and buffers of
+    zero bytes may be NULL, as an empty tensor's storage is.  The weights and
+    the gradient outputs stay required; negative sizes stay invalid.  The
+    backward calls, which write zero weight gradients, are checked on the
+    GPU."""
+    L = B.lib()
+    for act, Wg in (("gelu", None), ("swiglu", P(2))):
+        s = B.make_shape(0, 64, 128, 2, 0, act)
+        r = ctypes.byref(s)
+        assert B.workspace_bytes(s, False) == 0 and B.workspace_bytes(s, True) == 0
+        # (s, X, W1, Wg, W2, Y, A, U, G, ws, wsb, stream)
+        assert L.tp_mlp_fwd_shard(r, None, P(1), Wg, P(3), None, None, None, None, None, 0, None) == OK
+        assert L.tp_mlp_fwd_shard(r, None, None, Wg, P(3), None, None, None, None, None, 0, None) == INVALID
+        assert L.tp_mlp_fwd_shard(r, FAKE + 8, P(1), Wg, P(3), None, None, None, None, None, 0, None) == INVALID
+        assert L.tp_mlp_up_act_shard(r, None, P(1), Wg, None, None, None, None) == OK
+        assert L.tp_mlp_down_shard(r, None, P(3), None, None) == OK
+        assert L.tp_mlp_down_dgrad_act_shard(r, None, P(3), None, None, None, None) == OK
+        assert L.tp_mlp_up_dgrad_shard(r, None, P(1), Wg, None, None) == OK
+        # the weight-gradient outputs are still required
+        assert L.tp_mlp_down_wgrad_shard(r, None, None, None, None) == INVALID
+    # reductions, reduce-scatter and all-gather of empty blocks
+    nulls = (ctypes.c_void_p * 2)(None, None)
+    assert L.tp_mlp_reduce_partials_local(2, nulls, 0, 8, None, None, None) == OK
+    assert L.tp_mlp_reduce_partials_local(2, nulls, 0, 8, P(0), None, None) == OK     # bias given
+    assert L.tp_mlp_reduce_partials_local(2, None, 0, 8, None, None, None) == INVALID  # no host array
+    assert L.tp_mlp_reduce_scatter_local(2, nulls, 0, 8, 1, None, None, None, None) == OK
+    assert L.tp_mlp_all_gather_local(2, nulls, 0, 8, None, None) == OK
+    assert B.bias_grad_workspace_bytes(0, 64) == 0
+    # attention projections
+    a = B.make_attn_shape(0, 64, 8, 8, 64, 2, 0)
+    assert B.attn_workspace_bytes(a) == 0
+    assert L.tp_attn_qkv_shard(ctypes.byref(a), None, P(1), None, None, 0, None) == OK
+    assert L.tp_attn_out_shard(ctypes.byref(a), None, P(1), None, None, 0, None) == OK
+    # LayerNorm forward, fused reduce-scatter + LayerNorm, gradient sum
+    assert L.tp_sp_layernorm_fwd(0, 16, ctypes.c_float(1e-5), None, P(1), None, None, None, None, None) == OK
+    assert L.tp_sp_layernorm_fwd(0, 16, ctypes.c_float(1e-5), None, None, None, None, None, None, None) == INVALID
+    assert L.tp_sp_reduce_scatter_layernorm_local(2, nulls, 0, 16, 0, None, None, None, ctypes.c_float(1e-5), P(1),
+                                                  None, None, None, None, None) == OK
+    assert B.layernorm_bwd_workspace_bytes(0, 16) == 0
+    assert L.tp_sp_sum_grads_local(2, nulls, 0, None, None) == OK
+
+
 def test_reduce_rejects_partial_overlap():
     L = B.lib()
     p0, p1 = FAKE, FAKE + (1 << 20)
@@ -255,7 +299,7 @@ def test_all_gather_rejects_bad_arguments():
     ptrs = (ctypes.c_void_p * 2)(s0, s1)
     ag = L.tp_mlp_all_gather_local
     assert ag(2, ptrs, 4, 12, FAKE + (2 << 20), None) == INVALID          # cols % 8
-    assert ag(2, ptrs, 0, 8, FAKE + (2 << 20), None) == INVALID           # no rows
+    assert ag(2, ptrs, -1, 8, FAKE + (2 << 20), None) == INVALID          # negative rows
     assert ag(0, ptrs, 4, 8, FAKE + (2 << 20), None) == INVALID
     assert ag(2, ptrs, 4, 8, None, None) == INVALID
     assert ag(2, ptrs, 4, 8, s1 - 64, None) == INVALID                    # out (128 B) runs into shard 1
@@ -282,7 +326,7 @@ def test_small_batch_workspace_sizes():
 
 
 @pytest.mark.parametrize("shape,expect", [
-    (B.make_attn_shape(0, 64, 8, 8, 64, 2, 0), INVALID),        # no tokens
+    (B.make_attn_shape(-1, 64, 8, 8, 64, 2, 0), INVALID),       # negative token count
     (B.make_attn_shape(4, 60, 8, 8, 64, 2, 0), INVALID),        # h % 8
     (B.make_attn_shape(4, 64, 8, 8, 60, 2, 0), INVALID),        # head_dim % 8
     (B.make_attn_shape(4, 64, 6, 4, 64, 2, 0), INVALID),        # n_heads % n_kv
@@ -345,7 +389,7 @@ MB = 1 << 20
 def test_layernorm_fwd_rejects_bad_arguments():
     f = B.lib().tp_sp_layernorm_fwd
     x, g, y, m, r = FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 3 * MB, FAKE + 4 * MB
-    assert f(0, 16, 1e-5, x, g, None, y, m, r, None) == INVALID            # no rows
+    assert f(-1, 16, 1e-5, x, g, None, y, m, r, None) == INVALID           # negative rows
     assert f(4, 12, 1e-5, x, g, None, y, m, r, None) == INVALID            # cols % 8
     assert f(4, 16, 0.0, x, g, None, y, m, r, None) == INVALID             # eps must be > 0
     assert f(4, 16, -1.0, x, g, None, y, m, r, None) == INVALID
@@ -427,7 +471,7 @@ def test_layernorm_bwd_workspace_and_arguments():
     assert call(db=m) == INVALID                      # dbeta on the stash
     assert call(dres=FAKE + 10 * MB, dg=FAKE + 10 * MB) == INVALID   # dgamma on dres
     assert call(cols=12) == INVALID
-    assert call(rows=0) == INVALID
+    assert call(rows=-1) == INVALID
     assert call(cols=16400, wb=1 << 30) == UNSUPPORTED
 
 
@@ -436,7 +480,7 @@ def test_sum_grads_rejects_bad_arguments():
     g0, g1, out = FAKE, FAKE + MB, FAKE + 2 * MB
     ptrs = (ctypes.c_void_p * 2)(g0, g1)
     assert f(2, ptrs, 6, out, None) == INVALID        # n % 4
-    assert f(2, ptrs, 0, out, None) == INVALID
+    assert f(2, ptrs, -4, out, None) == INVALID
     assert f(0, ptrs, 8, out, None) == INVALID
     assert f(2, None, 8, out, None) == INVALID
     assert f(2, ptrs, 8, None, None) == INVALID

@@ -358,6 +358,31 @@ def test_split_equals_unsplit(act, t):
         np.testing.assert_allclose(np.hstack([r["dWg"] for r in bt]), b1[0]["dWg"], rtol=1e-13, atol=1e-12)
 
 
+@pytest.mark.parametrize("act", ["relu", "gelu", "swiglu"])
+def test_weight_gradients_add_over_row_blocks_and_vanish_on_none(act):
+    """The block treats tokens independently, so the weight gradients over a
+    batch (dW1_i = X^T dU_i, dW2_i = A_i^T dY, db2 = the column sum of dY, as
+    derived in "Parallelism Strategies #1 - Tensor Parallelism") are sums
+    over its token rows: they add over any split of the rows, and the empty
+    block, the identity of that sum, gives zero.  A mean over rows instead
+    of a sum, or a forward / input gradient that mixed rows, fails here."""
+    rng = np.random.default_rng(77)
+    N, h, F = 9, 16, 24
+    X, W1, W2, Wg, dY = (rng.standard_normal(s) for s in [(N, h), (h, F), (F, h), (h, F), (N, h)])
+    Wg = Wg if act == "swiglu" else None
+    full = oracle.shard_backward(act, X, W1, W2, dY, Wg)
+    blocks = [slice(0, 0), slice(0, 4), slice(4, 4), slice(4, N)]
+    parts = [oracle.shard_backward(act, X[b], W1, W2, dY[b], Wg) for b in blocks]
+    for k in ("dW1", "dW2") + (("dWg",) if Wg is not None else ()):
+        np.testing.assert_allclose(sum(p[k] for p in parts), full[k], rtol=1e-13, atol=1e-13)
+        assert parts[0][k].shape == full[k].shape and not np.any(parts[0][k]), k
+    np.testing.assert_allclose(np.vstack([p["dX"] for p in parts]), full["dX"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(sum(oracle.column_sum(dY[b]) for b in blocks), oracle.column_sum(dY), rtol=1e-13)
+    assert not np.any(oracle.column_sum(dY[:0])) and oracle.column_sum(dY[:0]).shape == (h,)
+    f0 = oracle.shard_forward(act, X[:0], W1, W2, Wg)
+    assert f0["Y"].shape == (0, h) and f0["A"].shape == (0, F)
+
+
 def test_column_block_contiguous_rank_order():
     F, t = 4096, 2
     assert oracle.column_block(0, t, F) == slice(0, 2048)      # W1[:, :2048]
