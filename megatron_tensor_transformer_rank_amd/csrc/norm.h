@@ -9,7 +9,8 @@
 namespace tpmlp {
 
 constexpr int64_t LN_MAX_COLS = 16384;  // 256 threads x 8 chunks of 8 columns
-constexpr int LN_MAX_SLABS = 64;        // row slabs of the backward's column sums
+constexpr int LN_MAX_SLABS = 64;        // row slabs of the backward's column sums (few rows)
+constexpr int LN_SLAB_BLOCKS = 512;     // row slabs of the one-pass backward (many rows)
 constexpr int LN_MIN_SLAB_ROWS = 8;     // rows per slab, at least
 
 // y = LayerNorm(x) row by row (gamma, beta bf16 [cols]; beta may be NULL);

@@ -19,11 +19,15 @@
 // stores it, and normalises that stored value: bit for bit what a separate
 // reduce-scatter followed by a LayerNorm of z computes.
 //
-// The backward runs as a column kernel, dgamma and dbeta over (512-column
-// strip, row slab) tiles with at most 64 slabs of partial rows, a kernel
-// that adds the slabs in slab order, and then the row kernel (dx, one row
-// per block, like the forward), last because dx may overwrite dy in place.
-// The column kernel re-reads x and dy but keeps every CU busy.
+// The backward, for many rows (4096 and more), is one pass over row slabs:
+// a block per slab forms dx row by row and keeps its columns' dgamma / dbeta
+// sums in registers, then a kernel adds the slabs' partial rows in slab
+// order.  For fewer rows it runs as a column kernel, dgamma and dbeta over
+// (512-column strip, row slab) tiles with at most 64 slabs of partial rows,
+// the slab sums, and then the row kernel (dx, one row per block, like the
+// forward), last because dx may overwrite dy in place: the column kernel
+// re-reads x and dy but keeps every CU busy where one block per slab would
+// leave most of them idle.
 #include "common.h"
 #include "norm.h"
 
@@ -33,6 +37,7 @@ constexpr int LN_THREADS = 256;
 constexpr int LN_WAVES = LN_THREADS / 64;
 constexpr int LN_BATCH = 4;  // ranks loaded before they are added
 constexpr int SS_GROUPS = 16;
+constexpr int SS_BATCH = 8;  // slab loads in flight per thread
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -77,6 +82,28 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
   for (int w = 1; w < NW; ++w) s += red[w];
   return s;
+}
+
+// Two block sums with one barrier: red is [2][NW] floats of LDS; the caller
+// alternates `slot` (0, 1, 0, ...) between consecutive calls, so a fast wave
+// writing the next call's values never meets a slow wave still reading this
+// call's.  Every thread returns the same two values.
+template <int NW>
+__device__ __forceinline__ void block_sum2(float& a, float& b, float (*red)[2][NW], int slot) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if ((threadIdx.x & 63) == 0) {
+    red[slot][0][threadIdx.x >> 6] = a;
+    red[slot][1][threadIdx.x >> 6] = b;
+  }
+  __syncthreads();
+  a = red[slot][0][0];
+  b = red[slot][1][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    a += red[slot][0][w];
+    b += red[slot][1][w];
+  }
 }
 
 }  // namespace
@@ -240,6 +267,107 @@ ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const fl
   }
 }
 
+// The backward in one pass over a slab of rows (many rows): block b takes
+// rows [b*rpb, min(rows, (b+1)*rpb)) one after another, LN_THREADS threads,
+// thread i holding chunks i, i + LN_THREADS, ... of a row.  Per row it forms
+// dx as ln_bwd_dx_kernel does (the same arithmetic in the same order, so the
+// same bits) and adds the row's dy * xhat and dy to its columns' dgamma /
+// dbeta sums in registers, in row order; the next row's loads are issued
+// before this row's sums.  At the end the block writes its slab's partial
+// dgamma / dbeta rows, which slab_sum_kernel adds in slab order.  dx may
+// coincide with dy or dres: a row is read whole before it is written.
+template <int J>
+__global__ void __launch_bounds__(LN_THREADS)
+ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
+                   const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx,
+                   int64_t rows, int64_t rpb, int cols8, int cols, float* __restrict__ part_g,
+                   float* __restrict__ part_b) {
+  __shared__ float red[2][2][LN_WAVES];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * rpb;
+  const int64_t r1 = r0 + rpb < rows ? r0 + rpb : rows;
+  float ag[J][8], ab[J][8];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[j][e] = ab[j][e] = 0.f;
+  u32x4 xv[J], dv[J], rv[J];
+  auto load = [&](int64_t r, u32x4 (&xa)[J], u32x4 (&da)[J], u32x4 (&ra)[J]) __attribute__((always_inline)) {
+    const int64_t base = r * cols8;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = tid + j * LN_THREADS;
+      const bool ok = r < r1 && q < cols8;
+      xa[j] = ok ? ld_nt(x, base + q) : u32x4{0u, 0u, 0u, 0u};
+      da[j] = ok ? ld_nt(dy, base + q) : u32x4{0u, 0u, 0u, 0u};
+      ra[j] = (dres && ok) ? ld_nt(dres, base + q) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  load(r0, xv, dv, rv);
+  for (int64_t r = r0; r < r1; ++r) {
+    u32x4 xn[J], dn[J], rn[J];
+    load(r + 1, xn, dn, rn);  // past the slab: no loads, zeros
+    const float mu = mean[r], rs = rstd[r];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = tid + j * LN_THREADS;
+      if (q < cols8) {
+        float xf[8], df[8], gm[8];
+        unpack8(xv[j], xf);
+        unpack8(dv[j], df);
+        unpack8(ld_c(gamma, q), gm);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xh = (xf[e] - mu) * rs;
+          const float g = df[e] * gm[e];
+          s1 += g;
+          s2 += g * xh;
+          ag[j][e] += df[e] * xh;
+          ab[j][e] += df[e];
+        }
+      }
+    }
+    block_sum2<LN_WAVES>(s1, s2, red, (int)((r - r0) & 1));
+    const float m1 = s1 / (float)cols, m2 = s2 / (float)cols;
+    const int64_t base = r * cols8;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = tid + j * LN_THREADS;
+      if (q < cols8) {
+        float xf[8], df[8], gm[8], o[8];
+        unpack8(xv[j], xf);
+        unpack8(dv[j], df);
+        unpack8(ld_c(gamma, q), gm);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = rs * (df[e] * gm[e] - m1 - (xf[e] - mu) * rs * m2);
+        if (dres) add8(o, rv[j]);
+        reinterpret_cast<u32x4*>(dx)[base + q] = pack8(o);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      xv[j] = xn[j];
+      dv[j] = dn[j];
+      rv[j] = rn[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int q = tid + j * LN_THREADS;
+    if (q < cols8) {
+      float* pg = part_g + (int64_t)blockIdx.x * cols + (int64_t)q * 8;
+      reinterpret_cast<float4*>(pg)[0] = make_float4(ag[j][0], ag[j][1], ag[j][2], ag[j][3]);
+      reinterpret_cast<float4*>(pg)[1] = make_float4(ag[j][4], ag[j][5], ag[j][6], ag[j][7]);
+      if (part_b) {
+        float* pb = part_b + (int64_t)blockIdx.x * cols + (int64_t)q * 8;
+        reinterpret_cast<float4*>(pb)[0] = make_float4(ab[j][0], ab[j][1], ab[j][2], ab[j][3]);
+        reinterpret_cast<float4*>(pb)[1] = make_float4(ab[j][4], ab[j][5], ab[j][6], ab[j][7]);
+      }
+    }
+  }
+}
+
 // dgamma / dbeta partial rows of one (column strip, row slab) tile: a lane
 // owns 8 adjacent columns (16-byte loads, a wave covers 512 columns), the 4
 // waves take interleaved rows of the slab, LN_DG_UNROLL rows of loads in
@@ -317,9 +445,20 @@ slab_sum_kernel(const float* __restrict__ part0, float* __restrict__ out0, const
   const int64_t c = (int64_t)blockIdx.x * 64 + c4 * 4;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < cols) {
-    for (int q = grp; q < slabs; q += SS_GROUPS) {
-      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)q * cols + c);
-      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    // SS_BATCH loads in flight, then added in increasing slab order
+    for (int q0 = grp; q0 < slabs; q0 += SS_GROUPS * SS_BATCH) {
+      float4 v[SS_BATCH];
+#pragma unroll
+      for (int u = 0; u < SS_BATCH; ++u) {
+        const int q = q0 + u * SS_GROUPS;
+        v[u] = q < slabs ? *reinterpret_cast<const float4*>(part + (int64_t)q * cols + c)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < SS_BATCH; ++u)
+        if (q0 + u * SS_GROUPS < slabs) {
+          a.x += v[u].x; a.y += v[u].y; a.z += v[u].z; a.w += v[u].w;
+        }
     }
   }
   red[grp][c4] = a;
@@ -354,6 +493,7 @@ namespace {
 // CU still holds enough loads in flight; 256 otherwise.  A function of the
 // row count only, so the fused and the separate forward pick the same.
 constexpr int LN_FEW_ROWS = 1024;
+constexpr int64_t LN_ONE_PASS_ROWS = 4096;  // measured: below it the two-pass form is as fast or faster
 int ln_nt(int64_t rows) { return rows < LN_FEW_ROWS ? 1024 : LN_THREADS; }
 
 // chunks per thread, the smallest instantiated J >= cols8 / nt
@@ -365,11 +505,18 @@ int ln_j(int64_t cols, int nt) {
   return 0;
 }
 
-// Row slabs of the dgamma / dbeta tiles: at least LN_MIN_SLAB_ROWS rows
-// each, at most LN_MAX_SLABS of them.
+// Many rows: the one-pass backward (ln_bwd_slab_kernel); few rows: the
+// column kernel, the slab sums, then the 1024-thread row kernel, which keep
+// every CU busy where a slab per block would leave most of them idle.
+bool bwd_one_pass(int64_t rows) { return rows >= LN_ONE_PASS_ROWS; }
+
+// Row slabs of the backward's dgamma / dbeta partial sums, at least
+// LN_MIN_SLAB_ROWS rows each: at most LN_SLAB_BLOCKS for the one-pass
+// kernel (one block per slab), at most LN_MAX_SLABS for the column kernel.
 void bwd_slabs(int64_t rows, int& slabs, int64_t& rpb) {
   int64_t nb = (rows + LN_MIN_SLAB_ROWS - 1) / LN_MIN_SLAB_ROWS;
-  if (nb > LN_MAX_SLABS) nb = LN_MAX_SLABS;
+  const int64_t cap = bwd_one_pass(rows) ? LN_SLAB_BLOCKS : LN_MAX_SLABS;
+  if (nb > cap) nb = cap;
   if (nb < 1) nb = 1;
   rpb = (rows + nb - 1) / nb;
   if (rpb < 1) rpb = 1;
@@ -436,22 +583,41 @@ hipError_t ln_bwd_launch(const uint16_t* x, const uint16_t* gamma, const float* 
                          float* dgamma, float* dbeta, float* part, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const dim3 blk(LN_THREADS);
-  // the column sums first: they read dy, which dx may overwrite in place
   int slabs;
   int64_t rpb;
   bwd_slabs(rows, slabs, rpb);
   float* part_g = part;
   float* part_b = dbeta ? part + (int64_t)slabs * cols : nullptr;
+  const int cols8 = (int)(cols / 8);
+  const dim3 sgrid((unsigned)((cols + 63) / 64), dbeta ? 2u : 1u);
+  if (bwd_one_pass(rows)) {
+#define LN_SLAB(J)                                                                                               \
+  hipLaunchKernelGGL((ln_bwd_slab_kernel<J>), dim3((unsigned)slabs), blk, 0, st, x, gamma, mean, rstd, dy, dres, \
+                     dx, rows, rpb, cols8, (int)cols, part_g, part_b)
+    switch (ln_j(cols, LN_THREADS)) {
+      case 1: LN_SLAB(1); break;
+      case 2: LN_SLAB(2); break;
+      case 3: LN_SLAB(3); break;
+      case 4: LN_SLAB(4); break;
+      case 6: LN_SLAB(6); break;
+      case 8: LN_SLAB(8); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef LN_SLAB
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, dgamma, part_b, dbeta, slabs, cols);
+    return hipGetLastError();
+  }
+  // the column sums first: they read dy, which dx may overwrite in place
   const int64_t strips = (cols + LN_DG_STRIP - 1) / LN_DG_STRIP;
   hipLaunchKernelGGL(ln_bwd_dgb_kernel, dim3((unsigned)(strips * slabs)), blk, 0, st, x, mean, rstd, dy, rows, cols,
                      rpb, part_g, part_b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 sgrid((unsigned)((cols + 63) / 64), dbeta ? 2u : 1u);
   hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, dgamma, part_b, dbeta, slabs, cols);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int cols8 = (int)(cols / 8);
   const int nt = ln_nt(rows);
 #define LN_BWD(NT, J)                                                                                            \
   hipLaunchKernelGGL((ln_bwd_dx_kernel<NT, J>), dim3((unsigned)rows), dim3(NT), 0, st, x, gamma, mean, rstd, dy, \

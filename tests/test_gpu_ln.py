@@ -90,7 +90,10 @@ SHAPES = [(901, 1, 8), (902, 3, 24), (903, 17, 264), (904, 64, 1032), (905, 5, 2
           (907, 33, 4104), (908, 9, 6152), (909, 300, 1024), (910, 6, 8200), (911, 4, 12288), (912, 3, 16384),
           (913, 260, 520),
           # 1024 rows and more: 256 threads per row (fewer rows use 1024)
-          (914, 1030, 2056), (915, 1024, 12296)]
+          (914, 1030, 2056), (915, 1024, 12296),
+          # 4096 rows and more: the one-pass backward over row slabs (a ragged
+          # last slab; one and several chunks per thread)
+          (916, 4100, 264), (917, 5003, 2056), (918, 4096, 8200)]
 
 
 @pytest.mark.parametrize("case", SHAPES, ids=[f"r{c[1]}_c{c[2]}" for c in SHAPES])
@@ -360,8 +363,9 @@ def test_layernorm_full_size(name, N, h, t):
     assert_close("dbeta", f64(db), dbr, rel_fro=1e-5, max_rel=1e-5)
 
 
-def test_layernorm_deterministic_and_workspace_contents_irrelevant():
-    rows, cols = 300, 2056
+@pytest.mark.parametrize("rows", [300, 4100])
+def test_layernorm_deterministic_and_workspace_contents_irrelevant(rows):
+    cols = 2056
     xb, dyb = I.gen_x(980, rows, cols), I.gen_dy(980, rows, cols)
     gb = I.gen_ln_weight(980, cols)
     bf = dict(dtype=torch.bfloat16, device="cuda")
@@ -385,10 +389,12 @@ def test_layernorm_deterministic_and_workspace_contents_irrelevant():
 
 
 @pytest.mark.parametrize("alias", ["dy", "dres"])
-def test_layernorm_backward_in_place(alias):
+@pytest.mark.parametrize("rows", [40, 4104])
+def test_layernorm_backward_in_place(alias, rows):
     """dx may be the dy or the dres buffer itself: the result (dx, dgamma,
-    dbeta) is bitwise the out-of-place one."""
-    rows, cols = 40, 1544
+    dbeta) is bitwise the out-of-place one, for the few-row form and the
+    one-pass form over row slabs."""
+    cols = 1544
     xb, dyb, drb = I.gen_x(985, rows, cols), I.gen_dy(985, rows, cols), I.normal_bf16([985, 3], (rows, cols))
     gb = I.gen_ln_weight(985, cols)
     bf = dict(dtype=torch.bfloat16, device="cuda")
