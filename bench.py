@@ -136,7 +136,7 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs one tensor-parallel rank's shard on a single "
+        print(f"bench.py measures one GPU: the benchmark runs one tensor-parallel rank's shard on a single "
               f"MI355X (the t shards of a group are run one after another on it); --gpus {args.gpus} "
               f"is not supported.", file=sys.stderr)
         sys.exit(2)
