@@ -55,7 +55,9 @@
  *   Streams    All work is enqueued on `stream` (0 = the null stream) and is
  *              never synchronised; inputs must stay valid until the stream
  *              has passed the work.  Asynchronous faults surface at the
- *              caller's next synchronisation.
+ *              caller's next synchronisation.  The library launches only
+ *              kernels (no memset, copy, allocation or synchronisation), so
+ *              its calls can be captured into a HIP graph on `stream`.
  *   Outputs    Overwritten, never accumulated into.
  *   Errors     Arguments are validated on the host before any launch; an
  *              invalid call returns TP_MLP_ERR_INVALID_ARG (a valid but
