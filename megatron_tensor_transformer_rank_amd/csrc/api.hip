@@ -348,8 +348,46 @@ hipError_t run_nn(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B
   return gemm_launch(GEMM_DOWN, 0, g, num_cu_current(), st);
 }
 
-// C [M, Nc] = A [M, K] @ B^T with B stored [Nc, K], bf16 out.
-hipError_t run_nt(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, void* C, hipStream_t st) {
+// k-slices for an NT product whose 256x192 tile grid fills at most half of
+// the CUs: up to one block per CU, at least NT_SPLIT_MIN_K of k per slice
+// (whole 64-deep k-tiles), at most NT_SPLIT_MAX slices.  0: no split.
+constexpr int NT_SPLIT_MIN_K = 1024;
+constexpr int NT_SPLIT_MAX = 8;
+int nt_slices(int64_t M, int64_t Nc, int64_t K, int num_cu) {
+  const int64_t tiles = ((M + 255) / 256) * ((Nc + 191) / 192);
+  if (tiles * 2 > num_cu) return 0;
+  int64_t s = num_cu / tiles;
+  if (s > K / NT_SPLIT_MIN_K) s = K / NT_SPLIT_MIN_K;
+  if (s > NT_SPLIT_MAX) s = NT_SPLIT_MAX;
+  return s >= 2 ? (int)s : 0;
+}
+
+// C [M, Nc] = A [M, K] @ B^T with B stored [Nc, K], bf16 out.  When the tile
+// grid leaves most CUs idle and `scratch` (device, float32, scratch_floats
+// of them, no contents needed) holds slices * M * Nc partials, the product
+// runs split along k into float32 partials, whose sum in slice order is
+// rounded to bf16 once.
+hipError_t run_nt(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, void* C, hipStream_t st,
+                  float* scratch = nullptr, uint64_t scratch_floats = 0) {
+  const int ncu = num_cu_current();
+  const int s = scratch ? nt_slices(M, Nc, K, ncu) : 0;
+  if (s > 0 && (uint64_t)s * (uint64_t)M * (uint64_t)Nc <= scratch_floats) {
+    GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
+    g.a[0] = g.a[1] = cu16(A);
+    g.a_bytes[0] = g.a_bytes[1] = nbytes(M, K);
+    g.lda = K;
+    g.b[0] = g.b[1] = cu16(B);
+    g.b_bytes[0] = g.b_bytes[1] = nbytes(Nc, K);
+    g.ldb = K;
+    g.kslice = (int)(((K + s - 1) / s + 63) / 64 * 64);
+    const int slices = (int)((K + g.kslice - 1) / g.kslice);
+    g.c0 = scratch;
+    g.ldc = Nc;
+    g.c_slice = M * Nc;
+    hipError_t e = gemm_launch(GEMM_NT_SPLITK, 0, g, ncu, st);
+    if (e != hipSuccess) return e;
+    return ksum_launch(scratch, slices, M * Nc, u16(C), st);
+  }
   GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
   g.a[0] = g.a[1] = cu16(A);
   g.a_bytes[0] = g.a_bytes[1] = nbytes(M, K);
@@ -785,7 +823,8 @@ tp_mlp_status tp_attn_out_bwd_shard(const tp_attn_shape* s, const void* dY, cons
                 {{dY, nbytes(a.N, a.h)}, {O_i, nbytes(a.N, a.q_cols)}, {Wo_i, nbytes(a.q_cols, a.h)}}))
     return TP_MLP_ERR_INVALID_ARG;
   if (a.N == 0) return hip_status(zero_f32_launch(dWo_i, a.q_cols * a.h, num_cu_current(), stream));
-  hipError_t e = run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream);
+  // dWo_i is written after dO_i: until then its storage holds dO_i's k-split partials
+  hipError_t e = run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream, dWo_i, (uint64_t)a.q_cols * a.h);
   if (e == hipSuccess) e = run_tn(a.q_cols, a.h, a.N, O_i, dY, dWo_i, stream);
   return hip_status(e);
 }
@@ -801,7 +840,9 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X, const
                 {{X, nbytes(a.N, a.h)}, {Wqkv_i, nbytes(a.h, a.qkv_cols)}, {dQKV_i, nbytes(a.N, a.qkv_cols)}}))
     return TP_MLP_ERR_INVALID_ARG;
   if (a.N == 0) return hip_status(zero_f32_launch(dWqkv_i, a.h * a.qkv_cols, num_cu_current(), stream));
-  hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV_i, Wqkv_i, dX_partial, stream);
+  // dWqkv_i is written after dX_partial: until then its storage may hold the k-split partials
+  hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV_i, Wqkv_i, dX_partial, stream, dWqkv_i,
+                        (uint64_t)a.h * a.qkv_cols);
   if (e == hipSuccess) e = run_tn(a.h, a.qkv_cols, a.N, X, dQKV_i, dWqkv_i, stream);
   return hip_status(e);
 }

@@ -12,7 +12,8 @@ enum Epi : int {
   EPI_ACT_FWD = 2,          // c0 = act(acc) bf16; e0 (or NULL) = acc bf16 (pre-activation stash)
   EPI_SWIGLU_FWD = 3,       // c0 = SiLU(gate) * up; e0 = gate stash, e1 = up stash (or NULL)
   EPI_ACT_BWD = 4,          // c0 = acc * act'(e0), e0 = pre-activation stash [M, lde]
-  EPI_SWIGLU_BWD = 5        // c0 row = [dG | dP] (ldc = 2*lde); e0 = gate, e1 = up stash (ld = lde)
+  EPI_SWIGLU_BWD = 5,       // c0 row = [dG | dP] (ldc = 2*lde); e0 = gate, e1 = up stash (ld = lde)
+  EPI_STORE_F32_SLICES = 6  // k-split: fp32 partial of slice s at c0 + s*c_slice, [M, ldc]
 };
 
 enum GemmKind : int {
@@ -21,7 +22,8 @@ enum GemmKind : int {
   GEMM_DOWN = 2,       // A_i @ W2_i
   GEMM_DGRAD_ACT = 3,  // dY @ W2_i^T with the activation derivative
   GEMM_WGRAD = 4,      // A^T @ B, both operands contiguous along m / n, fp32 out
-  GEMM_DGRAD = 5       // dU @ W^T (B read [n][k]), one or two k segments
+  GEMM_DGRAD = 5,      // dU @ W^T (B read [n][k]), one or two k segments
+  GEMM_NT_SPLITK = 6   // A @ B^T (B read [n][k]), one segment split along k: fp32 partial per slice
 };
 
 // The product runs over one or two k segments; segment s pairs A columns
@@ -50,8 +52,14 @@ struct GemmArgs {
   void* e0;
   void* e1;
   int64_t lde;
+  // split along k (GEMM_NT_SPLITK only: one segment, EPI_STORE_F32_SLICES):
+  // slice s of a tile covers k in [s*kslice, min(K[0], (s+1)*kslice)),
+  // kslice a multiple of 64, and stores its partial at c0 + s*c_slice
+  // floats.  kslice = 0: no split.
+  int kslice;
+  int64_t c_slice;
   // filled by the launcher
-  int tiles_m, tiles_n;
+  int tiles_m, tiles_n, ksplit;
 };
 
 // Largest operand buffer a GEMM accepts (bytes): buffer resources are 32-bit.

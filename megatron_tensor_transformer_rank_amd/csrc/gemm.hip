@@ -101,14 +101,24 @@ gemm_kernel(const GemmArgs g0, const GemmArgs g1, int nb0) {
   const int L = logical_of(blockIdx.x, gridDim.x);
   const bool second = L >= nb0;
   const GemmArgs g = second ? g1 : g0;
+  // k-split: the problem's tiles repeat once per slice
+  constexpr bool SPLIT = EPI == EPI_STORE_F32_SLICES;
+  int lt = second ? L - nb0 : L, slice = 0;
+  if constexpr (SPLIT) {
+    const int tiles = g.tiles_m * g.tiles_n;
+    slice = lt / tiles;
+    lt -= slice * tiles;
+  }
   int tm, tn;
-  tile_in(second ? L - nb0 : L, g.tiles_m, g.tiles_n, tm, tn);
+  tile_in(lt, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM;
   const int n0 = (BKD == 2) ? tn * (BN / 2) : tn * BN;
 
   const int nseg = g.nseg;
-  const int K0 = g.K[0], K1 = nseg > 1 ? g.K[1] : 0;
-  const int nk0 = (K0 + BK - 1) / BK;
+  const int kbase = SPLIT ? slice * g.kslice : 0;                      // first k of the slice
+  const int K0 = SPLIT ? min(g.K[0], kbase + g.kslice) : g.K[0];        // end of segment 0's range
+  const int K1 = nseg > 1 ? g.K[1] : 0;
+  const int nk0 = (K0 - kbase + BK - 1) / BK;
   const int nk = nk0 + (nseg > 1 ? (K1 + BK - 1) / BK : 0);
 
   // Buffer resource that starts `skip` bytes into an operand and ends with it
@@ -129,7 +139,7 @@ gemm_kernel(const GemmArgs g0, const GemmArgs g1, int nb0) {
   auto ktile = [&](int t) __attribute__((always_inline)) {
     KTile r;
     r.s1 = t >= nk0;
-    r.k0 = (r.s1 ? t - nk0 : t) * BK;
+    r.k0 = r.s1 ? (t - nk0) * BK : kbase + t * BK;
     const int Ks = r.s1 ? K1 : K0;
     r.kvalid = r.k0 < Ks ? Ks - r.k0 : 0;
     return r;
@@ -357,6 +367,14 @@ gemm_kernel(const GemmArgs g0, const GemmArgs g1, int nb0) {
           *reinterpret_cast<float4*>(dst) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
       }
+    } else if constexpr (EPI == EPI_STORE_F32_SLICES) {
+      float* part = static_cast<float*>(g.c0) + (int64_t)slice * g.c_slice + (int64_t)m * g.ldc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + q * QN + j * 16 + 4 * lq;
+        if (n < g.N)
+          *reinterpret_cast<float4*>(part + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
     } else if constexpr (EPI == EPI_ACT_FWD) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
@@ -473,7 +491,8 @@ hipError_t launch_cfg(GemmArgs g0, const GemmArgs* g1p, hipStream_t st) {
   auto tiles = [&](GemmArgs& g) {
     g.tiles_m = (g.M + BM - 1) / BM;
     g.tiles_n = (g.N + cols_per_tile - 1) / cols_per_tile;
-    return (int64_t)g.tiles_m * g.tiles_n;
+    g.ksplit = g.kslice > 0 ? (g.K[0] + g.kslice - 1) / g.kslice : 1;
+    return (int64_t)g.tiles_m * g.tiles_n * g.ksplit;
   };
   GemmArgs g1 = g1p ? *g1p : g0;
   const int64_t nb0 = tiles(g0);
@@ -518,6 +537,8 @@ hipError_t launch_kind(GemmKind kind, int act, const GemmArgs& g, const GemmArgs
       return launch_any<1, 1, EPI_STORE_F32_SPLIT, 0>(g, g1, t, st);
     case GEMM_DGRAD:
       return launch_any<0, 0, EPI_STORE_BF16, 0>(g, g1, t, st);
+    case GEMM_NT_SPLITK:
+      return launch_any<0, 0, EPI_STORE_F32_SLICES, 0>(g, g1, t, st);
   }
   return hipErrorInvalidValue;
 }
@@ -525,7 +546,9 @@ hipError_t launch_kind(GemmKind kind, int act, const GemmArgs& g, const GemmArgs
 }  // namespace
 
 hipError_t gemm_launch(GemmKind kind, int act, const GemmArgs& g, int num_cu, hipStream_t st) {
-  const TileCfg t = choose_tile(g.M, g.N, kind == GEMM_UP_SWIGLU, num_cu);
+  // a k-split repeats the tile grid once per slice: chosen as for M * slices rows
+  const int slices = g.kslice > 0 ? (g.K[0] + g.kslice - 1) / g.kslice : 1;
+  const TileCfg t = choose_tile(g.M * slices, g.N, kind == GEMM_UP_SWIGLU, num_cu);
   return launch_kind(kind, act, g, nullptr, t, st);
 }
 

@@ -9,7 +9,12 @@ rank: QKV_i, Y_i, dO_i, dWo_i, dX_i, dWqkv_i; summed over ranks: Y and dX
 key/value head's gradient summed over its replicas).  Shapes cover plain
 multi-head, grouped-query with key/value heads split across ranks and
 replicated on several ranks, ragged token counts, and the GPT-3-scale and
-Llama-3-70B-scale per-rank widths with sampled rows and columns.  With
+Llama-3-70B-scale per-rank widths with sampled rows and columns.  Input
+gradients whose tile grid fills at most half the CUs run split along k
+(float32 slice partials kept in the weight gradient's storage until it is
+computed): the GPT-3-scale dO, the small-batch cases at the 70B widths, and
+a ragged two-slice case; one case takes the unsplit fallback when that
+storage is too small.  With
 1 <= N <= 64 tokens the forward projections take the small-batch path
 (split-K products streaming each weight once); those token counts are
 covered for several head layouts and at the 70B per-rank widths.
@@ -130,6 +135,12 @@ GROUPS = [
     (703, 77, 384, 16, 8, 32, 4),      # grouped-query, key/value heads split 2 per rank
     (704, 300, 1032, 16, 4, 128, 8),   # 4 key/value heads over 8 ranks
     (705, 33, 136, 4, 1, 64, 1),       # multi-query, unsplit
+    # dO = dY @ W_o^T has few tiles here and runs split along k: 2 slices of
+    # 1088, the last ending mid k-tile (2056 = 32 k-tiles + 8)
+    (706, 333, 2056, 8, 8, 64, 4),
+    # a k-split would be chosen but dW_o (the partials' scratch) is too small
+    # for 2 x 4096 x 128 floats: one unsplit pass
+    (707, 4096, 2048, 8, 2, 64, 4),
 ]
 
 
