@@ -43,6 +43,12 @@ CASES = [
     (105, 530, 384, 1536, 1, "swiglu", False),   # unsplit block
     (106, 8, 64, 128, 2, "relu", False),         # a single partial tile
     (107, 2, 1032, 2080, 2, "gelu", False),      # two tokens (MFMA path, 1 row tile)
+    # the smallest shards the ABI takes: h = 8 and F_i = 8, over 8 and 16 ranks,
+    # and a whole block of 8 x 8 (the one-token path and wide tiles)
+    (108, 40, 8, 64, 8, "swiglu", True),
+    (109, 200, 8, 128, 16, "gelu", False),
+    (111, 1, 8, 8, 1, "gelu", True),
+    (112, 70, 8, 8, 1, "swiglu", False),
     # ReLU with one pre-activation of |U| = 9.3e-8 on rank 1, inside float32
     # accumulation error of zero: the GPU's decision there differs from the
     # exact sign, and both are valid (the comparison follows the GPU's)
