@@ -227,13 +227,39 @@ GEMM_SOURCES = ("gemm.hip", "gemm.h", "tiles.h", "common.h")
 GEMV_SOURCES = ("gemv.hip", "gemv.h", "common.h")
 
 
+def code_only(text: str) -> str:
+    """C/C++ source without its comments, trailing blanks and empty lines (a
+    change of comments alone does not change a kernel)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                       # string or character literal, copied whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash(files):
-    """sha256 over the named kernel sources (csrc/)."""
+    """sha256 over the code of the named kernel sources (csrc/), comments
+    excluded."""
     import hashlib
     hsh = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "megatron_tensor_transformer_rank_amd", "csrc", f), "rb") as fh:
-            hsh.update(fh.read())
+        with open(os.path.join(ROOT, "megatron_tensor_transformer_rank_amd", "csrc", f), encoding="utf-8") as fh:
+            hsh.update(code_only(fh.read()).encode())
     return hsh.hexdigest()
 
 

@@ -37,9 +37,10 @@
 //  * LDS layouts (16-byte chunks XOR-swizzled against bank conflicts):
 //      k-contiguous operand [row][64 k]: chunk c of row r at slot c ^ (r & 7),
 //        fragments read with ds_read_b128;
-//      m/n-contiguous operand [64 k][R]: chunk c of k-row r at c ^ 2(r & 3),
-//        fragments read with ds_read_b64_tr_b16 (the LDS transpose read), two
-//        per 8-k fragment.
+//      m/n-contiguous operand [64 k][R]: chunk c of k-row r at slot
+//        c ^ mn_swz(r) (2(r & 3), and bit 3 of r moving the two 16-lane
+//        halves of a read to different bank halves), fragments read with
+//        ds_read_b64_tr_b16 (the LDS transpose read), two per 8-k fragment.
 //  * The MFMA takes the operands swapped (B fragment first) so each lane holds
 //    4 consecutive output columns: 8-byte bf16 / 16-byte fp32 stores.
 //  * Block ids are remapped so consecutive tiles land on one XCD (blocks are
@@ -47,9 +48,13 @@
 //    M so the tiles an XCD runs together share operand panels in its L2.
 //  * Epilogues: plain bf16 / fp32 store (column split into two buffers),
 //    ReLU / GeLU with the pre-activation stash, SwiGLU with gate and up
-//    accumulated in the same wave (separate gate / up LDS regions), and the
-//    activation derivative reading the stash.  Group 0's epilogue overlaps
-//    group 1's last compute phase.
+//    accumulated in the same wave (separate gate / up LDS regions), the
+//    activation derivative reading the stash, and fp32 k-slice partials.
+//    Group 0's epilogue overlaps group 1's last compute phase.
+//  * One launch may carry two problems of the same kind (both weight
+//    gradients), their tiles sharing the waves; an NT product whose tile grid
+//    leaves most CUs idle may run split along k (each k-slice a repeat of the
+//    tile grid, fp32 partials summed afterwards in slice order).
 #include "common.h"
 #include "gemm.h"
 #include "tiles.h"
