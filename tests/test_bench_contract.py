@@ -30,3 +30,17 @@ def test_counter_summaries_parse():
         # None only when the kernels changed after the counters were taken
         if info is not None:
             assert info["bytes"] > 0 and info["algorithmic_bytes"] > 0
+
+
+def test_source_hash_ignores_comments_only():
+    """The counter summaries are keyed to the kernels' code: comments and
+    blank lines do not change the hash, any code (strings included) does."""
+    import bench
+    a = 'int f() { return 1; }  // one\n/* block\n comment */\nconst char* s = "x // not a comment";\n'
+    b = 'int f() { return 1; }\n\n// another comment\nconst char* s = "x // not a comment";   \n'
+    c = 'int f() { return 2; }\nconst char* s = "x // not a comment";\n'
+    d = 'int f() { return 1; }\nconst char* s = "x // still not one";\n'
+    assert bench.code_only(a) == bench.code_only(b)
+    assert bench.code_only(a) != bench.code_only(c)
+    assert bench.code_only(a) != bench.code_only(d)
+    assert "/*" not in bench.code_only(a) and "// one" not in bench.code_only(a)
