@@ -20,6 +20,7 @@ host cores on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -71,11 +72,18 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev):
     sw = w.act == "swiglu"
     N, h, Fi, t = w.N, w.h, w.Fi, w.t
     log(f"[bench] generating inputs for {w.name}: N={N} h={h} F_i={Fi} t={t} act={w.act}")
-    X, dY = to_dev(I.gen_x(w.wid, N, h)), to_dev(I.gen_dy(w.wid, N, h))
-    W1 = to_dev(I.gen_w_up_shard(w.wid, h, Fi, 0))
-    W2 = to_dev(I.gen_w_down_shard(w.wid, h, Fi, 0))
-    Wg = to_dev(I.gen_w_gate_shard(w.wid, h, Fi, 0)) if sw else None
-    b2 = to_dev(I.gen_b2(w.wid, h)) if w.bias else None
+    host = {"X": I.gen_x(w.wid, N, h), "dY": I.gen_dy(w.wid, N, h), "W1_i": I.gen_w_up_shard(w.wid, h, Fi, 0),
+            "W2_i": I.gen_w_down_shard(w.wid, h, Fi, 0)}
+    if sw:
+        host["Wg_i"] = I.gen_w_gate_shard(w.wid, h, Fi, 0)
+    if w.bias:
+        host["b2"] = I.gen_b2(w.wid, h)
+    # the bf16 bit patterns' digests: the inputs can be regenerated and checked
+    digests = {k: hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()[:16] for k, v in host.items()}
+    X, dY, W1, W2 = (to_dev(host[k]) for k in ("X", "dY", "W1_i", "W2_i"))
+    Wg = to_dev(host["Wg_i"]) if sw else None
+    b2 = to_dev(host["b2"]) if w.bias else None
+    del host
     shape = B.make_shape(N, h, w.F, t, 0, w.act)
     Y = torch.empty(N, h, dtype=bf, device=dev)
     A = torch.empty(N, Fi, dtype=bf, device=dev)
@@ -132,7 +140,7 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev):
     log(f"[bench] {w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {t_wall * 1e3 / steps:.3f} ms/step)")
     kern_ms = {name: float(np.mean([evs[s * nk + j].elapsed_time(evs[s * nk + j + 1]) for s in range(steps)]))
                for j, (name, _, _) in enumerate(kernels)}
-    return {"ms": ms, "tflops": tflops, "kern_ms": kern_ms, "flops": flops,
+    return {"ms": ms, "tflops": tflops, "kern_ms": kern_ms, "flops": flops, "inputs_sha256": digests,
             "gemms": [(n, fl) for n, fl, _ in kernels if fl > 0]}
 
 
@@ -182,7 +190,8 @@ def main():
         "config": {"workload": w.name, "N": N, "h": h, "F": w.F, "t": t, "F_i": Fi, "act": w.act,
                    "bias": w.bias, "step": "one rank fwd+bwd + local reduce of t partials (Y and dX)",
                    "flops_per_step": flops, "tokens_per_s": round(N / (ms * 1e-3), 1),
-                   "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
+                   "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                   "inputs_sha256": st["inputs_sha256"]},
         "roofline": roofline,
         "kernels_ms": {k: round(v, 4) for k, v in kern_ms.items()},
         "copy_probe": copy,
@@ -255,7 +264,6 @@ def code_only(text: str) -> str:
 def source_hash(files):
     """sha256 over the code of the named kernel sources (csrc/), comments
     excluded."""
-    import hashlib
     hsh = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "megatron_tensor_transformer_rank_amd", "csrc", f), encoding="utf-8") as fh:

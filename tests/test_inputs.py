@@ -43,3 +43,18 @@ def test_distribution_scale():
     w = inputs.gen_w_up_shard(4, 256, 512, 0).view(np.uint16)
     v = (w.astype(np.uint32) << 16).view(np.float32)
     assert abs(v.std() - 0.02) < 0.001
+
+
+def test_headline_inputs_are_the_recorded_bit_patterns():
+    """The benchmark records sha256 digests of the GPT-3 shard's inputs; the
+    seeded generator must keep producing exactly those bf16 bit patterns."""
+    import hashlib
+    import numpy as np
+    from megatron_tensor_transformer_rank_amd import inputs as I
+    from megatron_tensor_transformer_rank_amd.configs import WORKLOADS
+    w = WORKLOADS["gpt3_train_t8"]
+    got = {"X": I.gen_x(w.wid, w.N, w.h), "dY": I.gen_dy(w.wid, w.N, w.h),
+           "W1_i": I.gen_w_up_shard(w.wid, w.h, w.Fi, 0), "W2_i": I.gen_w_down_shard(w.wid, w.h, w.Fi, 0)}
+    want = {"X": "09a4ef6fbfa94e81", "dY": "2500d0d2a9f120c7", "W1_i": "a3d18f88a64d416b", "W2_i": "ac5c9430f95133f3"}
+    for k, v in got.items():
+        assert hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()[:16] == want[k], k
