@@ -66,7 +66,7 @@ def assert_relu_grad(name: str, gpu_dU, ref_dU, ref_dA, X, W1, rel_fro=REL_FRO, 
         ok = (np.abs(g) <= tol) | (np.abs(g - a) <= tol)
         assert np.all(ok), f"{name}: {int((~ok).sum())} of {int(amb.sum())} sign-ambiguous elements are neither 0 nor dA"
         ref_dU = np.array(ref_dU, dtype=np.float64)
-        ref_dU[amb] = np.where(np.abs(g) <= tol, 0.0, a)
+        ref_dU[amb] = np.where(np.abs(g - a) < np.abs(g), a, 0.0)   # the nearer of the two decisions
         gpu[amb] = ref_dU[amb]
     assert_close(name, gpu, ref_dU, rel_fro, max_rel)
     return ref_dU

@@ -56,3 +56,17 @@ def test_ambiguous_element_with_another_value_fails():
     g[5, 7] = dA[5, 7] + 2 * np.abs(dU).max()
     with pytest.raises(AssertionError):
         assert_relu_grad("dU", g, dU, dA, X, W1)
+
+
+def test_small_dA_decision_is_followed_downstream():
+    """Where dA itself is small, the GPU's positive decision (dU = dA) must
+    still be taken into the reference for the gradients computed from dU:
+    with one token, dW1 = x^T dU makes every column follow one decision."""
+    X, W1, U, dA, dU = _case()
+    dA = dA.copy()
+    dA[5, 7] = 1e-3 * np.abs(dA).max()          # small, below the elementwise tolerance
+    dU = oracle.act_backward("relu", dA, U)      # exact decision at U = 0: zero
+    g = dU.copy()
+    g[5, 7] = dA[5, 7]                           # the GPU decided positive
+    ref = assert_relu_grad("dU", g, dU, dA, X, W1)
+    assert ref[5, 7] == dA[5, 7]
