@@ -162,11 +162,15 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev):
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / steps
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_evs]))
+    # one step each: from the event before the dominant kernel to the same event of the next step
+    per_step = [dev_evs[s][0].elapsed_time(dev_evs[s + 1][0]) for s in range(steps - 1)]
     flops = w.flops_train()
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {w.name}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {t_wall * 1e3 / steps:.3f} ms/step; "
         f"{ms_all_events:.3f} ms/step with an event after every kernel); {dom} {dom_ms:.3f} ms")
     return {"ms": ms, "tflops": tflops, "kern_ms": kern_ms, "ms_all_events": ms_all_events, "dom": dom,
+            "step_ms_median": float(np.median(per_step)) if per_step else ms,
+            "step_ms_min": float(np.min(per_step)) if per_step else ms,
             "dom_ms": dom_ms, "flops": flops, "inputs_sha256": digests, "gemms": gemms}
 
 
@@ -222,6 +226,7 @@ def main():
         "roofline": roofline,
         "kernels_ms": {k: round(v, 4) for k, v in kern_ms.items()},
         "ms_per_step_event_per_kernel": round(st["ms_all_events"], 4),
+        "step_ms_median": round(st["step_ms_median"], 4), "step_ms_min": round(st["step_ms_min"], 4),
         "copy_probe": copy,
     }
 
@@ -545,6 +550,18 @@ def bench_ln(B, I, torch, to_dev, name, N, h, t):
     return out
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (None where absent)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, rows, I, target_s=10.0, cap_s=30.0):
     """The fp64 oracle (as it stands) on a bounded sample of the workload:
     chunks of `rows` token rows of rank 0's shard, forward + backward, on the
@@ -579,7 +596,7 @@ def cpu_baseline(w, rows, I, target_s=10.0, cap_s=30.0):
         r0 = (r0 + rows) % w.N
     fl = 6 * done_rows * w.h * w.Fi * (w.g + 1)
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "cpu_model": cpu_model(), "full_run": False, "seconds": round(dt, 3),
             "sample": f"{done_rows} token rows (chunks of {rows}, wrapping over the {w.N}) of rank 0's shard "
                       f"of {w.name}, forward + backward, {fl:.3e} algorithmic FLOPs; numpy float64 on the "
                       f"host BLAS; GPU/CPU ratio = value / this value"}
