@@ -62,7 +62,7 @@ def parse():
 def train_step(w, steps, warmup, B, I, torch, np, to_dev):
     """Time `steps` passes of rank 0's whole hot path for workload w: forward,
     reduce of the t partial sums (+ bias), backward (+ bias gradient), reduce
-    of the t dX partials, launched through the one-kernel entry points (the
+    of the t dX partials, launched through the step entry points (the
     composite entry points launch exactly these kernels in this order).
 
     Two timed passes of `steps` steps each, after `warmup` untimed ones:
@@ -116,9 +116,9 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev):
         ("up_act", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_act_shard(shape, X, W1, Wg, A, U, G)),
         ("down", 2 * N * h * Fi, lambda: B.tp_mlp_down_shard(shape, A, W2, Y)),
         ("reduce_y", 0, lambda: B.tp_mlp_reduce_partials_local([Y] + others_y, Yred, bias=b2)),
-        ("down_dgrad_act", 2 * N * h * Fi, lambda: B.tp_mlp_down_dgrad_act_shard(shape, dY, W2, U, G, dU)),
-        ("wgrad", 2 * N * h * Fi * (1 + w.g), lambda: B.tp_mlp_wgrad_shard(shape, X, A, dY, dU, dW1, dW2, dWg)),
-        ("up_dgrad", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_dgrad_shard(shape, dU, W1, Wg, dX)),
+        # dU and dW2 (one mixed launch at these sizes), then dX_partial and dW1 (dWg)
+        ("down_bwd", 4 * N * h * Fi, lambda: B.tp_mlp_down_bwd_shard(shape, dY, W2, U, G, A, dU, dW2)),
+        ("up_bwd", 4 * N * h * Fi * w.g, lambda: B.tp_mlp_up_bwd_shard(shape, X, dU, W1, Wg, dX, dW1, dWg)),
     ]
     if w.bias:
         kernels.append(("bias_grad", 0, lambda: B.tp_mlp_bias_grad(dY, db2, ws_db)))

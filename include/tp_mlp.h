@@ -307,6 +307,31 @@ tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i,
                                     const void* W1_i, const void* Wg_i,
                                     void* dX_partial, hipStream_t stream);
 
+/* The down-projection's backward, the first half of what tp_mlp_bwd_shard
+ * runs: dU_i as tp_mlp_down_dgrad_act_shard and dW2_i = A_i^T @ dY as
+ * tp_mlp_down_wgrad_shard.  Both need only the forward's outputs and dY, so
+ * they share one launch when their block tiles fill the GPU at least once
+ * (the tiles of the longer product are dispatched first, the other's fill
+ * in behind them); otherwise they run one after the other.  Each element is
+ * summed in the same order either way: the results are bitwise those of the
+ * separate calls.  N = 0: dW2_i is written as zeros. */
+tp_mlp_status tp_mlp_down_bwd_shard(const tp_mlp_shape* s, const void* dY,
+                                    const void* W2_i, const void* U_i,
+                                    const void* G_i, const void* A_i,
+                                    void* dU_i, float* dW2_i,
+                                    hipStream_t stream);
+
+/* The up-projection's backward, the second half of what tp_mlp_bwd_shard
+ * runs: dX_partial as tp_mlp_up_dgrad_shard and dW1_i (dWg_i) as
+ * tp_mlp_up_wgrad_shard, both from dU_i, in one launch or two as for
+ * tp_mlp_down_bwd_shard, bitwise equal to the separate calls.  N = 0: the
+ * weight gradients are written as zeros. */
+tp_mlp_status tp_mlp_up_bwd_shard(const tp_mlp_shape* s, const void* X,
+                                  const void* dU_i, const void* W1_i,
+                                  const void* Wg_i, void* dX_partial,
+                                  float* dW1_i, float* dWg_i,
+                                  hipStream_t stream);
+
 /* db2 = column sums of dY [rows, cols] (fp32 out [cols]): the gradient of the
  * output bias that is added once after the reduction.  Deterministic
  * (fixed-order float32 sums).  workspace: device scratch of at least

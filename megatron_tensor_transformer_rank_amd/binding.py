@@ -87,6 +87,8 @@ _SIGS = {
     "tp_mlp_up_wgrad_shard": [POINTER(Shape)] + [c_void_p] * 4 + [c_void_p],
     "tp_mlp_up_dgrad_shard": [POINTER(Shape)] + [c_void_p] * 4 + [c_void_p],
     "tp_mlp_wgrad_shard": [POINTER(Shape)] + [c_void_p] * 7 + [c_void_p],
+    "tp_mlp_down_bwd_shard": [POINTER(Shape)] + [c_void_p] * 7 + [c_void_p],
+    "tp_mlp_up_bwd_shard": [POINTER(Shape)] + [c_void_p] * 7 + [c_void_p],
     "tp_mlp_bias_grad": [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p],
     "tp_attn_qkv_shard": [POINTER(AttnShape)] + [c_void_p] * 4 + [c_size_t, c_void_p],
     "tp_attn_out_shard": [POINTER(AttnShape)] + [c_void_p] * 4 + [c_size_t, c_void_p],
@@ -317,6 +319,27 @@ def tp_mlp_up_dgrad_shard(shape: Shape, dU_i, W1_i, Wg_i, dX_partial, stream=Non
         ctypes.byref(shape), _p(dU_i, BF16, N * g * Fi, "dU_i"), _p(W1_i, BF16, h * Fi, "W1_i"),
         _p(Wg_i, BF16, h * Fi, "Wg_i", optional=True), _p(dX_partial, BF16, N * h, "dX_partial"),
         _stream(stream)))
+
+
+def tp_mlp_down_bwd_shard(shape: Shape, dY, W2_i, U_i, G_i, A_i, dU_i, dW2_i, stream=None):
+    """dU_i (dgrad through W2 with the activation derivative) and dW2_i =
+    A_i^T dY: the first half of the composite backward."""
+    N, h, Fi, g = shape.n_tokens, shape.hidden, shape.Fi, shape.g
+    _check("tp_mlp_down_bwd_shard", lib().tp_mlp_down_bwd_shard(
+        ctypes.byref(shape), _p(dY, BF16, N * h, "dY"), _p(W2_i, BF16, Fi * h, "W2_i"),
+        _p(U_i, BF16, N * Fi, "U_i"), _p(G_i, BF16, N * Fi, "G_i", optional=True), _p(A_i, BF16, N * Fi, "A_i"),
+        _p(dU_i, BF16, N * g * Fi, "dU_i"), _p(dW2_i, F32, Fi * h, "dW2_i"), _stream(stream)))
+
+
+def tp_mlp_up_bwd_shard(shape: Shape, X, dU_i, W1_i, Wg_i, dX_partial, dW1_i, dWg_i=None, stream=None):
+    """dX_partial = dU_i W1_i^T and dW1_i (dWg_i) = X^T dU_i: the second half
+    of the composite backward."""
+    N, h, Fi, g = shape.n_tokens, shape.hidden, shape.Fi, shape.g
+    _check("tp_mlp_up_bwd_shard", lib().tp_mlp_up_bwd_shard(
+        ctypes.byref(shape), _p(X, BF16, N * h, "X"), _p(dU_i, BF16, N * g * Fi, "dU_i"),
+        _p(W1_i, BF16, h * Fi, "W1_i"), _p(Wg_i, BF16, h * Fi, "Wg_i", optional=True),
+        _p(dX_partial, BF16, N * h, "dX_partial"), _p(dW1_i, F32, h * Fi, "dW1_i"),
+        _p(dWg_i, F32, h * Fi, "dWg_i", optional=True), _stream(stream)))
 
 
 def tp_mlp_bias_grad(dY, db2, workspace, stream=None):

@@ -177,8 +177,7 @@ hipError_t run_down(const Dims& d, const void* A, const void* W2, void* Y, hipSt
   return gemm_launch(GEMM_DOWN, d.act, g, num_cu_current(), st);
 }
 
-hipError_t run_dgrad_act(const Dims& d, const void* dY, const void* W2, const void* U, const void* G, void* dU,
-                         hipStream_t st) {
+GemmArgs dgrad_act_args(const Dims& d, const void* dY, const void* W2, const void* U, const void* G, void* dU) {
   GemmArgs g = one_segment((int)d.N, (int)d.Fi, (int)d.h);
   g.a[0] = g.a[1] = cu16(dY);
   g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.h);
@@ -196,7 +195,12 @@ hipError_t run_dgrad_act(const Dims& d, const void* dY, const void* W2, const vo
     g.ldc = d.Fi;
     g.e0 = const_cast<void*>(U);
   }
-  return gemm_launch(GEMM_DGRAD_ACT, d.act, g, num_cu_current(), st);
+  return g;
+}
+
+hipError_t run_dgrad_act(const Dims& d, const void* dY, const void* W2, const void* U, const void* G, void* dU,
+                         hipStream_t st) {
+  return gemm_launch(GEMM_DGRAD_ACT, d.act, dgrad_act_args(d, dY, W2, U, G, dU), num_cu_current(), st);
 }
 
 GemmArgs wgrad_down_args(const Dims& d, const void* A, const void* dY, float* dW2) {
@@ -255,7 +259,7 @@ hipError_t run_wgrads(const Dims& d, const void* X, const void* A, const void* d
                       num_cu_current(), st);
 }
 
-hipError_t run_dgrad_up(const Dims& d, const void* dU, const void* W1, const void* Wg, void* dX, hipStream_t st) {
+GemmArgs dgrad_up_args(const Dims& d, const void* dU, const void* W1, const void* Wg, void* dX) {
   GemmArgs g = one_segment((int)d.N, (int)d.h, (int)d.Fi);
   g.a[0] = g.a[1] = cu16(dU);
   g.a_bytes[0] = g.a_bytes[1] = nbytes(d.N, d.g * d.Fi);
@@ -274,7 +278,38 @@ hipError_t run_dgrad_up(const Dims& d, const void* dU, const void* W1, const voi
   }
   g.c0 = dX;
   g.ldc = d.h;
-  return gemm_launch(GEMM_DGRAD, d.act, g, num_cu_current(), st);
+  return g;
+}
+
+hipError_t run_dgrad_up(const Dims& d, const void* dU, const void* W1, const void* Wg, void* dX, hipStream_t st) {
+  return gemm_launch(GEMM_DGRAD, d.act, dgrad_up_args(d, dU, W1, Wg, dX), num_cu_current(), st);
+}
+
+// An input gradient and the weight gradient computed from the same inputs
+// run as one mixed grid of 256x256 tiles when those tiles fill every CU at
+// least once (gemm_launch_mixed); with fewer tiles, as two launches, each
+// with its own tile choice.  Either way each element is summed over k in
+// the same order, so the results are bitwise the same.
+int64_t tiles256(const GemmArgs& g) { return (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256); }
+hipError_t run_pair(GemmKind kp, int act, const GemmArgs& p, const GemmArgs& q, hipStream_t st) {
+  const int ncu = num_cu_current();
+  if (tiles256(p) + tiles256(q) >= ncu) return gemm_launch_mixed(kp, act, p, q, nullptr, st);
+  hipError_t e = gemm_launch(kp, act, p, ncu, st);
+  if (e == hipSuccess) e = gemm_launch(GEMM_WGRAD, act, q, ncu, st);
+  return e;
+}
+
+// The down-projection's backward: dU (dgrad through W2 with the activation
+// derivative) and dW2 = A_i^T dY.
+hipError_t run_down_bwd(const Dims& d, const void* dY, const void* W2, const void* U, const void* G, const void* A,
+                        void* dU, float* dW2, hipStream_t st) {
+  return run_pair(GEMM_DGRAD_ACT, d.act, dgrad_act_args(d, dY, W2, U, G, dU), wgrad_down_args(d, A, dY, dW2), st);
+}
+
+// The up-projection's backward: dX_partial = dU W1_i^T and dW1 (dWg) = X^T dU.
+hipError_t run_up_bwd(const Dims& d, const void* X, const void* dU, const void* W1, const void* Wg, void* dX,
+                      float* dW1, float* dWg, hipStream_t st) {
+  return run_pair(GEMM_DGRAD, d.act, dgrad_up_args(d, dU, W1, Wg, dX), wgrad_up_args(d, X, dU, dW1, dWg), st);
 }
 
 // ------------------------------------------------------- attention projections
@@ -684,6 +719,38 @@ tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i, con
   return hip_status(run_dgrad_up(d, dU_i, W1_i, Wg_i, dX_partial, stream));
 }
 
+tp_mlp_status tp_mlp_down_bwd_shard(const tp_mlp_shape* s, const void* dY, const void* W2_i, const void* U_i,
+                                    const void* G_i, const void* A_i, void* dU_i, float* dW2_i, hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  const bool sw = d.act == ACT_SWIGLU;
+  const uint64_t a = (uint64_t)d.N * d.Fi * 2, y = (uint64_t)d.N * d.h * 2;
+  if (!req_n(dY, y) || !req(W2_i) || !req_n(U_i, a) || !req_n(A_i, a) || !req_n(dU_i, a) || !req(dW2_i))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (sw ? !req_n(G_i, a) : G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dU_i, a * d.g}, {dW2_i, (uint64_t)d.Fi * d.h * 4}},
+                {{dY, y}, {W2_i, (uint64_t)d.Fi * d.h * 2}, {U_i, a}, {G_i, a}, {A_i, a}}))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (d.N == 0) return hip_status(zero_f32_launch(dW2_i, d.Fi * d.h, num_cu_current(), stream));
+  return hip_status(run_down_bwd(d, dY, W2_i, U_i, G_i, A_i, dU_i, dW2_i, stream));
+}
+
+tp_mlp_status tp_mlp_up_bwd_shard(const tp_mlp_shape* s, const void* X, const void* dU_i, const void* W1_i,
+                                  const void* Wg_i, void* dX_partial, float* dW1_i, float* dWg_i,
+                                  hipStream_t stream) {
+  Dims d;
+  if (const tp_mlp_status ss = shape_status(s, d)) return ss;
+  const bool sw = d.act == ACT_SWIGLU;
+  const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, du = (uint64_t)d.N * d.g * d.Fi * 2;
+  if (!req_n(X, x) || !req_n(dU_i, du) || !req(W1_i) || !req_n(dX_partial, x) || !req(dW1_i))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (sw ? (!req(Wg_i) || !req(dWg_i)) : (Wg_i != nullptr || dWg_i != nullptr)) return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dX_partial, x}, {dW1_i, w * 2}, {dWg_i, w * 2}}, {{X, x}, {dU_i, du}, {W1_i, w}, {Wg_i, w}}))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (d.N == 0) return hip_status(zero_wgrads(d, dW1_i, dWg_i, nullptr, stream));
+  return hip_status(run_up_bwd(d, X, dU_i, W1_i, Wg_i, dX_partial, dW1_i, dWg_i, stream));
+}
+
 tp_mlp_status tp_mlp_bias_grad(const void* dY, int64_t rows, int64_t cols, float* db2, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
   if (const tp_mlp_status bs = block_status(rows, cols)) return bs;
@@ -726,9 +793,8 @@ tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X, const void*
     if (e == hipSuccess) e = zero_f32_launch(db2, d.h, num_cu_current(), stream);
     return hip_status(e);
   }
-  hipError_t e = run_dgrad_act(d, dY, W2_i, U_i, G_i, dU_i, stream);
-  if (e == hipSuccess) e = run_wgrads(d, X, A_i, dY, dU_i, dW1_i, dWg_i, dW2_i, stream);
-  if (e == hipSuccess) e = run_dgrad_up(d, dU_i, W1_i, Wg_i, dX_partial, stream);
+  hipError_t e = run_down_bwd(d, dY, W2_i, U_i, G_i, A_i, dU_i, dW2_i, stream);
+  if (e == hipSuccess) e = run_up_bwd(d, X, dU_i, W1_i, Wg_i, dX_partial, dW1_i, dWg_i, stream);
   if (e == hipSuccess && db2 != nullptr)
     e = col_sum_launch(cu16(dY), d.N, d.h, db2, static_cast<float*>(workspace), stream);
   return hip_status(e);

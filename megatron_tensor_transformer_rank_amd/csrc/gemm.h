@@ -71,4 +71,12 @@ hipError_t gemm_launch(GemmKind kind, int act, const GemmArgs& g, int num_cu, hi
 // wave of each is filled by the other's.
 hipError_t gemm_launch2(GemmKind kind, int act, const GemmArgs& g0, const GemmArgs& g1, int num_cu, hipStream_t st);
 
+// An input gradient (kind kp: GEMM_DGRAD_ACT with activation act, or
+// GEMM_DGRAD) and weight gradients (GEMM_WGRAD: q0, and q1 unless NULL) in
+// one launch of 256x256 tiles: the problem with longer tiles is dispatched
+// first on every XCD and the other fills in behind it.  Each output element
+// is summed over k in the same order as in the separate launches.
+hipError_t gemm_launch_mixed(GemmKind kp, int act, const GemmArgs& p, const GemmArgs& q0, const GemmArgs* q1,
+                             hipStream_t st);
+
 }  // namespace tpmlp

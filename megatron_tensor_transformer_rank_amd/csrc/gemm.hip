@@ -82,13 +82,11 @@ __device__ __forceinline__ void tile_in(int logical, int tiles_m, int tiles_n, i
   tn = in_group / gsz;
 }
 
-// One launch may run two problems of the same kind (g0's nb0 tiles, then
-// g1's): the logical tiles of both are laid out over the XCDs together, so
-// neither leaves a partial last wave on its own.  A single problem passes
-// g1 = g0 and nb0 = the grid size.
+// One block tile of problem g: logical tile lt of its (XCD-ordered) grid;
+// with a k-split, lt also counts the slice (the tile grid repeats once per
+// slice).  smem holds the two LDS stages.
 template <int BM, int BN, int AK, int BKD, int EPI, int ACT>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
-gemm_kernel(const GemmArgs g0, const GemmArgs g1, int nb0) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs g, int lt, uint8_t* smem) {
   constexpr int HM = BM / 2;                 // rows per group
   constexpr int QN = BN / 4;                 // B-region columns per wave
   constexpr int TM = HM / 16, TN = QN / 16;  // 16x16 blocks per wave
@@ -98,17 +96,13 @@ gemm_kernel(const GemmArgs g0, const GemmArgs g1, int nb0) {
   constexpr int QF = BN / 8;                 // SwiGLU: features per wave
   static_assert(BKD != 2 || (BN == 128 || BN == 256), "SwiGLU tile width");
   static_assert(HM % 64 == 0 && QN % 16 == 0, "tile shape");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = w >> 2, q = w & 3;
-  const int L = logical_of(blockIdx.x, gridDim.x);
-  const bool second = L >= nb0;
-  const GemmArgs g = second ? g1 : g0;
   // k-split: the problem's tiles repeat once per slice
   constexpr bool SPLIT = EPI == EPI_STORE_F32_SLICES;
-  int lt = second ? L - nb0 : L, slice = 0;
+  int slice = 0;
   if constexpr (SPLIT) {
     const int tiles = g.tiles_m * g.tiles_n;
     slice = lt / tiles;
@@ -452,6 +446,65 @@ gemm_kernel(const GemmArgs g0, const GemmArgs g1, int nb0) {
   }
 }
 
+template <int BM, int BN>
+constexpr int stage_bytes() { return 2 * (BM / 2) * 128 + BN * 128; }
+
+// One launch may run two problems of the same kind (g0's nb0 tiles, then
+// g1's): the logical tiles of both are laid out over the XCDs together, so
+// neither leaves a partial last wave on its own.  A single problem passes
+// g1 = g0 and nb0 = the grid size.
+template <int BM, int BN, int AK, int BKD, int EPI, int ACT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
+gemm_kernel(const GemmArgs g0, const GemmArgs g1, int nb0) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * stage_bytes<BM, BN>()];
+  const int L = logical_of(blockIdx.x, gridDim.x);
+  const bool second = L >= nb0;
+  const GemmArgs g = second ? g1 : g0;
+  gemm_tile<BM, BN, AK, BKD, EPI, ACT>(g, second ? L - nb0 : L, smem);
+}
+
+// Mixed grid: the nf tiles of one problem and the tiles of another (a pair
+// of the same kind: gs0's ns0 tiles, then gs1's) share one launch.  Every
+// XCD runs its share of the first problem's tiles, then its share of the
+// second's: with the longer tiles first (the host orders them), the short
+// tiles fill in behind them and even out the CUs' finishing times, and the
+// tiles of the two problems end at different times, so their output writes
+// do not all fall together.
+//
+// Blocks are dispatched round-robin over the 8 XCDs: XCD x runs blocks
+// pid = x + 8j, j = 0, 1, ..., in order.
+__device__ __forceinline__ void mixed_of(int pid, int nf, int nb, bool& first, int& idx) {
+  const int x = pid & 7, j = pid >> 3;
+  const int fq = nf >> 3, fr = nf & 7;
+  const int cnt_f = fq + (x < fr ? 1 : 0);
+  const int start_f = x * fq + min(x, fr);
+  if (j < cnt_f) {
+    first = true;
+    idx = start_f + j;
+    return;
+  }
+  const int start_all = x * (nb >> 3) + min(x, nb & 7);  // blocks on XCDs before x
+  first = false;
+  idx = start_all - start_f + (j - cnt_f);
+}
+
+template <int BM, int BN, int AKp, int BKDp, int EPIp, int ACTp, int AKq, int BKDq, int EPIq, int ACTq>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
+gemm_mixed_kernel(const GemmArgs gp, const GemmArgs gq0, const GemmArgs gq1, int np, int nq0, int p_first) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * stage_bytes<BM, BN>()];
+  const int nb = gridDim.x;
+  bool first;
+  int idx;
+  mixed_of(blockIdx.x, p_first ? np : nb - np, nb, first, idx);
+  if (first == (p_first != 0)) {
+    gemm_tile<BM, BN, AKp, BKDp, EPIp, ACTp>(gp, idx, smem);
+  } else {
+    const bool second = idx >= nq0;
+    const GemmArgs g = second ? gq1 : gq0;
+    gemm_tile<BM, BN, AKq, BKDq, EPIq, ACTq>(g, second ? idx - nq0 : idx, smem);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: tile choice and launch.
 // ---------------------------------------------------------------------------
@@ -560,6 +613,46 @@ hipError_t gemm_launch(GemmKind kind, int act, const GemmArgs& g, int num_cu, hi
 hipError_t gemm_launch2(GemmKind kind, int act, const GemmArgs& g0, const GemmArgs& g1, int num_cu, hipStream_t st) {
   const TileCfg t = choose_tile(g0.M, g0.N, kind == GEMM_UP_SWIGLU, num_cu, g1.M, g1.N);
   return launch_kind(kind, act, g0, &g1, t, st);
+}
+
+namespace {
+
+int k_tiles(const GemmArgs& g) {
+  return (g.K[0] + BK - 1) / BK + (g.nseg > 1 ? (g.K[1] + BK - 1) / BK : 0);
+}
+
+template <int BM, int BN, int AKp, int BKDp, int EPIp, int ACTp>
+hipError_t launch_mixed_wgrad(GemmArgs p, GemmArgs q0, const GemmArgs* q1p, hipStream_t st) {
+  auto tiles = [](GemmArgs& g) {
+    g.tiles_m = (g.M + BM - 1) / BM;
+    g.tiles_n = (g.N + BN - 1) / BN;
+    g.ksplit = 1;
+    return (int64_t)g.tiles_m * g.tiles_n;
+  };
+  GemmArgs q1 = q1p ? *q1p : q0;
+  const int64_t np = tiles(p), nq0 = tiles(q0);
+  const int64_t nq = q1p ? nq0 + tiles(q1) : nq0;
+  if (!q1p) q1 = q0;
+  const int64_t nb = np + nq;
+  if (nb <= 0) return hipSuccess;
+  if (nb > 0x7fffffff) return hipErrorInvalidValue;
+  // the problem with more k-tiles per block tile is dispatched first
+  const int kq = q1p ? (k_tiles(q0) > k_tiles(q1) ? k_tiles(q0) : k_tiles(q1)) : k_tiles(q0);
+  const int p_first = k_tiles(p) >= kq ? 1 : 0;
+  hipLaunchKernelGGL((gemm_mixed_kernel<BM, BN, AKp, BKDp, EPIp, ACTp, 1, 1, EPI_STORE_F32_SPLIT, 0>), dim3((unsigned)nb),
+                     dim3(NT), 0, st, p, q0, q1, (int)np, (int)nq0, p_first);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gemm_launch_mixed(GemmKind kp, int act, const GemmArgs& p, const GemmArgs& q0, const GemmArgs* q1,
+                             hipStream_t st) {
+  if (kp == GEMM_DGRAD) return launch_mixed_wgrad<256, 256, 0, 0, EPI_STORE_BF16, 0>(p, q0, q1, st);
+  if (kp != GEMM_DGRAD_ACT) return hipErrorInvalidValue;
+  if (act == ACT_SWIGLU) return launch_mixed_wgrad<256, 256, 0, 0, EPI_SWIGLU_BWD, ACT_SWIGLU>(p, q0, q1, st);
+  if (act == ACT_RELU) return launch_mixed_wgrad<256, 256, 0, 0, EPI_ACT_BWD, ACT_RELU>(p, q0, q1, st);
+  return launch_mixed_wgrad<256, 256, 0, 0, EPI_ACT_BWD, ACT_GELU>(p, q0, q1, st);
 }
 
 }  // namespace tpmlp

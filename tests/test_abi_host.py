@@ -194,6 +194,21 @@ def test_step_entry_points_validate():
     assert wg(r, P(0), P(1), P(2), P(3), P(4), P(5), P(3), None) == INVALID               # dW2 on dU
     assert wg(r, P(0), P(1), P(2), P(3), P(4), P(4) + 1024, P(6), None) == INVALID        # dWg inside dW1
     assert wg(r, P(0), None, P(2), P(3), P(4), P(5), P(6), None) == INVALID
+    db = L.tp_mlp_down_bwd_shard                  # (s, dY, W2, U, G, A, dU, dW2)
+    assert db(r, P(0), P(1), P(2), None, P(4), P(5), P(6), None) == INVALID               # SwiGLU: gate stash needed
+    assert db(r, P(0), P(1), P(2), P(3), None, P(5), P(6), None) == INVALID               # no A
+    assert db(r, P(0), P(1), P(2), P(3), P(4), P(5), None, None) == INVALID               # no dW2
+    assert db(r, P(0), P(1), P(2), P(3), P(4), P(4), P(6), None) == INVALID               # dU on A
+    assert db(r, P(0), P(1), P(2), P(3), P(4), P(5), P(5) + 256, None) == INVALID         # dW2 inside dU
+    assert db(r, P(0), P(1), P(2), P(3), P(4) + 8, P(5), P(6), None) == INVALID           # misaligned A
+    ub = L.tp_mlp_up_bwd_shard                    # (s, X, dU, W1, Wg, dX, dW1, dWg)
+    assert ub(r, P(0), P(1), P(2), None, P(4), P(5), P(6), None) == INVALID               # SwiGLU: Wg needed
+    assert ub(r, P(0), P(1), P(2), P(3), P(4), P(5), None, None) == INVALID               # SwiGLU: dWg needed
+    assert ub(r, P(0), P(1), P(2), P(3), P(0), P(5), P(6), None) == INVALID               # dX on X
+    assert ub(r, P(0), P(1), P(2), P(3), P(4), P(5), P(5) + 1024, None) == INVALID        # dWg inside dW1
+    sg = B.make_shape(4, 64, 128, 2, 0, "gelu")
+    assert L.tp_mlp_up_bwd_shard(ctypes.byref(sg), P(0), P(1), P(2), P(3), P(4), P(5), None, None) == INVALID
+    assert L.tp_mlp_down_bwd_shard(ctypes.byref(sg), P(0), P(1), P(2), P(3), P(4), P(5), P(6), None) == INVALID
 
 
 def test_streaming_extents_past_the_limits_are_unsupported():
@@ -237,6 +252,9 @@ def test_empty_batch_calls_that_launch_nothing():
         assert L.tp_mlp_down_shard(r, None, P(3), None, None) == OK
         assert L.tp_mlp_down_dgrad_act_shard(r, None, P(3), None, None, None, None) == OK
         assert L.tp_mlp_up_dgrad_shard(r, None, P(1), Wg, None, None) == OK
+        # the pairs write zero weight gradients (on the GPU); here: what stays required
+        assert L.tp_mlp_down_bwd_shard(r, None, P(3), None, P(5) if Wg else None, None, None, None, None) == INVALID
+        assert L.tp_mlp_up_bwd_shard(r, None, None, None, Wg, None, P(6), P(7) if Wg else None, None) == INVALID
         # the weight-gradient outputs are still required
         assert L.tp_mlp_down_wgrad_shard(r, None, None, None, None) == INVALID
     # reductions, reduce-scatter and all-gather of empty blocks

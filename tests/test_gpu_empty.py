@@ -72,6 +72,14 @@ def test_empty_batch_forward_and_backward(act):
     torch.cuda.synchronize()
     assert not torch.any(dW1) and not torch.any(dW2) and (dWg is None or not torch.any(dWg))
     dW2.fill_(float("nan"))
+    B.tp_mlp_down_bwd_shard(s, dY, W2, U, G, A, dU, dW2)
+    for buf in (dW1, dWg):
+        if buf is not None:
+            buf.fill_(float("nan"))
+    B.tp_mlp_up_bwd_shard(s, X, dU, W1, Wg, dX, dW1, dWg)
+    torch.cuda.synchronize()
+    assert not torch.any(dW1) and not torch.any(dW2) and (dWg is None or not torch.any(dWg))
+    dW2.fill_(float("nan"))
     B.tp_mlp_down_wgrad_shard(s, A, dY, dW2)
     dW1.fill_(float("nan"))
     B.tp_mlp_up_wgrad_shard(s, X, dU, dW1, dWg)

@@ -290,3 +290,44 @@ def test_grouped_weight_gradients_bitwise_separate(N, h, F, t):
         out.append((dW1, dWg, dW2))
     for a, b in zip(*out):
         assert torch.equal(a, b)
+
+
+# Shapes whose backward pairs take the mixed grid (at least 256 tiles of
+# 256 x 256 per pair): GeLU with whole tiles, SwiGLU and ReLU ragged in every
+# dimension.
+@pytest.mark.parametrize("N,h,F,t,act", [(2048, 4096, 8192, 2, "gelu"), (1500, 4104, 6000, 2, "swiglu"),
+                                         (2100, 3000, 3504, 1, "relu")])
+def test_mixed_backward_bitwise_separate(N, h, F, t, act):
+    """tp_mlp_down_bwd_shard and tp_mlp_up_bwd_shard (one launch each here)
+    equal the one-product calls bitwise, and the composite backward equals
+    the two of them bitwise; the one-product calls are checked against the
+    oracle in the group tests."""
+    say(f"[mixed backward] N={N} h={h} F={F} t={t} {act}")
+    Fi, sw = F // t, act == "swiglu"
+    g = 2 if sw else 1
+    s = B.make_shape(N, h, F, t, 0, act)
+    X, dY = bf16_dev(I.gen_x(520, N, h)), bf16_dev(I.gen_dy(520, N, h))
+    W1 = bf16_dev(I.normal_bf16([520, 1], (h, Fi), I.WEIGHT_SIGMA))
+    Wg = bf16_dev(I.normal_bf16([520, 2], (h, Fi), I.WEIGHT_SIGMA)) if sw else None
+    W2 = bf16_dev(I.normal_bf16([520, 3], (Fi, h), I.WEIGHT_SIGMA))
+    A, U = bf16_dev(I.normal_bf16([520, 4], (N, Fi))), bf16_dev(I.normal_bf16([520, 5], (N, Fi)))
+    G = bf16_dev(I.normal_bf16([520, 6], (N, Fi))) if sw else None
+    bf, f32 = dict(dtype=torch.bfloat16, device="cuda"), dict(dtype=torch.float32, device="cuda")
+
+    def outs():
+        return (torch.empty(N, g * Fi, **bf), torch.empty(Fi, h, **f32), torch.empty(N, h, **bf),
+                torch.empty(h, Fi, **f32), torch.empty(h, Fi, **f32) if sw else None)
+    sep, mix, comp = outs(), outs(), outs()
+    B.tp_mlp_down_dgrad_act_shard(s, dY, W2, U, G, sep[0])
+    B.tp_mlp_down_wgrad_shard(s, A, dY, sep[1])
+    B.tp_mlp_up_dgrad_shard(s, sep[0], W1, Wg, sep[2])
+    B.tp_mlp_up_wgrad_shard(s, X, sep[0], sep[3], sep[4])
+    B.tp_mlp_down_bwd_shard(s, dY, W2, U, G, A, mix[0], mix[1])
+    B.tp_mlp_up_bwd_shard(s, X, mix[0], W1, Wg, mix[2], mix[3], mix[4])
+    B.tp_mlp_bwd_shard(s, X, W1, Wg, W2, dY, A, U, G, comp[0], comp[3], comp[4], comp[1], comp[2])
+    torch.cuda.synchronize()
+    for name, a, b, c in zip(("dU", "dW2", "dX", "dW1", "dWg"), sep, mix, comp):
+        if a is None:
+            continue
+        assert torch.equal(a, b), f"{name}: mixed launch differs from the separate calls"
+        assert torch.equal(b, c), f"{name}: composite differs from the step calls"

@@ -3,8 +3,8 @@
 The reduce-scatter and all-gather that replace the tensor-parallel region's
 all-reduce under sequence parallelism ("Tensor and sequence parallelism",
 section "Sequence parallelism") are tied to brute force on tiny inputs, to the
-page's identity "an all-reduce is a reduce-scatter plus an all-gather", and to
-an independent float64 torch computation of the unsplit block at the shape of
+decomposition of an all-reduce into a reduce-scatter followed by an
+all-gather that the page's section relies on, and to an independent float64 torch computation of the unsplit block at the shape of
 that page's TP=4 + sequence-parallel check (S=8, H=16, FFN=64): LayerNorm on
 each rank's rows, all-gather, the sharded MLP, reduce-scatter with the output
 bias once and the residual, against the unsplit x + MLP(LayerNorm(x)) + b2.
@@ -19,7 +19,9 @@ import oracle
 
 def test_sequence_block_matches_check_script_rows():
     S, t = 8, 4
-    # the check script's rows = slice(rank * S // tp, (rank + 1) * S // tp)
+    # contiguous row blocks of S / t rows each, rank 0 lowest (the sequence
+    # split of the TP=4 check, "Tensor and sequence parallelism", "The
+    # implementation")
     for r in range(t):
         assert oracle.sequence_block(r, t, S) == slice(r * S // t, (r + 1) * S // t)
     with pytest.raises(ValueError):
@@ -52,8 +54,10 @@ def test_reduce_scatter_brute_force(rank):
 
 @pytest.mark.parametrize("t", [2, 4, 8])
 def test_all_reduce_is_reduce_scatter_then_all_gather(t):
-    """The page: an all-reduce is exactly a reduce-scatter plus an
-    all-gather, so the volume is unchanged."""
+    """Summing every rank's partials and keeping one row block per rank,
+    then concatenating the blocks, gives the full all-reduce result ("Tensor
+    and sequence parallelism", section "Sequence parallelism": the two
+    collectives together move what the one all-reduce moves)."""
     rng = np.random.default_rng(t)
     rows, cols = 4 * t, 16
     P = [rng.standard_normal((rows, cols)) for _ in range(t)]

@@ -70,3 +70,27 @@ def test_small_dA_decision_is_followed_downstream():
     g[5, 7] = dA[5, 7]                           # the GPU decided positive
     ref = assert_relu_grad("dU", g, dU, dA, X, W1)
     assert ref[5, 7] == dA[5, 7]
+
+
+def test_ambiguous_element_near_zero_but_not_zero_fails():
+    """The zero decision is exactly zero in the GPU's epilogue (dA times 0),
+    so a small nonzero value that is not dA is a wrong result."""
+    X, W1, U, dA, dU = _case()
+    dA = dA.copy()
+    dA[5, 7] = np.abs(dA).max()                  # dA large: the two decisions far apart
+    dU = oracle.act_backward("relu", dA, U)
+    g = dU.copy()
+    g[5, 7] = 1e-3 * np.abs(dA).max()            # neither exactly 0 nor near dA
+    with pytest.raises(AssertionError):
+        assert_relu_grad("dU", g, dU, dA, X, W1)
+
+
+def test_dA_decision_error_counts_in_the_comparison():
+    """At an element decided as dA the GPU value is compared, not replaced:
+    a value off by more than the elementwise bound fails."""
+    X, W1, U, dA, dU = _case()
+    g = dU.copy()
+    tol = 3e-2 * np.abs(dA).max()
+    g[5, 7] = dA[5, 7] + 1.5 * tol
+    with pytest.raises(AssertionError):
+        assert_relu_grad("dU", g, dU, dA, X, W1)
