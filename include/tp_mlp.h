@@ -149,6 +149,28 @@ tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X,
                                void* U_i, void* G_i, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight decode/serving loops, harnesses that forbid allocation):
+ * tp_mlp_fwd_shard with the same arguments, results and kernels (bitwise the
+ * same outputs), but no workspace argument.  The k-split partials of the
+ * one-token and small-batch paths (1 <= N <= 64) live in a fixed 32 MiB
+ * array of device memory inside the library, one per GPU, held until the
+ * process ends; this call allocates nothing (no hipMalloc, no allocating
+ * library routine).  A shape whose partials need more than 32 MiB returns
+ * TP_MLP_ERR_WORKSPACE before any launch (tp_mlp_workspace_bytes(s, 0) gives
+ * the need; about 0.5 MiB per token at the 70B shard).  N > 64 takes the
+ * wide-tile path, which uses no scratch.  Every call on one GPU shares that
+ * GPU's array, so calls that may overlap in time on one GPU (different
+ * streams, or concurrent graphs) race on it: order them on one stream.  The
+ * array needs no initial contents and its contents between calls are
+ * meaningless.  TP_MLP_ERR_HIP if the array's device address cannot be
+ * queried on the current device. */
+tp_mlp_status tp_mlp_fwd_shard_noalloc(const tp_mlp_shape* s, const void* X,
+                                       const void* W1_i, const void* Wg_i,
+                                       const void* W2_i, void* Y_i, void* A_i,
+                                       void* U_i, void* G_i,
+                                       hipStream_t stream);
+
 /* Backward of one rank's shard ("Parallelism Strategies #1 - Tensor
  * Parallelism", sharded backward, in math layout).  dY is the same on every
  * rank (g's backward is the identity).

@@ -75,6 +75,7 @@ _lib = None
 
 _SIGS = {
     "tp_mlp_fwd_shard": [POINTER(Shape)] + [c_void_p] * 9 + [c_size_t, c_void_p],
+    "tp_mlp_fwd_shard_noalloc": [POINTER(Shape)] + [c_void_p] * 8 + [c_void_p],
     "tp_mlp_bwd_shard": [POINTER(Shape)] + [c_void_p] * 15 + [c_size_t, c_void_p],
     "tp_mlp_reduce_partials_local": [c_int32, POINTER(c_void_p), c_int64, c_int64, c_void_p, c_void_p, c_void_p],
     "tp_mlp_reduce_scatter_local": [c_int32, POINTER(c_void_p), c_int64, c_int64, c_int32, c_void_p, c_void_p,
@@ -203,6 +204,18 @@ def tp_mlp_fwd_shard(shape: Shape, X, W1_i, Wg_i, W2_i, Y_i, A_i, U_i=None, G_i=
             _p(U_i, BF16, N * Fi, "U_i", optional=True), _p(G_i, BF16, N * Fi, "G_i", optional=True)]
     wp, wb = _ws(workspace, 0)
     _check("tp_mlp_fwd_shard", lib().tp_mlp_fwd_shard(ctypes.byref(shape), *args, wp, wb, _stream(stream)))
+
+
+def tp_mlp_fwd_shard_noalloc(shape: Shape, X, W1_i, Wg_i, W2_i, Y_i, A_i, U_i=None, G_i=None, stream=None):
+    """tp_mlp_fwd_shard without a workspace: the library's fixed per-GPU
+    scratch holds the small-batch partials (calls on one GPU must not
+    overlap in time)."""
+    N, h, Fi = shape.n_tokens, shape.hidden, shape.Fi
+    args = [_p(X, BF16, N * h, "X"), _p(W1_i, BF16, h * Fi, "W1_i"),
+            _p(Wg_i, BF16, h * Fi, "Wg_i", optional=True), _p(W2_i, BF16, Fi * h, "W2_i"),
+            _p(Y_i, BF16, N * h, "Y_i"), _p(A_i, BF16, N * Fi, "A_i"),
+            _p(U_i, BF16, N * Fi, "U_i", optional=True), _p(G_i, BF16, N * Fi, "G_i", optional=True)]
+    _check("tp_mlp_fwd_shard_noalloc", lib().tp_mlp_fwd_shard_noalloc(ctypes.byref(shape), *args, _stream(stream)))
 
 
 def tp_mlp_bwd_shard(shape: Shape, X, W1_i, Wg_i, W2_i, dY, A_i, U_i, G_i, dU_i, dW1_i, dWg_i,

@@ -34,6 +34,26 @@ int num_cu_current() {
   return n;
 }
 
+// Scratch of the entry points that allocate nothing (tp_mlp_fwd_shard_noalloc):
+// a fixed array in device memory, one copy per GPU, held until the process
+// ends.  In host code `scratch` only names the symbol; its device address on
+// the current GPU is looked up once per device and kept in g_scratch.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[MAX_DEVICES];
+
+// The current device's copy of `scratch`, or NULL when the device or the
+// symbol cannot be queried.
+void* static_scratch_current() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool opt_aligned(const void* p) { return p == nullptr || aligned16(p); }
 bool req(const void* p) { return p != nullptr && aligned16(p); }
@@ -398,15 +418,15 @@ int nt_slices(int64_t M, int64_t Nc, int64_t K, int num_cu) {
 }
 
 // C [M, Nc] = A [M, K] @ B^T with B stored [Nc, K], bf16 out.  When the tile
-// grid leaves most CUs idle and `scratch` (device, float32, scratch_floats
+// grid leaves most CUs idle and `part` (device, float32, part_floats
 // of them, no contents needed) holds slices * M * Nc partials, the product
 // runs split along k into float32 partials, whose sum in slice order is
 // rounded to bf16 once.
 hipError_t run_nt(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, void* C, hipStream_t st,
-                  float* scratch = nullptr, uint64_t scratch_floats = 0) {
+                  float* part = nullptr, uint64_t part_floats = 0) {
   const int ncu = num_cu_current();
-  const int s = scratch ? nt_slices(M, Nc, K, ncu) : 0;
-  if (s > 0 && (uint64_t)s * (uint64_t)M * (uint64_t)Nc <= scratch_floats) {
+  const int s = part ? nt_slices(M, Nc, K, ncu) : 0;
+  if (s > 0 && (uint64_t)s * (uint64_t)M * (uint64_t)Nc <= part_floats) {
     GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
     g.a[0] = g.a[1] = cu16(A);
     g.a_bytes[0] = g.a_bytes[1] = nbytes(M, K);
@@ -416,12 +436,12 @@ hipError_t run_nt(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B
     g.ldb = K;
     g.kslice = (int)(((K + s - 1) / s + 63) / 64 * 64);
     const int slices = (int)((K + g.kslice - 1) / g.kslice);
-    g.c0 = scratch;
+    g.c0 = part;
     g.ldc = Nc;
     g.c_slice = M * Nc;
     hipError_t e = gemm_launch(GEMM_NT_SPLITK, 0, g, ncu, st);
     if (e != hipSuccess) return e;
-    return ksum_launch(scratch, slices, M * Nc, u16(C), st);
+    return ksum_launch(part, slices, M * Nc, u16(C), st);
   }
   GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
   g.a[0] = g.a[1] = cu16(A);
@@ -606,30 +626,39 @@ tp_mlp_status tp_mlp_down_shard(const tp_mlp_shape* s, const void* A_i, const vo
   return hip_status(run_down(d, A_i, W2_i, Y_i, stream));
 }
 
-tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X, const void* W1_i, const void* Wg_i,
-                               const void* W2_i, void* Y_i, void* A_i, void* U_i, void* G_i, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
-  Dims d;
+}  // extern "C"
+
+namespace {
+
+// The forward's argument checks; the scratch the shape needs (0 for the
+// wide-tile path) in need_bytes.
+tp_mlp_status fwd_check(const tp_mlp_shape* s, const void* X, const void* W1_i, const void* Wg_i, const void* W2_i,
+                        const void* Y_i, const void* A_i, const void* U_i, const void* G_i, const void* workspace,
+                        Dims& d, size_t& need_bytes) {
   if (const tp_mlp_status ss = shape_status(s, d)) return ss;
   const bool sw = d.act == ACT_SWIGLU;
-  {
-    const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
-    if (!req_n(X, x) || !req(W1_i) || !req(W2_i) || !req_n(Y_i, x) || !req_n(A_i, a)) return TP_MLP_ERR_INVALID_ARG;
-    if (!opt_aligned(U_i) || !opt_aligned(G_i) || !opt_aligned(Wg_i) || !opt_aligned(workspace))
-      return TP_MLP_ERR_INVALID_ARG;
-    if (sw != (Wg_i != nullptr)) return TP_MLP_ERR_INVALID_ARG;
-    if (!sw && G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
-    if (sw && d.N > 0 && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
-    const uint64_t ws_used = d.N == 1 ? decode_layout(d).total : (small_batch(d) ? skinny_layout(d).total : 0);
-    if (!spans_ok({{Y_i, x}, {A_i, a}, {U_i, a}, {G_i, a}, {ws_used ? workspace : nullptr, ws_used}},
-                  {{X, x}, {W1_i, w}, {Wg_i, w}, {W2_i, w}}))
-      return TP_MLP_ERR_INVALID_ARG;
-  }
-  if (d.N == 0) return TP_MLP_OK;  // no tokens: nothing to compute
+  const uint64_t x = (uint64_t)d.N * d.h * 2, w = (uint64_t)d.h * d.Fi * 2, a = (uint64_t)d.N * d.Fi * 2;
+  if (!req_n(X, x) || !req(W1_i) || !req(W2_i) || !req_n(Y_i, x) || !req_n(A_i, a)) return TP_MLP_ERR_INVALID_ARG;
+  if (!opt_aligned(U_i) || !opt_aligned(G_i) || !opt_aligned(Wg_i) || !opt_aligned(workspace))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (sw != (Wg_i != nullptr)) return TP_MLP_ERR_INVALID_ARG;
+  if (!sw && G_i != nullptr) return TP_MLP_ERR_INVALID_ARG;
+  if (sw && d.N > 0 && ((U_i == nullptr) != (G_i == nullptr))) return TP_MLP_ERR_INVALID_ARG;
+  need_bytes = d.N == 1 ? decode_layout(d).total : (small_batch(d) ? skinny_layout(d).total : 0);
+  if (!spans_ok({{Y_i, x}, {A_i, a}, {U_i, a}, {G_i, a}, {need_bytes ? workspace : nullptr, need_bytes}},
+                {{X, x}, {W1_i, w}, {Wg_i, w}, {W2_i, w}}))
+    return TP_MLP_ERR_INVALID_ARG;
+  return TP_MLP_OK;
+}
 
+// The forward's launches, after fwd_check: the workspace (when the shape
+// needs one) is device memory of at least the needed size.
+tp_mlp_status fwd_run(const Dims& d, const void* X, const void* W1_i, const void* Wg_i, const void* W2_i, void* Y_i,
+                      void* A_i, void* U_i, void* G_i, void* workspace, hipStream_t stream) {
+  const bool sw = d.act == ACT_SWIGLU;
+  if (d.N == 0) return TP_MLP_OK;  // no tokens: nothing to compute
   if (d.N == 1) {
     const DecodeLayout L = decode_layout(d);
-    if (workspace == nullptr || workspace_bytes < L.total) return TP_MLP_ERR_WORKSPACE;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     float* part_up = reinterpret_cast<float*>(ws + L.off_part_up);
     float* part_dn = reinterpret_cast<float*>(ws + L.off_part_down);
@@ -639,7 +668,6 @@ tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X, const void*
   }
   if (small_batch(d)) {
     const SkinnyLayout L = skinny_layout(d);
-    if (workspace == nullptr || workspace_bytes < L.total) return TP_MLP_ERR_WORKSPACE;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     return hip_status(skinny_launch(d.act, (int)d.N, cu16(X), cu16(sw ? Wg_i : W1_i), cu16(W1_i), cu16(W2_i),
                                     (int)d.h, (int)d.Fi, L.up, L.down, reinterpret_cast<float*>(ws + L.off_part_up),
@@ -649,6 +677,32 @@ tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X, const void*
   hipError_t e = run_up_act(d, X, W1_i, Wg_i, A_i, U_i, G_i, stream);
   if (e != hipSuccess) return TP_MLP_ERR_HIP;
   return hip_status(run_down(d, A_i, W2_i, Y_i, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X, const void* W1_i, const void* Wg_i,
+                               const void* W2_i, void* Y_i, void* A_i, void* U_i, void* G_i, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  size_t need = 0;
+  if (const tp_mlp_status st = fwd_check(s, X, W1_i, Wg_i, W2_i, Y_i, A_i, U_i, G_i, workspace, d, need)) return st;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return TP_MLP_ERR_WORKSPACE;
+  return fwd_run(d, X, W1_i, Wg_i, W2_i, Y_i, A_i, U_i, G_i, workspace, stream);
+}
+
+tp_mlp_status tp_mlp_fwd_shard_noalloc(const tp_mlp_shape* s, const void* X, const void* W1_i, const void* Wg_i,
+                                       const void* W2_i, void* Y_i, void* A_i, void* U_i, void* G_i,
+                                       hipStream_t stream) {
+  Dims d;
+  size_t need = 0;
+  if (const tp_mlp_status st = fwd_check(s, X, W1_i, Wg_i, W2_i, Y_i, A_i, U_i, G_i, nullptr, d, need)) return st;
+  if (need > STATIC_SCRATCH_BYTES) return TP_MLP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && d.N > 0 && (ws = static_scratch_current()) == nullptr) return TP_MLP_ERR_HIP;
+  return fwd_run(d, X, W1_i, Wg_i, W2_i, Y_i, A_i, U_i, G_i, ws, stream);
 }
 
 tp_mlp_status tp_mlp_down_dgrad_act_shard(const tp_mlp_shape* s, const void* dY, const void* W2_i, const void* U_i,

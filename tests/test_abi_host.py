@@ -513,3 +513,22 @@ def test_sum_grads_rejects_bad_arguments():
     big = (ctypes.c_void_p * 65)(*([FAKE] * 65))
     assert f(65, big, 8, out, None) == UNSUPPORTED
 
+
+
+def test_noalloc_forward_validates_and_refuses_shapes_beyond_its_scratch():
+    """tp_mlp_fwd_shard_noalloc checks its arguments as tp_mlp_fwd_shard does
+    and refuses a shape whose k-split partials exceed its fixed 32 MiB
+    scratch, before any launch (so this runs without a GPU)."""
+    L = B.lib()
+    fn = L.tp_mlp_fwd_shard_noalloc               # (s, X, W1, Wg, W2, Y, A, U, G, stream)
+    s = B.make_shape(64, 16384, 98304, 1, 0, "gelu")         # 40 MiB of partials, operands within limits
+    assert B.workspace_bytes(s, False) > 32 << 20
+    # (the 3 GiB weights need fake buffers further apart)
+    assert fn(ctypes.byref(s), P(0), P(4), None, P(8), P(12), P(13), P(14), None, None) == WORKSPACE
+    s = B.make_shape(8, 64, 128, 2, 0, "swiglu")
+    r = ctypes.byref(s)
+    assert fn(r, P(0), P(1), None, P(3), P(4), P(5), P(6), P(7), None) == INVALID           # SwiGLU: no gate
+    assert fn(r, P(0), P(1), P(2), P(3), P(0), P(5), P(6), P(7), None) == INVALID           # Y on X
+    assert fn(r, P(0) + 8, P(1), P(2), P(3), P(4), P(5), P(6), P(7), None) == INVALID       # misaligned X
+    s0 = B.make_shape(0, 64, 128, 2, 0, "gelu")                                              # no tokens: nothing to do
+    assert fn(ctypes.byref(s0), None, P(1), None, P(3), None, None, None, None, None) == OK
