@@ -55,11 +55,74 @@ def parse():
     p.add_argument("--no-ln", action="store_true")
     p.add_argument("--no-other", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=256)
     return p.parse_args()
 
 
-def train_step(w, steps, warmup, B, I, torch, np, to_dev):
+class GpuMetrics:
+    """The GPU's gfx clock (per XCD) and socket power from amdsmi's GPU
+    metrics table.  The table is refreshed about once a second, so a clock
+    figure needs a pass of about that length: see clock_pass.  None where
+    amdsmi or the metrics are not available."""
+
+    def __init__(self):
+        self.err, self._h = None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:  # no amdsmi, no permission, no device
+            self.err = f"{type(e).__name__}: {e}"
+
+    def read(self):
+        """(table counter, per-XCD clocks in MHz, socket power in W) or None."""
+        if self._h is None:
+            return None
+        try:
+            m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        except Exception as e:
+            self.err = f"{type(e).__name__}: {e}"
+            return None
+        clks = m.get("current_gfxclks")
+        vals = [float(v) for v in clks if isinstance(v, (int, float)) and 0 < v < 65535] if isinstance(clks, list) else []
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [float(m["current_gfxclk"])]
+        pw = m.get("current_socket_power")
+        return (m.get("system_clock_counter"), vals, float(pw) if isinstance(pw, (int, float)) else None)
+
+
+def clock_pass(step, torch, seconds=3.0, settle=1.2, batch=100):
+    """The gfx clock and socket power while `step` runs back to back for
+    `seconds`: distinct snapshots of the metrics table taken after `settle`
+    seconds (the table lags by up to about a second)."""
+    import statistics
+    gm = GpuMetrics()
+    if gm.read() is None:
+        return {"mhz_mean": None, "error": gm.err}
+    snaps, seen = [], set()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            step()
+        r = gm.read()
+        torch.cuda.synchronize()
+        if r and time.perf_counter() - t0 > settle and r[0] not in seen and r[1]:
+            seen.add(r[0])
+            snaps.append(r)
+    if not snaps:
+        return {"mhz_mean": None, "error": "no metrics snapshot during the pass"}
+    nx = max(len(v) for _, v, _ in snaps)
+    per_xcd = [round(statistics.mean(v[i] for _, v, _ in snaps if len(v) == nx), 1) for i in range(nx)]
+    pw = [p for _, _, p in snaps if p is not None]
+    return {"mhz_mean": round(statistics.mean(statistics.mean(v) for _, v, _ in snaps), 1),
+            "per_xcd_mhz_mean": per_xcd, "socket_power_w_mean": round(statistics.mean(pw), 1) if pw else None,
+            "snapshots": len(snaps), "pass_s": round(time.perf_counter() - t0, 2),
+            "source": "amdsmi GPU metrics (current_gfxclks, current_socket_power), distinct snapshots while the "
+                      "headline step runs back to back in a pass of its own right after the timed steps (the "
+                      "table refreshes about once a second, longer than the timed steps)"}
+
+
+def train_step(w, steps, warmup, B, I, torch, np, to_dev, clock_s=True):
     """Time `steps` passes of rank 0's whole hot path for workload w: forward,
     reduce of the t partial sums (+ bias), backward (+ bias gradient), reduce
     of the t dX partials, launched through the step entry points (the
@@ -160,6 +223,7 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev):
     e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    clk = clock_pass(lambda: [fn() for _, _, fn in kernels], torch) if clock_s else None
     ms = e0.elapsed_time(e1) / steps
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_evs]))
     # one step each: from the event before the dominant kernel to the same event of the next step
@@ -171,7 +235,7 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev):
     return {"ms": ms, "tflops": tflops, "kern_ms": kern_ms, "ms_all_events": ms_all_events, "dom": dom,
             "step_ms_median": float(np.median(per_step)) if per_step else ms,
             "step_ms_min": float(np.min(per_step)) if per_step else ms,
-            "dom_ms": dom_ms, "flops": flops, "inputs_sha256": digests, "gemms": gemms}
+            "dom_ms": dom_ms, "flops": flops, "inputs_sha256": digests, "gemms": gemms, "clock": clk}
 
 
 def main():
@@ -207,7 +271,9 @@ def main():
                 "traffic": traffic["bytes"] if traffic else None,
                 "flops_per_launch": dom_fl, "avg_launch_ms": round(st["dom_ms"], 4)}
     if traffic:
-        roofline["traffic_unit"] = "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        roofline["traffic_unit"] = ("bytes per launch the L2s fetch from and write to the fabric (FETCH_SIZE + "
+                                    "WRITE_SIZE: Infinity Cache hits included, so not HBM bytes alone), each "
+                                    "scaled by its reading for a device copy of known size")
         roofline["algorithmic_bytes"] = traffic["algorithmic_bytes"]
     log("[bench] per-kernel ms: " + ", ".join(f"{k}={v:.3f}" for k, v in kern_ms.items()))
     copy = copy_probe(torch)
@@ -228,6 +294,7 @@ def main():
         "ms_per_step_event_per_kernel": round(st["ms_all_events"], 4),
         "step_ms_median": round(st["step_ms_median"], 4), "step_ms_min": round(st["step_ms_min"], 4),
         "copy_probe": copy,
+        "gpu_clock": st["clock"],
     }
 
     torch.cuda.empty_cache()
@@ -241,7 +308,7 @@ def main():
         for name in ("mlp128_h1024_gelu_t2", "llama_7b_train_t2", "llama3_70b_prefill_t4"):
             if name == w.name:
                 continue
-            o = train_step(WORKLOADS[name], 10, 3, B, I, torch, np, to_dev)
+            o = train_step(WORKLOADS[name], 10, 3, B, I, torch, np, to_dev, clock_s=False)
             ow = WORKLOADS[name]
             other[name] = {"ms_per_step": round(o["ms"], 4), "TFLOP/s": round(o["tflops"], 1),
                            "frac_of_bf16_peak": round(o["tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -259,7 +326,13 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows, I)
+        gpu = {w.name: {"TFLOP/s": round(tflops, 2), "ms_per_step": round(ms, 4)}}
+        for name, o in result.get("other_configs", {}).items():
+            gpu[name] = {"TFLOP/s": o["TFLOP/s"], "ms_per_step": o["ms_per_step"]}
+        if "decode" in result:
+            gpu[result["decode"]["workload"]] = {"GB/s_of_weights": result["decode"]["value"],
+                                                 "us_per_token": result["decode"]["us_per_token"]}
+        result["cpu_baseline"] = cpu_baseline(w, I, list(CPU_ORACLE_ROWS), gpu)
     print(json.dumps(result), flush=True)
 
 
@@ -305,7 +378,8 @@ def source_hash(files):
 
 
 def counter_traffic(summary, files, kernel):
-    """HBM bytes per launch of `kernel`, from a committed rocprofv3 counter
+    """L2<->fabric bytes per launch of `kernel` (what the L2s fetch and write
+    back, Infinity Cache hits included), from a committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter
     reads for a plain copy of known size).  None when there is no summary or
     the kernel sources changed since the counters were taken."""
@@ -562,44 +636,82 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(w, rows, I, target_s=10.0, cap_s=30.0):
-    """The fp64 oracle (as it stands) on a bounded sample of the workload:
-    chunks of `rows` token rows of rank 0's shard, forward + backward, on the
-    host's BLAS threads, repeated (wrapping over the tokens) until about
-    target_s seconds of CPU work have run."""
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max(int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas")
+    except Exception:
+        return os.cpu_count()
+
+
+# Token rows of rank 0's shard the oracle is timed on: every row (None) for
+# the four smaller workloads; a stated quarter of the 70B prefill shard (its
+# full run is about 17 TFLOP of float64, some 20 s on 16 host threads).
+CPU_ORACLE_ROWS = {"mlp128_h1024_gelu_t2": None, "llama3_70b_decode_t4": None, "llama_7b_train_t2": None,
+                   "gpt3_train_t8": None, "llama3_70b_prefill_t4": 4096}
+
+
+def cpu_oracle_workload(w, rows, I, min_s=1.0):
+    """The fp64 oracle (as it stands) on rank 0's shard of workload w: the
+    forward (+ backward for the training workloads) over the first `rows`
+    token rows (all of them when None), on the host's BLAS threads, repeated
+    until at least min_s seconds have run; the time per pass is reported."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max(int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas")
-    except Exception:
-        cores = os.cpu_count()
-    rows = min(rows, w.N)
     f = oracle.bf16_bits_to_f64
     sw = w.act == "swiglu"
-    Xall = I.gen_x(w.wid, w.N, w.h)
-    dYall = I.gen_dy(w.wid, w.N, w.h)
+    n = w.N if rows is None else min(rows, w.N)
+    X = f(I.gen_x(w.wid, w.N, w.h)[:n])
+    dY = f(I.gen_dy(w.wid, w.N, w.h)[:n]) if w.backward else None
     W1 = f(I.gen_w_up_shard(w.wid, w.h, w.Fi, 0))
     W2 = f(I.gen_w_down_shard(w.wid, w.h, w.Fi, 0))
     Wg = f(I.gen_w_gate_shard(w.wid, w.h, w.Fi, 0)) if sw else None
-    log(f"[bench] cpu baseline: oracle on chunks of {rows} token rows, {cores} BLAS threads")
-    done_rows, dt, r0 = 0, 0.0, 0
-    while dt < target_s and dt < cap_s:
-        sl = slice(r0, r0 + rows)
-        X, dY = f(Xall[sl]), f(dYall[sl])
+    dt, reps = 0.0, 0
+    while dt < min_s:
         t0 = time.perf_counter()
         oracle.shard_forward(w.act, X, W1, W2, Wg)
-        oracle.shard_backward(w.act, X, W1, W2, dY, Wg)
+        if w.backward:
+            oracle.shard_backward(w.act, X, W1, W2, dY, Wg)
         dt += time.perf_counter() - t0
-        done_rows += X.shape[0]
-        r0 = (r0 + rows) % w.N
-    fl = 6 * done_rows * w.h * w.Fi * (w.g + 1)
-    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "cpu_model": cpu_model(), "full_run": False, "seconds": round(dt, 3),
-            "sample": f"{done_rows} token rows (chunks of {rows}, wrapping over the {w.N}) of rank 0's shard "
-                      f"of {w.name}, forward + backward, {fl:.3e} algorithmic FLOPs; numpy float64 on the "
-                      f"host BLAS; GPU/CPU ratio = value / this value"}
+        reps += 1
+    sec = dt / reps
+    fl = (6 if w.backward else 2) * n * w.h * w.Fi * (w.g + 1)
+    out = {"seconds_per_pass": round(sec, 4), "passes": reps, "token_rows": n, "full_run": n == w.N,
+           "flops_per_pass": fl, "TFLOP/s": round(fl / sec / 1e12, 5)}
+    if not w.backward:
+        out["us_per_token"] = round(sec / n * 1e6, 1)
+        out["GB/s_of_weights"] = round(w.weight_bytes() / (sec / n) / 1e9, 3)
+    return out
+
+
+def cpu_baseline(w, I, names, gpu):
+    """The fp64 oracle timed on the host cores, per workload (rank 0's shard;
+    a full run where CPU_ORACLE_ROWS says so, else the stated sample), beside
+    the GPU's figure for the same workload.  The top-level value is the
+    headline workload's."""
+    from megatron_tensor_transformer_rank_amd.configs import WORKLOADS
+    cores = blas_threads()
+    per = {}
+    for name in names:
+        ww = WORKLOADS[name]
+        log(f"[bench] cpu baseline: oracle on {name} ({'all' if CPU_ORACLE_ROWS[name] is None else CPU_ORACLE_ROWS[name]} "
+            f"token rows), {cores} BLAS threads")
+        r = cpu_oracle_workload(ww, CPU_ORACLE_ROWS[name], I)
+        g = gpu.get(name)
+        if g is not None:
+            r["gpu"] = g
+            key = "GB/s_of_weights" if not ww.backward else "TFLOP/s"
+            if key in g and r.get(key):
+                r["gpu_over_cpu"] = round(g[key] / r[key], 1)
+        per[name] = r
+    head = per[w.name]
+    return {"value": head["TFLOP/s"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "full_run": head["full_run"], "seconds": head["seconds_per_pass"],
+            "sample": f"{'all ' if head['full_run'] else ''}{head['token_rows']} token rows of rank 0's shard of {w.name}, "
+                      f"forward + backward, {head['flops_per_pass']:.3e} algorithmic FLOPs per pass; numpy float64 "
+                      f"on the host BLAS; per_workload gives every workload (full runs except where stated)",
+            "per_workload": per}
 
 
 if __name__ == "__main__":
