@@ -10,10 +10,10 @@ computes and which passages it follows.
 from . import attn, ln
 from .mlp import (ACTS, act_backward, act_forward, all_gather,
                   bf16_bits_to_f64, column_block, column_sum, reduce_partials,
-                  reduce_scatter, sequence_block, shard_backward,
+                  reduce_scatter, round_bf16, sequence_block, shard_backward,
                   shard_forward, shard_weights, tp_backward, tp_forward)
 
 __all__ = ["attn", "ln", "ACTS", "act_backward", "act_forward", "all_gather",
            "bf16_bits_to_f64", "column_block", "column_sum", "reduce_partials",
-           "reduce_scatter", "sequence_block", "shard_backward",
+           "reduce_scatter", "round_bf16", "sequence_block", "shard_backward",
            "shard_forward", "shard_weights", "tp_backward", "tp_forward"]

@@ -37,6 +37,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import mlp
+from .mlp import round_bf16
 
 EPS = 1e-5
 
@@ -95,17 +96,6 @@ def layer_norm_backward(dy, x, gamma, eps: float = EPS, dres=None):
     if dres is not None:
         dx = dx + _f64(dres)
     return dx, dgamma, dbeta
-
-
-def round_bf16(a):
-    """Nearest bfloat16 value of each float64 (ties to even): the storage
-    format of the activations that cross the all-gather.  bfloat16 keeps 8
-    significant bits (7 stored) and float32's exponent range; values are
-    finite and within that range here."""
-    a = _f64(a)
-    m, e = np.frexp(a)              # a = m * 2^e, 0.5 <= |m| < 1
-    scaled = m * 256.0               # 8 significant bits -> an integer part
-    return np.ldexp(np.round(scaled), e - 8)   # np.round: half to even
 
 
 def sum_shared_grads(grads):

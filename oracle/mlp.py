@@ -46,6 +46,12 @@ Readings taken where the pages are silent (each is pinned by a CPU test):
 * ReLU'(0) = 0.
 * dY is an input; it is the same on every rank.
 * Only the output bias b2 exists; db2 = column sums of dY, computed once.
+* By default nothing is rounded.  The bf16_storage variant rounds, where the
+  method stores them, exactly the tensors the pages keep in two bytes (the
+  activations and their stashes, partial sums, activation gradients and
+  partial input gradients, and the reduced sums); it is the reference for
+  outputs whose exact values cancel so strongly that that storage alone
+  exceeds the tolerance.
 
 Every function here has a pin in ``tests/test_oracle_pins.py`` (worked example
 from the pages, closed forms, brute force, finite differences, autograd of the
@@ -72,6 +78,18 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_bf16(a):
+    """Nearest bfloat16 value of each float64 (ties to even): the 2-byte
+    storage format of the activations, partial sums and gradients the pages
+    price their messages and buffers in.  bfloat16 keeps 8 significant bits
+    (7 stored) and float32's exponent range; values are finite and within
+    that range here."""
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)              # a = m * 2^e, 0.5 <= |m| < 1
+    scaled = m * 256.0               # 8 significant bits -> an integer part
+    return np.ldexp(np.round(scaled), e - 8)   # np.round: half to even
 
 
 # --------------------------------------------------------------------------
@@ -142,7 +160,7 @@ def act_backward(act: str, dA, U, G=None):
 # --------------------------------------------------------------------------
 # One rank's shard
 # --------------------------------------------------------------------------
-def shard_forward(act: str, X, W1_i, W2_i, Wg_i=None):
+def shard_forward(act: str, X, W1_i, W2_i, Wg_i=None, bf16_storage: bool = False):
     """Forward of one rank's shard.
 
     U_i = X @ W1_i (column-parallel, no communication), A_i = act(U_i)
@@ -151,17 +169,26 @@ def shard_forward(act: str, X, W1_i, W2_i, Wg_i=None):
     ("02 -- Tensor Parallelism", sections "Column-parallel", "Row-parallel",
     "The MLP pairing").
 
+    bf16_storage: the same arithmetic with every tensor the method keeps in
+    two bytes rounded to bfloat16 where it is stored: the pre-activations U_i
+    (and G_i) as stored, A_i rounded after the activation (computed from the
+    unrounded pre-activations) and used rounded by the down-projection, and
+    Y_i rounded.  Nothing else is rounded (the products are exact).
+
     Returns a dict with U, G (None unless SwiGLU), A and Y.
     """
     X = np.asarray(X, dtype=np.float64)
     U = X @ np.asarray(W1_i, dtype=np.float64)
     G = X @ np.asarray(Wg_i, dtype=np.float64) if act == "swiglu" else None
     A = act_forward(act, U, G)
+    if bf16_storage:
+        U, A = round_bf16(U), round_bf16(A)
+        G = round_bf16(G) if G is not None else None
     Y = A @ np.asarray(W2_i, dtype=np.float64)
-    return {"U": U, "G": G, "A": A, "Y": Y}
+    return {"U": U, "G": G, "A": A, "Y": round_bf16(Y) if bf16_storage else Y}
 
 
-def shard_backward(act: str, X, W1_i, W2_i, dY, Wg_i=None):
+def shard_backward(act: str, X, W1_i, W2_i, dY, Wg_i=None, bf16_storage: bool = False):
     """Backward of one rank's shard for an output gradient dY that is the same
     on every rank.
 
@@ -173,7 +200,11 @@ def shard_backward(act: str, X, W1_i, W2_i, dY, Wg_i=None):
     derivation, math layout; "02 -- Tensor Parallelism", section
     "Column-parallel", backward).
 
-    The forward quantities are recomputed from X and the weights exactly.
+    The forward quantities are recomputed from X and the weights (with
+    bf16_storage, as shard_forward stores them: the activation derivative is
+    taken on the stored pre-activations and dW2 on the stored A_i; dU_i (dG_i,
+    dP_i) and dX_i are rounded to bfloat16 where they are stored, dA_i and the
+    weight gradients are not).
     Returns a dict with dA, dU (SwiGLU: the up gradient dP), dG (None unless
     SwiGLU), dW1 (SwiGLU: dW_up), dWg (None unless SwiGLU), dW2 and dX.
     """
@@ -181,23 +212,25 @@ def shard_backward(act: str, X, W1_i, W2_i, dY, Wg_i=None):
     W1_i = np.asarray(W1_i, dtype=np.float64)
     W2_i = np.asarray(W2_i, dtype=np.float64)
     dY = np.asarray(dY, dtype=np.float64)
-    fwd = shard_forward(act, X, W1_i, W2_i, Wg_i)
+    rnd = round_bf16 if bf16_storage else (lambda a: a)
+    fwd = shard_forward(act, X, W1_i, W2_i, Wg_i, bf16_storage)
     dA = dY @ W2_i.T
     dW2 = fwd["A"].T @ dY
     if act == "swiglu":
         Wg_i = np.asarray(Wg_i, dtype=np.float64)
         dG, dU = act_backward(act, dA, fwd["U"], fwd["G"])
+        dG, dU = rnd(dG), rnd(dU)
         dW1 = X.T @ dU
         dWg = X.T @ dG
         dX = dG @ Wg_i.T + dU @ W1_i.T
     else:
-        dU = act_backward(act, dA, fwd["U"])
+        dU = rnd(act_backward(act, dA, fwd["U"]))
         dG = None
         dW1 = X.T @ dU
         dWg = None
         dX = dU @ W1_i.T
     return {"dA": dA, "dU": dU, "dG": dG, "dW1": dW1, "dWg": dWg,
-            "dW2": dW2, "dX": dX}
+            "dW2": dW2, "dX": rnd(dX)}
 
 
 # --------------------------------------------------------------------------
@@ -240,26 +273,31 @@ def reduce_partials(partials, bias=None):
     return out
 
 
-def tp_forward(act: str, X, W1, W2, t: int, Wg=None, b2=None):
+def tp_forward(act: str, X, W1, W2, t: int, Wg=None, b2=None, bf16_storage: bool = False):
     """Every rank's shard forward, then the partial sums reduced and the bias
-    added once.  Returns (Y, per-rank list of shard_forward dicts)."""
+    added once (with bf16_storage, the shards as shard_forward stores them and
+    the reduced sum rounded to bfloat16).  Returns (Y, per-rank list of
+    shard_forward dicts)."""
     ranks = []
     for r in range(t):
         W1_i, W2_i, Wg_i = shard_weights(W1, W2, r, t, Wg)
-        ranks.append(shard_forward(act, X, W1_i, W2_i, Wg_i))
+        ranks.append(shard_forward(act, X, W1_i, W2_i, Wg_i, bf16_storage))
     Y = reduce_partials([f["Y"] for f in ranks], b2)
-    return Y, ranks
+    return (round_bf16(Y) if bf16_storage else Y), ranks
 
 
-def tp_backward(act: str, X, W1, W2, dY, t: int, Wg=None):
+def tp_backward(act: str, X, W1, W2, dY, t: int, Wg=None, bf16_storage: bool = False):
     """Every rank's shard backward; dX = sum of the partial input gradients in
-    rank order; db2 = column sums of dY (once).  Returns (dX, db2, per-rank
-    list of shard_backward dicts)."""
+    rank order; db2 = column sums of dY (once).  With bf16_storage, the shards
+    as shard_backward stores them and the reduced dX rounded to bfloat16.
+    Returns (dX, db2, per-rank list of shard_backward dicts)."""
     ranks = []
     for r in range(t):
         W1_i, W2_i, Wg_i = shard_weights(W1, W2, r, t, Wg)
-        ranks.append(shard_backward(act, X, W1_i, W2_i, dY, Wg_i))
+        ranks.append(shard_backward(act, X, W1_i, W2_i, dY, Wg_i, bf16_storage))
     dX = reduce_partials([b["dX"] for b in ranks])
+    if bf16_storage:
+        dX = round_bf16(dX)
     db2 = np.asarray(dY, dtype=np.float64).sum(axis=0)
     return dX, db2, ranks
 

@@ -5,7 +5,7 @@ The constants pasted into common.h are read back from the header, checked to
 be the fit script's output, and evaluated in float32 in the kernels' order
 (Horner in t, one exponential) against scipy's erfc and the exact GeLU and
 its derivative (u * Phi(u) and Phi(u) + u * phi(u), Phi from erfc).  The
-bounds are the ones the header states; they are far below bf16's 2^-9
+bounds are the ones the header states; they are far below bf16's 2^-8 (unit roundoff)
 rounding of the epilogue's outputs."""
 import os
 import re
@@ -74,7 +74,7 @@ def test_gelu_and_derivative_against_exact():
     phi = np.exp(-0.5 * u64 * u64) / np.sqrt(2 * np.pi)
     gelu = u64 * cdf.astype(np.float64)
     grad = (u.astype(np.float32) * pdf + cdf).astype(np.float64)
-    # relative to the function's scale: far below the bf16 rounding (2^-9) of the outputs
+    # relative to the function's scale: far below the bf16 rounding (2^-8) of the outputs
     assert np.abs(gelu - u64 * Phi).max() <= 2e-6 * np.maximum(np.abs(u64 * Phi), 1e-3).max()
     m = np.abs(u64) > 1e-3
     assert np.max(np.abs(gelu - u64 * Phi)[m] / np.abs(u64 * Phi)[m]) <= 5e-6

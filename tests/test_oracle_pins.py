@@ -401,3 +401,116 @@ def test_bf16_decode_exact():
     assert vals[4] == 1.0 + 2.0 ** -7
     assert vals[5] == 0.0 and math.copysign(1, vals[5]) < 0
     assert vals[6] == 3.140625
+
+
+# ---------------------------------------------------------------------------
+# The bfloat16-storage variant: the same arithmetic, with the tensors the
+# method keeps in two bytes rounded where they are stored
+# ---------------------------------------------------------------------------
+def test_bf16_storage_equals_exact_on_the_worked_example():
+    """Every value of the worked example is a small integer, exact in
+    bfloat16: the storage variant gives the same results as the exact
+    oracle, forward and backward, split and unsplit."""
+    g, X, W1, W2 = _worked()
+    for t in (1, g["t"]):
+        Y, ranks = oracle.tp_forward("relu", X, W1, W2, t)
+        Ys, ranks_s = oracle.tp_forward("relu", X, W1, W2, t, bf16_storage=True)
+        assert np.array_equal(Y, Ys) and Ys[0].tolist() == g["output"]
+        for a, b in zip(ranks, ranks_s):
+            for k in ("U", "A", "Y"):
+                assert np.array_equal(a[k], b[k])
+        for dy in ([[1.0, 0.0]], [[0.0, 1.0]], [[1.0, 1.0]]):
+            dY = np.array(dy)
+            dX, _, br = oracle.tp_backward("relu", X, W1, W2, dY, t)
+            dXs, _, brs = oracle.tp_backward("relu", X, W1, W2, dY, t, bf16_storage=True)
+            assert np.array_equal(dX, dXs)
+            for a, b in zip(br, brs):
+                for k in ("dA", "dU", "dW1", "dW2", "dX"):
+                    assert np.array_equal(a[k], b[k])
+
+
+def _torch_bf16(v):
+    """bfloat16 rounding through torch's float64 -> bfloat16 conversion (not
+    the oracle's round_bf16), for the brute-force storage check."""
+    import torch
+    return float(torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).to(torch.float64))
+
+
+def _bf_storage_shard(act, X, W1, W2, Wg, dY):
+    """Pure-Python loops with the method's stores rounded: U (and G) stashed,
+    A from the unrounded pre-activations then rounded, Y rounded; the
+    activation derivative on the stashes, dU (dG, dP) rounded, dW2 from the
+    stored A, dX rounded."""
+    N, h, F = len(X), len(X[0]), len(W1[0])
+    U = [[sum(X[n][k] * W1[k][f] for k in range(h)) for f in range(F)] for n in range(N)]
+    G = [[sum(X[n][k] * Wg[k][f] for k in range(h)) for f in range(F)] for n in range(N)] if act == "swiglu" else None
+    A = [[_torch_bf16(_bf_act(act, U[n][f], G[n][f] if G else None)) for f in range(F)] for n in range(N)]
+    Us = [[_torch_bf16(U[n][f]) for f in range(F)] for n in range(N)]
+    Gs = [[_torch_bf16(G[n][f]) for f in range(F)] for n in range(N)] if G else None
+    Y = [[_torch_bf16(sum(A[n][f] * W2[f][j] for f in range(F))) for j in range(h)] for n in range(N)]
+    dA = [[sum(dY[n][j] * W2[f][j] for j in range(h)) for f in range(F)] for n in range(N)]
+    dP = [[0.0] * F for _ in range(N)]
+    dG = [[0.0] * F for _ in range(N)]
+    for n in range(N):
+        for f in range(F):
+            u = Us[n][f]
+            if act == "relu":
+                dP[n][f] = _torch_bf16(dA[n][f] * (1.0 if u > 0 else 0.0))
+            elif act == "gelu":
+                d = 0.5 * (1.0 + math.erf(u / math.sqrt(2.0))) + u * math.exp(-0.5 * u * u) / math.sqrt(2 * math.pi)
+                dP[n][f] = _torch_bf16(dA[n][f] * d)
+            else:
+                gg = Gs[n][f]
+                s = 1.0 / (1.0 + math.exp(-gg))
+                dG[n][f] = _torch_bf16(dA[n][f] * u * s * (1.0 + gg * (1.0 - s)))
+                dP[n][f] = _torch_bf16(dA[n][f] * gg * s)
+    dX = [[_torch_bf16(sum(dP[n][f] * W1[k][f] + (dG[n][f] * Wg[k][f] if act == "swiglu" else 0.0)
+                           for f in range(F))) for k in range(h)] for n in range(N)]
+    dW2 = [[sum(A[n][f] * dY[n][j] for n in range(N)) for j in range(h)] for f in range(F)]
+    dW1 = [[sum(X[n][k] * dP[n][f] for n in range(N)) for f in range(F)] for k in range(h)]
+    return {"U": Us, "G": Gs, "A": A, "Y": Y, "dU": dP, "dG": dG, "dX": dX, "dW1": dW1, "dW2": dW2}
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu", "swiglu"])
+def test_bf16_storage_brute_force(act):
+    """The storage variant of one shard against pure-Python loops that round
+    through torch's conversion: the same stores, the same values."""
+    rng = np.random.default_rng(11)
+    N, h, F = 3, 5, 4
+    X, W1, W2, Wg, dY = (rng.standard_normal(s) for s in [(N, h), (h, F), (F, h), (h, F), (N, h)])
+    Wg = Wg if act == "swiglu" else None
+    f = oracle.shard_forward(act, X, W1, W2, Wg, bf16_storage=True)
+    b = oracle.shard_backward(act, X, W1, W2, dY, Wg, bf16_storage=True)
+    ref = _bf_storage_shard(act, X.tolist(), W1.tolist(), W2.tolist(), Wg.tolist() if Wg is not None else None,
+                            dY.tolist())
+    for k, got in (("U", f["U"]), ("A", f["A"]), ("Y", f["Y"]), ("dU", b["dU"]), ("dX", b["dX"]),
+                   ("dW1", b["dW1"]), ("dW2", b["dW2"])):
+        np.testing.assert_allclose(got, np.array(ref[k]), rtol=1e-12, atol=1e-14, err_msg=k)
+    if act == "swiglu":
+        np.testing.assert_allclose(f["G"], np.array(ref["G"]), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(b["dG"], np.array(ref["dG"]), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_bf16_storage_rounding_bounds(act):
+    """Each stored tensor is the exact one computed from the stored inputs,
+    rounded once: within half a bfloat16 unit (2^-8 relative) of it; the
+    reduced sums likewise over the stored partials."""
+    rng = np.random.default_rng(12)
+    N, h, F, t = 7, 16, 24, 3
+    X, W1, W2, Wg, dY = (rng.standard_normal(s) for s in [(N, h), (h, F), (F, h), (h, F), (N, h)])
+    Wg = Wg if act == "swiglu" else None
+    Y, ranks = oracle.tp_forward(act, X, W1, W2, t, Wg=Wg, bf16_storage=True)
+    dX, _, branks = oracle.tp_backward(act, X, W1, W2, dY, t, Wg=Wg, bf16_storage=True)
+    half_ulp = lambda v: 2.0 ** -8 * np.abs(v) * (1 + 1e-12)   # 8 significant bits: unit roundoff 2^-8
+    for r, (fr, br) in enumerate(zip(ranks, branks)):
+        W1_i, W2_i, Wg_i = oracle.shard_weights(W1, W2, r, t, Wg)
+        exact_A = oracle.act_forward(act, X @ W1_i, X @ Wg_i if Wg is not None else None)
+        assert np.all(np.abs(fr["A"] - exact_A) <= half_ulp(exact_A))
+        assert np.all(np.abs(fr["Y"] - fr["A"] @ W2_i) <= half_ulp(fr["A"] @ W2_i))
+        dXe = br["dU"] @ W1_i.T + (br["dG"] @ Wg_i.T if Wg is not None else 0.0)
+        assert np.all(np.abs(br["dX"] - dXe) <= half_ulp(dXe))
+    Ye = sum(f["Y"] for f in ranks)
+    assert np.all(np.abs(Y - Ye) <= half_ulp(Ye))
+    dXe = sum(b["dX"] for b in branks)
+    assert np.all(np.abs(dX - dXe) <= half_ulp(dXe))
