@@ -505,11 +505,15 @@ def bench_attn(args, B, I, torch, np, to_dev, N=2048, h=12288, heads=96, kv=96, 
     dWo, dWqkv = torch.empty(qc, h, dtype=f32, device="cuda"), torch.empty(h, wc, dtype=f32, device="cuda")
     dX = torch.empty(N, h, dtype=bf, device="cuda")
 
+    ws_do = B.alloc_workspace(B.attn_out_dgrad_workspace_bytes(s))
+
     def step():
         B.tp_attn_qkv_shard(s, X, Wqkv, QKV)       # N > 64: no workspace
         B.tp_attn_out_shard(s, O, Wo, Y)
-        B.tp_attn_out_bwd_shard(s, dY, O, Wo, dO, dWo)
-        B.tp_attn_qkv_bwd_shard(s, X, Wqkv, dQKV, dWqkv, dX)
+        # dO alone (the attention core's backward needs only it); then dX, dW_qkv
+        # and the deferred dW_o in one launch
+        B.tp_attn_out_dgrad_shard(s, dY, Wo, dO, workspace=ws_do)
+        B.tp_attn_qkv_bwd_out_wgrad_shard(s, X, Wqkv, dQKV, dY, O, dWqkv, dX, dWo)
     for _ in range(3):
         step()
     torch.cuda.synchronize()
@@ -528,7 +532,9 @@ def bench_attn(args, B, I, torch, np, to_dev, N=2048, h=12288, heads=96, kv=96, 
     small = bench_attn_small(B, I, torch, to_dev)
     return {"small_batch_llama3_70b_t4": small,"workload": f"gpt3_attn_t{t}: N={N} h={h} heads={heads} head_dim={d} t={t} (qkv {wc}, o {qc} cols/rank)",
             "ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "flops_per_step": flops, "step": "QKV fwd, O fwd, O bwd (dO, dW_o), QKV bwd (dX, dW_qkv)"}
+            "flops_per_step": flops,
+            "step": "QKV fwd, O fwd, dO (k-split), then dX + dW_qkv + dW_o (the output projection's weight "
+                    "gradient deferred into the QKV backward's launch)"}
 
 
 def bench_attn_small(B, I, torch, to_dev, h=8192, heads=64, kv=8, d=128, t=4):

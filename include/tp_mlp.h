@@ -446,6 +446,40 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X,
                                     float* dWqkv_i, void* dX_partial,
                                     hipStream_t stream);
 
+/* The same backward split for callers that schedule the output
+ * projection's weight gradient late: the attention core's backward needs
+ * only dO_i, and dWo_i = O_i^T @ dY can wait to share a launch with the QKV
+ * projection's backward (both are weight gradients over the tokens).
+ *
+ * dO_i = dY @ Wo_i^T -> bf16 [N, qc], alone.  When its tile grid would leave
+ * most CUs idle it runs split along k into float32 partials in the
+ * workspace, summed in slice order and rounded once (the same arithmetic as
+ * tp_attn_out_bwd_shard's dO_i, which borrows dWo_i's storage instead).
+ *   workspace  tp_attn_out_dgrad_workspace_bytes(s) bytes of device scratch
+ *              (no initial contents needed; NULL when that is 0); missing or
+ *              smaller: TP_MLP_ERR_WORKSPACE. */
+size_t tp_attn_out_dgrad_workspace_bytes(const tp_attn_shape* s);
+tp_mlp_status tp_attn_out_dgrad_shard(const tp_attn_shape* s, const void* dY,
+                                      const void* Wo_i, void* dO_i,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* tp_attn_qkv_bwd_shard's dX_partial and dWqkv_i together with the output
+ * projection's deferred dWo_i = O_i^T @ dY (fp32 [qc, h]), in one launch when
+ * the block tiles fill the GPU (dX_partial's tiles first, the two weight
+ * gradients' filling in behind them), else one after the other.  Each
+ * element is summed in the same order as in the separate calls. */
+tp_mlp_status tp_attn_qkv_bwd_out_wgrad_shard(const tp_attn_shape* s,
+                                              const void* X,
+                                              const void* Wqkv_i,
+                                              const void* dQKV_i,
+                                              const void* dY,
+                                              const void* O_i,
+                                              float* dWqkv_i,
+                                              void* dX_partial,
+                                              float* dWo_i,
+                                              hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * LayerNorm of the sequence-parallel region ("Tensor and sequence
  * parallelism", section "Sequence parallelism" and its check script;

@@ -95,6 +95,8 @@ _SIGS = {
     "tp_attn_out_shard": [POINTER(AttnShape)] + [c_void_p] * 4 + [c_size_t, c_void_p],
     "tp_attn_out_bwd_shard": [POINTER(AttnShape)] + [c_void_p] * 5 + [c_void_p],
     "tp_attn_qkv_bwd_shard": [POINTER(AttnShape)] + [c_void_p] * 5 + [c_void_p],
+    "tp_attn_out_dgrad_shard": [POINTER(AttnShape)] + [c_void_p] * 4 + [c_size_t, c_void_p],
+    "tp_attn_qkv_bwd_out_wgrad_shard": [POINTER(AttnShape)] + [c_void_p] * 8 + [c_void_p],
     "tp_sp_layernorm_fwd": [c_int64, c_int64, c_float] + [c_void_p] * 6 + [c_void_p],
     "tp_sp_reduce_scatter_layernorm_local": [c_int32, POINTER(c_void_p), c_int64, c_int64, c_int32, c_void_p,
                                              c_void_p, c_void_p, c_float] + [c_void_p] * 5 + [c_void_p],
@@ -121,6 +123,8 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_bias_grad_workspace_bytes.restype = c_size_t
         L.tp_attn_workspace_bytes.argtypes = [POINTER(AttnShape)]
         L.tp_attn_workspace_bytes.restype = c_size_t
+        L.tp_attn_out_dgrad_workspace_bytes.argtypes = [POINTER(AttnShape)]
+        L.tp_attn_out_dgrad_workspace_bytes.restype = c_size_t
         L.tp_sp_layernorm_bwd_workspace_bytes.argtypes = [c_int64, c_int64]
         L.tp_sp_layernorm_bwd_workspace_bytes.restype = c_size_t
         L.tp_mlp_status_string.argtypes = [c_int32]
@@ -143,6 +147,10 @@ def bias_grad_workspace_bytes(rows: int, cols: int) -> int:
 
 def attn_workspace_bytes(shape: AttnShape) -> int:
     return int(lib().tp_attn_workspace_bytes(ctypes.byref(shape)))
+
+
+def attn_out_dgrad_workspace_bytes(shape: AttnShape) -> int:
+    return int(lib().tp_attn_out_dgrad_workspace_bytes(ctypes.byref(shape)))
 
 
 def layernorm_bwd_workspace_bytes(rows: int, cols: int) -> int:
@@ -396,6 +404,26 @@ def tp_attn_qkv_bwd_shard(shape: AttnShape, X, Wqkv_i, dQKV_i, dWqkv_i, dX_parti
         ctypes.byref(shape), _p(X, BF16, N * h, "X"), _p(Wqkv_i, BF16, h * w, "Wqkv_i"),
         _p(dQKV_i, BF16, N * w, "dQKV_i"), _p(dWqkv_i, F32, h * w, "dWqkv_i"),
         _p(dX_partial, BF16, N * h, "dX_partial"), _stream(stream)))
+
+
+def tp_attn_out_dgrad_shard(shape: AttnShape, dY, Wo_i, dO_i, workspace=None, stream=None):
+    """dO_i = dY Wo_i^T alone (k-split partials in the workspace)."""
+    N, h, qc = shape.n_tokens, shape.hidden, shape.q_cols
+    wp, wb = _ws(workspace, 0)
+    _check("tp_attn_out_dgrad_shard", lib().tp_attn_out_dgrad_shard(
+        ctypes.byref(shape), _p(dY, BF16, N * h, "dY"), _p(Wo_i, BF16, qc * h, "Wo_i"),
+        _p(dO_i, BF16, N * qc, "dO_i"), wp, wb, _stream(stream)))
+
+
+def tp_attn_qkv_bwd_out_wgrad_shard(shape: AttnShape, X, Wqkv_i, dQKV_i, dY, O_i, dWqkv_i, dX_partial, dWo_i,
+                                    stream=None):
+    """dX_partial, dWqkv_i and the deferred dWo_i = O_i^T dY in one call."""
+    N, h, qc, wc = shape.n_tokens, shape.hidden, shape.q_cols, shape.qkv_cols
+    _check("tp_attn_qkv_bwd_out_wgrad_shard", lib().tp_attn_qkv_bwd_out_wgrad_shard(
+        ctypes.byref(shape), _p(X, BF16, N * h, "X"), _p(Wqkv_i, BF16, h * wc, "Wqkv_i"),
+        _p(dQKV_i, BF16, N * wc, "dQKV_i"), _p(dY, BF16, N * h, "dY"), _p(O_i, BF16, N * qc, "O_i"),
+        _p(dWqkv_i, F32, h * wc, "dWqkv_i"), _p(dX_partial, BF16, N * h, "dX_partial"),
+        _p(dWo_i, F32, qc * h, "dWo_i"), _stream(stream)))
 
 
 # ------------------------------------------- sequence-parallel LayerNorm

@@ -470,6 +470,62 @@ hipError_t run_tn(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B
   return gemm_launch(GEMM_WGRAD, 0, g, num_cu_current(), st);
 }
 
+// The unsplit NT product of run_nt and the TN product of run_tn as GEMM
+// arguments (for the mixed launches).
+GemmArgs nt_args(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, void* C) {
+  GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
+  g.a[0] = g.a[1] = cu16(A);
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(M, K);
+  g.lda = K;
+  g.b[0] = g.b[1] = cu16(B);
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(Nc, K);
+  g.ldb = K;
+  g.c0 = C;
+  g.ldc = Nc;
+  return g;
+}
+GemmArgs tn_args(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, float* C) {
+  GemmArgs g = one_segment((int)M, (int)Nc, (int)K);
+  g.a[0] = g.a[1] = cu16(A);
+  g.a_bytes[0] = g.a_bytes[1] = nbytes(K, M);
+  g.lda = M;
+  g.b[0] = g.b[1] = cu16(B);
+  g.b_bytes[0] = g.b_bytes[1] = nbytes(K, Nc);
+  g.ldb = Nc;
+  g.c0 = g.c1 = C;
+  g.ldc = Nc;
+  g.c_split = (int)Nc;
+  return g;
+}
+
+// The attention QKV projection's backward: dX = dQKV Wqkv^T and dWqkv =
+// X^T dQKV, and (dWo_i non-NULL) the output projection's weight gradient
+// dWo = O^T dY, deferred to share the launch.  One mixed grid when the
+// 256x256 tiles fill every CU at least once; otherwise dX (split along k
+// into part_floats of part when its tiles leave most CUs idle) and then the
+// weight gradients.
+hipError_t run_attn_qkv_bwd(const AttnDims& a, const void* X, const void* Wqkv, const void* dQKV, float* dWqkv,
+                            void* dX, const void* dY, const void* O, float* dWo, float* part, uint64_t part_floats,
+                            hipStream_t st) {
+  const GemmArgs p = nt_args(a.N, a.h, a.qkv_cols, dQKV, Wqkv, dX);
+  const GemmArgs q0 = tn_args(a.h, a.qkv_cols, a.N, X, dQKV, dWqkv);
+  GemmArgs q1 = q0;
+  if (dWo) q1 = tn_args(a.q_cols, a.h, a.N, O, dY, dWo);
+  if (tiles256(p) + tiles256(q0) + (dWo ? tiles256(q1) : 0) >= num_cu_current())
+    return gemm_launch_mixed(GEMM_DGRAD, 0, p, q0, dWo ? &q1 : nullptr, st);
+  hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV, Wqkv, dX, st, part, part_floats);
+  if (e == hipSuccess) e = gemm_launch(GEMM_WGRAD, 0, q0, num_cu_current(), st);
+  if (e == hipSuccess && dWo) e = gemm_launch(GEMM_WGRAD, 0, q1, num_cu_current(), st);
+  return e;
+}
+
+// Float32 partials the output projection's input gradient dO = dY Wo^T
+// splits into along k (0: not split).
+uint64_t attn_dO_part_floats(const AttnDims& a) {
+  const int s = nt_slices(a.N, a.q_cols, a.h, num_cu_current());
+  return s > 0 ? (uint64_t)s * (uint64_t)a.N * (uint64_t)a.q_cols : 0;
+}
+
 // Extents of a [rows, cols] block for the streaming kernels (reductions,
 // gather, column sums): cols / 8 is an int there, and byte counts of the
 // block must not overflow 64 bits.  rows may be 0 (an empty block).
@@ -960,11 +1016,53 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X, const
                 {{X, nbytes(a.N, a.h)}, {Wqkv_i, nbytes(a.h, a.qkv_cols)}, {dQKV_i, nbytes(a.N, a.qkv_cols)}}))
     return TP_MLP_ERR_INVALID_ARG;
   if (a.N == 0) return hip_status(zero_f32_launch(dWqkv_i, a.h * a.qkv_cols, num_cu_current(), stream));
-  // dWqkv_i is written after dX_partial: until then its storage may hold the k-split partials
-  hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV_i, Wqkv_i, dX_partial, stream, dWqkv_i,
-                        (uint64_t)a.h * a.qkv_cols);
-  if (e == hipSuccess) e = run_tn(a.h, a.qkv_cols, a.N, X, dQKV_i, dWqkv_i, stream);
-  return hip_status(e);
+  // unmixed, dWqkv_i is written after dX_partial: until then its storage may hold the k-split partials
+  return hip_status(run_attn_qkv_bwd(a, X, Wqkv_i, dQKV_i, dWqkv_i, dX_partial, nullptr, nullptr, nullptr,
+                                     dWqkv_i, (uint64_t)a.h * a.qkv_cols, stream));
+}
+
+size_t tp_attn_out_dgrad_workspace_bytes(const tp_attn_shape* s) {
+  AttnDims a;
+  if (attn_status(s, a) != TP_MLP_OK || a.N == 0) return 0;
+  return round256(attn_dO_part_floats(a) * sizeof(float));
+}
+
+tp_mlp_status tp_attn_out_dgrad_shard(const tp_attn_shape* s, const void* dY, const void* Wo_i, void* dO_i,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AttnDims a;
+  if (const tp_mlp_status ss = attn_status(s, a)) return ss;
+  if (!req_n(dY, nbytes(a.N, a.h)) || !req(Wo_i) || !req_n(dO_i, nbytes(a.N, a.q_cols)) || !opt_aligned(workspace))
+    return TP_MLP_ERR_INVALID_ARG;
+  const uint64_t pf = a.N > 0 ? attn_dO_part_floats(a) : 0;
+  if (pf > 0 && (workspace == nullptr || workspace_bytes < pf * sizeof(float))) return TP_MLP_ERR_WORKSPACE;
+  if (!spans_ok({{dO_i, nbytes(a.N, a.q_cols)}, {pf ? workspace : nullptr, pf * sizeof(float)}},
+                {{dY, nbytes(a.N, a.h)}, {Wo_i, nbytes(a.q_cols, a.h)}}))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (a.N == 0) return TP_MLP_OK;
+  return hip_status(run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream, static_cast<float*>(workspace), pf));
+}
+
+tp_mlp_status tp_attn_qkv_bwd_out_wgrad_shard(const tp_attn_shape* s, const void* X, const void* Wqkv_i,
+                                              const void* dQKV_i, const void* dY, const void* O_i, float* dWqkv_i,
+                                              void* dX_partial, float* dWo_i, hipStream_t stream) {
+  AttnDims a;
+  if (const tp_mlp_status ss = attn_status(s, a)) return ss;
+  if (!req_n(X, nbytes(a.N, a.h)) || !req(Wqkv_i) || !req_n(dQKV_i, nbytes(a.N, a.qkv_cols)) || !req(dWqkv_i) ||
+      !req_n(dX_partial, nbytes(a.N, a.h)) || !req_n(dY, nbytes(a.N, a.h)) || !req_n(O_i, nbytes(a.N, a.q_cols)) ||
+      !req(dWo_i))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (!spans_ok({{dWqkv_i, (uint64_t)a.h * a.qkv_cols * 4}, {dX_partial, nbytes(a.N, a.h)},
+                 {dWo_i, (uint64_t)a.q_cols * a.h * 4}},
+                {{X, nbytes(a.N, a.h)}, {Wqkv_i, nbytes(a.h, a.qkv_cols)}, {dQKV_i, nbytes(a.N, a.qkv_cols)},
+                 {dY, nbytes(a.N, a.h)}, {O_i, nbytes(a.N, a.q_cols)}}))
+    return TP_MLP_ERR_INVALID_ARG;
+  if (a.N == 0) {
+    hipError_t e = zero_f32_launch(dWqkv_i, a.h * a.qkv_cols, num_cu_current(), stream);
+    if (e == hipSuccess) e = zero_f32_launch(dWo_i, a.q_cols * a.h, num_cu_current(), stream);
+    return hip_status(e);
+  }
+  return hip_status(run_attn_qkv_bwd(a, X, Wqkv_i, dQKV_i, dWqkv_i, dX_partial, dY, O_i, dWo_i, dWqkv_i,
+                                     (uint64_t)a.h * a.qkv_cols, stream));
 }
 
 tp_mlp_status tp_sp_layernorm_fwd(int64_t rows, int64_t cols, float eps, const void* x, const void* gamma,

@@ -532,3 +532,26 @@ def test_noalloc_forward_validates_and_refuses_shapes_beyond_its_scratch():
     assert fn(r, P(0) + 8, P(1), P(2), P(3), P(4), P(5), P(6), P(7), None) == INVALID       # misaligned X
     s0 = B.make_shape(0, 64, 128, 2, 0, "gelu")                                              # no tokens: nothing to do
     assert fn(ctypes.byref(s0), None, P(1), None, P(3), None, None, None, None, None) == OK
+
+
+def test_attn_deferred_wgrad_entry_points_validate():
+    """tp_attn_out_dgrad_shard and tp_attn_qkv_bwd_out_wgrad_shard check their
+    arguments before any launch; the dO workspace is sized for its k-split."""
+    L = B.lib()
+    s = B.make_attn_shape(2048, 12288, 96, 96, 128, 8, 7)
+    r = ctypes.byref(s)
+    need = B.attn_out_dgrad_workspace_bytes(s)
+    assert need >= 4 * 2048 * 1536 * 4                 # dO = dY Wo^T splits along k at this shape
+    od = L.tp_attn_out_dgrad_shard                     # (s, dY, Wo, dO, ws, wsb)
+    assert od(r, P(0), P(1), P(2), None, 0, None) == WORKSPACE
+    assert od(r, P(0), P(1), P(2), P(3), need - 256, None) == WORKSPACE
+    assert od(r, P(0), P(1), P(0), P(3), need, None) == INVALID        # dO on dY
+    assert od(r, P(0), P(1), P(2), P(2), need, None) == INVALID        # workspace on dO
+    assert od(r, P(0), None, P(2), P(3), need, None) == INVALID
+    small = B.make_attn_shape(4096, 512, 8, 8, 64, 1, 0)               # a full grid: no split, no workspace
+    assert B.attn_out_dgrad_workspace_bytes(small) == 0
+    qw = L.tp_attn_qkv_bwd_out_wgrad_shard             # (s, X, Wqkv, dQKV, dY, O, dWqkv, dX, dWo)
+    assert qw(r, P(0), P(1), P(2), P(3), P(4), P(5), P(6), None, None) == INVALID   # no dWo
+    assert qw(r, P(0), P(1), P(2), P(3), P(4), P(5), P(6), P(5), None) == INVALID   # dWo on dWqkv
+    assert qw(r, P(0), P(1), P(2), P(3), P(4), P(5), P(3), P(7), None) == INVALID   # dX on dY
+    assert qw(r, P(0), P(1), P(2), None, P(4), P(5), P(6), P(7), None) == INVALID   # no dY

@@ -186,3 +186,33 @@ def test_attn_small_batch_llama3_70b_widths(N):
     48 sampled weight-gradient columns."""
     run_attn_group(820 + N, N, 8192, 64, 8, 128, 4, ncols=48)
 
+
+
+@pytest.mark.parametrize("N,h,nh,nkv,d,t", [(2048, 12288, 96, 96, 128, 8), (333, 2056, 8, 8, 64, 4)])
+def test_deferred_out_wgrad_equals_the_separate_calls(N, h, nh, nkv, d, t):
+    """tp_attn_out_dgrad_shard (dO alone, k-split partials in a workspace)
+    and tp_attn_qkv_bwd_out_wgrad_shard (dX, dWqkv and the deferred dWo in
+    one call: one mixed launch at the GPT-3 per-rank shape, three at the
+    smaller one) give bitwise what tp_attn_out_bwd_shard and
+    tp_attn_qkv_bwd_shard give; those are checked against the oracle
+    above."""
+    say(f"[attn deferred] N={N} h={h} heads={nh} kv={nkv} d={d} t={t}")
+    s = B.make_attn_shape(N, h, nh, nkv, d, t, t - 1)
+    qc, wc = s.q_cols, s.qkv_cols
+    sig = I.WEIGHT_SIGMA
+    X, dY = bf16_dev(I.normal_bf16([730, 0], (N, h))), bf16_dev(I.normal_bf16([730, 1], (N, h)))
+    Wqkv, Wo = bf16_dev(I.normal_bf16([730, 2], (h, wc), sig)), bf16_dev(I.normal_bf16([730, 3], (qc, h), sig))
+    O, dQKV = bf16_dev(I.normal_bf16([730, 4], (N, qc))), bf16_dev(I.normal_bf16([730, 5], (N, wc)))
+    bf, f32 = dict(dtype=torch.bfloat16, device="cuda"), dict(dtype=torch.float32, device="cuda")
+    dO_a, dO_b = torch.empty(N, qc, **bf), torch.empty(N, qc, **bf)
+    dWo_a, dWo_b = torch.empty(qc, h, **f32), torch.empty(qc, h, **f32)
+    dW_a, dW_b = torch.empty(h, wc, **f32), torch.empty(h, wc, **f32)
+    dX_a, dX_b = torch.empty(N, h, **bf), torch.empty(N, h, **bf)
+    B.tp_attn_out_bwd_shard(s, dY, O, Wo, dO_a, dWo_a)
+    B.tp_attn_qkv_bwd_shard(s, X, Wqkv, dQKV, dW_a, dX_a)
+    ws = B.alloc_workspace(B.attn_out_dgrad_workspace_bytes(s))
+    B.tp_attn_out_dgrad_shard(s, dY, Wo, dO_b, workspace=ws)
+    B.tp_attn_qkv_bwd_out_wgrad_shard(s, X, Wqkv, dQKV, dY, O, dW_b, dX_b, dWo_b)
+    torch.cuda.synchronize()
+    for name, a, b in (("dO", dO_a, dO_b), ("dWo", dWo_a, dWo_b), ("dWqkv", dW_a, dW_b), ("dX", dX_a, dX_b)):
+        assert torch.equal(a, b), f"{name} differs"
