@@ -102,7 +102,7 @@ tp_mlp_status shape_status(const tp_mlp_shape* s, Dims& d) {
 
 struct DecodeLayout {
   GemvPlan up, down;
-  size_t off_part_up, off_part_down, total;
+  size_t off_part_up, off_part_down, off_cnt, total;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -141,6 +141,8 @@ DecodeLayout decode_layout(const Dims& d) {
   off = round256(off + L.up.part_floats * sizeof(float));
   L.off_part_down = off;
   off = round256(off + L.down.part_floats * sizeof(float));
+  L.off_cnt = off;  // one counter per column strip of the down-projection
+  off = round256(off + (size_t)L.down.strips * sizeof(int));
   L.total = off;
   return L;
 }
@@ -718,8 +720,9 @@ tp_mlp_status fwd_run(const Dims& d, const void* X, const void* W1_i, const void
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     float* part_up = reinterpret_cast<float*>(ws + L.off_part_up);
     float* part_dn = reinterpret_cast<float*>(ws + L.off_part_down);
+    int* cnt = reinterpret_cast<int*>(ws + L.off_cnt);
     return hip_status(decode_launch(d.act, cu16(X), cu16(sw ? Wg_i : W1_i), cu16(W1_i), cu16(W2_i), (int)d.h,
-                                    (int)d.Fi, L.up, L.down, part_up, part_dn, u16(A_i), u16(sw ? G_i : U_i),
+                                    (int)d.Fi, L.up, L.down, part_up, part_dn, cnt, u16(A_i), u16(sw ? G_i : U_i),
                                     u16(sw ? U_i : nullptr), u16(Y_i), stream));
   }
   if (small_batch(d)) {

@@ -9,8 +9,11 @@
 // with non-temporal loads (streamed data is not kept in the caches), and
 // accumulates in float32 registers.
 //
-// Three launches, no cross-block synchronisation inside a kernel (an
-// agent-scope fence per block costs more than the whole stream):
+// Two launches.  No block waits for another; the down-projection's k-split
+// partials are summed by the last block of each column strip to finish (an
+// agent-scope fence per block, which writes back the XCD's whole L2, costs
+// more than the whole stream, so the partials go through device-scope
+// stores and loads instead, see gemv_partial):
 //   1. up:    blocks = 512-column strips x matrices x k-splits; a block's 16
 //             waves take interleaved rows of its k range, each lane keeping 8
 //             weight loads in flight in a rolling pipeline; the waves meet in
@@ -21,8 +24,8 @@
 //             in fixed order, applies the activation and rounds A to bf16
 //             (the value the MFMA path would read back), while the block's
 //             first weight loads are in flight.  Blocks of the first column
-//             strip also write A_i and the stash.
-//   3. final: adds the down-projection's k-split partials in fixed order and
+//             strip also write A_i and the stash.  The last block of each
+//             strip adds the strip's k-split partials in fixed order and
 //             rounds Y_i to bf16.
 // The result is deterministic.
 #include "common.h"
@@ -50,13 +53,24 @@ __device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
 // loads form a rolling pipeline: slot u holds row j = step * GV_UNROLL + u,
 // and is refilled with row j + GV_UNROLL as soon as it has been consumed, so
 // GV_UNROLL loads stay in flight per lane through the whole k range.
-template <int NMAT, int PRO, int ACT>
+//
+// FIN = 1 (the down-projection): the block's partial row is written with
+// device-scope stores (they reach the memory side that every XCD sees, past
+// the XCD's own L2), the block waits for them to complete and then bumps its
+// strip's counter; the block that finds every other k-split of its strip
+// counted is the last one, and adds the strip's partials (read with
+// device-scope loads) in k-split order into Y, then zeroes the counter.  The
+// counters are zeroed beforehand by the up-projection kernel of the same
+// call (zero_cnt), so the workspace needs no initial contents.
+template <int NMAT, int PRO, int ACT, int FIN>
 __global__ void __launch_bounds__(GV_THREADS)
 gemv_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
              int K, int ncols, int KR, float* __restrict__ part, const float* __restrict__ pg, int ks_up,
-             uint16_t* __restrict__ a_out, uint16_t* __restrict__ st0, uint16_t* __restrict__ st1) {
+             uint16_t* __restrict__ a_out, uint16_t* __restrict__ st0, uint16_t* __restrict__ st1,
+             int* __restrict__ cnt, int ncnt, uint16_t* __restrict__ y) {
   __shared__ float xs[GV_MAX_KR];
   __shared__ float red[GV_WAVES][GV_STRIP];
+  __shared__ int last;
 
   const int S = (ncols + GV_STRIP - 1) / GV_STRIP;
   const int b = blockIdx.x;
@@ -69,6 +83,8 @@ gemv_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, co
   const int ke = min(K, kb + KR);
 
   const uint16_t* Wm = (NMAT == 2 && mat == 1) ? W1 : W0;
+  if (PRO == 0 && cnt != nullptr && b == 0)  // the next kernel's strip counters start at zero
+    for (int i = tid; i < ncnt; i += GV_THREADS) __hip_atomic_store(cnt + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int col = s * GV_STRIP + lane * 8;
   const bool cok = col < ncols;
   const uint16_t* base = Wm + col + (int64_t)(kb + w) * ncols;
@@ -148,7 +164,36 @@ gemv_partial(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W0, co
       float t = red[0][c];
 #pragma unroll
       for (int q = 1; q < GV_WAVES; ++q) t += red[q][c];
-      part[((int64_t)ks * NMAT + mat) * ncols + gc] = t;
+      float* dst = part + ((int64_t)ks * NMAT + mat) * ncols + gc;
+      if constexpr (FIN) __hip_atomic_store(dst, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else *dst = t;
+    }
+  }
+  if constexpr (FIN) {
+    const int nks = gridDim.x / S;  // k-splits of this strip (NMAT = 1)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores have completed
+    __syncthreads();
+    if (tid == 0) last = __hip_atomic_fetch_add(cnt + s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nks - 1;
+    __syncthreads();
+    if (last) {
+      for (int c = tid; c < GV_STRIP; c += GV_THREADS) {
+        const int gc = s * GV_STRIP + c;
+        if (gc >= ncols) continue;
+        float t = 0.f;
+        constexpr int QB = 16;
+        for (int q0 = 0; q0 < nks; q0 += QB) {
+          float pv[QB];
+#pragma unroll
+          for (int u = 0; u < QB; ++u)
+            pv[u] = q0 + u < nks ? __hip_atomic_load(part + (int64_t)(q0 + u) * ncols + gc, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0.f;
+#pragma unroll
+          for (int u = 0; u < QB; ++u) t += pv[u];
+        }
+        y[gc] = (uint16_t)f32_to_bf16_rne(t);
+      }
+      if (tid == 0) __hip_atomic_store(cnt + s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -207,30 +252,28 @@ GemvPlan gemv_plan(int K, int ncols, int nmat, int target_blocks) {
 
 hipError_t decode_launch(int act, const uint16_t* x, const uint16_t* Wa, const uint16_t* Wb, const uint16_t* W2,
                          int h, int Fi, const GemvPlan& up, const GemvPlan& down, float* part_up, float* part_down,
-                         uint16_t* A, uint16_t* st0, uint16_t* st1, uint16_t* Y, hipStream_t st) {
+                         int* cnt, uint16_t* A, uint16_t* st0, uint16_t* st1, uint16_t* Y, hipStream_t st) {
   const dim3 blk(GV_THREADS);
   if (act == ACT_SWIGLU) {
-    hipLaunchKernelGGL((gemv_partial<2, 0, 0>), dim3(up.strips * 2 * up.ks), blk, 0, st, x, Wa, Wb, h, Fi, up.kr,
-                       part_up, nullptr, 0, nullptr, nullptr, nullptr);
+    hipLaunchKernelGGL((gemv_partial<2, 0, 0, 0>), dim3(up.strips * 2 * up.ks), blk, 0, st, x, Wa, Wb, h, Fi, up.kr,
+                       part_up, nullptr, 0, nullptr, nullptr, nullptr, cnt, down.strips, nullptr);
   } else {
-    hipLaunchKernelGGL((gemv_partial<1, 0, 0>), dim3(up.strips * up.ks), blk, 0, st, x, Wa, Wa, h, Fi, up.kr,
-                       part_up, nullptr, 0, nullptr, nullptr, nullptr);
+    hipLaunchKernelGGL((gemv_partial<1, 0, 0, 0>), dim3(up.strips * up.ks), blk, 0, st, x, Wa, Wa, h, Fi, up.kr,
+                       part_up, nullptr, 0, nullptr, nullptr, nullptr, cnt, down.strips, nullptr);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gd(down.strips * down.ks);
   if (act == ACT_SWIGLU)
-    hipLaunchKernelGGL((gemv_partial<1, 1, ACT_SWIGLU>), gd, blk, 0, st, nullptr, W2, W2, Fi, h, down.kr, part_down,
-                       part_up, up.ks, A, st0, st1);
+    hipLaunchKernelGGL((gemv_partial<1, 1, ACT_SWIGLU, 1>), gd, blk, 0, st, nullptr, W2, W2, Fi, h, down.kr,
+                       part_down, part_up, up.ks, A, st0, st1, cnt, down.strips, Y);
   else if (act == ACT_RELU)
-    hipLaunchKernelGGL((gemv_partial<1, 1, ACT_RELU>), gd, blk, 0, st, nullptr, W2, W2, Fi, h, down.kr, part_down,
-                       part_up, up.ks, A, st0, nullptr);
+    hipLaunchKernelGGL((gemv_partial<1, 1, ACT_RELU, 1>), gd, blk, 0, st, nullptr, W2, W2, Fi, h, down.kr, part_down,
+                       part_up, up.ks, A, st0, nullptr, cnt, down.strips, Y);
   else
-    hipLaunchKernelGGL((gemv_partial<1, 1, ACT_GELU>), gd, blk, 0, st, nullptr, W2, W2, Fi, h, down.kr, part_down,
-                       part_up, up.ks, A, st0, nullptr);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return ksum_launch(part_down, down.ks, h, Y, st);
+    hipLaunchKernelGGL((gemv_partial<1, 1, ACT_GELU, 1>), gd, blk, 0, st, nullptr, W2, W2, Fi, h, down.kr, part_down,
+                       part_up, up.ks, A, st0, nullptr, cnt, down.strips, Y);
+  return hipGetLastError();
 }
 
 hipError_t ksum_launch(const float* part, int ks, int64_t n, uint16_t* out, hipStream_t st) {
