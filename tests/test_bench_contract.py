@@ -2,6 +2,7 @@
 refused with a message (the build runs one rank's shard on one MI355X), and
 the committed counter summaries parse (their traffic is reported only while
 their source hash matches the kernels)."""
+import json
 import os
 import subprocess
 import sys
@@ -22,10 +23,18 @@ def test_more_than_one_gpu_is_refused(n):
 def test_counter_summaries_parse():
     sys.path.insert(0, ROOT)
     import bench
-    for summary, files, kernel in (("gemm_hbm_traffic_gpt3_train_t8.md", bench.GEMM_SOURCES, "wgrad"),
-                                   ("gemv_hbm_traffic_llama3_70b_decode_t4.md", bench.GEMV_SOURCES, "decode")):
+    # the GEMM summary covers every launch of the timed step (bench.py's kernel names); the
+    # decode summary the whole one-token call
+    cases = [("gemm_hbm_traffic_gpt3_train_t8.md", bench.GEMM_SOURCES, k)
+             for k in ("up_act", "down", "reduce_y", "down_bwd", "up_bwd", "reduce_dx")]
+    cases.append(("gemv_hbm_traffic_llama3_70b_decode_t4.md", bench.GEMV_SOURCES, "decode"))
+    for summary, files, kernel in cases:
         path = os.path.join(ROOT, "profiles", summary)
         assert os.path.exists(path), summary
+        with open(path) as fh:
+            line = [ln for ln in fh if ln.startswith("traffic_json: ")]
+        assert len(line) == 1, summary
+        assert kernel in json.loads(line[0][len("traffic_json: "):])["kernels"], (summary, kernel)
         info = bench.counter_traffic(summary, files, kernel)
         # None only when the kernels changed after the counters were taken
         if info is not None:

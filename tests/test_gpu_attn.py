@@ -141,6 +141,8 @@ GROUPS = [
     # a k-split would be chosen but dW_o (the partials' scratch) is too small
     # for 2 x 4096 x 128 floats: one unsplit pass
     (707, 4096, 2048, 8, 2, 64, 4),
+    # unsplit, 96 output tiles per forward projection, ragged in h
+    (708, 2000, 2824, 16, 4, 128, 1),
 ]
 
 

@@ -56,6 +56,12 @@ CASES = [
     # one token, ReLU, an ambiguous pre-activation whose dA is small: the
     # GPU's decision must be followed into dW1 = x^T dU column by column
     (8080, 1, 1720, 3136, 7, "relu", False),
+    # unsplit blocks of 88 to 100 output tiles per product, ragged in every
+    # dimension (N, h and F_i a few rows or columns past a 256-tile edge,
+    # and k past a 64-deep k-tile)
+    (120, 2000, 2824, 2760, 1, "gelu", True),
+    (121, 1000, 5400, 2824, 1, "swiglu", False),
+    (122, 2310, 2312, 2312, 1, "relu", False),
 ]
 
 
