@@ -22,12 +22,13 @@
 // The backward, for many rows (4096 and more), is one pass over row slabs:
 // a block per slab forms dx row by row and keeps its columns' dgamma / dbeta
 // sums in registers, then a kernel adds the slabs' partial rows in slab
-// order.  For fewer rows it runs as a column kernel, dgamma and dbeta over
+// order.  For fewer rows it runs as column tiles, dgamma and dbeta over
 // (512-column strip, row slab) tiles with at most 64 slabs of partial rows,
-// the slab sums, and then the row kernel (dx, one row per block, like the
-// forward), last because dx may overwrite dy in place: the column kernel
-// re-reads x and dy but keeps every CU busy where one block per slab would
-// leave most of them idle.
+// beside the row kernel (dx, one row per block, like the forward) in the same
+// launch, then the slab sums; when dx overwrites dy in place the column
+// kernel, the slab sums and the row kernel run one after another.  The
+// column tiles re-read x and dy but keep every CU busy where one block per
+// slab would leave most of them idle.
 #include "common.h"
 #include "norm.h"
 
@@ -212,15 +213,14 @@ ln_fwd_kernel(PartialPtrs pp, int t, int64_t row0, const uint16_t* __restrict__ 
 }
 
 // One row per block of NT threads: xhat = (x - mean) * rstd, g = dy * gamma,
-// dx = rstd * (g - sum(g)/h - xhat * sum(g * xhat)/h) (+ dres).
+// dx = rstd * (g - sum(g)/h - xhat * sum(g * xhat)/h) (+ dres).  red: the
+// block's [2][NT/64] floats of LDS.
 template <int NT, int J>
-__global__ void __launch_bounds__(NT)
-ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
-                 const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int cols8,
-                 int cols) {
-  __shared__ float red[2][NT / 64];
+__device__ __forceinline__ void ln_dx_row(int64_t r, const uint16_t* x, const uint16_t* __restrict__ gamma,
+                                          const float* __restrict__ mean, const float* __restrict__ rstd,
+                                          const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int cols8, int cols,
+                                          float (*red)[NT / 64]) {
   const int tid = threadIdx.x;
-  const int64_t r = blockIdx.x;
   const int64_t base = r * cols8;
   const float mu = mean[r], rs = rstd[r];
   // dres is loaded with x and dy: one round trip to memory per row
@@ -265,6 +265,15 @@ ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const fl
       reinterpret_cast<u32x4*>(dx)[base + q] = pack8(o);
     }
   }
+}
+
+template <int NT, int J>
+__global__ void __launch_bounds__(NT)
+ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
+                 const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int cols8,
+                 int cols) {
+  __shared__ float red[2][NT / 64];
+  ln_dx_row<NT, J>(blockIdx.x, x, gamma, mean, rstd, dy, dres, dx, cols8, cols, red);
 }
 
 // The backward in one pass over a slab of rows (many rows): block b takes
@@ -375,18 +384,22 @@ ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const 
 constexpr int LN_DG_STRIP = 512;
 constexpr int LN_DG_UNROLL = 4;
 
-__global__ void __launch_bounds__(LN_THREADS)
-ln_bwd_dgb_kernel(const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
-                  const uint16_t* __restrict__ dy, int64_t rows, int64_t cols, int64_t rpb,
-                  float* __restrict__ part_g, float* __restrict__ part_b) {
-  __shared__ float red[LN_WAVES][LN_DG_STRIP];
+// The tile's code for one group of LN_THREADS threads (gtid = the thread's
+// index in its group; red = the group's [LN_WAVES][LN_DG_STRIP] floats of
+// LDS).  Every thread of the block reaches the same barriers: a group whose
+// tile is past the last one (live = false) loads and stores nothing.
+__device__ __forceinline__ void ln_dgb_tile(int tile, bool live, int gtid, const uint16_t* __restrict__ x,
+                                            const float* __restrict__ mean, const float* __restrict__ rstd,
+                                            const uint16_t* __restrict__ dy, int64_t rows, int64_t cols, int64_t rpb,
+                                            float* __restrict__ part_g, float* __restrict__ part_b,
+                                            float (*red)[LN_DG_STRIP]) {
   const int strips = (int)((cols + LN_DG_STRIP - 1) / LN_DG_STRIP);
-  const int strip = blockIdx.x % strips, slab = blockIdx.x / strips;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int strip = tile % strips, slab = tile / strips;
+  const int lane = gtid & 63, w = gtid >> 6;
   const int64_t r0 = (int64_t)slab * rpb;
-  const int64_t r1 = r0 + rpb < rows ? r0 + rpb : rows;
+  const int64_t r1 = !live ? r0 : (r0 + rpb < rows ? r0 + rpb : rows);
   const int64_t c = (int64_t)strip * LN_DG_STRIP + lane * 8;
-  const bool cok = c < cols;
+  const bool cok = live && c < cols;
   float ag[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, ab[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int64_t rb = r0 + w; rb < r1; rb += LN_WAVES * LN_DG_UNROLL) {
     u32x4 xv[LN_DG_UNROLL], dv[LN_DG_UNROLL];
@@ -416,18 +429,52 @@ ln_bwd_dgb_kernel(const uint16_t* __restrict__ x, const float* __restrict__ mean
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[w][lane * 8 + e] = ag[e];
   __syncthreads();
-  for (int cc = tid; cc < LN_DG_STRIP; cc += LN_THREADS) {
-    const int64_t gc = (int64_t)strip * LN_DG_STRIP + cc;
-    if (gc < cols) part_g[(int64_t)slab * cols + gc] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
-  }
+  if (live)
+    for (int cc = gtid; cc < LN_DG_STRIP; cc += LN_THREADS) {
+      const int64_t gc = (int64_t)strip * LN_DG_STRIP + cc;
+      if (gc < cols) part_g[(int64_t)slab * cols + gc] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
+    }
   if (!part_b) return;
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[w][lane * 8 + e] = ab[e];
   __syncthreads();
-  for (int cc = tid; cc < LN_DG_STRIP; cc += LN_THREADS) {
-    const int64_t gc = (int64_t)strip * LN_DG_STRIP + cc;
-    if (gc < cols) part_b[(int64_t)slab * cols + gc] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
+  if (live)
+    for (int cc = gtid; cc < LN_DG_STRIP; cc += LN_THREADS) {
+      const int64_t gc = (int64_t)strip * LN_DG_STRIP + cc;
+      if (gc < cols) part_b[(int64_t)slab * cols + gc] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
+    }
+}
+
+__global__ void __launch_bounds__(LN_THREADS)
+ln_bwd_dgb_kernel(const uint16_t* __restrict__ x, const float* __restrict__ mean, const float* __restrict__ rstd,
+                  const uint16_t* __restrict__ dy, int64_t rows, int64_t cols, int64_t rpb,
+                  float* __restrict__ part_g, float* __restrict__ part_b) {
+  __shared__ float red[LN_WAVES][LN_DG_STRIP];
+  ln_dgb_tile(blockIdx.x, true, threadIdx.x, x, mean, rstd, dy, rows, cols, rpb, part_g, part_b, red);
+}
+
+// The two independent halves of the few-row backward in one launch, when dx
+// does not overwrite dy: blocks [0, ndg) take NT / 256 dgamma / dbeta tiles
+// each (one per group of 256 threads, tile = NT / 256 * block + group, the
+// arithmetic of ln_bwd_dgb_kernel), blocks [ndg, ndg + rows) one dx row each
+// (ln_bwd_dx_kernel's arithmetic).  Same bits as the two kernels.
+template <int NT, int J>
+__global__ void __launch_bounds__(NT)
+ln_bwd_few_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
+                  const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int cols8,
+                  int64_t rows, int64_t cols, int64_t rpb, int ntiles, int ndg, float* __restrict__ part_g,
+                  float* __restrict__ part_b) {
+  constexpr int GROUPS = NT / LN_THREADS;
+  __shared__ float red_g[GROUPS][LN_WAVES][LN_DG_STRIP];
+  __shared__ float red_x[2][NT / 64];
+  if ((int)blockIdx.x < ndg) {
+    const int grp = threadIdx.x / LN_THREADS;
+    const int tile = (int)blockIdx.x * GROUPS + grp;
+    ln_dgb_tile(tile, tile < ntiles, threadIdx.x % LN_THREADS, x, mean, rstd, dy, rows, cols, rpb, part_g, part_b,
+                red_g[grp]);
+  } else {
+    ln_dx_row<NT, J>((int64_t)blockIdx.x - ndg, x, gamma, mean, rstd, dy, dres, dx, cols8, (int)cols, red_x);
   }
 }
 
@@ -609,16 +656,47 @@ hipError_t ln_bwd_launch(const uint16_t* x, const uint16_t* gamma, const float* 
     hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, dgamma, part_b, dbeta, slabs, cols);
     return hipGetLastError();
   }
-  // the column sums first: they read dy, which dx may overwrite in place
   const int64_t strips = (cols + LN_DG_STRIP - 1) / LN_DG_STRIP;
-  hipLaunchKernelGGL(ln_bwd_dgb_kernel, dim3((unsigned)(strips * slabs)), blk, 0, st, x, mean, rstd, dy, rows, cols,
-                     rpb, part_g, part_b);
+  const int ntiles = (int)(strips * slabs);
+  const int nt = ln_nt(rows);
+  if (dx != dy) {
+    // dx leaves dy intact: the column partials and the dx rows in one launch,
+    // then the slab sums
+    const int ndg = (ntiles + nt / LN_THREADS - 1) / (nt / LN_THREADS);
+    const dim3 grid((unsigned)(ndg + rows)), fb(nt);
+#define LN_FEW(NT, J)                                                                                               \
+  hipLaunchKernelGGL((ln_bwd_few_kernel<NT, J>), grid, fb, 0, st, x, gamma, mean, rstd, dy, dres, dx, cols8, rows, \
+                     cols, rpb, ntiles, ndg, part_g, part_b)
+    const int j = ln_j(cols, nt);
+    if (nt == 1024) {
+      if (j == 1) LN_FEW(1024, 1);
+      else if (j == 2) LN_FEW(1024, 2);
+      else return hipErrorInvalidValue;
+    } else {
+      switch (j) {
+        case 1: LN_FEW(LN_THREADS, 1); break;
+        case 2: LN_FEW(LN_THREADS, 2); break;
+        case 3: LN_FEW(LN_THREADS, 3); break;
+        case 4: LN_FEW(LN_THREADS, 4); break;
+        case 6: LN_FEW(LN_THREADS, 6); break;
+        case 8: LN_FEW(LN_THREADS, 8); break;
+        default: return hipErrorInvalidValue;
+      }
+    }
+#undef LN_FEW
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, dgamma, part_b, dbeta, slabs, cols);
+    return hipGetLastError();
+  }
+  // dx overwrites dy: the column sums first, as they read dy
+  hipLaunchKernelGGL(ln_bwd_dgb_kernel, dim3((unsigned)ntiles), blk, 0, st, x, mean, rstd, dy, rows, cols, rpb,
+                     part_g, part_b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(slab_sum_kernel, sgrid, blk, 0, st, part_g, dgamma, part_b, dbeta, slabs, cols);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nt = ln_nt(rows);
 #define LN_BWD(NT, J)                                                                                            \
   hipLaunchKernelGGL((ln_bwd_dx_kernel<NT, J>), dim3((unsigned)rows), dim3(NT), 0, st, x, gamma, mean, rstd, dy, \
                      dres, dx, cols8, (int)cols)

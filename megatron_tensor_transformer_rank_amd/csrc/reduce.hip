@@ -12,7 +12,7 @@
 // once, with non-temporal loads, up to four ranks at a time; float32
 // accumulation in rank order, then the bias, then the residual, and one
 // rounding to bf16.  Up to four ranks: one block per output row with the
-// whole row's loads in flight; more ranks: a grid-stride loop with two
+// whole row's loads in flight; more ranks: a grid-stride loop with four
 // chunks per thread.
 #include "common.h"
 #include "reduce.h"
@@ -20,7 +20,7 @@
 namespace tpmlp {
 
 constexpr int RD_THREADS = 256;
-constexpr int RD_UNROLL = 2;   // output chunks per thread per iteration
+constexpr int RD_UNROLL = 4;   // output chunks per thread per iteration
 constexpr int RD_BATCH = 4;    // ranks loaded before they are added
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
