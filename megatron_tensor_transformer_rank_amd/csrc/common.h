@@ -20,16 +20,18 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w <
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float32 -> bfloat16 bits, round to nearest, ties to even; NaN -> quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// Two float32 -> two bfloat16 (lo in bits 0..15), round to nearest, ties to
+// even, denormals kept, NaN -> a quiet NaN: one v_cvt_pk_bf16_f32, which
+// gives the bits of the integer rounding u + 0x7fff + ((u >> 16) & 1) of the
+// float's pattern u for every non-NaN input (checked against it over every
+// 8th float32 pattern on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // ---------------------------------------------------------------------------
 // Activations (float32).  GeLU is the exact erf form, u * Phi(u).
