@@ -298,11 +298,33 @@ def test_grouped_weight_gradients_bitwise_separate(N, h, F, t):
         assert torch.equal(a, b)
 
 
+def _t256(m, n):
+    return ((m + 255) // 256) * ((n + 255) // 256)
+
+
+def _mixed_sweep(seed=20261203, n=8):
+    """Seeded shapes whose two backward pairs both take the mixed grid on 256
+    CUs (at least 256 tiles of 256 x 256 per pair), with tile counts that do
+    not divide evenly over the 8 XCDs."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        N = int(rng.integers(1200, 3201))
+        h, Fi = 8 * int(rng.integers(200, 601)), 8 * int(rng.integers(200, 601))
+        act = ["relu", "gelu", "swiglu"][int(rng.integers(0, 3))]
+        g = 2 if act == "swiglu" else 1
+        down = _t256(N, Fi) + _t256(Fi, h)           # dU, dW2
+        up = _t256(N, h) + _t256(h, g * Fi)          # dX, dW1 (dWg | dWu)
+        if down >= 256 and up >= 256 and (down % 8 or up % 8):
+            out.append((N, h, Fi, 1, act))
+    return out
+
+
 # Shapes whose backward pairs take the mixed grid (at least 256 tiles of
 # 256 x 256 per pair): GeLU with whole tiles, SwiGLU and ReLU ragged in every
-# dimension.
+# dimension, and a seeded sweep.
 @pytest.mark.parametrize("N,h,F,t,act", [(2048, 4096, 8192, 2, "gelu"), (1500, 4104, 6000, 2, "swiglu"),
-                                         (2100, 3000, 3504, 1, "relu")])
+                                         (2100, 3000, 3504, 1, "relu")] + _mixed_sweep())
 def test_mixed_backward_bitwise_separate(N, h, F, t, act):
     """tp_mlp_down_bwd_shard and tp_mlp_up_bwd_shard (one launch each here)
     equal the one-product calls bitwise, and the composite backward equals
