@@ -456,9 +456,9 @@ def bench_decode(args, w, B, I, torch, np, to_dev):
     gbs = wbytes / (us * 1e-6) / 1e9
     traffic = counter_traffic(f"gemv_hbm_traffic_{w.name}.md", GEMV_SOURCES, "decode")
     log(f"[bench] decode: {us:.2f} us/token cold ({gbs:.0f} GB/s), {us_warm:.2f} us warm")
-    # small-batch decode (2 <= N <= 64 takes the split-K MFMA path), same rotated weights
+    # small-batch decode (2 <= N <= 128 takes the split-K MFMA path), same rotated weights
     small = {}
-    for nb in (8, 32):
+    for nb in (8, 32, 128):
         xb = to_dev(I.normal_bf16([w.wid, 40, nb], (nb, h)))
         sb = B.make_shape(nb, h, w.F, w.t, 0, w.act)
         wsb = B.alloc_workspace(B.workspace_bytes(sb, False))
@@ -508,7 +508,7 @@ def bench_attn(args, B, I, torch, np, to_dev, N=2048, h=12288, heads=96, kv=96, 
     ws_do = B.alloc_workspace(B.attn_out_dgrad_workspace_bytes(s))
 
     def step():
-        B.tp_attn_qkv_shard(s, X, Wqkv, QKV)       # N > 64: no workspace
+        B.tp_attn_qkv_shard(s, X, Wqkv, QKV)       # N > 128: no workspace
         B.tp_attn_out_shard(s, O, Wo, Y)
         # dO alone (the attention core's backward needs only it); then dX, dW_qkv
         # and the deferred dW_o in one launch

@@ -133,11 +133,12 @@ typedef struct {
  * Three regimes, picked by N:
  *   N == 1       one-token decode: split-K GEMVs that read each weight once
  *                (HBM bound), float32 k-split partials in the workspace;
- *   2 <= N <= 64 small-batch decode: split-K MFMA products that also read
+ *   2 <= N <= 128 small batches: split-K MFMA products that also read
  *                each weight once, float32 k-split partials in the workspace
  *                ("02 -- Tensor Parallelism": decode batches stay memory
- *                bound);
- *   N > 64       the wide-tile MFMA GEMMs, which need no workspace.
+ *                bound; up to 128 tokens this is also 2.2-2.6x faster than
+ *                the wide tiles, whose 128-row tiles leave most CUs idle);
+ *   N > 128      the wide-tile MFMA GEMMs, which need no workspace.
  * All three produce the same quantities to the same tolerance.  workspace:
  * device memory of at least tp_mlp_workspace_bytes(s, 0) bytes, no initial
  * contents required; NULL is allowed when that size is 0.  Calls that share
@@ -153,12 +154,12 @@ tp_mlp_status tp_mlp_fwd_shard(const tp_mlp_shape* s, const void* X,
  * capture, tight decode/serving loops, harnesses that forbid allocation):
  * tp_mlp_fwd_shard with the same arguments, results and kernels (bitwise the
  * same outputs), but no workspace argument.  The k-split partials of the
- * one-token and small-batch paths (1 <= N <= 64) live in a fixed 32 MiB
+ * one-token and small-batch paths (1 <= N <= 128) live in a fixed 64 MiB
  * array of device memory inside the library, one per GPU, held until the
  * process ends; this call allocates nothing (no hipMalloc, no allocating
- * library routine).  A shape whose partials need more than 32 MiB returns
+ * library routine).  A shape whose partials need more than 64 MiB returns
  * TP_MLP_ERR_WORKSPACE before any launch (tp_mlp_workspace_bytes(s, 0) gives
- * the need; about 0.5 MiB per token at the 70B shard).  N > 64 takes the
+ * the need; about 0.5 MiB per token at the 70B shard).  N > 128 takes the
  * wide-tile path, which uses no scratch.  Every call on one GPU shares that
  * GPU's array, so calls that may overlap in time on one GPU (different
  * streams, or concurrent graphs) race on it: order them on one stream.  The
@@ -405,7 +406,7 @@ typedef struct {
 } tp_attn_shape;
 
 /* Workspace bytes the forward projections need for shape s: nonzero only
- * when 1 <= n_tokens <= 64, where tp_attn_qkv_shard and tp_attn_out_shard
+ * when 1 <= n_tokens <= 128, where tp_attn_qkv_shard and tp_attn_out_shard
  * take the small-batch path (split-K products that stream each weight once,
  * then a fixed-order sum of the k-splits, the arithmetic of the MLP's
  * small-batch path); 0 for larger N or an invalid shape. */

@@ -373,7 +373,7 @@ def tp_mlp_bias_grad(dY, db2, workspace, stream=None):
 # ------------------------------------------------------ attention projections
 def tp_attn_qkv_shard(shape: AttnShape, X, Wqkv_i, QKV_i, workspace=None, stream=None):
     """QKV_i = X @ Wqkv_i; workspace: attn_workspace_bytes(shape) bytes (needed
-    only for 1 <= N <= 64)."""
+    only for 1 <= N <= 128)."""
     N, h, w = shape.n_tokens, shape.hidden, shape.qkv_cols
     wp, wb = _ws(workspace, 0)
     _check("tp_attn_qkv_shard", lib().tp_attn_qkv_shard(

@@ -38,7 +38,7 @@ int num_cu_current() {
 // a fixed array in device memory, one copy per GPU, held until the process
 // ends.  In host code `scratch` only names the symbol; its device address on
 // the current GPU is looked up once per device and kept in g_scratch.
-constexpr size_t STATIC_SCRATCH_BYTES = (size_t)32 << 20;
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;
 static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
 std::atomic<void*> g_scratch[MAX_DEVICES];
 

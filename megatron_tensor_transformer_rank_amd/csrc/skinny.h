@@ -9,10 +9,10 @@
 
 namespace tpmlp {
 
-constexpr int SK_MAX_N = 64;  // largest token count of the small-batch path
+constexpr int SK_MAX_N = 128;  // largest token count of the small-batch path
 
 struct SkinnyPlan {
-  int rows;       // token rows padded to the MFMA tile (16, 32 or 64)
+  int rows;       // token rows padded to the MFMA tile (16, 32, 64 or 128)
   int strips;     // 256-column strips of one weight matrix
   int ks, kt;     // k-splits, 64-deep k-tiles per split
   size_t part_floats;

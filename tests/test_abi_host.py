@@ -48,7 +48,7 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    assert B.workspace_bytes(B.make_shape(128, 1024, 4096, 2, 0, "gelu"), False) == 0
+    assert B.workspace_bytes(B.make_shape(129, 1024, 4096, 2, 0, "gelu"), False) == 0
     dec = B.workspace_bytes(B.make_shape(1, 8192, 28672, 4, 0, "swiglu"), False)
     assert dec > 0 and dec % 256 == 0
     # bias-gradient scratch: at most 64 row slabs of float32 columns
@@ -329,15 +329,15 @@ def test_all_gather_rejects_bad_arguments():
 
 
 def test_small_batch_workspace_sizes():
-    """2 <= N <= 64 uses the split-K small-batch path, which needs float32
-    partials; N == 65 goes to the wide-tile GEMMs, which need none."""
+    """2 <= N <= 128 uses the split-K small-batch path, which needs float32
+    partials; N == 129 goes to the wide-tile GEMMs, which need none."""
     prev = 0
-    for N in (2, 16, 17, 32, 33, 64):
+    for N in (2, 16, 17, 32, 33, 64, 65, 96, 128):
         ws = B.workspace_bytes(B.make_shape(N, 8192, 28672, 4, 0, "swiglu"), False)
         assert ws > 0 and ws % 256 == 0
         assert ws >= prev
         prev = ws
-    assert B.workspace_bytes(B.make_shape(65, 8192, 28672, 4, 0, "swiglu"), False) == 0
+    assert B.workspace_bytes(B.make_shape(129, 8192, 28672, 4, 0, "swiglu"), False) == 0
     s = B.make_shape(8, 64, 128, 2, 0, "gelu")
     assert _fwd(s) == WORKSPACE                                  # small batch needs workspace
     assert _fwd(s, ws=P(8), wsb=B.workspace_bytes(s, False) - 1) == WORKSPACE
@@ -372,20 +372,20 @@ def test_attn_rejects_bad_pointers_and_reports_widths():
     assert L.tp_attn_out_shard(r, P(0), P(1) + 2, P(2), None, 0, None) == INVALID
     assert L.tp_attn_out_bwd_shard(r, P(0), P(1), P(2), P(3), None, None) == INVALID
     assert L.tp_attn_qkv_bwd_shard(r, P(0), P(1), P(2), P(3) + 4, P(4), None) == INVALID
-    # overlaps (N = 65 here: the wide-tile path, no workspace)
-    s65 = B.make_attn_shape(65, 64, 8, 2, 64, 4, 1)
-    r65 = ctypes.byref(s65)
-    assert L.tp_attn_qkv_shard(r65, P(0), P(1), P(0), None, 0, None) == INVALID        # QKV on X
-    assert L.tp_attn_out_shard(r65, P(0), P(1), P(1), None, 0, None) == INVALID        # Y on Wo
-    assert L.tp_attn_out_bwd_shard(r65, P(0), P(1), P(2), P(0), P(4), None) == INVALID  # dO on dY
-    assert L.tp_attn_qkv_bwd_shard(r65, P(0), P(1), P(2), P(3), P(3), None) == INVALID  # dX on dWqkv
+    # overlaps (N = 129 here: the wide-tile path, no workspace)
+    s129 = B.make_attn_shape(129, 64, 8, 2, 64, 4, 1)
+    r129 = ctypes.byref(s129)
+    assert L.tp_attn_qkv_shard(r129, P(0), P(1), P(0), None, 0, None) == INVALID        # QKV on X
+    assert L.tp_attn_out_shard(r129, P(0), P(1), P(1), None, 0, None) == INVALID        # Y on Wo
+    assert L.tp_attn_out_bwd_shard(r129, P(0), P(1), P(2), P(0), P(4), None) == INVALID  # dO on dY
+    assert L.tp_attn_qkv_bwd_shard(r129, P(0), P(1), P(2), P(3), P(3), None) == INVALID  # dX on dWqkv
 
 
 def test_attn_small_batch_workspace():
-    """1 <= N <= 64 tokens take the small-batch path, which needs float32
-    k-split partials; N = 65 goes to the wide tiles, which need none."""
+    """1 <= N <= 128 tokens take the small-batch path, which needs float32
+    k-split partials; N = 129 goes to the wide tiles, which need none."""
     L = B.lib()
-    for N in (1, 2, 17, 64):
+    for N in (1, 2, 17, 64, 65, 128):
         s = B.make_attn_shape(N, 8192, 64, 8, 128, 4, 0)     # 70B heads, t = 4
         need = B.attn_workspace_bytes(s)
         assert need > 0 and need % 256 == 0
@@ -397,7 +397,7 @@ def test_attn_small_batch_workspace():
         assert L.tp_attn_out_shard(r, P(0), P(1), P(2), P(3) + 8, need, None) == WORKSPACE  # alignment
         assert L.tp_attn_qkv_shard(r, P(0), P(1), P(2), P(2), need, None) == INVALID      # workspace on the output
         assert L.tp_attn_qkv_shard(r, P(0), P(1), P(2), P(1), need, None) == INVALID      # workspace on the weight
-    assert B.attn_workspace_bytes(B.make_attn_shape(65, 8192, 64, 8, 128, 4, 0)) == 0
+    assert B.attn_workspace_bytes(B.make_attn_shape(129, 8192, 64, 8, 128, 4, 0)) == 0
 
 
 # ------------------------------------------- sequence-parallel LayerNorm
@@ -517,12 +517,12 @@ def test_sum_grads_rejects_bad_arguments():
 
 def test_noalloc_forward_validates_and_refuses_shapes_beyond_its_scratch():
     """tp_mlp_fwd_shard_noalloc checks its arguments as tp_mlp_fwd_shard does
-    and refuses a shape whose k-split partials exceed its fixed 32 MiB
+    and refuses a shape whose k-split partials exceed its fixed 64 MiB
     scratch, before any launch (so this runs without a GPU)."""
     L = B.lib()
     fn = L.tp_mlp_fwd_shard_noalloc               # (s, X, W1, Wg, W2, Y, A, U, G, stream)
-    s = B.make_shape(64, 16384, 98304, 1, 0, "gelu")         # 40 MiB of partials, operands within limits
-    assert B.workspace_bytes(s, False) > 32 << 20
+    s = B.make_shape(128, 16384, 98304, 1, 0, "gelu")        # 80 MiB of partials, operands within limits
+    assert B.workspace_bytes(s, False) > 64 << 20
     # (the 3 GiB weights need fake buffers further apart)
     assert fn(ctypes.byref(s), P(0), P(4), None, P(8), P(12), P(13), P(14), None, None) == WORKSPACE
     s = B.make_shape(8, 64, 128, 2, 0, "swiglu")

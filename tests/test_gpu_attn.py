@@ -15,7 +15,7 @@ gradients whose tile grid fills at most half the CUs run split along k
 computed): the GPT-3-scale dO, the small-batch cases at the 70B widths, and
 a ragged two-slice case; one case takes the unsplit fallback when that
 storage is too small.  With
-1 <= N <= 64 tokens the forward projections take the small-batch path
+1 <= N <= 128 tokens the forward projections take the small-batch path
 (split-K products streaming each weight once); those token counts are
 covered for several head layouts and at the 70B per-rank widths.
 """
@@ -76,7 +76,7 @@ def run_attn_group(wid, N, h, nh, nkv, d, t, rows=None, ncols=None):
         dWo = torch.empty(s.q_cols, h, dtype=torch.float32, device="cuda")
         dWqkv = torch.empty(h, s.qkv_cols, dtype=torch.float32, device="cuda")
         dX = torch.empty(N, h, **bf)
-        ws = B.alloc_workspace(B.attn_workspace_bytes(s))   # 1 <= N <= 64: small-batch path
+        ws = B.alloc_workspace(B.attn_workspace_bytes(s))   # 1 <= N <= 128: small-batch path
         B.tp_attn_qkv_shard(s, Xd, Wqkv, QKV, workspace=ws)
         B.tp_attn_out_shard(s, bf16_dev(O_b), Wo, Y, workspace=ws)
         B.tp_attn_out_bwd_shard(s, dYd, bf16_dev(O_b), Wo, dO, dWo)
@@ -171,8 +171,10 @@ SMALL = [
     (712, 2, 264, 8, 2, 64, 4),        # replicated key/value heads
     (713, 16, 520, 16, 8, 32, 4),
     (714, 33, 1544, 16, 4, 128, 8),    # ragged: 33 rows, h tail past 256-column strips
-    (715, 64, 136, 4, 1, 64, 1),       # multi-query, the path's largest N
-    (716, 65, 264, 8, 8, 64, 2),       # just past it: wide tiles
+    (715, 64, 136, 4, 1, 64, 1),       # multi-query, the 64-row tile's largest N
+    (717, 100, 520, 8, 4, 64, 2),      # the 128-row tile, ragged rows
+    (718, 128, 264, 8, 8, 64, 2),      # the path's largest N
+    (716, 129, 264, 8, 8, 64, 2),      # just past it: wide tiles
 ]
 
 

@@ -1,16 +1,17 @@
-"""GPU parity of the small-batch decode path (2 <= N <= 64 tokens) against
+"""GPU parity of the small-batch decode path (2 <= N <= 128 tokens) against
 the fp64 oracle, through the C ABI.
 
-tp_mlp_fwd_shard routes 2 <= N <= 64 to split-K MFMA products that stream
+tp_mlp_fwd_shard routes 2 <= N <= 128 to split-K MFMA products that stream
 each weight once; the backward stays on the wide-tile GEMMs.  Checked:
 
 * whole tensor-parallel groups (forward on this path, backward on the GEMMs,
   the partials reduced) at token counts on both sides of every row-tile
-  boundary (16, 32) and at the path's edges (2 and 64; 65 goes to the GEMMs),
+  boundary (16, 32, 64) and at the path's edges (2 and 128; 129 goes to the
+  GEMMs),
   with ragged h and F_i (k-split and column-strip tails), all activations,
   with and without the stash;
 * the Llama-3-70B-shaped decode shard at full size (h = 8192, F_i = 7168,
-  SwiGLU) for batches of 2, 8, 32 and 64 tokens: A_i, the stashes and Y_i of
+  SwiGLU) for batches of 2, 8, 32, 64 and 128 tokens: A_i, the stashes and Y_i of
   rank 0 against the oracle;
 * the result does not depend on which buffer held the workspace before
   (two calls, the second on a dirtied workspace, bitwise equal).
@@ -45,7 +46,11 @@ GROUPS = [
     (305, 32, 1024, 4096, 2, "gelu", True),
     (306, 33, 136, 512, 1, "relu", False),
     (307, 64, 392, 2 * 520, 2, "swiglu", True),
-    (308, 65, 392, 2 * 520, 2, "swiglu", True),    # just past the path: wide-tile GEMMs
+    (308, 65, 392, 2 * 520, 2, "swiglu", True),    # first count on the 128-row tile
+    (330, 96, 4104, 2 * 776, 2, "gelu", False),    # 128-row tile: k tail and an 8-wide strip
+    (331, 127, 264, 3 * 392, 3, "relu", True),
+    (332, 128, 1032, 2 * 1040, 2, "swiglu", False),
+    (333, 129, 392, 2 * 520, 2, "swiglu", True),   # just past the path: wide-tile GEMMs
 ]
 
 
@@ -81,7 +86,7 @@ def test_small_batch_without_stash(act):
     assert_close("Y", f64(Y), Yref)
 
 
-@pytest.mark.parametrize("N", [2, 8, 32, 64])
+@pytest.mark.parametrize("N", [2, 8, 32, 64, 128])
 def test_small_batch_llama3_70b_shard_full_size(N):
     w = WORKLOADS["llama3_70b_decode_t4"]
     h, Fi = w.h, w.Fi
