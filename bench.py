@@ -175,11 +175,18 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev, clock_s=True):
     torch.cuda.synchronize()
 
     ws_db = B.alloc_workspace(B.bias_grad_workspace_bytes(N, h)) if w.bias else None
-    kernels = [
-        ("up_act", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_act_shard(shape, X, W1, Wg, A, U, G)),
-        ("down", 2 * N * h * Fi, lambda: B.tp_mlp_down_shard(shape, A, W2, Y)),
+    if ws_f is not None:
+        # a forward that needs a workspace takes the small-batch split-K path
+        # (N <= 128), which only the composite call runs
+        kernels = [("fwd", 2 * N * h * Fi * (w.g + 1),
+                    lambda: B.tp_mlp_fwd_shard(shape, X, W1, Wg, W2, Y, A, U, G, ws_f))]
+    else:
+        kernels = [("up_act", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_act_shard(shape, X, W1, Wg, A, U, G)),
+                   ("down", 2 * N * h * Fi, lambda: B.tp_mlp_down_shard(shape, A, W2, Y))]
+    kernels += [
         ("reduce_y", 0, lambda: B.tp_mlp_reduce_partials_local([Y] + others_y, Yred, bias=b2)),
-        # dU and dW2 (one mixed launch at these sizes), then dX_partial and dW1 (dWg)
+        # dU and dW2, then dX_partial and dW1 (dWg): one mixed launch each when their tiles fill
+        # the GPU; with few tokens the split-K input gradient, then the weight gradient
         ("down_bwd", 4 * N * h * Fi, lambda: B.tp_mlp_down_bwd_shard(shape, dY, W2, U, G, A, dU, dW2)),
         ("up_bwd", 4 * N * h * Fi * w.g, lambda: B.tp_mlp_up_bwd_shard(shape, X, dU, W1, Wg, dX, dW1, dWg)),
     ]

@@ -189,6 +189,10 @@ tp_mlp_status tp_mlp_fwd_shard_noalloc(const tp_mlp_shape* s, const void* X,
  *     tp_mlp_reduce_partials_local with bias NULL.
  *   db2 = sum over rows of dY -> fp32 [h], or NULL to skip.  The output bias
  *     is added once, so pass db2 on one rank only.
+ * With 1 <= N <= 128 tokens the two input gradients (dU_i, dX_partial) run
+ * as split-K products whose float32 partials are kept in dW2_i and dW1_i
+ * before those are written (as tp_mlp_down_bwd_shard and
+ * tp_mlp_up_bwd_shard do); otherwise on the wide tiles.
  * Inputs A_i, U_i (and G_i for SwiGLU) are the forward's outputs; U_i is
  * required.  The products need no workspace; db2 != NULL needs
  * tp_mlp_workspace_bytes(s, 1) bytes of device scratch (no initial contents
@@ -337,7 +341,11 @@ tp_mlp_status tp_mlp_up_dgrad_shard(const tp_mlp_shape* s, const void* dU_i,
  * (the tiles of the longer product are dispatched first, the other's fill
  * in behind them); otherwise they run one after the other.  Each element is
  * summed in the same order either way: the results are bitwise those of the
- * separate calls.  N = 0: dW2_i is written as zeros. */
+ * separate calls.  Exception, 1 <= N <= 128 with h >= N: dU_i runs as a
+ * split-K product (the few token rows leave the wide tiles' grid nearly
+ * empty) whose float32 partials are kept in dW2_i before dW2_i is computed;
+ * dW2_i is still bitwise that of the separate call, dU_i equal to it up to
+ * the order of its float32 sums.  N = 0: dW2_i is written as zeros. */
 tp_mlp_status tp_mlp_down_bwd_shard(const tp_mlp_shape* s, const void* dY,
                                     const void* W2_i, const void* U_i,
                                     const void* G_i, const void* A_i,
@@ -347,8 +355,11 @@ tp_mlp_status tp_mlp_down_bwd_shard(const tp_mlp_shape* s, const void* dY,
 /* The up-projection's backward, the second half of what tp_mlp_bwd_shard
  * runs: dX_partial as tp_mlp_up_dgrad_shard and dW1_i (dWg_i) as
  * tp_mlp_up_wgrad_shard, both from dU_i, in one launch or two as for
- * tp_mlp_down_bwd_shard, bitwise equal to the separate calls.  N = 0: the
- * weight gradients are written as zeros. */
+ * tp_mlp_down_bwd_shard, bitwise equal to the separate calls.  Exception,
+ * 1 <= N <= 128 with F_i >= g*N (g = 2 for SwiGLU, else 1): dX_partial runs
+ * as a split-K product whose partials are kept in dW1_i first, equal to the
+ * separate call up to the order of its float32 sums.  N = 0: the weight
+ * gradients are written as zeros. */
 tp_mlp_status tp_mlp_up_bwd_shard(const tp_mlp_shape* s, const void* X,
                                   const void* dU_i, const void* W1_i,
                                   const void* Wg_i, void* dX_partial,

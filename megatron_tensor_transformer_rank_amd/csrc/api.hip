@@ -4,6 +4,7 @@
 // Every check runs before the first launch, so an invalid call enqueues
 // nothing.  No exception crosses the ABI; nothing is printed.
 #include <atomic>
+#include <climits>
 #include <cstring>
 #include <initializer_list>
 #include <new>
@@ -121,8 +122,8 @@ bool small_batch(const Dims& d) { return d.N >= 2 && d.N <= SK_MAX_N; }
 
 SkinnyLayout skinny_layout(const Dims& d) {
   SkinnyLayout L;
-  L.up = skinny_plan((int)d.N, (int)d.h, (int)d.Fi, d.g, SKINNY_TARGET_BLOCKS);
-  L.down = skinny_plan((int)d.N, (int)d.Fi, (int)d.h, 1, SKINNY_TARGET_BLOCKS);
+  L.up = skinny_plan((int)d.N, (int)d.h, (int)d.Fi, d.g, SKINNY_TARGET_BLOCKS, INT_MAX);
+  L.down = skinny_plan((int)d.N, (int)d.Fi, (int)d.h, 1, SKINNY_TARGET_BLOCKS, INT_MAX);
   size_t off = 0;
   L.off_part_up = off;
   off = round256(off + L.up.part_floats * sizeof(float));
@@ -321,16 +322,38 @@ hipError_t run_pair(GemmKind kp, int act, const GemmArgs& p, const GemmArgs& q, 
   return e;
 }
 
+// With few tokens (1 <= N <= SK_MAX_N) the input gradients have a handful of
+// row tiles but a long k: they run as the small-batch split-K product, whose
+// float32 partials live in the weight gradient's storage (the same call
+// writes it only afterwards), with at most as many k-splits as fit there.
+// The weight gradient (k = N) then runs on the wide tiles.
+bool small_bwd(const Dims& d) { return d.N >= 1 && d.N <= SK_MAX_N; }
+
 // The down-projection's backward: dU (dgrad through W2 with the activation
 // derivative) and dW2 = A_i^T dY.
 hipError_t run_down_bwd(const Dims& d, const void* dY, const void* W2, const void* U, const void* G, const void* A,
                         void* dU, float* dW2, hipStream_t st) {
+  if (small_bwd(d) && d.h >= d.N) {  // partials [ks][N][F_i] in dW2 [F_i][h]: ks <= h / N
+    const SkinnyPlan p = skinny_plan((int)d.N, (int)d.h, (int)d.Fi, 1, SKINNY_TARGET_BLOCKS, (int)(d.h / d.N));
+    hipError_t e = skinny_dgrad_act_launch(d.act, (int)d.N, cu16(dY), cu16(W2), (int)d.h, (int)d.Fi, p, dW2,
+                                           cu16(U), cu16(G), u16(dU), st);
+    if (e == hipSuccess) e = gemm_launch(GEMM_WGRAD, d.act, wgrad_down_args(d, A, dY, dW2), num_cu_current(), st);
+    return e;
+  }
   return run_pair(GEMM_DGRAD_ACT, d.act, dgrad_act_args(d, dY, W2, U, G, dU), wgrad_down_args(d, A, dY, dW2), st);
 }
 
 // The up-projection's backward: dX_partial = dU W1_i^T and dW1 (dWg) = X^T dU.
 hipError_t run_up_bwd(const Dims& d, const void* X, const void* dU, const void* W1, const void* Wg, void* dX,
                       float* dW1, float* dWg, hipStream_t st) {
+  if (small_bwd(d) && d.Fi >= d.g * d.N) {  // partials [ks][g][N][h] in dW1 [h][F_i]: ks <= F_i / (g N)
+    const SkinnyPlan p =
+        skinny_plan((int)d.N, (int)d.Fi, (int)d.h, d.g, SKINNY_TARGET_BLOCKS, (int)(d.Fi / (d.g * d.N)));
+    hipError_t e = skinny_dgrad_up_launch(d.act, (int)d.N, cu16(dU), cu16(W1), cu16(Wg), (int)d.h, (int)d.Fi, p,
+                                          dW1, u16(dX), st);
+    if (e == hipSuccess) e = gemm_launch(GEMM_WGRAD, d.act, wgrad_up_args(d, X, dU, dW1, dWg), num_cu_current(), st);
+    return e;
+  }
   return run_pair(GEMM_DGRAD, d.act, dgrad_up_args(d, dU, W1, Wg, dX), wgrad_up_args(d, X, dU, dW1, dWg), st);
 }
 
@@ -368,10 +391,10 @@ tp_mlp_status attn_status(const tp_attn_shape* s, AttnDims& a) {
 // once through the split-K small-batch product instead of wide tiles.
 bool attn_small(const AttnDims& a) { return a.N >= 1 && a.N <= SK_MAX_N; }
 SkinnyPlan attn_qkv_plan(const AttnDims& a) {
-  return skinny_plan((int)a.N, (int)a.h, (int)a.qkv_cols, 1, SKINNY_TARGET_BLOCKS);
+  return skinny_plan((int)a.N, (int)a.h, (int)a.qkv_cols, 1, SKINNY_TARGET_BLOCKS, INT_MAX);
 }
 SkinnyPlan attn_out_plan(const AttnDims& a) {
-  return skinny_plan((int)a.N, (int)a.q_cols, (int)a.h, 1, SKINNY_TARGET_BLOCKS);
+  return skinny_plan((int)a.N, (int)a.q_cols, (int)a.h, 1, SKINNY_TARGET_BLOCKS, INT_MAX);
 }
 size_t attn_workspace(const AttnDims& a) {
   if (!attn_small(a)) return 0;

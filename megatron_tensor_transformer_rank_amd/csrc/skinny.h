@@ -19,8 +19,9 @@ struct SkinnyPlan {
 };
 
 // Split-K plan for X [N, K] @ W [K, ncols] over nmat matrices side by side,
-// aiming at target_blocks blocks.
-SkinnyPlan skinny_plan(int N, int K, int ncols, int nmat, int target_blocks);
+// aiming at target_blocks blocks with at most max_ks k-splits (and at most
+// K / (2N), which keeps the float32 partials within the weight's bytes).
+SkinnyPlan skinny_plan(int N, int K, int ncols, int nmat, int target_blocks, int max_ks);
 
 // Small-batch forward of one rank's shard: A = act(X @ [Wa, Wb]) (SwiGLU: Wa
 // = gate, Wb = up; otherwise Wa = W1, Wb unused), Y = A @ W2.  part_up /
@@ -31,6 +32,22 @@ hipError_t skinny_launch(int act, int N, const uint16_t* X, const uint16_t* Wa, 
                          const uint16_t* W2, int h, int Fi, const SkinnyPlan& up, const SkinnyPlan& down,
                          float* part_up, float* part_down, uint16_t* A, uint16_t* st0, uint16_t* st1, uint16_t* Y,
                          hipStream_t st);
+
+// Small-batch backward, input gradients (1 <= N <= SK_MAX_N), with the
+// weights read k-contiguous (W2_i [F_i, h] and W1_i, Wg_i [h, F_i] as
+// stored):
+//   dgrad_act: dA = dY @ W2^T as split-K partials (plan from
+//     skinny_plan(N, h, F_i, 1, ...)), then dU = dA * act'(U) (SwiGLU:
+//     [dG | dP] from G, U), bf16.
+//   dgrad_up:  dX = dU @ W1^T (SwiGLU: dG @ Wg^T + dP @ W1^T, the two k
+//     segments as matrices 0 and 1 of the plan skinny_plan(N, F_i, h, 2,
+//     ...)), the partials summed with one rounding.
+// part holds p.part_floats floats (no initial contents needed).
+hipError_t skinny_dgrad_act_launch(int act, int N, const uint16_t* dY, const uint16_t* W2, int h, int Fi,
+                                   const SkinnyPlan& p, float* part, const uint16_t* U, const uint16_t* G,
+                                   uint16_t* dU, hipStream_t st);
+hipError_t skinny_dgrad_up_launch(int act, int N, const uint16_t* dU, const uint16_t* W1, const uint16_t* Wg, int h,
+                                  int Fi, const SkinnyPlan& p, float* part, uint16_t* dX, hipStream_t st);
 
 // Y [N, ncols] (bf16) = X [N, K] @ W [K, ncols] for 1 <= N <= SK_MAX_N:
 // split-K partials (plan p from skinny_plan(N, K, ncols, 1, ...)), then their

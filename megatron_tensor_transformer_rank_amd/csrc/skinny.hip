@@ -38,11 +38,11 @@ constexpr int SK_THREADS = 256;
 constexpr int SK_COLS = 256;  // columns per block
 constexpr int SK_BK = 64;
 
-template <int MB, int NMAT>
+template <int MB, int NMAT, bool NT>
 __global__ void __launch_bounds__(SK_THREADS)
-skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_bytes, const uint16_t* W0,
-               const uint16_t* W1, uint32_t w_bytes, int K, int ncols, int strips, int kt_per_split,
-               float* __restrict__ part) {
+skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_bytes, int64_t x1_off,
+               const uint16_t* W0, const uint16_t* W1, uint32_t w_bytes, int K, int ncols, int strips,
+               int kt_per_split, float* __restrict__ part) {
   constexpr int TM = MB / 16;                // 16-row blocks (all waves)
   constexpr int TN = 4;                      // 16-column blocks per wave
   constexpr int W_BYTES = SK_COLS * 128;     // [64 k][256 cols]
@@ -67,19 +67,28 @@ skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_by
   const int nt = min(nkt, t0 + kt_per_split) - t0;
   const uint16_t* Wm = (NMAT == 2 && mat == 1) ? W1 : W0;
 
-  // weight tile DMA: [64 k][256 cols] of Wm starting at row k0
+  // weight tile DMA: [64 k][256 cols] of Wm from k-row k0 (Wm is [K][ncols]),
+  // or with NT the 256 rows col0.. of Wm [ncols][K] from column k0, stored
+  // k-contiguous like the activations
   DmaMN<SK_COLS> dw;
-  dw.init(col0, ncols, ncols, lane, w);
-  const uint32_t ldw2 = (uint32_t)ncols * 2u;
+  DmaK<SK_COLS> dwk;
+  if constexpr (NT)
+    dwk.init(col0, ncols, K, lane, w);
+  else
+    dw.init(col0, ncols, ncols, lane, w);
+  const uint32_t wk_step = NT ? 2u : (uint32_t)ncols * 2u;  // bytes per k of the weight tile's origin
   // activation tile DMA: instruction i = w + 4j covers rows 8i .. 8i+7, eight
   // 16-byte chunks per row, chunk c of row r at slot c ^ (r & 7); rows past N
-  // (and the padding instructions when MB = 16) read zeros
+  // (and the padding instructions when MB = 16) read zeros.  Matrix 1 of a
+  // pair whose activations sit side by side in one buffer reads from column
+  // x1_off.
   const int kc = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+  const uint32_t xcol = (uint32_t)((mat == 1 ? x1_off : 0) * 2);
   uint32_t xoff[NIX];
 #pragma unroll
   for (int j = 0; j < NIX; ++j) {
     const int row = (w + 4 * j) * 8 + (lane >> 3);
-    xoff[j] = (row < N && row < MB) ? (uint32_t)((int64_t)row * ldx * 2) + (uint32_t)kc * 2u : OOB;
+    xoff[j] = (row < N && row < MB) ? (uint32_t)((int64_t)row * ldx * 2) + xcol + (uint32_t)kc * 2u : OOB;
   }
   auto shifted = [](const uint16_t* p, uint32_t bytes, uint32_t skip) __attribute__((always_inline)) {
     const uint64_t a = reinterpret_cast<uint64_t>(p) + skip;
@@ -94,8 +103,13 @@ skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_by
     const bool live = i < nt;
     const int k0 = (t0 + i) * SK_BK;
     const int kvalid = live ? K - k0 : 0;
-    const rsrc_t rw = shifted(Wm, live ? w_bytes : 0u, (uint32_t)k0 * ldw2);
-    static_for<NIW>([&](auto J) __attribute__((always_inline)) { dw.template issue<decltype(J)::value>(rw, st, w); });
+    const rsrc_t rw = shifted(Wm, live ? w_bytes : 0u, (uint32_t)k0 * wk_step);
+    static_for<NIW>([&](auto J) __attribute__((always_inline)) {
+      if constexpr (NT)
+        dwk.template issue<decltype(J)::value>(rw, st, kvalid, w);
+      else
+        dw.template issue<decltype(J)::value>(rw, st, w);
+    });
     const rsrc_t rx = shifted(X, live ? x_bytes : 0u, (uint32_t)k0 * 2u);
 #pragma unroll
     for (int j = 0; j < NIX; ++j) dma16(rx, st + W_BYTES + (w + 4 * j) * 1024, kc < kvalid ? xoff[j] : OOB);
@@ -104,7 +118,10 @@ skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_by
   // fragment addressing within a stage
   const uint32_t a_off0 = W_BYTES + kfrag_off(0, 0, lane), a_off1 = W_BYTES + kfrag_off(0, 1, lane);
   uint32_t b_col[TN];
-  {
+  if constexpr (NT) {
+    b_col[0] = kfrag_off(w * 64, 0, lane);
+    b_col[1] = kfrag_off(w * 64, 1, lane);
+  } else {
     const uint32_t kb = mn_kbase<SK_COLS>(lane);
 #pragma unroll
     for (int j = 0; j < TN; ++j) b_col[j] = kb + mn_coloff<SK_COLS>(w * 64, j, lane);
@@ -138,8 +155,13 @@ skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_by
     constexpr int RS = SK_COLS * 2;
     static_for<TN>([&](auto J) __attribute__((always_inline)) {
       constexpr int jj = decltype(J)::value;
-      bf[0][jj] = ld_tr2<0, 4 * RS>(sa + b_col[jj]);
-      bf[1][jj] = ld_tr2<32 * RS, 36 * RS>(sa + b_col[jj]);
+      if constexpr (NT) {
+        bf[0][jj] = ld_b128<jj * 2048>(sa + b_col[0]);
+        bf[1][jj] = ld_b128<jj * 2048>(sa + b_col[1]);
+      } else {
+        bf[0][jj] = ld_tr2<0, 4 * RS>(sa + b_col[jj]);
+        bf[1][jj] = ld_tr2<32 * RS, 36 * RS>(sa + b_col[jj]);
+      }
     });
     // the fragments are consumed only after this wait: the reads and MFMAs
     // are volatile asm, so they keep this order
@@ -202,13 +224,55 @@ skinny_act(const float* __restrict__ part, int ks, int64_t n, uint16_t* __restri
   }
 }
 
-SkinnyPlan skinny_plan(int N, int K, int ncols, int nmat, int target_blocks) {
+// Backward through the activation: dA[e] = sum_q part[q][e] (k-split order)
+// over the flattened [N, F_i], then dU = dA * act'(U) (bf16 [N, F_i]), or for
+// SwiGLU the row [dG | dP] of dU [N, 2 F_i] from the stashes G, U.  The same
+// arithmetic as the wide-tile GEMM's epilogue, on a differently ordered dA.
+template <int ACT>
+__global__ void __launch_bounds__(256)
+skinny_act_bwd(const float* __restrict__ part, int ks, int64_t n, int Fi, const uint16_t* __restrict__ U,
+               const uint16_t* __restrict__ G, uint16_t* __restrict__ dU) {
+  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < n; e += (int64_t)gridDim.x * 256 * 4) {
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < ks; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)q * n + e);
+      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+    const float da[4] = {sum.x, sum.y, sum.z, sum.w};
+    const uint2 ub = *reinterpret_cast<const uint2*>(U + e);
+    const float uu[4] = {bf16lo(ub.x), bf16hi(ub.x), bf16lo(ub.y), bf16hi(ub.y)};
+    if constexpr (ACT == ACT_SWIGLU) {
+      const uint2 gb = *reinterpret_cast<const uint2*>(G + e);
+      const float gg[4] = {bf16lo(gb.x), bf16hi(gb.x), bf16lo(gb.y), bf16hi(gb.y)};
+      float dg[4], dp[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) swiglu_grad_f(da[r], gg[r], uu[r], dg[r], dp[r]);
+      // F_i % 8 == 0: the four elements share one row
+      const int64_t row = e / Fi, f = e - row * Fi;
+      uint16_t* out = dU + row * 2 * Fi + f;
+      *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+      *reinterpret_cast<uint2*>(out + Fi) = make_uint2(pack_bf16x2(dp[0], dp[1]), pack_bf16x2(dp[2], dp[3]));
+    } else {
+      float d[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[r] = da[r] * act_grad_f<ACT>(uu[r]);
+      *reinterpret_cast<uint2*>(dU + e) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+    }
+  }
+}
+
+SkinnyPlan skinny_plan(int N, int K, int ncols, int nmat, int target_blocks, int max_ks) {
   SkinnyPlan p;
   p.rows = N <= 16 ? 16 : (N <= 32 ? 32 : (N <= 64 ? 64 : 128));
   p.strips = (ncols + SK_COLS - 1) / SK_COLS;
   const int nkt = (K + SK_BK - 1) / SK_BK;
+  // no more splits than keep the float32 partials (ks N ncols 4 bytes) within
+  // the weight's own bytes (K ncols 2): past that, writing and re-reading them
+  // costs more than the extra blocks gain (at 128 tokens and h = 1024 the
+  // forward took 29.9 us with 4 and 8 splits against 31.9 with 16 and 32)
+  const int traffic_ks = max(1, K / (2 * N));
   int ks = target_blocks / (p.strips * nmat);
-  ks = max(1, min(ks, nkt));
+  ks = max(1, min(min(min(ks, max_ks), traffic_ks), nkt));
   p.kt = (nkt + ks - 1) / ks;
   p.ks = (nkt + p.kt - 1) / p.kt;  // every split non-empty
   p.part_floats = (size_t)p.ks * nmat * N * ncols;
@@ -217,24 +281,30 @@ SkinnyPlan skinny_plan(int N, int K, int ncols, int nmat, int target_blocks) {
 
 namespace {
 
-template <int NMAT>
-hipError_t partial_launch(const SkinnyPlan& p, int N, const uint16_t* X, int64_t ldx, const uint16_t* W0,
-                          const uint16_t* W1, int K, int ncols, float* part, hipStream_t st) {
+// x1_off: the element offset of matrix 1's activations from X (NMAT = 2
+// with NT: two k segments whose activations sit side by side in one row)
+template <int NMAT, bool NT, int MB>
+void partial_one(const SkinnyPlan& p, dim3 grid, int N, const uint16_t* X, int64_t ldx, uint32_t x_bytes,
+                 int64_t x1_off, const uint16_t* W0, const uint16_t* W1, uint32_t w_bytes, int K, int ncols,
+                 float* part, hipStream_t st) {
+  hipLaunchKernelGGL((skinny_partial<MB, NMAT, NT>), grid, dim3(SK_THREADS), 0, st, X, N, ldx, x_bytes, x1_off, W0,
+                     W1, w_bytes, K, ncols, p.strips, p.kt, part);
+}
+
+template <int NMAT, bool NT>
+hipError_t partial_launch(const SkinnyPlan& p, int N, const uint16_t* X, int64_t ldx, int64_t x1_off,
+                          const uint16_t* W0, const uint16_t* W1, int K, int ncols, float* part, hipStream_t st) {
   const uint32_t x_bytes = (uint32_t)((int64_t)N * ldx * 2);
   const uint32_t w_bytes = (uint32_t)((int64_t)K * ncols * 2);
-  const dim3 grid(p.strips * NMAT * p.ks), blk(SK_THREADS);
+  const dim3 grid(p.strips * NMAT * p.ks);
   if (p.rows == 16)
-    hipLaunchKernelGGL((skinny_partial<16, NMAT>), grid, blk, 0, st, X, N, ldx, x_bytes, W0, W1, w_bytes, K, ncols,
-                       p.strips, p.kt, part);
+    partial_one<NMAT, NT, 16>(p, grid, N, X, ldx, x_bytes, x1_off, W0, W1, w_bytes, K, ncols, part, st);
   else if (p.rows == 32)
-    hipLaunchKernelGGL((skinny_partial<32, NMAT>), grid, blk, 0, st, X, N, ldx, x_bytes, W0, W1, w_bytes, K, ncols,
-                       p.strips, p.kt, part);
+    partial_one<NMAT, NT, 32>(p, grid, N, X, ldx, x_bytes, x1_off, W0, W1, w_bytes, K, ncols, part, st);
   else if (p.rows == 64)
-    hipLaunchKernelGGL((skinny_partial<64, NMAT>), grid, blk, 0, st, X, N, ldx, x_bytes, W0, W1, w_bytes, K, ncols,
-                       p.strips, p.kt, part);
+    partial_one<NMAT, NT, 64>(p, grid, N, X, ldx, x_bytes, x1_off, W0, W1, w_bytes, K, ncols, part, st);
   else
-    hipLaunchKernelGGL((skinny_partial<128, NMAT>), grid, blk, 0, st, X, N, ldx, x_bytes, W0, W1, w_bytes, K, ncols,
-                       p.strips, p.kt, part);
+    partial_one<NMAT, NT, 128>(p, grid, N, X, ldx, x_bytes, x1_off, W0, W1, w_bytes, K, ncols, part, st);
   return hipGetLastError();
 }
 
@@ -249,8 +319,8 @@ hipError_t skinny_launch(int act, int N, const uint16_t* X, const uint16_t* Wa, 
                          const uint16_t* W2, int h, int Fi, const SkinnyPlan& up, const SkinnyPlan& down,
                          float* part_up, float* part_down, uint16_t* A, uint16_t* st0, uint16_t* st1, uint16_t* Y,
                          hipStream_t st) {
-  hipError_t e = act == ACT_SWIGLU ? partial_launch<2>(up, N, X, h, Wa, Wb, h, Fi, part_up, st)
-                                   : partial_launch<1>(up, N, X, h, Wa, Wa, h, Fi, part_up, st);
+  hipError_t e = act == ACT_SWIGLU ? partial_launch<2, false>(up, N, X, h, 0, Wa, Wb, h, Fi, part_up, st)
+                                   : partial_launch<1, false>(up, N, X, h, 0, Wa, Wa, h, Fi, part_up, st);
   if (e != hipSuccess) return e;
   const int64_t n_act = (int64_t)N * Fi;
   const dim3 ga(act_blocks(n_act)), ba(256);
@@ -262,14 +332,39 @@ hipError_t skinny_launch(int act, int N, const uint16_t* X, const uint16_t* Wa, 
     hipLaunchKernelGGL(skinny_act<ACT_GELU>, ga, ba, 0, st, part_up, up.ks, n_act, A, st0, nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = partial_launch<1>(down, N, A, Fi, W2, W2, Fi, h, part_down, st);
+  e = partial_launch<1, false>(down, N, A, Fi, 0, W2, W2, Fi, h, part_down, st);
   if (e != hipSuccess) return e;
   return ksum_launch(part_down, down.ks, (int64_t)N * h, Y, st);
 }
 
+hipError_t skinny_dgrad_act_launch(int act, int N, const uint16_t* dY, const uint16_t* W2, int h, int Fi,
+                                   const SkinnyPlan& p, float* part, const uint16_t* U, const uint16_t* G,
+                                   uint16_t* dU, hipStream_t st) {
+  hipError_t e = partial_launch<1, true>(p, N, dY, h, 0, W2, W2, h, Fi, part, st);
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)N * Fi;
+  const dim3 ga(act_blocks(n)), ba(256);
+  if (act == ACT_SWIGLU)
+    hipLaunchKernelGGL(skinny_act_bwd<ACT_SWIGLU>, ga, ba, 0, st, part, p.ks, n, Fi, U, G, dU);
+  else if (act == ACT_RELU)
+    hipLaunchKernelGGL(skinny_act_bwd<ACT_RELU>, ga, ba, 0, st, part, p.ks, n, Fi, U, nullptr, dU);
+  else
+    hipLaunchKernelGGL(skinny_act_bwd<ACT_GELU>, ga, ba, 0, st, part, p.ks, n, Fi, U, nullptr, dU);
+  return hipGetLastError();
+}
+
+hipError_t skinny_dgrad_up_launch(int act, int N, const uint16_t* dU, const uint16_t* W1, const uint16_t* Wg, int h,
+                                  int Fi, const SkinnyPlan& p, float* part, uint16_t* dX, hipStream_t st) {
+  const bool sw = act == ACT_SWIGLU;
+  const hipError_t e = sw ? partial_launch<2, true>(p, N, dU, 2 * (int64_t)Fi, Fi, Wg, W1, Fi, h, part, st)
+                          : partial_launch<1, true>(p, N, dU, Fi, 0, W1, W1, Fi, h, part, st);
+  if (e != hipSuccess) return e;
+  return ksum_launch(part, p.ks * (sw ? 2 : 1), (int64_t)N * h, dX, st);
+}
+
 hipError_t skinny_product_launch(int N, const uint16_t* X, const uint16_t* W, int K, int ncols, const SkinnyPlan& p,
                                  float* part, uint16_t* Y, hipStream_t st) {
-  const hipError_t e = partial_launch<1>(p, N, X, K, W, W, K, ncols, part, st);
+  const hipError_t e = partial_launch<1, false>(p, N, X, K, 0, W, W, K, ncols, part, st);
   if (e != hipSuccess) return e;
   return ksum_launch(part, p.ks, (int64_t)N * ncols, Y, st);
 }

@@ -1,8 +1,13 @@
-"""GPU parity of the small-batch decode path (2 <= N <= 128 tokens) against
-the fp64 oracle, through the C ABI.
+"""GPU parity of the small-batch path (up to 128 tokens) against the fp64
+oracle, through the C ABI.
 
 tp_mlp_fwd_shard routes 2 <= N <= 128 to split-K MFMA products that stream
-each weight once; the backward stays on the wide-tile GEMMs.  Checked:
+each weight once.  In the backward (1 <= N <= 128) the two input gradients
+(dU through W2 and the activation, dX_partial through W1) run as split-K
+products too, their float32 partials kept in the weight gradient's storage
+before the weight gradient (k = N) runs on the wide tiles; a shape whose
+weight-gradient storage cannot hold one split (h < N for dU, F_i < g*N for
+dX) keeps the wide tiles.  Checked:
 
 * whole tensor-parallel groups (forward on this path, backward on the GEMMs,
   the partials reduced) at token counts on both sides of every row-tile
@@ -14,7 +19,14 @@ each weight once; the backward stays on the wide-tile GEMMs.  Checked:
   SwiGLU) for batches of 2, 8, 32, 64 and 128 tokens: A_i, the stashes and Y_i of
   rank 0 against the oracle;
 * the result does not depend on which buffer held the workspace before
-  (two calls, the second on a dirtied workspace, bitwise equal).
+  (two calls, the second on a dirtied workspace, bitwise equal);
+* the backward step calls (tp_mlp_down_bwd_shard, tp_mlp_up_bwd_shard) equal
+  the composite backward bitwise, their weight gradients equal the
+  one-product calls bitwise, and their input gradients agree with the
+  one-product calls (the wide tiles, a different summation order) to the
+  parity bound;
+* the 70B shard's backward at full size for 8 and 128 tokens against the
+  oracle (dU, dX_i, and sampled weight-gradient columns).
 """
 from __future__ import annotations
 
@@ -51,6 +63,9 @@ GROUPS = [
     (331, 127, 264, 3 * 392, 3, "relu", True),
     (332, 128, 1032, 2 * 1040, 2, "swiglu", False),
     (333, 129, 392, 2 * 520, 2, "swiglu", True),   # just past the path: wide-tile GEMMs
+    (334, 96, 64, 2 * 80, 2, "swiglu", False),     # h < N and F_i < 2N: the backward keeps the wide tiles
+    (335, 40, 520, 2 * 56, 2, "gelu", True),       # F_i = 56: one k-split fits dX's partials
+    (336, 1, 2056, 2 * 1544, 2, "relu", False),    # one token: split-K backward
 ]
 
 
@@ -129,3 +144,84 @@ def test_small_batch_deterministic_and_workspace_contents_irrelevant():
         torch.cuda.synchronize()
         outs.append((Y.clone(), A.clone()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# (wid, N, h, F, t, act)
+BWD_STEPS = [(340, 1, 1032, 2 * 776, 2, "swiglu"), (341, 8, 4104, 2 * 1544, 2, "gelu"),
+             (342, 77, 1544, 3 * 1032, 3, "relu"), (343, 128, 1024, 4096, 2, "gelu"),
+             (344, 128, 2056, 2 * 2064, 2, "swiglu")]
+
+
+@pytest.mark.parametrize("case", BWD_STEPS, ids=[f"N{c[1]}_h{c[2]}_F{c[3]}_{c[5]}" for c in BWD_STEPS])
+def test_small_batch_backward_step_calls(case):
+    wid, N, h, F, t, act = case
+    say(f"[small batch backward steps] N={N} h={h} F={F} t={t} {act}")
+    Fi, sw = F // t, act == "swiglu"
+    g = 2 if sw else 1
+    s = B.make_shape(N, h, F, t, 0, act)
+    X, dY = bf16_dev(I.gen_x(wid, N, h)), bf16_dev(I.gen_dy(wid, N, h))
+    W1 = bf16_dev(I.normal_bf16([wid, 1], (h, Fi), I.WEIGHT_SIGMA))
+    Wg = bf16_dev(I.normal_bf16([wid, 2], (h, Fi), I.WEIGHT_SIGMA)) if sw else None
+    W2 = bf16_dev(I.normal_bf16([wid, 3], (Fi, h), I.WEIGHT_SIGMA))
+    A, U = bf16_dev(I.normal_bf16([wid, 4], (N, Fi))), bf16_dev(I.normal_bf16([wid, 5], (N, Fi)))
+    G = bf16_dev(I.normal_bf16([wid, 6], (N, Fi))) if sw else None
+    bf, f32 = dict(dtype=torch.bfloat16, device="cuda"), dict(dtype=torch.float32, device="cuda")
+
+    def outs():
+        return (torch.empty(N, g * Fi, **bf), torch.empty(Fi, h, **f32), torch.empty(N, h, **bf),
+                torch.empty(h, Fi, **f32), torch.empty(h, Fi, **f32) if sw else None)
+    sep, steps, comp = outs(), outs(), outs()
+    B.tp_mlp_down_dgrad_act_shard(s, dY, W2, U, G, sep[0])
+    B.tp_mlp_down_wgrad_shard(s, A, dY, sep[1])
+    B.tp_mlp_down_bwd_shard(s, dY, W2, U, G, A, steps[0], steps[1])
+    # the up-projection's calls on the same dU
+    B.tp_mlp_up_dgrad_shard(s, steps[0], W1, Wg, sep[2])
+    B.tp_mlp_up_wgrad_shard(s, X, steps[0], sep[3], sep[4])
+    B.tp_mlp_up_bwd_shard(s, X, steps[0], W1, Wg, steps[2], steps[3], steps[4])
+    B.tp_mlp_bwd_shard(s, X, W1, Wg, W2, dY, A, U, G, comp[0], comp[3], comp[4], comp[1], comp[2])
+    torch.cuda.synchronize()
+    for name, a, b, c in zip(("dU", "dW2", "dX", "dW1", "dWg"), sep, steps, comp):
+        if a is None:
+            continue
+        assert torch.equal(b, c), f"{name}: composite differs from the step calls"
+        if name.startswith("dW"):
+            assert torch.equal(a, b), f"{name}: differs from the one-product call"
+        else:
+            assert_close(name, f64(b), f64(a))
+
+
+@pytest.mark.parametrize("N", [8, 128])
+def test_small_batch_backward_llama3_70b_shard_full_size(N):
+    """Rank 0 of the 70B shard (h = 8192, F_i = 7168, SwiGLU): forward, then
+    the backward through the composite call; dU and dX_i whole, 64 sampled
+    columns of each weight gradient."""
+    w = WORKLOADS["llama3_70b_decode_t4"]
+    h, Fi = w.h, w.Fi
+    say(f"[small batch backward full size] N={N} h={h} F_i={Fi} swiglu")
+    Xb, dYb = I.normal_bf16([w.wid, 41, N], (N, h)), I.normal_bf16([w.wid, 42, N], (N, h))
+    W1b = I.gen_w_up_shard(w.wid, h, Fi, 0)
+    Wgb = I.gen_w_gate_shard(w.wid, h, Fi, 0)
+    W2b = I.gen_w_down_shard(w.wid, h, Fi, 0)
+    f = oracle.bf16_bits_to_f64
+    ref = oracle.shard_backward("swiglu", f(Xb), f(W1b), f(W2b), f(dYb), f(Wgb))
+    shape = B.make_shape(N, h, w.F, w.t, 0, "swiglu")
+    bf, f32 = dict(dtype=torch.bfloat16, device="cuda"), dict(dtype=torch.float32, device="cuda")
+    X, dY = bf16_dev(Xb), bf16_dev(dYb)
+    W1, Wg, W2 = bf16_dev(W1b), bf16_dev(Wgb), bf16_dev(W2b)
+    Y, A = torch.empty(N, h, **bf), torch.empty(N, Fi, **bf)
+    U, G = torch.empty(N, Fi, **bf), torch.empty(N, Fi, **bf)
+    ws = B.alloc_workspace(B.workspace_bytes(shape, False))
+    B.tp_mlp_fwd_shard(shape, X, W1, Wg, W2, Y, A, U, G, ws)
+    dU, dX = torch.empty(N, 2 * Fi, **bf), torch.empty(N, h, **bf)
+    dW1, dWg, dW2 = torch.empty(h, Fi, **f32), torch.empty(h, Fi, **f32), torch.empty(Fi, h, **f32)
+    B.tp_mlp_bwd_shard(shape, X, W1, Wg, W2, dY, A, U, G, dU, dW1, dWg, dW2, dX)
+    torch.cuda.synchronize()
+    du = f64(dU)
+    assert_close("dG", du[:, :Fi], ref["dG"])
+    assert_close("dP", du[:, Fi:], ref["dU"])
+    assert_close("dX_i", f64(dX), ref["dX"])
+    rng = np.random.default_rng(N)
+    cf, ch = np.sort(rng.choice(Fi, 64, replace=False)), np.sort(rng.choice(h, 64, replace=False))
+    assert_close("dW1 cols", dW1[:, cf].cpu().double().numpy(), ref["dW1"][:, cf])
+    assert_close("dWg cols", dWg[:, cf].cpu().double().numpy(), ref["dWg"][:, cf])
+    assert_close("dW2 cols", dW2[:, ch].cpu().double().numpy(), ref["dW2"][:, ch])
