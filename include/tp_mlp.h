@@ -443,7 +443,12 @@ tp_mlp_status tp_attn_out_shard(const tp_attn_shape* s, const void* O_i,
 /* Backward of the output projection for dY [N, h] (the same on every rank):
  *   dO_i  = dY @ Wo_i^T  -> bf16 [N, qc]  (input of the attention core's
  *                                          backward)
- *   dWo_i = O_i^T @ dY   -> fp32 [qc, h]                               */
+ *   dWo_i = O_i^T @ dY   -> fp32 [qc, h]
+ * With 1 <= N <= 128 tokens (and h >= N) dO_i runs as the small-batch
+ * split-K product, whose float32 partials are kept in dWo_i before dWo_i is
+ * computed, as long as those partials (written and read back) stay within
+ * Wo_i's bytes; otherwise on the wide tiles, split along k the same way when
+ * their grid leaves most CUs idle. */
 tp_mlp_status tp_attn_out_bwd_shard(const tp_attn_shape* s, const void* dY,
                                     const void* O_i, const void* Wo_i,
                                     void* dO_i, float* dWo_i,
@@ -452,7 +457,10 @@ tp_mlp_status tp_attn_out_bwd_shard(const tp_attn_shape* s, const void* dY,
 /* Backward of the QKV projection for dQKV_i [N, qkvc] (the attention core's
  * gradient, laid out like QKV_i):
  *   dX_partial = dQKV_i @ Wqkv_i^T -> bf16 [N, h]  (sum over ranks)
- *   dWqkv_i    = X^T @ dQKV_i      -> fp32 [h, qkvc]                    */
+ *   dWqkv_i    = X^T @ dQKV_i      -> fp32 [h, qkvc]
+ * With 1 <= N <= 128 tokens (and qkvc >= N) dX_partial runs as the
+ * small-batch split-K product with its partials in dWqkv_i, then dWqkv_i, as
+ * long as those partials stay within Wqkv_i's bytes (as for dO_i). */
 tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X,
                                     const void* Wqkv_i, const void* dQKV_i,
                                     float* dWqkv_i, void* dX_partial,
@@ -463,10 +471,11 @@ tp_mlp_status tp_attn_qkv_bwd_shard(const tp_attn_shape* s, const void* X,
  * only dO_i, and dWo_i = O_i^T @ dY can wait to share a launch with the QKV
  * projection's backward (both are weight gradients over the tokens).
  *
- * dO_i = dY @ Wo_i^T -> bf16 [N, qc], alone.  When its tile grid would leave
- * most CUs idle it runs split along k into float32 partials in the
- * workspace, summed in slice order and rounded once (the same arithmetic as
- * tp_attn_out_bwd_shard's dO_i, which borrows dWo_i's storage instead).
+ * dO_i = dY @ Wo_i^T -> bf16 [N, qc], alone.  With 1 <= N <= 128 tokens, or
+ * when its tile grid would leave most CUs idle, it runs split along k into
+ * float32 partials in the workspace, summed in slice order and rounded once
+ * (the same splits and arithmetic as tp_attn_out_bwd_shard's dO_i, which
+ * borrows dWo_i's storage instead: the same bits).
  *   workspace  tp_attn_out_dgrad_workspace_bytes(s) bytes of device scratch
  *              (no initial contents needed; NULL when that is 0); missing or
  *              smaller: TP_MLP_ERR_WORKSPACE. */
@@ -479,8 +488,10 @@ tp_mlp_status tp_attn_out_dgrad_shard(const tp_attn_shape* s, const void* dY,
 /* tp_attn_qkv_bwd_shard's dX_partial and dWqkv_i together with the output
  * projection's deferred dWo_i = O_i^T @ dY (fp32 [qc, h]), in one launch when
  * the block tiles fill the GPU (dX_partial's tiles first, the two weight
- * gradients' filling in behind them), else one after the other.  Each
- * element is summed in the same order as in the separate calls. */
+ * gradients' filling in behind them), else one after the other (with
+ * 1 <= N <= 128 tokens: dX_partial as in tp_attn_qkv_bwd_shard, then both
+ * weight gradients in one launch).  Each element is summed in the same order
+ * as in the separate calls: the results are bitwise theirs. */
 tp_mlp_status tp_attn_qkv_bwd_out_wgrad_shard(const tp_attn_shape* s,
                                               const void* X,
                                               const void* Wqkv_i,

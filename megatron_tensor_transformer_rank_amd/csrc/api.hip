@@ -442,13 +442,32 @@ int nt_slices(int64_t M, int64_t Nc, int64_t K, int num_cu) {
   return s >= 2 ? (int)s : 0;
 }
 
-// C [M, Nc] = A [M, K] @ B^T with B stored [Nc, K], bf16 out.  When the tile
-// grid leaves most CUs idle and `part` (device, float32, part_floats
-// of them, no contents needed) holds slices * M * Nc partials, the product
+// An NT product with 1 <= M <= SK_MAX_N rows may run on the small-batch
+// split-K kernel with at most skinny_cap k-splits (the number the weight
+// gradient's storage holds, passed alike by every call that must give the
+// same bits), and does while its partials, written and read back
+// (2 ks M Nc 4 bytes), stay below the weight's bytes (K Nc 2): past that the
+// wide tiles, themselves split along k when their grid is small, were as
+// fast or faster on the attention projections' input gradients (70B widths
+// at 128 tokens: dO 43 against 36 us).
+bool skinny_nt_pays(const SkinnyPlan& p, int64_t M, int64_t K) { return 4 * (int64_t)p.ks * M < K; }
+int cap_of(int64_t storage_floats, int64_t M, int64_t Nc) {
+  return (int)std::min<int64_t>(storage_floats / (M * Nc), INT_MAX);
+}
+
+// C [M, Nc] = A [M, K] @ B^T with B stored [Nc, K], bf16 out.  With few rows
+// and room in `part` (device, float32, part_floats of them, no contents
+// needed), the small-batch split-K product as above; else, when the tile grid
+// leaves most CUs idle and `part` holds slices * M * Nc partials, the product
 // runs split along k into float32 partials, whose sum in slice order is
 // rounded to bf16 once.
 hipError_t run_nt(int64_t M, int64_t Nc, int64_t K, const void* A, const void* B, void* C, hipStream_t st,
-                  float* part = nullptr, uint64_t part_floats = 0) {
+                  float* part = nullptr, uint64_t part_floats = 0, int skinny_cap = 0) {
+  if (part && skinny_cap >= 1 && M >= 1 && M <= SK_MAX_N) {
+    const SkinnyPlan p = skinny_plan((int)M, (int)K, (int)Nc, 1, SKINNY_TARGET_BLOCKS, skinny_cap);
+    if (skinny_nt_pays(p, M, K) && p.part_floats <= part_floats)
+      return skinny_product_launch((int)M, cu16(A), cu16(B), (int)K, (int)Nc, p, part, u16(C), st, true);
+  }
   const int ncu = num_cu_current();
   const int s = part ? nt_slices(M, Nc, K, ncu) : 0;
   if (s > 0 && (uint64_t)s * (uint64_t)M * (uint64_t)Nc <= part_floats) {
@@ -536,6 +555,16 @@ hipError_t run_attn_qkv_bwd(const AttnDims& a, const void* X, const void* Wqkv, 
   const GemmArgs q0 = tn_args(a.h, a.qkv_cols, a.N, X, dQKV, dWqkv);
   GemmArgs q1 = q0;
   if (dWo) q1 = tn_args(a.q_cols, a.h, a.N, O, dY, dWo);
+  const int cap = part && a.N >= 1 ? cap_of((int64_t)part_floats, a.N, a.h) : 0;
+  if (cap >= 1 && a.N <= SK_MAX_N &&
+      skinny_nt_pays(skinny_plan((int)a.N, (int)a.qkv_cols, (int)a.h, 1, SKINNY_TARGET_BLOCKS, cap), a.N,
+                     a.qkv_cols)) {
+    // few tokens: dX as the split-K product, then the weight gradient(s) in one launch
+    hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV, Wqkv, dX, st, part, part_floats, cap);
+    if (e != hipSuccess) return e;
+    return dWo ? gemm_launch2(GEMM_WGRAD, 0, q0, q1, num_cu_current(), st)
+               : gemm_launch(GEMM_WGRAD, 0, q0, num_cu_current(), st);
+  }
   if (tiles256(p) + tiles256(q0) + (dWo ? tiles256(q1) : 0) >= num_cu_current())
     return gemm_launch_mixed(GEMM_DGRAD, 0, p, q0, dWo ? &q1 : nullptr, st);
   hipError_t e = run_nt(a.N, a.h, a.qkv_cols, dQKV, Wqkv, dX, st, part, part_floats);
@@ -544,9 +573,20 @@ hipError_t run_attn_qkv_bwd(const AttnDims& a, const void* X, const void* Wqkv, 
   return e;
 }
 
+// k-splits of dO = dY Wo^T on the small-batch kernel: as many as dW_o's
+// storage holds (h / N), in tp_attn_out_bwd_shard and tp_attn_out_dgrad_shard
+// alike.
+int dO_cap(const AttnDims& a) { return a.N >= 1 ? cap_of(a.q_cols * a.h, a.N, a.q_cols) : 0; }
+
 // Float32 partials the output projection's input gradient dO = dY Wo^T
-// splits into along k (0: not split).
+// splits into along k (0: not split).  With few tokens, the small-batch
+// plan with as many splits as dW_o's storage would hold (h / N), the plan
+// tp_attn_out_bwd_shard runs, so that both give the same dO.
 uint64_t attn_dO_part_floats(const AttnDims& a) {
+  if (a.N >= 1 && a.N <= SK_MAX_N && a.h >= a.N) {
+    const SkinnyPlan p = skinny_plan((int)a.N, (int)a.h, (int)a.q_cols, 1, SKINNY_TARGET_BLOCKS, dO_cap(a));
+    if (skinny_nt_pays(p, a.N, a.h)) return p.part_floats;
+  }
   const int s = nt_slices(a.N, a.q_cols, a.h, num_cu_current());
   return s > 0 ? (uint64_t)s * (uint64_t)a.N * (uint64_t)a.q_cols : 0;
 }
@@ -1026,7 +1066,7 @@ tp_mlp_status tp_attn_out_bwd_shard(const tp_attn_shape* s, const void* dY, cons
     return TP_MLP_ERR_INVALID_ARG;
   if (a.N == 0) return hip_status(zero_f32_launch(dWo_i, a.q_cols * a.h, num_cu_current(), stream));
   // dWo_i is written after dO_i: until then its storage holds dO_i's k-split partials
-  hipError_t e = run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream, dWo_i, (uint64_t)a.q_cols * a.h);
+  hipError_t e = run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream, dWo_i, (uint64_t)a.q_cols * a.h, dO_cap(a));
   if (e == hipSuccess) e = run_tn(a.q_cols, a.h, a.N, O_i, dY, dWo_i, stream);
   return hip_status(e);
 }
@@ -1065,7 +1105,8 @@ tp_mlp_status tp_attn_out_dgrad_shard(const tp_attn_shape* s, const void* dY, co
                 {{dY, nbytes(a.N, a.h)}, {Wo_i, nbytes(a.q_cols, a.h)}}))
     return TP_MLP_ERR_INVALID_ARG;
   if (a.N == 0) return TP_MLP_OK;
-  return hip_status(run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream, static_cast<float*>(workspace), pf));
+  return hip_status(
+      run_nt(a.N, a.q_cols, a.h, dY, Wo_i, dO_i, stream, static_cast<float*>(workspace), pf, dO_cap(a)));
 }
 
 tp_mlp_status tp_attn_qkv_bwd_out_wgrad_shard(const tp_attn_shape* s, const void* X, const void* Wqkv_i,

@@ -49,10 +49,11 @@ hipError_t skinny_dgrad_act_launch(int act, int N, const uint16_t* dY, const uin
 hipError_t skinny_dgrad_up_launch(int act, int N, const uint16_t* dU, const uint16_t* W1, const uint16_t* Wg, int h,
                                   int Fi, const SkinnyPlan& p, float* part, uint16_t* dX, hipStream_t st);
 
-// Y [N, ncols] (bf16) = X [N, K] @ W [K, ncols] for 1 <= N <= SK_MAX_N:
-// split-K partials (plan p from skinny_plan(N, K, ncols, 1, ...)), then their
-// sum in k-split order with one rounding.  part holds p.part_floats floats.
+// Y [N, ncols] (bf16) = X [N, K] @ W [K, ncols] (w_nt: @ W^T with W stored
+// [ncols, K]) for 1 <= N <= SK_MAX_N: split-K partials (plan p from
+// skinny_plan(N, K, ncols, 1, ...)), then their sum in k-split order with one
+// rounding.  part holds p.part_floats floats.
 hipError_t skinny_product_launch(int N, const uint16_t* X, const uint16_t* W, int K, int ncols, const SkinnyPlan& p,
-                                 float* part, uint16_t* Y, hipStream_t st);
+                                 float* part, uint16_t* Y, hipStream_t st, bool w_nt = false);
 
 }  // namespace tpmlp

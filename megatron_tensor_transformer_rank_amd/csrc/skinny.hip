@@ -363,8 +363,9 @@ hipError_t skinny_dgrad_up_launch(int act, int N, const uint16_t* dU, const uint
 }
 
 hipError_t skinny_product_launch(int N, const uint16_t* X, const uint16_t* W, int K, int ncols, const SkinnyPlan& p,
-                                 float* part, uint16_t* Y, hipStream_t st) {
-  const hipError_t e = partial_launch<1, false>(p, N, X, K, 0, W, W, K, ncols, part, st);
+                                 float* part, uint16_t* Y, hipStream_t st, bool w_nt) {
+  const hipError_t e = w_nt ? partial_launch<1, true>(p, N, X, K, 0, W, W, K, ncols, part, st)
+                            : partial_launch<1, false>(p, N, X, K, 0, W, W, K, ncols, part, st);
   if (e != hipSuccess) return e;
   return ksum_launch(part, p.ks, (int64_t)N * ncols, Y, st);
 }

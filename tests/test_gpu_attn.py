@@ -12,12 +12,14 @@ replicated on several ranks, ragged token counts, and the GPT-3-scale and
 Llama-3-70B-scale per-rank widths with sampled rows and columns.  Input
 gradients whose tile grid fills at most half the CUs run split along k
 (float32 slice partials kept in the weight gradient's storage until it is
-computed): the GPT-3-scale dO, the small-batch cases at the 70B widths, and
-a ragged two-slice case; one case takes the unsplit fallback when that
-storage is too small.  With
+computed): the GPT-3-scale dO and a ragged two-slice case; one case takes
+the unsplit fallback when that storage is too small.  With
 1 <= N <= 128 tokens the forward projections take the small-batch path
-(split-K products streaming each weight once); those token counts are
-covered for several head layouts and at the 70B per-rank widths.
+(split-K products streaming each weight once), and so do the backward's
+input gradients dO and dX (their partials kept in dW_o's and dW_qkv's
+storage); those token counts are covered for several head layouts and at
+the 70B per-rank widths, and the deferred pair stays bitwise equal to the
+plain backward calls there too.
 """
 from __future__ import annotations
 
@@ -134,7 +136,7 @@ GROUPS = [
     (702, 200, 264, 8, 2, 64, 4),      # 2 key/value heads over 4 ranks: each replicated on 2
     (703, 77, 384, 16, 8, 32, 4),      # grouped-query, key/value heads split 2 per rank
     (704, 300, 1032, 16, 4, 128, 8),   # 4 key/value heads over 8 ranks
-    (705, 33, 136, 4, 1, 64, 1),       # multi-query, unsplit
+    (705, 33, 136, 4, 1, 64, 1),       # multi-query
     # dO = dY @ W_o^T has few tiles here and runs split along k: 2 slices of
     # 1088, the last ending mid k-tile (2056 = 32 k-tiles + 8)
     (706, 333, 2056, 8, 8, 64, 4),
@@ -183,7 +185,7 @@ def test_attn_small_batch_matches_oracle(case):
     run_attn_group(*case)
 
 
-@pytest.mark.parametrize("N", [8, 32])
+@pytest.mark.parametrize("N", [8, 32, 128])
 def test_attn_small_batch_llama3_70b_widths(N):
     """Every rank of the 70B attention block (t = 4: 16 query heads and 2
     key/value heads of 128 per rank) at a decode batch of N tokens; all rows,
@@ -192,12 +194,15 @@ def test_attn_small_batch_llama3_70b_widths(N):
 
 
 
-@pytest.mark.parametrize("N,h,nh,nkv,d,t", [(2048, 12288, 96, 96, 128, 8), (333, 2056, 8, 8, 64, 4)])
+@pytest.mark.parametrize("N,h,nh,nkv,d,t", [(2048, 12288, 96, 96, 128, 8), (333, 2056, 8, 8, 64, 4),
+                                            (8, 8192, 64, 8, 128, 4), (100, 1032, 8, 4, 64, 2),
+                                            (1, 520, 8, 8, 64, 2)])
 def test_deferred_out_wgrad_equals_the_separate_calls(N, h, nh, nkv, d, t):
     """tp_attn_out_dgrad_shard (dO alone, k-split partials in a workspace)
     and tp_attn_qkv_bwd_out_wgrad_shard (dX, dWqkv and the deferred dWo in
     one call: one mixed launch at the GPT-3 per-rank shape, three at the
-    smaller one) give bitwise what tp_attn_out_bwd_shard and
+    333-token one; with up to 128 tokens the split-K dX and both weight
+    gradients in one launch) give bitwise what tp_attn_out_bwd_shard and
     tp_attn_qkv_bwd_shard give; those are checked against the oracle
     above."""
     say(f"[attn deferred] N={N} h={h} heads={nh} kv={nkv} d={d} t={t}")
