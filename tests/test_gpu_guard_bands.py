@@ -1,8 +1,11 @@
-"""Guard bands around the outputs of the decode, small-batch, LayerNorm,
-attention small-batch and sequence-parallel kernels: every output buffer is
-a view into a larger buffer filled with a canary value, and after two runs
-(whose outputs must be bitwise identical) the canaries must be untouched.
-Shapes have ragged tails (columns past the last full strip or chunk)."""
+"""Guard bands around the outputs of the decode, small-batch (forward and
+backward), LayerNorm, attention small-batch (forward and backward) and
+sequence-parallel kernels: every output buffer is a view into a larger
+buffer filled with a canary value, and after two runs (whose outputs must be
+bitwise identical) the canaries must be untouched.  The few-token backward
+keeps its k-split partials in the weight gradients' storage, so those are
+guarded too.  Shapes have ragged tails (columns past the last full strip or
+chunk)."""
 from __future__ import annotations
 
 import sys
@@ -94,9 +97,36 @@ def test_layernorm_guard_bands():
     twice(lambda: B.tp_sp_sum_grads_local(grads, total), gs)
 
 
-def test_attention_small_batch_guard_bands():
-    print("[guard] attention small batch", file=sys.stderr, flush=True)
-    N, h, nh, nkv, d, t = 33, 1032, 16, 4, 72, 4    # 72-wide heads: qkv columns not a multiple of 256
+@pytest.mark.parametrize("N", [1, 17, 128])
+def test_small_batch_backward_guard_bands(N):
+    print(f"[guard] backward N={N}", file=sys.stderr, flush=True)
+    h, F, t = 1032, 2 * 776, 2
+    Fi = F // t
+    s = B.make_shape(N, h, F, t, 0, "swiglu")
+    W1b, W2b, Wgb = I.gen_full_weights(603, h, F, t, True)
+    c = oracle.column_block(0, t, F)
+    W1, W2, Wg = (bf16_dev(np.ascontiguousarray(a)) for a in (W1b[:, c], W2b[c, :], Wgb[:, c]))
+    X, dY = bf16_dev(I.gen_x(603 + N, N, h)), bf16_dev(I.gen_dy(603 + N, N, h))
+    A, U, G = (bf16_dev(I.normal_bf16([603, k, N], (N, Fi))) for k in range(3))
+    g = Guards()
+    f32 = torch.float32
+    dU, dX = g.out("dU", (N, 2 * Fi)), g.out("dX", (N, h))
+    dW1, dWg, dW2 = g.out("dW1", (h, Fi), f32), g.out("dWg", (h, Fi), f32), g.out("dW2", (Fi, h), f32)
+    twice(lambda: B.tp_mlp_bwd_shard(s, X, W1, Wg, W2, dY, A, U, G, dU, dW1, dWg, dW2, dX), g)
+
+    def steps():
+        B.tp_mlp_down_bwd_shard(s, dY, W2, U, G, A, dU, dW2)
+        B.tp_mlp_up_bwd_shard(s, X, dU, W1, Wg, dX, dW1, dWg)
+    twice(steps, g)
+
+
+# 72-wide heads: qkv columns not a multiple of 256; at 8 tokens and h = 2056
+# the backward's input gradients take the split-K kernel, at 33 tokens and
+# h = 1032 the wide tiles
+@pytest.mark.parametrize("N,h", [(33, 1032), (8, 2056)])
+def test_attention_small_batch_guard_bands(N, h):
+    print(f"[guard] attention small batch N={N} h={h}", file=sys.stderr, flush=True)
+    nh, nkv, d, t = 16, 4, 72, 4
     s = B.make_attn_shape(N, h, nh, nkv, d, t, 1)
     X = bf16_dev(I.normal_bf16([602, 0], (N, h)))
     Wqkv = bf16_dev(I.normal_bf16([602, 1], (h, s.qkv_cols), 0.02))
@@ -110,6 +140,24 @@ def test_attention_small_batch_guard_bands():
         B.tp_attn_qkv_shard(s, X, Wqkv, QKV, workspace=ws)
         B.tp_attn_out_shard(s, O, Wo, Y, workspace=ws)
     twice(run, g)
+
+    # the backwards: dO's and dX's k-split partials in dW_o's and dW_qkv's storage
+    dY = bf16_dev(I.normal_bf16([602, 4], (N, h)))
+    dQKV = bf16_dev(I.normal_bf16([602, 5], (N, s.qkv_cols)))
+    f32 = torch.float32
+    dO, dX = g.out("dO", (N, s.q_cols)), g.out("dX", (N, h))
+    dWo, dWqkv = g.out("dWo", (s.q_cols, h), f32), g.out("dWqkv", (h, s.qkv_cols), f32)
+
+    def bwd():
+        B.tp_attn_out_bwd_shard(s, dY, O, Wo, dO, dWo)
+        B.tp_attn_qkv_bwd_shard(s, X, Wqkv, dQKV, dWqkv, dX)
+    twice(bwd, g)
+    wsd = B.alloc_workspace(B.attn_out_dgrad_workspace_bytes(s))
+
+    def deferred():
+        B.tp_attn_out_dgrad_shard(s, dY, Wo, dO, workspace=wsd)
+        B.tp_attn_qkv_bwd_out_wgrad_shard(s, X, Wqkv, dQKV, dY, O, dWqkv, dX, dWo)
+    twice(deferred, g)
 
 
 def test_sequence_parallel_boundary_guard_bands():

@@ -108,7 +108,8 @@ def test_mlp_shard_on_a_side_stream_and_in_a_graph(N, act):
 
 def test_layernorm_and_attention_on_a_side_stream_and_in_a_graph():
     """The fused reduce-scatter + LayerNorm, its backward (one-pass form at
-    4096 rows), and the attention projections (small-batch and wide)."""
+    4096 rows), and the attention projections with both backwards
+    (small-batch and wide)."""
     print("[graph] layernorm + attention", file=sys.stderr, flush=True)
     t, rows, cols = 2, 8192, 520
     n = rows // t
@@ -121,7 +122,8 @@ def test_layernorm_and_attention_on_a_side_stream_and_in_a_graph():
     dg, db = torch.empty(cols, dtype=F32, device="cuda"), torch.empty(cols, dtype=F32, device="cuda")
     ws_ln = B.alloc_workspace(B.layernorm_bwd_workspace_bytes(n, cols))
     h, nh, nkv, d = 512, 8, 4, 64
-    shapes = [B.make_attn_shape(Na, h, nh, nkv, d, t, 1) for Na in (16, 96)]
+    # 8 tokens: split-K forward and backward; 96: split-K forward, wide backward
+    shapes = [B.make_attn_shape(Na, h, nh, nkv, d, t, 1) for Na in (8, 96)]
     Wqkv = bf16_dev(I.normal_bf16([1251, 1], (h, shapes[0].qkv_cols), 0.02))
     Wo = bf16_dev(I.normal_bf16([1251, 2], (shapes[0].q_cols, h), 0.02))
     att = []
@@ -131,13 +133,24 @@ def test_layernorm_and_attention_on_a_side_stream_and_in_a_graph():
         Oa = bf16_dev(I.normal_bf16([1251, 4, Na], (Na, sa.q_cols)))
         att.append((sa, Xa, Oa, torch.empty(Na, sa.qkv_cols, **e), torch.empty(Na, h, **e),
                     B.alloc_workspace(B.attn_workspace_bytes(sa))))
+    # backward buffers: dY and dQKV in; dO, dW_o, dX, dW_qkv out
+    bwd = []
+    for sa in shapes:
+        Na = sa.n_tokens
+        bwd.append((bf16_dev(I.normal_bf16([1251, 5, Na], (Na, h))),
+                    bf16_dev(I.normal_bf16([1251, 6, Na], (Na, sa.qkv_cols))),
+                    torch.empty(Na, sa.q_cols, **e), torch.empty(sa.q_cols, h, dtype=F32, device="cuda"),
+                    torch.empty(Na, h, **e), torch.empty(h, sa.qkv_cols, dtype=F32, device="cuda")))
 
     def run():
         B.tp_sp_reduce_scatter_layernorm_local(parts, 1, z, gm, y, residual=res, beta=bt, mean=mean, rstd=rstd)
         B.tp_sp_layernorm_bwd(z, gm, mean, rstd, dy, dx, dg, dbeta=db, workspace=ws_ln)
-        for sa, Xa, Oa, QKV, Ya, wsa in att:
+        for (sa, Xa, Oa, QKV, Ya, wsa), (dYa, dQa, dOa, dWoa, dXa, dWa) in zip(att, bwd):
             B.tp_attn_qkv_shard(sa, Xa, Wqkv, QKV, workspace=wsa)
             B.tp_attn_out_shard(sa, Oa, Wo, Ya, workspace=wsa)
+            B.tp_attn_out_bwd_shard(sa, dYa, Oa, Wo, dOa, dWoa)
+            B.tp_attn_qkv_bwd_shard(sa, Xa, Wqkv, dQa, dWa, dXa)
 
-    outs = [z, y, mean, rstd, dx, dg, db] + [o for a in att for o in (a[3], a[4])]
+    outs = [z, y, mean, rstd, dx, dg, db] + [o for a in att for o in (a[3], a[4])] + \
+        [o for b in bwd for o in b[2:]]
     capture_and_replay(run, outs)
