@@ -183,13 +183,19 @@ def train_step(w, steps, warmup, B, I, torch, np, to_dev, clock_s=True):
     else:
         kernels = [("up_act", 2 * N * h * Fi * w.g, lambda: B.tp_mlp_up_act_shard(shape, X, W1, Wg, A, U, G)),
                    ("down", 2 * N * h * Fi, lambda: B.tp_mlp_down_shard(shape, A, W2, Y))]
-    kernels += [
-        ("reduce_y", 0, lambda: B.tp_mlp_reduce_partials_local([Y] + others_y, Yred, bias=b2)),
-        # dU and dW2, then dX_partial and dW1 (dWg): one mixed launch each when their tiles fill
-        # the GPU; with few tokens the split-K input gradient, then the weight gradient
-        ("down_bwd", 4 * N * h * Fi, lambda: B.tp_mlp_down_bwd_shard(shape, dY, W2, U, G, A, dU, dW2)),
-        ("up_bwd", 4 * N * h * Fi * w.g, lambda: B.tp_mlp_up_bwd_shard(shape, X, dU, W1, Wg, dX, dW1, dWg)),
-    ]
+    kernels += [("reduce_y", 0, lambda: B.tp_mlp_reduce_partials_local([Y] + others_y, Yred, bias=b2))]
+    if ws_f is not None:
+        # few tokens: the composite backward (split-K input gradients, then both
+        # weight gradients in one launch)
+        kernels += [("bwd", 4 * N * h * Fi * (w.g + 1),
+                     lambda: B.tp_mlp_bwd_shard(shape, X, W1, Wg, W2, dY, A, U, G, dU, dW1, dWg, dW2, dX))]
+    else:
+        # dU and dW2, then dX_partial and dW1 (dWg): one mixed launch each when their
+        # tiles fill the GPU
+        kernels += [
+            ("down_bwd", 4 * N * h * Fi, lambda: B.tp_mlp_down_bwd_shard(shape, dY, W2, U, G, A, dU, dW2)),
+            ("up_bwd", 4 * N * h * Fi * w.g, lambda: B.tp_mlp_up_bwd_shard(shape, X, dU, W1, Wg, dX, dW1, dWg)),
+        ]
     if w.bias:
         kernels.append(("bias_grad", 0, lambda: B.tp_mlp_bias_grad(dY, db2, ws_db)))
     kernels.append(("reduce_dx", 0, lambda: B.tp_mlp_reduce_partials_local([dX] + others_dx, dXred)))

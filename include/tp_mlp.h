@@ -192,7 +192,9 @@ tp_mlp_status tp_mlp_fwd_shard_noalloc(const tp_mlp_shape* s, const void* X,
  * With 1 <= N <= 128 tokens the two input gradients (dU_i, dX_partial) run
  * as split-K products whose float32 partials are kept in dW2_i and dW1_i
  * before those are written (as tp_mlp_down_bwd_shard and
- * tp_mlp_up_bwd_shard do); otherwise on the wide tiles.
+ * tp_mlp_up_bwd_shard do), and when the two weight gradients' tiles would
+ * not fill the GPU even once they then share one launch (the same bits as
+ * the step calls); otherwise on the wide tiles.
  * Inputs A_i, U_i (and G_i for SwiGLU) are the forward's outputs; U_i is
  * required.  The products need no workspace; db2 != NULL needs
  * tp_mlp_workspace_bytes(s, 1) bytes of device scratch (no initial contents

@@ -329,14 +329,29 @@ hipError_t run_pair(GemmKind kp, int act, const GemmArgs& p, const GemmArgs& q, 
 // The weight gradient (k = N) then runs on the wide tiles.
 bool small_bwd(const Dims& d) { return d.N >= 1 && d.N <= SK_MAX_N; }
 
+// dU on the split-K kernel, its partials [ks][N][F_i] in dW2 [F_i][h] (ks <= h / N)
+hipError_t run_down_dgrad_small(const Dims& d, const void* dY, const void* W2, const void* U, const void* G, void* dU,
+                                float* dW2, hipStream_t st) {
+  const SkinnyPlan p = skinny_plan((int)d.N, (int)d.h, (int)d.Fi, 1, SKINNY_TARGET_BLOCKS, (int)(d.h / d.N));
+  return skinny_dgrad_act_launch(d.act, (int)d.N, cu16(dY), cu16(W2), (int)d.h, (int)d.Fi, p, dW2, cu16(U), cu16(G),
+                                 u16(dU), st);
+}
+
+// dX on the split-K kernel, its partials [ks][g][N][h] in dW1 [h][F_i] (ks <= F_i / (g N))
+hipError_t run_up_dgrad_small(const Dims& d, const void* dU, const void* W1, const void* Wg, void* dX, float* dW1,
+                              hipStream_t st) {
+  const SkinnyPlan p =
+      skinny_plan((int)d.N, (int)d.Fi, (int)d.h, d.g, SKINNY_TARGET_BLOCKS, (int)(d.Fi / (d.g * d.N)));
+  return skinny_dgrad_up_launch(d.act, (int)d.N, cu16(dU), cu16(W1), cu16(Wg), (int)d.h, (int)d.Fi, p, dW1, u16(dX),
+                                st);
+}
+
 // The down-projection's backward: dU (dgrad through W2 with the activation
 // derivative) and dW2 = A_i^T dY.
 hipError_t run_down_bwd(const Dims& d, const void* dY, const void* W2, const void* U, const void* G, const void* A,
                         void* dU, float* dW2, hipStream_t st) {
-  if (small_bwd(d) && d.h >= d.N) {  // partials [ks][N][F_i] in dW2 [F_i][h]: ks <= h / N
-    const SkinnyPlan p = skinny_plan((int)d.N, (int)d.h, (int)d.Fi, 1, SKINNY_TARGET_BLOCKS, (int)(d.h / d.N));
-    hipError_t e = skinny_dgrad_act_launch(d.act, (int)d.N, cu16(dY), cu16(W2), (int)d.h, (int)d.Fi, p, dW2,
-                                           cu16(U), cu16(G), u16(dU), st);
+  if (small_bwd(d) && d.h >= d.N) {
+    hipError_t e = run_down_dgrad_small(d, dY, W2, U, G, dU, dW2, st);
     if (e == hipSuccess) e = gemm_launch(GEMM_WGRAD, d.act, wgrad_down_args(d, A, dY, dW2), num_cu_current(), st);
     return e;
   }
@@ -346,11 +361,8 @@ hipError_t run_down_bwd(const Dims& d, const void* dY, const void* W2, const voi
 // The up-projection's backward: dX_partial = dU W1_i^T and dW1 (dWg) = X^T dU.
 hipError_t run_up_bwd(const Dims& d, const void* X, const void* dU, const void* W1, const void* Wg, void* dX,
                       float* dW1, float* dWg, hipStream_t st) {
-  if (small_bwd(d) && d.Fi >= d.g * d.N) {  // partials [ks][g][N][h] in dW1 [h][F_i]: ks <= F_i / (g N)
-    const SkinnyPlan p =
-        skinny_plan((int)d.N, (int)d.Fi, (int)d.h, d.g, SKINNY_TARGET_BLOCKS, (int)(d.Fi / (d.g * d.N)));
-    hipError_t e = skinny_dgrad_up_launch(d.act, (int)d.N, cu16(dU), cu16(W1), cu16(Wg), (int)d.h, (int)d.Fi, p,
-                                          dW1, u16(dX), st);
+  if (small_bwd(d) && d.Fi >= d.g * d.N) {
+    hipError_t e = run_up_dgrad_small(d, dU, W1, Wg, dX, dW1, st);
     if (e == hipSuccess) e = gemm_launch(GEMM_WGRAD, d.act, wgrad_up_args(d, X, dU, dW1, dWg), num_cu_current(), st);
     return e;
   }
@@ -969,8 +981,19 @@ tp_mlp_status tp_mlp_bwd_shard(const tp_mlp_shape* s, const void* X, const void*
     if (e == hipSuccess) e = zero_f32_launch(db2, d.h, num_cu_current(), stream);
     return hip_status(e);
   }
-  hipError_t e = run_down_bwd(d, dY, W2_i, U_i, G_i, A_i, dU_i, dW2_i, stream);
-  if (e == hipSuccess) e = run_up_bwd(d, X, dU_i, W1_i, Wg_i, dX_partial, dW1_i, dWg_i, stream);
+  hipError_t e;
+  const GemmArgs wd = wgrad_down_args(d, A_i, dY, dW2_i), wu = wgrad_up_args(d, X, dU_i, dW1_i, dWg_i);
+  if (small_bwd(d) && d.h >= d.N && d.Fi >= d.g * d.N && tiles256(wd) + tiles256(wu) <= num_cu_current()) {
+    // few tokens and small weights: both input gradients on the split-K kernel
+    // (partials in dW2_i, then dW1_i, as in the step calls), then both weight
+    // gradients in one launch, which alone would each leave most CUs idle
+    e = run_down_dgrad_small(d, dY, W2_i, U_i, G_i, dU_i, dW2_i, stream);
+    if (e == hipSuccess) e = run_up_dgrad_small(d, dU_i, W1_i, Wg_i, dX_partial, dW1_i, stream);
+    if (e == hipSuccess) e = gemm_launch2(GEMM_WGRAD, d.act, wd, wu, num_cu_current(), stream);
+  } else {
+    e = run_down_bwd(d, dY, W2_i, U_i, G_i, A_i, dU_i, dW2_i, stream);
+    if (e == hipSuccess) e = run_up_bwd(d, X, dU_i, W1_i, Wg_i, dX_partial, dW1_i, dWg_i, stream);
+  }
   if (e == hipSuccess && db2 != nullptr)
     e = col_sum_launch(cu16(dY), d.N, d.h, db2, static_cast<float*>(workspace), stream);
   return hip_status(e);
