@@ -72,8 +72,8 @@ def test_group_matches_oracle(case):
 
 @pytest.mark.parametrize("act", ["gelu", "swiglu", "relu"])
 def test_decode_one_token(act):
-    """N = 1 routes the forward to the split-K GEMV path (the backward stays
-    on the MFMA path)."""
+    """N = 1 routes the forward to the split-K GEMV path and the backward's
+    input gradients to the small-batch split-K MFMA kernel."""
     run_group(200 + len(act), 1, 1024, 3 * 1024, 2, act, False)
 
 
