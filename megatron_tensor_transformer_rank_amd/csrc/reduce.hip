@@ -235,7 +235,15 @@ col_sum_pass2(const float* __restrict__ part, int slabs, int64_t cols, float* __
   const int64_t c = (int64_t)blockIdx.x * RD_THREADS + threadIdx.x;
   if (c >= cols) return;
   float s = 0.f;
-  for (int q = 0; q < slabs; ++q) s += part[(int64_t)q * cols + c];
+  // eight slabs' loads in flight at a time, added in slab order
+  for (int q0 = 0; q0 < slabs; q0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = q0 + u < slabs ? part[(int64_t)(q0 + u) * cols + c] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u < slabs) s += v[u];
+  }
   db[c] = s;
 }
 

@@ -37,6 +37,7 @@ namespace tpmlp {
 constexpr int SK_THREADS = 256;
 constexpr int SK_COLS = 256;  // columns per block
 constexpr int SK_BK = 64;
+constexpr int SK_QB = 8;  // k-split partials loaded together by the activation kernels
 
 template <int MB, int NMAT, bool NT>
 __global__ void __launch_bounds__(SK_THREADS)
@@ -206,12 +207,23 @@ skinny_act(const float* __restrict__ part, int ks, int64_t n, uint16_t* __restri
     float4 sum[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) sum[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int q = 0; q < ks; ++q)
+    // SK_QB splits' loads in flight at a time, then added in split order
+    for (int q0 = 0; q0 < ks; q0 += SK_QB) {
+      float4 v[SK_QB][NMAT];
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)q * NMAT + m) * n + e);
-        sum[m].x += v.x; sum[m].y += v.y; sum[m].z += v.z; sum[m].w += v.w;
-      }
+      for (int u = 0; u < SK_QB; ++u)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+          v[u][m] = q0 + u < ks ? *reinterpret_cast<const float4*>(part + ((int64_t)(q0 + u) * NMAT + m) * n + e)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < SK_QB; ++u)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+          if (q0 + u < ks) {
+            sum[m].x += v[u][m].x; sum[m].y += v[u][m].y; sum[m].z += v[u][m].z; sum[m].w += v[u][m].w;
+          }
+    }
     float a[4];
     const float g[4] = {sum[0].x, sum[0].y, sum[0].z, sum[0].w};
     const float u[4] = {sum[NMAT - 1].x, sum[NMAT - 1].y, sum[NMAT - 1].z, sum[NMAT - 1].w};
@@ -233,16 +245,26 @@ __global__ void __launch_bounds__(256)
 skinny_act_bwd(const float* __restrict__ part, int ks, int64_t n, int Fi, const uint16_t* __restrict__ U,
                const uint16_t* __restrict__ G, uint16_t* __restrict__ dU) {
   for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < n; e += (int64_t)gridDim.x * 256 * 4) {
+    // the stashes' loads first, then SK_QB splits' loads in flight at a time,
+    // added in split order
+    const uint2 ub = *reinterpret_cast<const uint2*>(U + e);
+    const uint2 gb = ACT == ACT_SWIGLU ? *reinterpret_cast<const uint2*>(G + e) : make_uint2(0u, 0u);
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int q = 0; q < ks; ++q) {
-      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)q * n + e);
-      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    for (int q0 = 0; q0 < ks; q0 += SK_QB) {
+      float4 v[SK_QB];
+#pragma unroll
+      for (int u = 0; u < SK_QB; ++u)
+        v[u] = q0 + u < ks ? *reinterpret_cast<const float4*>(part + (int64_t)(q0 + u) * n + e)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < SK_QB; ++u)
+        if (q0 + u < ks) {
+          sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w;
+        }
     }
     const float da[4] = {sum.x, sum.y, sum.z, sum.w};
-    const uint2 ub = *reinterpret_cast<const uint2*>(U + e);
     const float uu[4] = {bf16lo(ub.x), bf16hi(ub.x), bf16lo(ub.y), bf16hi(ub.y)};
     if constexpr (ACT == ACT_SWIGLU) {
-      const uint2 gb = *reinterpret_cast<const uint2*>(G + e);
       const float gg[4] = {bf16lo(gb.x), bf16hi(gb.x), bf16lo(gb.y), bf16hi(gb.y)};
       float dg[4], dp[4];
 #pragma unroll
