@@ -187,9 +187,10 @@ hipError_t gather_launch(const PartialPtrs& shards, int t, int64_t shard_rows, i
 
 // db2[c] = sum_r dY[r][c], deterministic in two passes.  Pass 1: block
 // (column strip of 512, row slab) -- each lane owns 8 columns (16-byte loads,
-// a wave covers 1 KiB of a row), the 4 waves take interleaved rows, their sums
-// meet in LDS in fixed order and the slab's float32 partial row goes to the
-// workspace.  Pass 2: one thread per column adds the slab partials in order.
+// a wave covers 1 KiB of a row, eight of its rows in flight), the 4 waves
+// take interleaved rows, their sums meet in LDS in fixed order and the
+// slab's float32 partial row goes to the workspace.  Pass 2: one thread per
+// column adds the slab partials in order.
 constexpr int CS_STRIP = 512;
 
 int col_sum_slabs(int64_t rows) {
@@ -211,12 +212,22 @@ col_sum_pass1(const uint16_t* __restrict__ dY, int64_t rows, int64_t cols, int s
   const int64_t c = (int64_t)strip * CS_STRIP + lane * 8;
   float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (c < cols) {
-    for (int64_t r = r0 + w; r < r1; r += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(dY + r * cols + c);
-      a[0] += bf16lo(v.x); a[1] += bf16hi(v.x);
-      a[2] += bf16lo(v.y); a[3] += bf16hi(v.y);
-      a[4] += bf16lo(v.z); a[5] += bf16hi(v.z);
-      a[6] += bf16lo(v.w); a[7] += bf16hi(v.w);
+    // eight of the wave's rows loaded together, then added in row order
+    for (int64_t rb = r0 + w; rb < r1; rb += 4 * 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t r = rb + 4 * u;
+        v[u] = r < r1 ? *reinterpret_cast<const uint4*>(dY + r * cols + c) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (rb + 4 * u < r1) {
+          a[0] += bf16lo(v[u].x); a[1] += bf16hi(v[u].x);
+          a[2] += bf16lo(v[u].y); a[3] += bf16hi(v[u].y);
+          a[4] += bf16lo(v[u].z); a[5] += bf16hi(v[u].z);
+          a[6] += bf16lo(v[u].w); a[7] += bf16hi(v[u].w);
+        }
     }
   }
 #pragma unroll
