@@ -491,8 +491,43 @@ def bench_decode(args, w, B, I, torch, np, to_dev):
         small[str(nb)] = {"us_per_step": round(usb, 3), "GB/s_of_weights": round(wbytes / (usb * 1e-6) / 1e9, 1),
                           "tokens_per_s": round(nb / (usb * 1e-6), 1)}
         log(f"[bench] small-batch decode N={nb}: {usb:.2f} us ({wbytes / (usb * 1e-6) / 1e9:.0f} GB/s of weights)")
+    # few-token backward (the split-K input gradients, then the weight gradients), same rotated
+    # weights: bytes = the weights read once + the float32 weight gradients written once
+    small_bwd = {}
+    f32 = torch.float32
+    dW1, dW2 = torch.empty(h, Fi, dtype=f32, device="cuda"), torch.empty(Fi, h, dtype=f32, device="cuda")
+    dWg = torch.empty(h, Fi, dtype=f32, device="cuda") if sw else None
+    bwd_bytes = wbytes * 3
+    for nb in (8, 128):
+        sb = B.make_shape(nb, h, w.F, w.t, 0, w.act)
+        xb = to_dev(I.normal_bf16([w.wid, 40, nb], (nb, h)))
+        dyb = to_dev(I.normal_bf16([w.wid, 43, nb], (nb, h)))
+        Ab, Ub = (to_dev(I.normal_bf16([w.wid, 44 + k, nb], (nb, Fi))) for k in range(2))
+        Gb = to_dev(I.normal_bf16([w.wid, 46, nb], (nb, Fi))) if sw else None
+        dUb = torch.empty(nb, w.g * Fi, dtype=bf, device="cuda")
+        dXb = torch.empty(nb, h, dtype=bf, device="cuda")
+
+        def bwd(i):
+            a, g, b = sets[i % nsets]
+            B.tp_mlp_bwd_shard(sb, xb, a, g, b, dyb, Ab, Ub, Gb, dUb, dW1, dWg, dW2, dXb)
+        for i in range(6):
+            bwd(i)
+        torch.cuda.synchronize()
+        nbw = max(10, n // 4)
+        e0.record(stream)
+        for i in range(nbw):
+            bwd(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        usb = e0.elapsed_time(e1) * 1e3 / nbw
+        small_bwd[str(nb)] = {"us_per_step": round(usb, 3), "GB/s": round(bwd_bytes / (usb * 1e-6) / 1e9, 1)}
+        log(f"[bench] small-batch backward N={nb}: {usb:.2f} us ({bwd_bytes / (usb * 1e-6) / 1e9:.0f} GB/s of "
+            f"weights read and float32 gradients written)")
+    del dW1, dW2, dWg
     return {"workload": w.name, "value": round(gbs, 1), "unit": "GB/s", "us_per_token": round(us, 3),
             "small_batch": small,
+            "small_batch_backward": small_bwd,
+            "small_batch_backward_bytes": bwd_bytes,
             "us_per_token_windows": [round(v, 3) for v in windows], "calls_per_window": n,
             "bytes_per_token": wbytes, "weight_sets_rotated": nsets,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
