@@ -1,5 +1,6 @@
-// Small-batch path (2 <= N <= 128 tokens): split-K MFMA GEMMs for
-// gfx950 that stream each weight once.
+// Small-batch path (up to 128 tokens): split-K MFMA GEMMs for gfx950 that
+// stream each weight once -- the forward for 2 <= N <= 128 and the
+// backward's input gradients for 1 <= N <= 128.
 //
 // With a handful of tokens every weight byte is still used by only N
 // multiply-adds, so the forward is bound by reading the shards from HBM, as
@@ -20,12 +21,21 @@
 //   4. k-split sum:           Y = bf16(sum of the partials), the one-token
 //                             path's final reduction
 //
+// The backward's input gradients read their weights k-contiguous as stored
+// (NT: W2 [F_i, h] and W1, Wg [h, F_i] are [output column][k]), with the
+// partials in the weight gradient's storage (the caller writes it later):
+//   dU: skinny_partial<.., 1, NT> (dY @ W2^T), then skinny_act_bwd (the sum,
+//       then dU = dA * act'(U), SwiGLU's [dG | dP] from G and U);
+//   dX: skinny_partial<.., g, NT> (dU @ W1^T; SwiGLU's dG @ Wg^T and
+//       dP @ W1^T as matrices 0 and 1), then the k-split sum over both.
+//
 // skinny_partial: 256 threads = 4 waves; the block's tile is MB token rows
 // (N padded to 16, 32, 64 or 128) x 256 columns, each wave owning 64
 // columns.  Four LDS stages (three at 128 rows), each [64 k][256] of the
-// weight (n-contiguous, read with the LDS transpose read) and [MB][64 k] of
-// the activations; the DMA of tile t+3 (t+2) is issued as tile t's fragments
-// are read, so about 100 KiB per CU stay in flight.  One barrier per 64-deep
+// weight (n-contiguous, read with the LDS transpose read; with NT [256][64 k],
+// k-contiguous like the activations and read with ds_read_b128) and
+// [MB][64 k] of the activations; the DMA of tile t+3 (t+2) is issued as tile
+// t's fragments are read, so about 100 KiB per CU stay in flight.  One barrier per 64-deep
 // k-tile.  The MFMA work per byte is small (2*MB flops per weight element).
 #include "common.h"
 #include "gemv.h"
