@@ -379,15 +379,17 @@ ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const 
 
 // dgamma / dbeta partial rows of one (column strip, row slab) tile: a lane
 // owns 8 adjacent columns (16-byte loads, a wave covers 512 columns), the 4
-// waves take interleaved rows of the slab, LN_DG_UNROLL rows of loads in
-// flight, and their sums meet in LDS in wave order.
+// waves take interleaved rows of the slab, UNROLL rows of loads in flight
+// (four; two in the 1024-thread few-row kernel, whose registers are held to
+// 64 so that two blocks share a CU), and their sums meet in LDS in wave
+// order.  The rows are added in the same order either way.
 constexpr int LN_DG_STRIP = 512;
-constexpr int LN_DG_UNROLL = 4;
 
 // The tile's code for one group of LN_THREADS threads (gtid = the thread's
 // index in its group; red = the group's [LN_WAVES][LN_DG_STRIP] floats of
 // LDS).  Every thread of the block reaches the same barriers: a group whose
 // tile is past the last one (live = false) loads and stores nothing.
+template <int UNROLL>
 __device__ __forceinline__ void ln_dgb_tile(int tile, bool live, int gtid, const uint16_t* __restrict__ x,
                                             const float* __restrict__ mean, const float* __restrict__ rstd,
                                             const uint16_t* __restrict__ dy, int64_t rows, int64_t cols, int64_t rpb,
@@ -401,17 +403,17 @@ __device__ __forceinline__ void ln_dgb_tile(int tile, bool live, int gtid, const
   const int64_t c = (int64_t)strip * LN_DG_STRIP + lane * 8;
   const bool cok = live && c < cols;
   float ag[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, ab[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t rb = r0 + w; rb < r1; rb += LN_WAVES * LN_DG_UNROLL) {
-    u32x4 xv[LN_DG_UNROLL], dv[LN_DG_UNROLL];
+  for (int64_t rb = r0 + w; rb < r1; rb += LN_WAVES * UNROLL) {
+    u32x4 xv[UNROLL], dv[UNROLL];
 #pragma unroll
-    for (int u = 0; u < LN_DG_UNROLL; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int64_t r = rb + (int64_t)u * LN_WAVES;
       const bool ok = cok && r < r1;
       xv[u] = ok ? ld_nt(x + r * cols + c, 0) : u32x4{0u, 0u, 0u, 0u};
       dv[u] = ok ? ld_nt(dy + r * cols + c, 0) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < LN_DG_UNROLL; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int64_t r = rb + (int64_t)u * LN_WAVES;
       if (cok && r < r1) {
         const float mu = mean[r], rs = rstd[r];
@@ -451,7 +453,7 @@ ln_bwd_dgb_kernel(const uint16_t* __restrict__ x, const float* __restrict__ mean
                   const uint16_t* __restrict__ dy, int64_t rows, int64_t cols, int64_t rpb,
                   float* __restrict__ part_g, float* __restrict__ part_b) {
   __shared__ float red[LN_WAVES][LN_DG_STRIP];
-  ln_dgb_tile(blockIdx.x, true, threadIdx.x, x, mean, rstd, dy, rows, cols, rpb, part_g, part_b, red);
+  ln_dgb_tile<4>(blockIdx.x, true, threadIdx.x, x, mean, rstd, dy, rows, cols, rpb, part_g, part_b, red);
 }
 
 // The two independent halves of the few-row backward in one launch, when dx
@@ -460,7 +462,7 @@ ln_bwd_dgb_kernel(const uint16_t* __restrict__ x, const float* __restrict__ mean
 // arithmetic of ln_bwd_dgb_kernel), blocks [ndg, ndg + rows) one dx row each
 // (ln_bwd_dx_kernel's arithmetic).  Same bits as the two kernels.
 template <int NT, int J>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT, NT == 1024 ? 8 : 1)
 ln_bwd_few_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
                   const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx, int cols8,
                   int64_t rows, int64_t cols, int64_t rpb, int ntiles, int ndg, float* __restrict__ part_g,
@@ -471,8 +473,8 @@ ln_bwd_few_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const f
   if ((int)blockIdx.x < ndg) {
     const int grp = threadIdx.x / LN_THREADS;
     const int tile = (int)blockIdx.x * GROUPS + grp;
-    ln_dgb_tile(tile, tile < ntiles, threadIdx.x % LN_THREADS, x, mean, rstd, dy, rows, cols, rpb, part_g, part_b,
-                red_g[grp]);
+    ln_dgb_tile<NT == 1024 ? 2 : 4>(tile, tile < ntiles, threadIdx.x % LN_THREADS, x, mean, rstd, dy, rows, cols,
+                                     rpb, part_g, part_b, red_g[grp]);
   } else {
     ln_dx_row<NT, J>((int64_t)blockIdx.x - ndg, x, gamma, mean, rstd, dy, dres, dx, cols8, (int)cols, red_x);
   }
