@@ -585,6 +585,36 @@ def bench_attn(args, B, I, torch, np, to_dev, N=2048, h=12288, heads=96, kv=96, 
                     "gradient deferred into the QKV backward's launch)"}
 
 
+def graph_time(torch, calls, windows=5):
+    """Microseconds per call of `calls` (closures enqueuing library calls on
+    the current stream), captured into one HIP graph on a side stream and
+    replayed: the GPU time of launch-bound sequences without the host's
+    per-call launch overhead (what a caller that captures its loop sees).
+    The median over `windows` replays, after one untimed replay."""
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for c in calls[:3]:
+            c()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(windows + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+        s.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / len(calls))
+    del g
+    return float(sorted(ts[1:])[len(ts[1:]) // 2])
+
+
 def bench_attn_small(B, I, torch, to_dev, h=8192, heads=64, kv=8, d=128, t=4):
     """The forward attention projections (QKV and output) of one rank of the
     70B block at decode batches of 8 and 32 tokens: the small-batch path,
@@ -619,12 +649,17 @@ def bench_attn_small(B, I, torch, to_dev, h=8192, heads=64, kv=8, d=128, t=4):
             step(i)
         e1.record(torch.cuda.current_stream())
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / n
+        us_eager = e0.elapsed_time(e1) * 1e3 / n
+        us = graph_time(torch, [lambda i=i: step(i) for i in range(n)])
         out[str(N)] = {"us_per_step": round(us, 2), "GB/s_of_weights": round(wbytes / (us * 1e-6) / 1e9, 1),
-                       "frac_of_hbm_peak": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-        log(f"[bench] attention projections 70b t=4, N={N}: {us:.1f} us ({wbytes / (us * 1e-6) / 1e9:.0f} GB/s of weights)")
+                       "frac_of_hbm_peak": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                       "us_per_step_eager": round(us_eager, 2)}
+        log(f"[bench] attention projections 70b t=4, N={N}: {us:.1f} us ({wbytes / (us * 1e-6) / 1e9:.0f} GB/s of "
+            f"weights; {us_eager:.1f} us launched one call at a time)")
     out["weight_bytes"] = wbytes
-    out["step"] = "QKV projection + output projection forward (small-batch path), weights rotated over 5 copies"
+    out["step"] = ("QKV projection + output projection forward (small-batch path), weights rotated over 5 copies; "
+                   "us_per_step from 100 steps captured into a HIP graph and replayed, us_per_step_eager with "
+                   "each call launched from the host")
     return out
 
 
@@ -633,7 +668,9 @@ def bench_ln(B, I, torch, to_dev, name, N, h, t):
     bias + residual + LayerNorm forward over its N/t rows (reading its block
     of all t partial sums), and the LayerNorm backward with the residual
     branch's gradient, dgamma and dbeta.  GB/s on algorithmic bytes (every
-    operand read once, every output written once)."""
+    operand read once, every output written once); the calls are timed as 20
+    captured into a HIP graph and replayed (`us`), and launched one at a time
+    from the host (`us_eager`)."""
     bf, f32 = torch.bfloat16, torch.float32
     n = N // t
     parts = [to_dev(I.normal_bf16([990, 1, k], (N, h))) for k in range(t)]
@@ -666,12 +703,14 @@ def bench_ln(B, I, torch, to_dev, name, N, h, t):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        us_eager = e0.elapsed_time(e1) * 1e3 / reps
+        us = graph_time(torch, [fn] * reps)
         gbs = nbytes[key] / (us * 1e-6) / 1e9
         out[key] = {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                    "algorithmic_bytes": nbytes[key]}
+                    "algorithmic_bytes": nbytes[key], "us_eager": round(us_eager, 2)}
     log(f"[bench] sp layernorm {name}: fused rs+ln fwd {out['fwd']['us']:.1f} us ({out['fwd']['GB/s']:.0f} GB/s), "
-        f"bwd {out['bwd']['us']:.1f} us ({out['bwd']['GB/s']:.0f} GB/s)")
+        f"bwd {out['bwd']['us']:.1f} us ({out['bwd']['GB/s']:.0f} GB/s); launched one call at a time "
+        f"{out['fwd']['us_eager']:.1f} / {out['bwd']['us_eager']:.1f} us")
     out["workload"] = f"{name}: {N} tokens, h={h}, t={t}: {n} rows per rank"
     out["fwd"]["step"] = "reduce-scatter of t partials + bias + residual -> z, LayerNorm(z) -> y (one kernel)"
     out["bwd"]["step"] = "LayerNorm backward + residual gradient -> dx; dgamma, dbeta (row kernel + slab sums)"

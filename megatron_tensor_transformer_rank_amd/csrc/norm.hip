@@ -380,9 +380,9 @@ ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const 
 // dgamma / dbeta partial rows of one (column strip, row slab) tile: a lane
 // owns 8 adjacent columns (16-byte loads, a wave covers 512 columns), the 4
 // waves take interleaved rows of the slab, UNROLL rows of loads in flight
-// (four; two in the 1024-thread few-row kernel, whose registers are held to
-// 64 so that two blocks share a CU), and their sums meet in LDS in wave
-// order.  The rows are added in the same order either way.
+// (four; one in the 1024-thread few-row kernel, whose registers are held to
+// 64 without spilling so that two blocks share a CU), and their sums meet in
+// LDS in wave order.  The rows are added in the same order either way.
 constexpr int LN_DG_STRIP = 512;
 
 // The tile's code for one group of LN_THREADS threads (gtid = the thread's
@@ -473,7 +473,7 @@ ln_bwd_few_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const f
   if ((int)blockIdx.x < ndg) {
     const int grp = threadIdx.x / LN_THREADS;
     const int tile = (int)blockIdx.x * GROUPS + grp;
-    ln_dgb_tile<NT == 1024 ? 2 : 4>(tile, tile < ntiles, threadIdx.x % LN_THREADS, x, mean, rstd, dy, rows, cols,
+    ln_dgb_tile<NT == 1024 ? 1 : 4>(tile, tile < ntiles, threadIdx.x % LN_THREADS, x, mean, rstd, dy, rows, cols,
                                      rpb, part_g, part_b, red_g[grp]);
   } else {
     ln_dx_row<NT, J>((int64_t)blockIdx.x - ndg, x, gamma, mean, rstd, dy, dres, dx, cols8, (int)cols, red_x);
