@@ -1,9 +1,11 @@
-"""A seeded sweep of shapes through whole tensor-parallel groups on the GPU,
+"""Seeded sweeps of shapes through whole tensor-parallel groups on the GPU,
 against the fp64 oracle: N from 1 to 600 tokens (the one-token decode, the
 small-batch path and the wide tiles), h and F_i any multiples of 8 (ragged
 tiles, k tails and column strips), t from 1 to 4, all three activations, with
-and without the output bias.  The cases are fixed by the seed below, so every
-run checks the same ones."""
+and without the output bias; and a second sweep at 1 to 129 tokens, where
+the backward's input gradients take the split-K kernel (or keep the wide
+tiles when the weight gradient cannot hold one split: h < N, F_i < g N).
+The cases are fixed by the seeds below, so every run checks the same ones."""
 from __future__ import annotations
 
 import numpy as np
@@ -14,28 +16,30 @@ from tests.helpers import run_group
 pytestmark = pytest.mark.gpu
 
 
-def _cases(seed=20261202, n=24):
+def _cases(seed=20261202, n=24, wid0=1100, few=False):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        # token counts from each regime: 1, small batches, just past 64, larger
-        N = int(rng.choice([1, int(rng.integers(2, 65)), int(rng.integers(65, 200)), int(rng.integers(200, 601))]))
+        if few:
+            N = int(rng.integers(1, 130))
+        else:
+            # token counts from each regime: 1, small batches, 65-199, larger
+            N = int(rng.choice([1, int(rng.integers(2, 65)), int(rng.integers(65, 200)),
+                                int(rng.integers(200, 601))]))
         h = 8 * int(rng.integers(1, 161))
         t = int(rng.integers(1, 5))
         Fi = 8 * int(rng.integers(1, 201))
         act = ["relu", "gelu", "swiglu"][int(rng.integers(0, 3))]
         bias = bool(rng.integers(0, 2))
-        out.append((1100 + i, N, h, Fi * t, t, act, bias))
+        out.append((wid0 + i, N, h, Fi * t, t, act, bias))
     return out
 
 
-CASES = _cases()
+CASES = _cases() + _cases(seed=20261203, n=16, wid0=1140, few=True)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"N{c[1]}_h{c[2]}_F{c[3]}_t{c[4]}_{c[5]}{'_b' if c[6] else ''}"
                                              for c in CASES])
 def test_random_shape_group_matches_oracle(case):
     wid, N, h, F, t, act, bias = case
-    # one-token calls go through the decode path; the backward runs on the
-    # GEMMs for every N
     run_group(wid, N, h, F, t, act, bias)
