@@ -180,6 +180,27 @@ SMALL = [
 ]
 
 
+def _small_sweep(seed=20261204, n=8):
+    """Seeded few-token head layouts, h large enough (1032-4104) that the
+    backward's input gradients take the split-K kernel at most of them."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        t = int(rng.choice([1, 2, 4]))
+        nkv = int(rng.choice([1, 2, 4, 8]))
+        nh = nkv * int(rng.choice([1, 2, 4]))
+        if nh % t or (nkv % t and t % nkv):
+            continue
+        d = 8 * int(rng.integers(4, 17))
+        h = 8 * int(rng.integers(129, 514))
+        N = int(rng.integers(1, 65))
+        out.append((740 + len(out), N, h, nh, nkv, d, t))
+    return out
+
+
+SMALL += _small_sweep()
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[f"N{c[1]}_h{c[2]}_H{c[3]}_kv{c[4]}_t{c[6]}" for c in SMALL])
 def test_attn_small_batch_matches_oracle(case):
     run_attn_group(*case)
