@@ -29,9 +29,9 @@
 //   dX: skinny_partial<.., g, NT> (dU @ W1^T; SwiGLU's dG @ Wg^T and
 //       dP @ W1^T as matrices 0 and 1), then the k-split sum over both.
 //
-// skinny_partial: 256 threads = 4 waves; the block's tile is MB token rows
-// (N padded to 16, 32, 64 or 128) x 256 columns, each wave owning 64
-// columns.  Four LDS stages (three at 128 rows), each [64 k][256] of the
+// skinny_partial: 4 waves (8 at 128 rows: two groups of 4, each owning 64 of
+// the rows); the block's tile is MB token rows (N padded to 16, 32, 64 or
+// 128) x 256 columns, each wave owning 64 columns.  Four LDS stages (three at 128 rows), each [64 k][256] of the
 // weight (n-contiguous, read with the LDS transpose read; with NT [256][64 k],
 // k-contiguous like the activations and read with ds_read_b128) and
 // [MB][64 k] of the activations; the DMA of tile t+3 (t+2) is issued as tile
@@ -44,18 +44,24 @@
 
 namespace tpmlp {
 
-constexpr int SK_THREADS = 256;
 constexpr int SK_COLS = 256;  // columns per block
 constexpr int SK_BK = 64;
 constexpr int SK_QB = 8;  // k-split partials loaded together by the activation kernels
 
+// Waves per block: 4, or 8 for 128 token rows (two groups of four, each
+// owning 64 of the rows), so that each SIMD runs two waves and one's LDS
+// reads and waits overlap the other's MFMAs.
+template <int MB>
+constexpr int sk_waves() { return MB == 128 ? 8 : 4; }
+
 template <int MB, int NMAT, bool NT>
-__global__ void __launch_bounds__(SK_THREADS)
+__global__ void __launch_bounds__(64 * sk_waves<MB>())
 skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_bytes, int64_t x1_off,
                const uint16_t* W0, const uint16_t* W1, uint32_t w_bytes, int K, int ncols, int strips,
                int kt_per_split, float* __restrict__ part) {
-  constexpr int TM = MB / 16;                // 16-row blocks (all waves)
-  constexpr int TN = 4;                      // 16-column blocks per wave
+  constexpr int GROUPS = sk_waves<MB>() / 4;  // wave groups, each owning MB / GROUPS rows
+  constexpr int TM = MB / 16 / GROUPS;        // 16-row blocks per wave
+  constexpr int TN = 4;                       // 16-column blocks per wave
   constexpr int W_BYTES = SK_COLS * 128;     // [64 k][256 cols]
   constexpr int NIX = MB / 32 > 0 ? MB / 32 : 1;  // activation DMA instructions per wave
   constexpr int X_BYTES = NIX * 4 * 1024;   // [MB rows][64 k], rounded up to whole instructions
@@ -63,12 +69,15 @@ skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_by
   // four LDS stages (three tiles in flight); three (two in flight) for 128
   // token rows, whose activation tile doubles the stage
   constexpr int SK_STAGES = MB == 128 ? 3 : 4;
-  constexpr int NIW = SK_COLS / 32;          // weight DMA instructions per wave
-  constexpr int NI = NIW + NIX;
+  constexpr int NIW = SK_COLS / 32;          // weight DMA instructions per wave of a group
+  constexpr int NI = (NIW + NIX) / GROUPS;   // DMA instructions a wave issues per tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SK_STAGES * STAGE];
 
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // wave w of group grp: columns 64 w .. of the tile, rows grp * MB / GROUPS ..;
+  // the group's DMA share is every GROUPS-th block of the four-wave pattern
+  const int wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = wg & 3, grp = wg >> 2;
   const int b = blockIdx.x;
   const int s = b % strips, rest = b / strips;
   const int mat = rest % NMAT, q = rest / NMAT;
@@ -116,18 +125,24 @@ skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_by
     const int kvalid = live ? K - k0 : 0;
     const rsrc_t rw = shifted(Wm, live ? w_bytes : 0u, (uint32_t)k0 * wk_step);
     static_for<NIW>([&](auto J) __attribute__((always_inline)) {
-      if constexpr (NT)
-        dwk.template issue<decltype(J)::value>(rw, st, kvalid, w);
-      else
-        dw.template issue<decltype(J)::value>(rw, st, w);
+      constexpr int jj = decltype(J)::value;
+      if (GROUPS == 1 || jj / (NIW / GROUPS) == grp) {
+        if constexpr (NT)
+          dwk.template issue<jj>(rw, st, kvalid, w);
+        else
+          dw.template issue<jj>(rw, st, w);
+      }
     });
     const rsrc_t rx = shifted(X, live ? x_bytes : 0u, (uint32_t)k0 * 2u);
 #pragma unroll
-    for (int j = 0; j < NIX; ++j) dma16(rx, st + W_BYTES + (w + 4 * j) * 1024, kc < kvalid ? xoff[j] : OOB);
+    for (int j = 0; j < NIX; ++j)
+      if (GROUPS == 1 || j / (NIX / GROUPS) == grp)
+        dma16(rx, st + W_BYTES + (w + 4 * j) * 1024, kc < kvalid ? xoff[j] : OOB);
   };
 
   // fragment addressing within a stage
-  const uint32_t a_off0 = W_BYTES + kfrag_off(0, 0, lane), a_off1 = W_BYTES + kfrag_off(0, 1, lane);
+  const uint32_t a_row0 = W_BYTES + (uint32_t)grp * TM * 2048;  // the group's first row block
+  const uint32_t a_off0 = a_row0 + kfrag_off(0, 0, lane), a_off1 = a_row0 + kfrag_off(0, 1, lane);
   uint32_t b_col[TN];
   if constexpr (NT) {
     b_col[0] = kfrag_off(w * 64, 0, lane);
@@ -188,12 +203,12 @@ skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_by
   asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // last MFMA results written before they are read
   wait_vmcnt<0>();  // no DMA may land after the block has left
 
-  // lane holds rows n = 16i + l16, columns col0 + 64w + 16j + 4lq .. +3
+  // lane holds rows n = grp * 16 TM + 16i + l16, columns col0 + 64w + 16j + 4lq .. +3
   const int l16 = lane & 15, lq = lane >> 4;
   float* dst = part + (int64_t)(q * NMAT + mat) * N * ncols;
 #pragma unroll
   for (int ii = 0; ii < TM; ++ii) {
-    const int n = ii * 16 + l16;
+    const int n = (grp * TM + ii) * 16 + l16;
     if (n >= N) continue;
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) {
@@ -319,8 +334,8 @@ template <int NMAT, bool NT, int MB>
 void partial_one(const SkinnyPlan& p, dim3 grid, int N, const uint16_t* X, int64_t ldx, uint32_t x_bytes,
                  int64_t x1_off, const uint16_t* W0, const uint16_t* W1, uint32_t w_bytes, int K, int ncols,
                  float* part, hipStream_t st) {
-  hipLaunchKernelGGL((skinny_partial<MB, NMAT, NT>), grid, dim3(SK_THREADS), 0, st, X, N, ldx, x_bytes, x1_off, W0,
-                     W1, w_bytes, K, ncols, p.strips, p.kt, part);
+  hipLaunchKernelGGL((skinny_partial<MB, NMAT, NT>), grid, dim3(64 * sk_waves<MB>()), 0, st, X, N, ldx, x_bytes,
+                     x1_off, W0, W1, w_bytes, K, ncols, p.strips, p.kt, part);
 }
 
 template <int NMAT, bool NT>
