@@ -550,6 +550,14 @@ def test_attn_deferred_wgrad_entry_points_validate():
     assert od(r, P(0), None, P(2), P(3), need, None) == INVALID
     small = B.make_attn_shape(4096, 512, 8, 8, 64, 1, 0)               # a full grid: no split, no workspace
     assert B.attn_out_dgrad_workspace_bytes(small) == 0
+    # few tokens at the 70B widths: the split-K kernel's partials (as many
+    # splits as dW_o would hold, h / N, and at least one)
+    for N in (1, 8, 32):
+        few = B.make_attn_shape(N, 8192, 64, 8, 128, 4, 0)
+        need_few = B.attn_out_dgrad_workspace_bytes(few)
+        assert need_few % 256 == 0 and N * few.q_cols * 4 <= need_few <= (8192 // N) * N * few.q_cols * 4 + 255
+        fr = ctypes.byref(few)
+        assert od(fr, P(0), P(1), P(2), P(3), need_few - 256, None) == WORKSPACE
     qw = L.tp_attn_qkv_bwd_out_wgrad_shard             # (s, X, Wqkv, dQKV, dY, O, dWqkv, dX, dWo)
     assert qw(r, P(0), P(1), P(2), P(3), P(4), P(5), P(6), None, None) == INVALID   # no dWo
     assert qw(r, P(0), P(1), P(2), P(3), P(4), P(5), P(6), P(5), None) == INVALID   # dWo on dWqkv
