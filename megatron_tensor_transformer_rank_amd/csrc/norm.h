@@ -10,7 +10,10 @@ namespace tpmlp {
 
 constexpr int64_t LN_MAX_COLS = 16384;  // 256 threads x 8 chunks of 8 columns
 constexpr int LN_MAX_SLABS = 64;        // row slabs of the backward's column sums (few rows)
-constexpr int LN_SLAB_BLOCKS = 512;     // row slabs of the one-pass backward (many rows)
+// row slabs of the one-pass backward (many rows): 256-thread blocks up to
+// 4096 columns (four per CU), 512-thread blocks over 4096 (one per CU)
+constexpr int LN_SLAB_BLOCKS_NARROW = 1024;
+constexpr int LN_SLAB_BLOCKS_WIDE = 256;
 constexpr int LN_MIN_SLAB_ROWS = 8;     // rows per slab, at least
 
 // y = LayerNorm(x) row by row (gamma, beta bf16 [cols]; beta may be NULL);

@@ -20,9 +20,9 @@
 // reduce-scatter followed by a LayerNorm of z computes.
 //
 // The backward, for many rows (4096 and more), is one pass over row slabs:
-// a block per slab forms dx row by row and keeps its columns' dgamma / dbeta
-// sums in registers, then a kernel adds the slabs' partial rows in slab
-// order.  For fewer rows it runs as column tiles, dgamma and dbeta over
+// a block per slab (every S-th row, so that the grid sweeps the tensors in
+// row order) forms dx row by row and keeps its columns' dgamma / dbeta sums
+// in registers, then a kernel adds the slabs' partial rows in slab order.  For fewer rows it runs as column tiles, dgamma and dbeta over
 // (512-column strip, row slab) tiles with at most 64 slabs of partial rows,
 // beside the row kernel (dx, one row per block, like the forward) in the same
 // launch, then the slab sums; when dx overwrites dy in place the column
@@ -276,25 +276,24 @@ ln_bwd_dx_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const fl
   ln_dx_row<NT, J>(blockIdx.x, x, gamma, mean, rstd, dy, dres, dx, cols8, cols, red);
 }
 
-// The backward in one pass over a slab of rows (many rows): block b takes
-// rows [b*rpb, min(rows, (b+1)*rpb)) one after another, LN_THREADS threads,
-// thread i holding chunks i, i + LN_THREADS, ... of a row.  Per row it forms
-// dx as ln_bwd_dx_kernel does (the same arithmetic in the same order, so the
-// same bits) and adds the row's dy * xhat and dy to its columns' dgamma /
+// The backward in one pass (many rows): block b of S takes the rows b,
+// b + S, b + 2S, ... one after another, so that at any moment the grid's
+// blocks read neighbouring rows and sweep each tensor front to back.  NT
+// threads per row (256 up to 4096 columns, 512 over that), thread i holding
+// chunks i, i + NT, ... of a row.  Per row it forms dx with the arithmetic of
+// ln_dx_row and adds the row's dy * xhat and dy to its columns' dgamma /
 // dbeta sums in registers, in row order; the next row's loads are issued
-// before this row's sums.  At the end the block writes its slab's partial
-// dgamma / dbeta rows, which slab_sum_kernel adds in slab order.  dx may
-// coincide with dy or dres: a row is read whole before it is written.
-template <int J>
-__global__ void __launch_bounds__(LN_THREADS)
+// before this row's sums.  At the end the block writes its partial dgamma /
+// dbeta rows, which slab_sum_kernel adds in block order.  dx may coincide
+// with dy or dres: a row is read whole before it is written.
+template <int NT, int J>
+__global__ void __launch_bounds__(NT)
 ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
                    const float* __restrict__ rstd, const uint16_t* dy, const uint16_t* dres, uint16_t* dx,
-                   int64_t rows, int64_t rpb, int cols8, int cols, float* __restrict__ part_g,
-                   float* __restrict__ part_b) {
-  __shared__ float red[2][2][LN_WAVES];
+                   int64_t rows, int cols8, int cols, float* __restrict__ part_g, float* __restrict__ part_b) {
+  __shared__ float red[2][2][NT / 64];
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * rpb;
-  const int64_t r1 = r0 + rpb < rows ? r0 + rpb : rows;
+  const int64_t step = gridDim.x;
   float ag[J][8], ab[J][8];
 #pragma unroll
   for (int j = 0; j < J; ++j)
@@ -305,22 +304,23 @@ ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const 
     const int64_t base = r * cols8;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int q = tid + j * LN_THREADS;
-      const bool ok = r < r1 && q < cols8;
+      const int q = tid + j * NT;
+      const bool ok = r < rows && q < cols8;
       xa[j] = ok ? ld_nt(x, base + q) : u32x4{0u, 0u, 0u, 0u};
       da[j] = ok ? ld_nt(dy, base + q) : u32x4{0u, 0u, 0u, 0u};
       ra[j] = (dres && ok) ? ld_nt(dres, base + q) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  load(r0, xv, dv, rv);
-  for (int64_t r = r0; r < r1; ++r) {
+  load(blockIdx.x, xv, dv, rv);
+  int slot = 0;
+  for (int64_t r = blockIdx.x; r < rows; r += step, slot ^= 1) {
     u32x4 xn[J], dn[J], rn[J];
-    load(r + 1, xn, dn, rn);  // past the slab: no loads, zeros
+    load(r + step, xn, dn, rn);  // past the last row: no loads, zeros
     const float mu = mean[r], rs = rstd[r];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int q = tid + j * LN_THREADS;
+      const int q = tid + j * NT;
       if (q < cols8) {
         float xf[8], df[8], gm[8];
         unpack8(xv[j], xf);
@@ -337,12 +337,12 @@ ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const 
         }
       }
     }
-    block_sum2<LN_WAVES>(s1, s2, red, (int)((r - r0) & 1));
+    block_sum2<NT / 64>(s1, s2, red, slot);
     const float m1 = s1 / (float)cols, m2 = s2 / (float)cols;
     const int64_t base = r * cols8;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int q = tid + j * LN_THREADS;
+      const int q = tid + j * NT;
       if (q < cols8) {
         float xf[8], df[8], gm[8], o[8];
         unpack8(xv[j], xf);
@@ -363,7 +363,7 @@ ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const 
   }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int q = tid + j * LN_THREADS;
+    const int q = tid + j * NT;
     if (q < cols8) {
       float* pg = part_g + (int64_t)blockIdx.x * cols + (int64_t)q * 8;
       reinterpret_cast<float4*>(pg)[0] = make_float4(ag[j][0], ag[j][1], ag[j][2], ag[j][3]);
@@ -559,17 +559,28 @@ int ln_j(int64_t cols, int nt) {
 // every CU busy where a slab per block would leave most of them idle.
 bool bwd_one_pass(int64_t rows) { return rows >= LN_ONE_PASS_ROWS; }
 
+// Threads per row of the one-pass backward: 256 up to 4096 columns (one or
+// two chunks per thread, four blocks per CU), 512 over that (two to four
+// chunks, one block per CU).  Measured on 4096 x 8192, 8192 x 8192,
+// 16384 x 4096 and 4100 x 12288 against 256 threads with up to four chunks
+// and other slab counts.
+int bwd_slab_nt(int64_t cols) { return cols / 8 > 2 * LN_THREADS ? 512 : LN_THREADS; }
+
 // Row slabs of the backward's dgamma / dbeta partial sums, at least
-// LN_MIN_SLAB_ROWS rows each: at most LN_SLAB_BLOCKS for the one-pass
-// kernel (one block per slab), at most LN_MAX_SLABS for the column kernel.
-void bwd_slabs(int64_t rows, int& slabs, int64_t& rpb) {
+// LN_MIN_SLAB_ROWS rows each.  The one-pass kernel: one block per slab, at
+// most LN_SLAB_BLOCKS_NARROW 256-thread or LN_SLAB_BLOCKS_WIDE 512-thread
+// blocks, the slab being every slabs-th row.  The column kernel: at most
+// LN_MAX_SLABS runs of rpb consecutive rows.
+void bwd_slabs(int64_t rows, int64_t cols, int& slabs, int64_t& rpb) {
   int64_t nb = (rows + LN_MIN_SLAB_ROWS - 1) / LN_MIN_SLAB_ROWS;
-  const int64_t cap = bwd_one_pass(rows) ? LN_SLAB_BLOCKS : LN_MAX_SLABS;
+  const int64_t cap = !bwd_one_pass(rows)                   ? LN_MAX_SLABS
+                      : bwd_slab_nt(cols) == LN_THREADS ? LN_SLAB_BLOCKS_NARROW
+                                                        : LN_SLAB_BLOCKS_WIDE;
   if (nb > cap) nb = cap;
   if (nb < 1) nb = 1;
   rpb = (rows + nb - 1) / nb;
   if (rpb < 1) rpb = 1;
-  slabs = (int)((rows + rpb - 1) / rpb);
+  slabs = bwd_one_pass(rows) ? (int)nb : (int)((rows + rpb - 1) / rpb);
 }
 
 template <bool FUSED>
@@ -623,7 +634,7 @@ hipError_t ln_fwd_fused_launch(const PartialPtrs& pp, int t, int64_t rows, int64
 size_t ln_bwd_workspace_bytes(int64_t rows, int64_t cols) {
   int slabs;
   int64_t rpb;
-  bwd_slabs(rows, slabs, rpb);
+  bwd_slabs(rows, cols, slabs, rpb);
   return (size_t)2 * (size_t)slabs * (size_t)cols * sizeof(float);
 }
 
@@ -634,23 +645,26 @@ hipError_t ln_bwd_launch(const uint16_t* x, const uint16_t* gamma, const float* 
   const dim3 blk(LN_THREADS);
   int slabs;
   int64_t rpb;
-  bwd_slabs(rows, slabs, rpb);
+  bwd_slabs(rows, cols, slabs, rpb);
   float* part_g = part;
   float* part_b = dbeta ? part + (int64_t)slabs * cols : nullptr;
   const int cols8 = (int)(cols / 8);
   const dim3 sgrid((unsigned)((cols + 63) / 64), dbeta ? 2u : 1u);
   if (bwd_one_pass(rows)) {
-#define LN_SLAB(J)                                                                                               \
-  hipLaunchKernelGGL((ln_bwd_slab_kernel<J>), dim3((unsigned)slabs), blk, 0, st, x, gamma, mean, rstd, dy, dres, \
-                     dx, rows, rpb, cols8, (int)cols, part_g, part_b)
-    switch (ln_j(cols, LN_THREADS)) {
-      case 1: LN_SLAB(1); break;
-      case 2: LN_SLAB(2); break;
-      case 3: LN_SLAB(3); break;
-      case 4: LN_SLAB(4); break;
-      case 6: LN_SLAB(6); break;
-      case 8: LN_SLAB(8); break;
-      default: return hipErrorInvalidValue;
+#define LN_SLAB(NT, J)                                                                                          \
+  hipLaunchKernelGGL((ln_bwd_slab_kernel<NT, J>), dim3((unsigned)slabs), dim3(NT), 0, st, x, gamma, mean, rstd, dy, \
+                     dres, dx, rows, cols8, (int)cols, part_g, part_b)
+    const int snt = bwd_slab_nt(cols);
+    const int64_t need = (cols8 + snt - 1) / snt;
+    if (snt == 512) {
+      if (need == 2) LN_SLAB(512, 2);
+      else if (need == 3) LN_SLAB(512, 3);
+      else if (need == 4) LN_SLAB(512, 4);
+      else return hipErrorInvalidValue;
+    } else {
+      if (need == 1) LN_SLAB(LN_THREADS, 1);
+      else if (need == 2) LN_SLAB(LN_THREADS, 2);
+      else return hipErrorInvalidValue;
     }
 #undef LN_SLAB
     hipError_t e = hipGetLastError();

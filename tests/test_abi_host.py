@@ -457,15 +457,20 @@ def test_layernorm_fused_rejects_bad_arguments():
 def test_layernorm_bwd_workspace_and_arguments():
     ws = B.layernorm_bwd_workspace_bytes
     # row slabs of at least 8 rows; dgamma and dbeta partials.  Below 4096
-    # rows at most 64 slabs (the column kernel), from 4096 rows at most 512
-    # (one block per slab in the one-pass kernel)
+    # rows at most 64 slabs (the column kernel); from 4096 rows one block per
+    # slab in the one-pass kernel, at most 1024 of 256 threads up to 4096
+    # columns and 256 of 512 threads over that
     assert ws(1, 8) == 2 * 1 * 8 * 4
     assert ws(17, 8) == 2 * 3 * 8 * 4                # 3 slabs of 6 rows
     assert ws(256, 12288) == 2 * 32 * 12288 * 4
     assert ws(1000, 16) == 2 * 63 * 16 * 4           # 64 slabs of 16 rows cover 1000 in 63
     assert ws(4095, 16) == 2 * 64 * 16 * 4
-    assert ws(4096, 8192) == 2 * 512 * 8192 * 4      # 512 slabs of 8 rows
-    assert ws(4100, 16) == 2 * 456 * 16 * 4          # 512 slabs of 9 rows cover 4100 in 456
+    assert ws(4096, 8192) == 2 * 256 * 8192 * 4      # 512 threads per row: 256 slabs of 16 rows
+    assert ws(4100, 16) == 2 * 513 * 16 * 4          # every 513th row: 513 slabs of 7 or 8 rows
+    assert ws(4096, 4096) == 2 * 512 * 4096 * 4      # 256 threads per row, 8 rows per slab
+    assert ws(16384, 4096) == 2 * 1024 * 4096 * 4
+    assert ws(4096, 4104) == 2 * 256 * 4104 * 4
+    assert ws(5000, 16384) == 2 * 256 * 16384 * 4
     assert ws(0, 16) == 0 and ws(4, 12) == 0 and ws(4, 16392) == 0
     f = B.lib().tp_sp_layernorm_bwd
     x, g, m, r, dy, dx, dg, db, w = (FAKE + i * MB for i in range(9))

@@ -91,9 +91,10 @@ SHAPES = [(901, 1, 8), (902, 3, 24), (903, 17, 264), (904, 64, 1032), (905, 5, 2
           (913, 260, 520),
           # 1024 rows and more: 256 threads per row (fewer rows use 1024)
           (914, 1030, 2056), (915, 1024, 12296),
-          # 4096 rows and more: the one-pass backward over row slabs (a ragged
-          # last slab; one and several chunks per thread)
-          (916, 4100, 264), (917, 5003, 2056), (918, 4096, 8200)]
+          # 4096 rows and more: the one-pass backward over row slabs (slabs of
+          # unequal row counts; 256 threads per row with one and two chunks
+          # each, 512 threads over 4096 columns with two to four)
+          (916, 4100, 264), (917, 5003, 2056), (921, 4097, 4104), (918, 4096, 8200), (919, 4099, 12296)]
 
 
 @pytest.mark.parametrize("case", SHAPES, ids=[f"r{c[1]}_c{c[2]}" for c in SHAPES])
