@@ -311,6 +311,14 @@ ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const 
       ra[j] = (dres && ok) ? ld_nt(dres, base + q) : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  // the thread's gamma chunks stay in registers: reloaded per row, their
+  // latency (behind the streaming traffic) sat on every row's path
+  u32x4 gp[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int q = tid + j * NT;
+    gp[j] = q < cols8 ? ld_c(gamma, q) : u32x4{0u, 0u, 0u, 0u};
+  }
   load(blockIdx.x, xv, dv, rv);
   int slot = 0;
   for (int64_t r = blockIdx.x; r < rows; r += step, slot ^= 1) {
@@ -325,7 +333,7 @@ ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const 
         float xf[8], df[8], gm[8];
         unpack8(xv[j], xf);
         unpack8(dv[j], df);
-        unpack8(ld_c(gamma, q), gm);
+        unpack8(gp[j], gm);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float xh = (xf[e] - mu) * rs;
@@ -347,7 +355,7 @@ ln_bwd_slab_kernel(const uint16_t* x, const uint16_t* __restrict__ gamma, const 
         float xf[8], df[8], gm[8], o[8];
         unpack8(xv[j], xf);
         unpack8(dv[j], df);
-        unpack8(ld_c(gamma, q), gm);
+        unpack8(gp[j], gm);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = rs * (df[e] * gm[e] - m1 - (xf[e] - mu) * rs * m2);
         if (dres) add8(o, rv[j]);
