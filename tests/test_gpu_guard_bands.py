@@ -97,6 +97,27 @@ def test_layernorm_guard_bands():
     twice(lambda: B.tp_sp_sum_grads_local(grads, total), gs)
 
 
+@pytest.mark.parametrize("rows,cols", [(4097, 2056), (4100, 4104), (4099, 12296)])
+def test_layernorm_one_pass_backward_guard_bands(rows, cols):
+    """The one-pass backward over row slabs (4096 rows and more): 256 threads
+    per row with a ragged last chunk, and 512 threads with two and four
+    chunks per thread, the last partly past the row; the slabs hold unequal
+    row counts.  The workspace is guarded too."""
+    print(f"[guard] layernorm one pass rows={rows} cols={cols}", file=sys.stderr, flush=True)
+    x = bf16_dev(I.gen_x(604, rows, cols))
+    gm = bf16_dev(I.gen_ln_weight(604, cols))
+    dy, dres = bf16_dev(I.gen_dy(604, rows, cols)), bf16_dev(I.normal_bf16([604, 3], (rows, cols)))
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    B.tp_sp_layernorm_fwd(x, gm, torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda"), mean=mean, rstd=rstd)
+    g = Guards()
+    dx = g.out("dx", (rows, cols))
+    dg, db = g.out("dgamma", (cols,), torch.float32), g.out("dbeta", (cols,), torch.float32)
+    wsb = B.layernorm_bwd_workspace_bytes(rows, cols)
+    ws = g.out("workspace", (wsb // 4,), torch.float32)
+    twice(lambda: B.tp_sp_layernorm_bwd(x, gm, mean, rstd, dy, dx, dg, dbeta=db, dres=dres, workspace=ws), g)
+
+
 @pytest.mark.parametrize("N", [1, 17, 128])
 def test_small_batch_backward_guard_bands(N):
     print(f"[guard] backward N={N}", file=sys.stderr, flush=True)

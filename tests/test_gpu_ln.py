@@ -395,12 +395,11 @@ def test_layernorm_deterministic_and_workspace_contents_irrelevant(rows):
 
 
 @pytest.mark.parametrize("alias", ["dy", "dres"])
-@pytest.mark.parametrize("rows", [40, 4104])
-def test_layernorm_backward_in_place(alias, rows):
+@pytest.mark.parametrize("rows,cols", [(40, 1544), (4104, 1544), (4100, 8200)])
+def test_layernorm_backward_in_place(alias, rows, cols):
     """dx may be the dy or the dres buffer itself: the result (dx, dgamma,
     dbeta) is bitwise the out-of-place one, for the few-row form and the
-    one-pass form over row slabs."""
-    cols = 1544
+    one-pass form over row slabs (256 and 512 threads per row)."""
     xb, dyb, drb = I.gen_x(985, rows, cols), I.gen_dy(985, rows, cols), I.normal_bf16([985, 3], (rows, cols))
     gb = I.gen_ln_weight(985, cols)
     bf = dict(dtype=torch.bfloat16, device="cuda")
