@@ -16,11 +16,14 @@ struct SkinnyPlan {
   int strips;     // 256-column strips of one weight matrix
   int ks, kt;     // k-splits, 64-deep k-tiles per split
   size_t part_floats;
+  int rtiles;     // row tiles of `rows` rows each (the grid's second dimension)
 };
 
 // Split-K plan for X [N, K] @ W [K, ncols] over nmat matrices side by side,
 // aiming at target_blocks blocks with at most max_ks k-splits (and at most
-// K / (2N), which keeps the float32 partials within the weight's bytes).
+// K / (2N), which keeps the float32 partials within the weight's bytes);
+// when that leaves the grid at half the target or less, the rows are split
+// into tiles as well.  The partials' layout does not depend on the tiles.
 SkinnyPlan skinny_plan(int N, int K, int ncols, int nmat, int target_blocks, int max_ks);
 
 // Small-batch forward of one rank's shard: A = act(X @ [Wa, Wb]) (SwiGLU: Wa

@@ -31,7 +31,9 @@
 //
 // skinny_partial: 4 waves (8 at 128 rows: two groups of 4, each owning 64 of
 // the rows); the block's tile is MB token rows (N padded to 16, 32, 64 or
-// 128) x 256 columns, each wave owning 64 columns.  Four LDS stages (three at 128 rows), each [64 k][256] of the
+// 128; or, when the weights are too small to give every CU a block, tiles of
+// 32 or 64 of the rows, the grid's second dimension) x 256 columns, each
+// wave owning 64 columns.  Four LDS stages (three at 128 rows), each [64 k][256] of the
 // weight (n-contiguous, read with the LDS transpose read; with NT [256][64 k],
 // k-contiguous like the activations and read with ds_read_b128) and
 // [MB][64 k] of the activations; the DMA of tile t+3 (t+2) is issued as tile
@@ -103,12 +105,14 @@ skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_by
   // pair whose activations sit side by side in one buffer reads from column
   // x1_off.
   const int kc = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+  const int row0 = blockIdx.y * MB;  // the block's row tile
   const uint32_t xcol = (uint32_t)((mat == 1 ? x1_off : 0) * 2);
   uint32_t xoff[NIX];
 #pragma unroll
   for (int j = 0; j < NIX; ++j) {
     const int row = (w + 4 * j) * 8 + (lane >> 3);
-    xoff[j] = (row < N && row < MB) ? (uint32_t)((int64_t)row * ldx * 2) + xcol + (uint32_t)kc * 2u : OOB;
+    xoff[j] = (row0 + row < N && row < MB) ? (uint32_t)((int64_t)(row0 + row) * ldx * 2) + xcol + (uint32_t)kc * 2u
+                                           : OOB;
   }
   auto shifted = [](const uint16_t* p, uint32_t bytes, uint32_t skip) __attribute__((always_inline)) {
     const uint64_t a = reinterpret_cast<uint64_t>(p) + skip;
@@ -203,12 +207,12 @@ skinny_partial(const uint16_t* __restrict__ X, int N, int64_t ldx, uint32_t x_by
   asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // last MFMA results written before they are read
   wait_vmcnt<0>();  // no DMA may land after the block has left
 
-  // lane holds rows n = grp * 16 TM + 16i + l16, columns col0 + 64w + 16j + 4lq .. +3
+  // lane holds rows n = row0 + grp * 16 TM + 16i + l16, columns col0 + 64w + 16j + 4lq .. +3
   const int l16 = lane & 15, lq = lane >> 4;
   float* dst = part + (int64_t)(q * NMAT + mat) * N * ncols;
 #pragma unroll
   for (int ii = 0; ii < TM; ++ii) {
-    const int n = (grp * TM + ii) * 16 + l16;
+    const int n = row0 + (grp * TM + ii) * 16 + l16;
     if (n >= N) continue;
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) {
@@ -323,6 +327,24 @@ SkinnyPlan skinny_plan(int N, int K, int ncols, int nmat, int target_blocks, int
   p.kt = (nkt + ks - 1) / ks;
   p.ks = (nkt + p.kt - 1) / p.kt;  // every split non-empty
   p.part_floats = (size_t)p.ks * nmat * N * ncols;
+  // A grid well below the target (small weights: few strips, few splits
+  // under the caps) takes the rows in tiles of 32 (else 64), as many tiles as
+  // fit the target.  Each row tile reads the whole weight tile again, which
+  // at these sizes the caches hold.  Measured on the 128-token training
+  // shard (h = 1024, F_i = 2048): step 65.5 -> 50.5 us from a graph (32 of
+  // 256 blocks per product before).
+  p.rtiles = 1;
+  const int blocks = p.strips * nmat * p.ks;
+  const int rt_max = target_blocks / blocks;
+  if (rt_max >= 2 && N > 32) {
+    if ((N + 31) / 32 <= rt_max) {
+      p.rows = 32;
+      p.rtiles = (N + 31) / 32;
+    } else if (N > 64 && (N + 63) / 64 <= rt_max) {
+      p.rows = 64;
+      p.rtiles = (N + 63) / 64;
+    }
+  }
   return p;
 }
 
@@ -343,7 +365,7 @@ hipError_t partial_launch(const SkinnyPlan& p, int N, const uint16_t* X, int64_t
                           const uint16_t* W0, const uint16_t* W1, int K, int ncols, float* part, hipStream_t st) {
   const uint32_t x_bytes = (uint32_t)((int64_t)N * ldx * 2);
   const uint32_t w_bytes = (uint32_t)((int64_t)K * ncols * 2);
-  const dim3 grid(p.strips * NMAT * p.ks);
+  const dim3 grid(p.strips * NMAT * p.ks, p.rtiles);
   if (p.rows == 16)
     partial_one<NMAT, NT, 16>(p, grid, N, X, ldx, x_bytes, x1_off, W0, W1, w_bytes, K, ncols, part, st);
   else if (p.rows == 32)
