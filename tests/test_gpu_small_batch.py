@@ -12,9 +12,10 @@ dX) keeps the wide tiles.  Checked:
 * whole tensor-parallel groups (forward on this path, backward on the GEMMs,
   the partials reduced) at token counts on both sides of every row-tile
   boundary (16, 32, 64) and at the path's edges (2 and 128; 129 goes to the
-  GEMMs),
-  with ragged h and F_i (k-split and column-strip tails), all activations,
-  with and without the stash;
+  GEMMs), with ragged h and F_i (k-split and column-strip tails), all
+  activations, with and without the stash.  Small weights split the rows
+  into two to four 32-row tiles; larger ones keep one 64- or 128-row tile,
+  or take two 64-row tiles;
 * the Llama-3-70B-shaped decode shard at full size (h = 8192, F_i = 7168,
   SwiGLU) for batches of 2, 8, 32, 64 and 128 tokens: A_i, the stashes and Y_i of
   rank 0 against the oracle;
@@ -58,14 +59,21 @@ GROUPS = [
     (305, 32, 1024, 4096, 2, "gelu", True),
     (306, 33, 136, 512, 1, "relu", False),
     (307, 64, 392, 2 * 520, 2, "swiglu", True),
-    (308, 65, 392, 2 * 520, 2, "swiglu", True),    # first count on the 128-row tile
-    (330, 96, 4104, 2 * 776, 2, "gelu", False),    # 128-row tile: k tail and an 8-wide strip
+    (308, 65, 392, 2 * 520, 2, "swiglu", True),    # first count past 64 rows: three 32-row tiles
+    (330, 96, 4104, 2 * 776, 2, "gelu", False),    # k tail and an 8-wide strip
     (331, 127, 264, 3 * 392, 3, "relu", True),
     (332, 128, 1032, 2 * 1040, 2, "swiglu", False),
     (333, 129, 392, 2 * 520, 2, "swiglu", True),   # just past the path: wide-tile GEMMs
     (334, 96, 64, 2 * 80, 2, "swiglu", False),     # h < N and F_i < 2N: the backward keeps the wide tiles
     (335, 40, 520, 2 * 56, 2, "gelu", True),       # F_i = 56: one k-split fits dX's partials
     (336, 1, 2056, 2 * 1544, 2, "relu", False),    # one token: split-K backward
+    # Smaller weights than these split the rows into 32-row tiles; these keep
+    # the 64- and 128-row tiles: one 64-row tile; 128-row tiles for the gate/up
+    # product and dX with two 64-row tiles for the down product and dU (k
+    # tail, 8-wide last strip)
+    (337, 48, 4104, 2 * 4104, 2, "gelu", False),
+    (338, 100, 2056, 2 * 2056, 2, "swiglu", True),
+    (339, 72, 3080, 2 * 1544, 2, "swiglu", False),
 ]
 
 
