@@ -102,6 +102,23 @@ def test_layernorm_matches_oracle(case):
     run_ln(*case)
 
 
+def _one_pass_sweep(seed=20261206, n=8, wid0=1450):
+    """Seeded one-pass backward shapes (4096 rows and more): any width that is
+    a multiple of 8 up to 16384, with and without the residual gradient."""
+    rng = np.random.default_rng(seed)
+    return [(wid0 + i, int(rng.integers(4096, 4400)), 8 * int(rng.integers(1, 2049)), bool(rng.integers(0, 2)))
+            for i in range(n)]
+
+
+SWEEP = _one_pass_sweep()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"r{c[1]}_c{c[2]}{'_dres' if c[3] else ''}" for c in SWEEP])
+def test_layernorm_one_pass_sweep(case):
+    wid, rows, cols, dres = case
+    run_ln(wid, rows, cols, with_dres=dres)
+
+
 @pytest.mark.parametrize("with_beta,stash,with_dres,with_dbeta", [(False, True, True, False), (True, False, False, True),
                                                                   (False, True, False, True)])
 def test_layernorm_options(with_beta, stash, with_dres, with_dbeta):
