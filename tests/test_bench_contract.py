@@ -23,9 +23,10 @@ def test_more_than_one_gpu_is_refused(n):
 def test_counter_summaries_parse():
     sys.path.insert(0, ROOT)
     import bench
-    # the GEMM summary covers every launch of the timed step (bench.py's kernel names); the
-    # decode summary the whole one-token call
-    cases = [("gemm_hbm_traffic_gpt3_train_t8.md", bench.GEMM_SOURCES, k)
+    # each GEMM summary covers every launch of its workload's timed step (bench.py's kernel
+    # names; bench.py --workload picks the workload); the decode summary the whole one-token call
+    cases = [(f"gemm_hbm_traffic_{w}.md", bench.GEMM_SOURCES, k)
+             for w in ("gpt3_train_t8", "llama_7b_train_t2", "llama3_70b_prefill_t4")
              for k in ("up_act", "down", "reduce_y", "down_bwd", "up_bwd", "reduce_dx")]
     cases.append(("gemv_hbm_traffic_llama3_70b_decode_t4.md", bench.GEMV_SOURCES, "decode"))
     for summary, files, kernel in cases:
